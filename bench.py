@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hymba hybrid-head layer forward on one MI355X.
+
+Workload (value): prefill of one bf16 layer, batch 8 x 2048 tokens plus 128 meta
+tokens, d_model 2048, 16 q heads x 128 with 4 kv heads, full causal attention, SSM
+inner dim 4096 with state 16.  A step is one whole pass of the layer (in_proj,
+attention, x_proj, dt_proj, selective scan, norm + fusion, out_proj) over the batch;
+inputs and weights are resident in HBM.  tokens/s counts the 8 x 2048 real tokens.
+
+Also reported: decode of the same layer shape with a 1024-key sliding window,
+batch 128, ring cache of 1024 slots plus 128 meta entries, 256 consecutive steps
+timed as one span (tokens/s = 128 * 256 / span); the per-stage HIP-event timings; the
+roofline of the dominant kernel; and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-layer prefill tokens/s + decode tokens/s on 1 MI355X; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_VALU_TFLOPS = 157.3       # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="X tokens of the oracle's CPU sample (one sequence)")
+    return ap.parse_args()
+
+
+def stage_work(dims, B, L):
+    """Algorithmic work per prefill launch of each stage (flops or bytes)."""
+    M, d, Di, N, R = dims.n_meta, dims.d_model, dims.d_inner, dims.d_state, dims.dt_rank
+    rows = M + B * L
+    qw = dims.q_width
+    W = dims.window
+    pairs_seq = sum(min(i + 1, W) if W > 0 else i + 1 for i in range(L)) + L * M
+    pairs_meta = M * (M + 1) // 2
+    attn_flops = 4 * dims.head_dim * dims.n_q_heads * (B * pairs_seq + pairs_meta)
+    return {
+        "in_proj": ("mfma", 2.0 * rows * dims.n_in * d),
+        "attn": ("mfma", float(attn_flops)),
+        "x_proj": ("mfma", 2.0 * rows * dims.n_xproj * Di),
+        "dt_proj": ("mfma", 2.0 * rows * Di * R),
+        # bytes: x, G (bf16), dt (fp32), y (bf16) per (row, channel); B, C per row; h once
+        "scan": ("hbm", float(rows * (Di * 10 + 8 * N) + B * Di * N * 4)),
+        # bytes: read O and Y_ssm, write F (bf16)
+        "norm": ("hbm", float(rows * (qw + Di) * 2 * 2)),
+        "out_proj": ("mfma", 2.0 * rows * dims.f_width * d),
+    }
+
+
+def roofline_entry(bound, work, avg_ms):
+    if bound == "mfma":
+        achieved = work / (avg_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    achieved = work / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4)}
+
+
+def traffic_for(kernel_stage):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/traffic.json), only
+    while the kernel source it was taken on is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_stage)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "hybrid_attention_ssm_proj_amd", "csrc", rec["source"])
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec["bytes_per_launch"] if h == rec["source_sha"] else None
+
+
+def cpu_baseline(tokens):
+    """The oracle (fp64 numpy) on one sequence of the prefill workload, `tokens` X tokens
+    plus the 128 meta tokens."""
+    import numpy as np
+    import oracle as orc
+    from synth import CASES, gen_layer_weights, gen_activations
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    case = CASES[1]
+    dims = case.dims
+    w = gen_layer_weights(dims, case.case_id)
+    _, meta, _, x = gen_activations(dims, case.case_id, 1, tokens)
+    t0 = time.perf_counter()
+    orc.prefill(dims, w, meta, x)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one sequence of the prefill workload: {tokens} tokens + "
+                      f"{dims.n_meta} meta tokens (fp64 numpy), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this layer is built and measured on a single "
+              f"MI355X; requested --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hybrid_attention_ssm_proj_amd as hy
+    from synth import CASES, gen_layer_weights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    case = CASES[1]
+    dims = case.dims
+    B, L = case.batch, case.seq_len
+    log(f"[bench] prefill workload {case.name}: B={B} L={L} M={dims.n_meta}")
+    w = gen_layer_weights(dims, case.case_id)
+    layer = hy.HymbaLayer(dims, w.torch, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1001)
+    meta = torch.randn(dims.n_meta, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    x = torch.randn(B, L, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    y = torch.empty(B, L, dims.d_model, dtype=torch.bfloat16, device=dev)
+    y_meta = torch.empty(dims.n_meta, dims.d_model, dtype=torch.bfloat16, device=dev)
+    h = torch.empty(B, dims.d_inner, dims.d_state, dtype=torch.float32, device=dev)
+    pos = torch.empty(B, dtype=torch.int32, device=dev)
+    state = hy.make_state(h, pos)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.prefill(meta, x, state_out=state, y=y, y_meta=y_meta, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hy.hymba_timer_enable(True)
+    for i in range(len(hy.STAGES)):
+        hy.hymba_timer_read(i)  # forget warm-up launches
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    hy.hymba_timer_enable(False)
+    stages = {}
+    for i, name in enumerate(hy.STAGES):
+        ms, n = hy.hymba_timer_read(i)
+        if n:
+            stages[name] = {"avg_ms": ms / n, "launches": n}
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = B * L
+    value = tokens / (elapsed / args.steps)
+    log(f"[bench] prefill {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s")
+
+    work = stage_work(dims, B, L)
+    stage_report = {}
+    for name, rec in stages.items():
+        if name in work:
+            bound, wk = work[name]
+            stage_report[name] = {"avg_ms": round(rec["avg_ms"], 4),
+                                  **roofline_entry(bound, wk, rec["avg_ms"])}
+        else:
+            stage_report[name] = {"avg_ms": round(rec["avg_ms"], 4)}
+    dominant = max((n for n in stage_report if n in work), key=lambda n: stage_report[n]["avg_ms"])
+    bound, wk = work[dominant]
+    roof = roofline_entry(bound, wk, stages[dominant]["avg_ms"])
+    roof["kernel"] = dominant
+    roof["traffic"] = traffic_for(dominant)
+    log(f"[bench] stages: " + ", ".join(f"{k} {v['avg_ms']:.3f} ms" for k, v in stage_report.items()))
+
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(hy, torch, dev, args)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle sample")
+        cpu = cpu_baseline(args.cpu_tokens)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hymba hybrid-head layer prefill, bf16, B=8, L=2048, 128 meta "
+                               "tokens, d=2048, 16x128 q / 4 kv heads, full causal, Di=4096, N=16",
+                   "global_batch": B, "seq_len": L, "n_meta": dims.n_meta},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "stages": stage_report,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(hy, torch, dev, args):
+    from synth import CASES, gen_layer_weights
+    case = CASES[4]
+    dims = case.dims
+    B, S, prior = case.batch, case.ring_slots, case.prior_tokens
+    log(f"[bench] decode workload {case.name}: B={B} ring={S} prior={prior}")
+    w = gen_layer_weights(dims, case.case_id)
+    layer = hy.HymbaLayer(dims, w.torch, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1004)
+    Hkv, M, dh = dims.n_kv_heads, dims.n_meta, dims.head_dim
+    kv = {n: torch.zeros(shape, dtype=torch.bfloat16, device=dev) for n, shape in (
+        ("k_meta", (Hkv, M, dh)), ("v_meta", (Hkv, M, dh)), ("k", (B, Hkv, S, dh)),
+        ("v", (B, Hkv, S, dh)))}
+    h = torch.zeros(B, dims.d_inner, dims.d_state, dtype=torch.float32, device=dev)
+    pos = torch.zeros(B, dtype=torch.int32, device=dev)
+    kvs = hy.make_kv(kv["k_meta"], kv["v_meta"], kv["k"], kv["v"])
+    sts = hy.make_state(h, pos)
+    # state: the library's own prefill over `prior` N(0,1) tokens per sequence, in
+    # batch slices (fills the ring with the last 1024 positions and h, pos = prior).
+    meta = torch.randn(M, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    slice_b = 16
+    for b0 in range(0, B, slice_b):
+        xs = torch.randn(slice_b, prior, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+        sub_kv = hy.make_kv(kv["k_meta"], kv["v_meta"], kv["k"][b0:b0 + slice_b],
+                            kv["v"][b0:b0 + slice_b])
+        sub_st = hy.make_state(h[b0:b0 + slice_b], pos[b0:b0 + slice_b])
+        layer.prefill(meta, xs, kv_out=sub_kv, state_out=sub_st)
+        del xs
+    torch.cuda.synchronize()
+    layer._ws = None
+    torch.cuda.empty_cache()
+    steps = args.decode_steps
+    xin = torch.randn(steps + 4, B, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    yout = torch.empty(B, dims.d_model, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for s in range(4):  # warm-up steps advance the state like any other step
+        layer.decode(xin[steps + s], kvs, sts, y=yout, stream=stream)
+    torch.cuda.synchronize()
+    hy.hymba_timer_enable(True)
+    for i in range(len(hy.STAGES)):
+        hy.hymba_timer_read(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        layer.decode(xin[s], kvs, sts, y=yout, stream=stream)
+    torch.cuda.synchronize()
+    span = time.perf_counter() - t0
+    hy.hymba_timer_enable(False)
+    st = {}
+    total_kernel_ms = 0.0
+    for i, name in enumerate(hy.STAGES):
+        ms, n = hy.hymba_timer_read(i)
+        if n:
+            st[name] = round(ms / n * 1e3, 2)  # us per step
+            total_kernel_ms += ms
+    # algorithmic bytes per step: weights, ring K/V read, meta K/V, state read + write
+    wbytes = 2 * (dims.n_in * dims.d_model + dims.n_xproj * dims.d_inner +
+                  dims.d_inner * dims.dt_rank + dims.d_model * dims.f_width)
+    ring_bytes = B * dims.n_kv_heads * min(S, dims.window) * dims.head_dim * 2 * 2
+    meta_bytes = dims.n_kv_heads * M * dh * 2 * 2
+    h_bytes = B * dims.d_inner * dims.d_state * 4 * 2
+    step_bytes = wbytes + ring_bytes + meta_bytes + h_bytes
+    us = span / steps * 1e6
+    tps = B * steps / span
+    log(f"[bench] decode {us:.1f} us/step, {tps / 1e6:.3f} M tokens/s")
+    return {"value": round(tps, 1), "unit": "tokens/s", "us_per_step": round(us, 2),
+            "steps": steps, "batch": B,
+            "workload": "decode, bf16, B=128, 1 token per sequence after 4096 prior tokens, "
+                        "window 1024 ring + 128 meta entries, same layer shape",
+            "hbm_bytes_per_step": step_bytes,
+            "hbm_frac_of_peak": round(step_bytes / (span / steps) / 1e9 / PEAK_HBM_GBS, 4),
+            "stage_us": st}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+"""Python binding of libhymba, the gfx950 Hymba hybrid-head layer library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libhymba.so; torch is used for device memory and streams.  The functions named
+hymba_* mirror the C ABI in include/hymba.h one to one.  Importing this module does
+not touch the GPU; the first call loads the library and raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "HymbaError", "LayerDesc", "LayerWeights", "KV", "SSMState", "load_library",
+    "hymba_layer_prefill", "hymba_layer_decode", "hymba_layer_workspace_bytes",
+    "hymba_status_str", "hymba_abi_version", "hymba_last_hip_error", "hymba_timer_enable",
+    "hymba_timer_read", "hymba_op_gemm", "hymba_op_copy", "HymbaLayer", "STAGES",
+    "DTYPE_F32", "DTYPE_BF16", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhymba.so")
+DTYPE_F32, DTYPE_BF16 = 0, 1
+STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE",
+          4: "ERR_ALIGNMENT", 5: "ERR_HIP"}
+STAGES = ["in_proj", "attn", "x_proj", "dt_proj", "scan", "norm", "out_proj", "kv_write"]
+
+
+class HymbaError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if hip_error:
+            msg += f" (hipError {hip_error})"
+        super().__init__(msg)
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "d_model", "n_q_heads", "n_kv_heads", "head_dim", "d_inner", "d_state", "dt_rank",
+        "n_meta", "window", "kv_share", "dtype")] + [
+        ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+
+    @classmethod
+    def from_dims(cls, dims) -> "LayerDesc":
+        return cls(dims.d_model, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.d_inner,
+                   dims.d_state, dims.dt_rank, dims.n_meta, dims.window, dims.kv_share,
+                   DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, dims.rms_eps,
+                   dims.softmax_scale)
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_in", "w_x", "w_dt", "w_out", "dt_bias", "A", "D", "beta_attn", "beta_ssm")]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k_meta", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slots", ctypes.c_int32)]
+
+
+class SSMState(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libhymba.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libhymba.so not built at {LIB_PATH}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int64
+    sig = {
+        "hymba_layer_prefill": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P,
+                                      P, I32, I32, ctypes.POINTER(KV), ctypes.POINTER(KV),
+                                      ctypes.POINTER(SSMState), P, P, P, SZ, P]),
+        "hymba_layer_decode": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P,
+                                     I32, ctypes.POINTER(KV), ctypes.POINTER(SSMState), P, P, SZ,
+                                     P]),
+        "hymba_layer_workspace_bytes": (SZ, [ctypes.POINTER(LayerDesc), I32, I32, I32]),
+        "hymba_status_str": (ctypes.c_char_p, [I32]),
+        "hymba_abi_version": (I32, []),
+        "hymba_last_hip_error": (I32, []),
+        "hymba_timer_enable": (I32, [I32]),
+        "hymba_timer_read": (I32, [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
+        "hymba_op_gemm": (I32, [I32, P, I64, P, I64, P, I64, I32, I32, I32, I32, P]),
+        "hymba_op_copy": (I32, [P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (None for None); ints pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise HymbaError(status, where, load_library().hymba_last_hip_error())
+
+
+def _ref(obj):
+    return ctypes.byref(obj) if obj is not None else None
+
+
+# ----------------------------------------------------------------- raw ABI mirrors
+
+def hymba_abi_version() -> int:
+    return load_library().hymba_abi_version()
+
+
+def hymba_status_str(status: int) -> str:
+    return load_library().hymba_status_str(status).decode()
+
+
+def hymba_last_hip_error() -> int:
+    return load_library().hymba_last_hip_error()
+
+
+def hymba_layer_workspace_bytes(desc: LayerDesc, batch: int, seq_len: int, mode: int) -> int:
+    return load_library().hymba_layer_workspace_bytes(ctypes.byref(desc), batch, seq_len, mode)
+
+
+def hymba_layer_prefill(desc, weights, meta, x, batch, seq_len, kv_in, kv_out, state_out, y,
+                        y_meta, workspace, workspace_bytes, stream=None, check=True) -> int:
+    st = load_library().hymba_layer_prefill(
+        ctypes.byref(desc), ctypes.byref(weights), _ptr(meta), _ptr(x), batch, seq_len,
+        _ref(kv_in), _ref(kv_out), _ref(state_out), _ptr(y), _ptr(y_meta), _ptr(workspace),
+        workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "hymba_layer_prefill")
+    return st
+
+
+def hymba_layer_decode(desc, weights, x, batch, kv, state, y, workspace, workspace_bytes,
+                       stream=None, check=True) -> int:
+    st = load_library().hymba_layer_decode(
+        ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, _ref(kv), _ref(state), _ptr(y),
+        _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "hymba_layer_decode")
+    return st
+
+
+def hymba_timer_enable(on: bool) -> None:
+    _check(load_library().hymba_timer_enable(1 if on else 0), "hymba_timer_enable")
+
+
+def hymba_timer_read(stage: int):
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check(load_library().hymba_timer_read(stage, ctypes.byref(ms), ctypes.byref(n)),
+           "hymba_timer_read")
+    return ms.value, n.value
+
+
+def hymba_op_gemm(dtype, a, lda, b, ldb, c, ldc, c_dtype, m, n, k, stream=None) -> None:
+    _check(load_library().hymba_op_gemm(dtype, _ptr(a), lda, _ptr(b), ldb, _ptr(c), ldc, c_dtype,
+                                        m, n, k, _stream(stream)), "hymba_op_gemm")
+
+
+def hymba_op_copy(src, dst, nbytes, stream=None) -> None:
+    _check(load_library().hymba_op_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
+           "hymba_op_copy")
+
+
+# ----------------------------------------------------------------- convenience
+
+class HymbaLayer:
+    """One layer's weights on the device plus the descriptor; allocates workspace and
+    outputs with torch and calls the ABI.  `w` maps the weight names of
+    hymba_layer_weights to device tensors."""
+
+    def __init__(self, dims, w: dict, device="cuda"):
+        import torch
+        self.dims = dims
+        self.desc = LayerDesc.from_dims(dims)
+        self.w = {k: v.to(device).contiguous() for k, v in w.items()}
+        self.weights = LayerWeights(*[self.w[n].data_ptr() for n, _ in LayerWeights._fields_])
+        self.device = device
+        self.store = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+        self._ws = None
+
+    def workspace(self, nbytes: int):
+        import torch
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def prefill(self, meta, x, kv_in: Optional[KV] = None, kv_out: Optional[KV] = None,
+                state_out: Optional[SSMState] = None, y=None, y_meta=None, stream=None):
+        import torch
+        B, L = x.shape[0], x.shape[1]
+        d = self.dims.d_model
+        if y is None:
+            y = torch.empty(B, L, d, dtype=self.store, device=self.device)
+        if y_meta is None:
+            y_meta = torch.empty(self.dims.n_meta, d, dtype=self.store, device=self.device)
+        nb = hymba_layer_workspace_bytes(self.desc, B, L, 0)
+        ws = self.workspace(nb)
+        hymba_layer_prefill(self.desc, self.weights, meta, x, B, L, kv_in, kv_out, state_out, y,
+                            y_meta, ws, ws.numel(), stream)
+        return y, y_meta
+
+    def decode(self, x, kv: KV, state: SSMState, y=None, stream=None):
+        import torch
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty(B, self.dims.d_model, dtype=self.store, device=self.device)
+        nb = hymba_layer_workspace_bytes(self.desc, B, kv.slots, 1)
+        ws = self.workspace(nb)
+        hymba_layer_decode(self.desc, self.weights, x, B, kv, state, y, ws, ws.numel(), stream)
+        return y
+
+
+def make_kv(k_meta, v_meta, k, v) -> KV:
+    return KV(_ptr(k_meta), _ptr(v_meta), _ptr(k), _ptr(v), int(k.shape[2]))
+
+
+def make_state(h, pos) -> SSMState:
+    return SSMState(_ptr(h), _ptr(pos))

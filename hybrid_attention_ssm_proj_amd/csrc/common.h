@@ -1,0 +1,56 @@
+// Shared device helpers for the gfx950 kernels of libhymba.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hymba {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(16))) float floatx16;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE (v_cvt_pk_bf16_f32)
+
+// 16-byte vector of raw bits, used for copies and vector loads.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// MFMA D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.  Lane l supplies
+// row (l % 16) of A and column (l % 16) of B, 8 consecutive k each (block l / 16);
+// it receives D rows 4 * (l / 16) + r, r = 0..3, at column (l % 16).
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b,
+                                                const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float softplus_f(float z) {
+  // log(1 + e^z); above 20 the correction e^-z is below fp32 resolution of z.
+  return z > 20.f ? z : log1pf(__expf(z));
+}
+__device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
+
+}  // namespace hymba

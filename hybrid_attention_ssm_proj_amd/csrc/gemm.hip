@@ -1,0 +1,359 @@
+// Projection GEMMs of the hybrid-head layer: in_proj (Z = X~ W_in^T), x_proj
+// ([delta | B | C] = Xs W_x^T), dt_proj (dt = softplus(delta W_dt^T + b)) and
+// out_proj (Y = F W_out^T).  Source: the in_proj / out_proj terms of the design
+// formulation in "Hymba: A Hybrid-head Architecture for Small Language Models"
+// (outta.ai summary); dt, B, C are linear maps of the SSM input (Mamba).
+//
+// bf16 path: LDS double-buffered MFMA (v_mfma_f32_16x16x32_bf16) tiles with fp32
+// accumulation.  Operands are both K-contiguous ([rows, K] and [cols, K]); the MFMA is
+// issued as (B-tile, A-tile) so each lane ends with 4 consecutive output columns of
+// one row, which the epilogue writes with a single vector store.
+// fp32 path: a plain LDS-tiled VALU GEMM with the same epilogues.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace hymba {
+
+// --------------------------------------------------------------------- epilogues
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float v[4], int valid, bool vec_ok);
+
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, const float v[4], int valid, bool vec_ok) {
+  if (valid >= 4 && vec_ok) {
+    bf16x4 o;
+    o[0] = (bf16)v[0];
+    o[1] = (bf16)v[1];
+    o[2] = (bf16)v[2];
+    o[3] = (bf16)v[3];
+    *(bf16x4*)p = o;
+  } else {
+    for (int r = 0; r < valid && r < 4; ++r) p[r] = (bf16)v[r];
+  }
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float v[4], int valid, bool vec_ok) {
+  if (valid >= 4 && vec_ok) {
+    *(floatx4*)p = floatx4{v[0], v[1], v[2], v[3]};
+  } else {
+    for (int r = 0; r < valid && r < 4; ++r) p[r] = v[r];
+  }
+}
+
+// Every epilogue receives the accumulator values of output (m, n..n+3).
+template <typename T, EpiKind K>
+struct Epilogue {
+  GemmOutput o;
+  __device__ __forceinline__ void operator()(int m, int n, const float v[4], int M, int N) const {
+    if (m >= M || n >= N) return;
+    const int valid = N - n;
+    if constexpr (K == EpiKind::Store) {
+      T* base;
+      int64_t ld;
+      int mm;
+      if (m < o.c_split) {
+        base = (T*)o.c0;
+        ld = o.ldc0;
+        mm = m;
+      } else {
+        base = (T*)o.c1;
+        ld = o.ldc1;
+        mm = m - o.c_split;
+      }
+      if (base == nullptr) return;
+      T* p = base + mm * ld + n;
+      store4<T>(p, v, valid, ((uintptr_t)p & (4 * sizeof(T) - 1)) == 0);
+    } else if constexpr (K == EpiKind::StoreF32) {
+      float* p = (float*)o.c0 + m * o.ldc0 + n;
+      store4<float>(p, v, valid, ((uintptr_t)p & 15) == 0);
+    } else if constexpr (K == EpiKind::XProj) {
+      if (n < o.split_col) {  // split_col is a multiple of 4: a group never straddles
+        T* p = (T*)o.c0 + m * o.ldc0 + n;
+        store4<T>(p, v, o.split_col - n, ((uintptr_t)p & (4 * sizeof(T) - 1)) == 0);
+      } else {
+        float* p = (float*)o.c1 + m * o.ldc1 + (n - o.split_col);
+        store4<float>(p, v, valid, ((uintptr_t)p & 15) == 0);
+      }
+    } else {  // Softplus
+      float w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (n + r < N) ? softplus_f(v[r] + o.bias[n + r]) : 0.f;
+      float* p = (float*)o.c0 + m * o.ldc0 + n;
+      store4<float>(p, w, valid, ((uintptr_t)p & 15) == 0);
+    }
+  }
+};
+
+// --------------------------------------------------------------------- tile order
+
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Renumber so every XCD
+// owns a contiguous range of the grouped tile order, keeping the A rows and B
+// columns a range touches in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int pid, int nbm, int nbn, int group_m, int& bm,
+                                            int& bn) {
+  const int nblk = nbm * nbn;
+  const int per = nblk / 8, rem = nblk % 8;
+  const int xcd = pid % 8, idx = pid / 8;
+  const int t = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const int span = group_m * nbn;
+  const int grp = t / span;
+  const int first = grp * group_m;
+  const int gsz = min(nbm - first, group_m);
+  const int in = t - grp * span;
+  bm = first + in % gsz;
+  bn = in / gsz;
+}
+
+// --------------------------------------------------------------------- bf16 MFMA
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct MfmaCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int NT = WM * WN * kWave;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int LDS = BK + 8;  // row pitch in bf16: 16-byte pad spreads rows over banks
+  static constexpr int CPR = BK / 8;  // 16-byte chunks per row
+  static constexpr int A_CH = BM * CPR / NT;
+  static constexpr int B_CH = BN * CPR / NT;
+  static constexpr size_t SMEM = (size_t)2 * (BM + BN) * LDS * sizeof(bf16);
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "loader must tile evenly");
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && BK % 32 == 0, "MFMA tiling");
+};
+
+template <typename Cfg, typename Epi>
+__global__ __launch_bounds__(Cfg::NT) void gemm_bf16_kernel(GemmOperands g, Epi epi) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  bf16* As = (bf16*)smem_raw;
+  bf16* Bs = As + 2 * Cfg::BM * Cfg::LDS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  const int nbm = (g.M + Cfg::BM - 1) / Cfg::BM, nbn = (g.N + Cfg::BN - 1) / Cfg::BN;
+  int bm, bn;
+  tile_coords(blockIdx.x, nbm, nbn, 8, bm, bn);
+  const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
+
+  // Per-thread loader state: fixed rows across the K loop.
+  const bf16* a_src[Cfg::A_CH];
+  int a_dst[Cfg::A_CH], a_kc[Cfg::A_CH];
+#pragma unroll
+  for (int j = 0; j < Cfg::A_CH; ++j) {
+    const int q = tid + j * Cfg::NT, r = q / Cfg::CPR, kc = (q % Cfg::CPR) * 8;
+    const int row = m0 + r;
+    const bf16* base = nullptr;
+    if (row < g.M)
+      base = row < g.a_split ? (const bf16*)g.a0 + (int64_t)row * g.lda0
+                             : (const bf16*)g.a1 + (int64_t)(row - g.a_split) * g.lda1;
+    a_src[j] = base ? base + kc : nullptr;
+    a_dst[j] = r * Cfg::LDS + kc;
+    a_kc[j] = kc;
+  }
+  const bf16* b_src[Cfg::B_CH];
+  int b_dst[Cfg::B_CH], b_kc[Cfg::B_CH];
+#pragma unroll
+  for (int j = 0; j < Cfg::B_CH; ++j) {
+    const int q = tid + j * Cfg::NT, r = q / Cfg::CPR, kc = (q % Cfg::CPR) * 8;
+    const int col = n0 + r;
+    b_src[j] = col < g.N ? (const bf16*)g.b + (int64_t)col * g.ldb + kc : nullptr;
+    b_dst[j] = r * Cfg::LDS + kc;
+    b_kc[j] = kc;
+  }
+
+  u32x4 ra[Cfg::A_CH], rb[Cfg::B_CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < Cfg::A_CH; ++j)
+      ra[j] = (a_src[j] && k0 + a_kc[j] < g.K) ? *(const u32x4*)(a_src[j] + k0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < Cfg::B_CH; ++j)
+      rb[j] = (b_src[j] && k0 + b_kc[j] < g.K) ? *(const u32x4*)(b_src[j] + k0) : u32x4{0, 0, 0, 0};
+  };
+  auto sstore = [&](int buf) {
+    bf16* as = As + buf * Cfg::BM * Cfg::LDS;
+    bf16* bs = Bs + buf * Cfg::BN * Cfg::LDS;
+#pragma unroll
+    for (int j = 0; j < Cfg::A_CH; ++j) *(u32x4*)(as + a_dst[j]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < Cfg::B_CH; ++j) *(u32x4*)(bs + b_dst[j]) = rb[j];
+  };
+
+  floatx4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = (g.K + Cfg::BK - 1) / Cfg::BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  const int frag_row = lane & 15, frag_k = (lane >> 4) * 8;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * Cfg::BK);
+    const bf16* as = As + buf * Cfg::BM * Cfg::LDS + (wm * Cfg::TM + frag_row) * Cfg::LDS + frag_k;
+    const bf16* bs = Bs + buf * Cfg::BN * Cfg::LDS + (wn * Cfg::TN + frag_row) * Cfg::LDS + frag_k;
+#pragma unroll
+    for (int ks = 0; ks < Cfg::BK / 32; ++ks) {
+      bf16x8 af[Cfg::FM], bfr[Cfg::FN];
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i) af[i] = *(const bf16x8*)(as + i * 16 * Cfg::LDS + ks * 32);
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) bfr[j] = *(const bf16x8*)(bs + j * 16 * Cfg::LDS + ks * 32);
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma16x16x32(bfr[j], af[i], acc[i][j]);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // acc[i][j] holds C^T for the (i, j) 16x16 block: lane -> row frag_row, columns
+  // 4 * (lane / 16) + 0..3.
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int m = m0 + wm * Cfg::TM + i * 16 + frag_row;
+      const int n = n0 + wn * Cfg::TN + j * 16 + (lane >> 4) * 4;
+      const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      epi(m, n, v, g.M, g.N);
+    }
+}
+
+template <typename Cfg, typename Epi>
+static hipError_t run_bf16(const GemmOperands& op, const Epi& epi, hipStream_t s) {
+  const int nbm = (op.M + Cfg::BM - 1) / Cfg::BM, nbn = (op.N + Cfg::BN - 1) / Cfg::BN;
+  auto kern = gemm_bf16_kernel<Cfg, Epi>;
+  static bool attr_done = false;  // per instantiation
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  kern<<<dim3(nbm * nbn), dim3(Cfg::NT), Cfg::SMEM, s>>>(op, epi);
+  return hipGetLastError();
+}
+
+// Large: in_proj / out_proj prefill.  Narrow: few output columns (x_proj) or mid
+// sizes.  Skinny: decode (M = batch) where the weight stream dominates.
+using CfgLarge = MfmaCfg<256, 128, 64, 2, 2>;
+using CfgNarrow = MfmaCfg<128, 64, 64, 2, 2>;
+using CfgSkinny = MfmaCfg<64, 64, 64, 2, 2>;
+
+template <typename Epi>
+static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShape shape,
+                                hipStream_t s) {
+  switch (shape) {
+    case GemmShape::Large:
+      if constexpr (std::is_same_v<Epi, Epilogue<bf16, EpiKind::Store>>)
+        return run_bf16<CfgLarge>(op, epi, s);
+      else
+        return run_bf16<CfgNarrow>(op, epi, s);
+    case GemmShape::Narrow:
+      return run_bf16<CfgNarrow>(op, epi, s);
+    default:
+      return run_bf16<CfgSkinny>(op, epi, s);
+  }
+}
+
+hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmShape shape,
+                            hipStream_t s) {
+  if (op.M <= 0 || op.N <= 0) return hipSuccess;
+  // The wide tile is kept for plain stores; epilogues with per-element math use the
+  // narrower tiles (fewer live accumulators, no spills).
+  if (shape == GemmShape::Large && out.kind != EpiKind::Store) shape = GemmShape::Narrow;
+  switch (out.kind) {
+    case EpiKind::Store:
+      return dispatch_bf16(op, Epilogue<bf16, EpiKind::Store>{out}, shape, s);
+    case EpiKind::StoreF32:
+      return dispatch_bf16(op, Epilogue<bf16, EpiKind::StoreF32>{out}, shape, s);
+    case EpiKind::XProj:
+      return dispatch_bf16(op, Epilogue<bf16, EpiKind::XProj>{out}, shape, s);
+    default:
+      return dispatch_bf16(op, Epilogue<bf16, EpiKind::Softplus>{out}, shape, s);
+  }
+}
+
+// --------------------------------------------------------------------- fp32 VALU
+
+// 64 x 64 tile, BK = 16, 256 threads with 4 x 4 outputs each.
+template <typename Epi>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmOperands g, Epi epi) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int nbm = (g.M + 63) / 64, nbn = (g.N + 63) / 64;
+  int bm, bn;
+  tile_coords(blockIdx.x, nbm, nbn, 8, bm, bn);
+  const int m0 = bm * 64, n0 = bn * 64;
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + j * 256, r = q / 16, kk = q % 16;
+      const int row = m0 + r, col = n0 + r, k = k0 + kk;
+      float av = 0.f, bv = 0.f;
+      if (row < g.M && k < g.K) {
+        const float* base = row < g.a_split ? (const float*)g.a0 + (int64_t)row * g.lda0
+                                            : (const float*)g.a1 + (int64_t)(row - g.a_split) * g.lda1;
+        av = base[k];
+      }
+      if (col < g.N && k < g.K) bv = ((const float*)g.b)[(int64_t)col * g.ldb + k];
+      As[kk][r] = av;
+      Bs[kk][r] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kk][ty * 4 + i];
+        b[i] = Bs[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) epi(m0 + ty * 4 + i, n0 + tx * 4, acc[i], g.M, g.N);
+}
+
+template <typename Epi>
+static void run_f32(const GemmOperands& op, const Epi& epi, int nblk, hipStream_t s) {
+  gemm_f32_kernel<Epi><<<dim3(nblk), dim3(256), 0, s>>>(op, epi);
+}
+
+hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStream_t s) {
+  if (op.M <= 0 || op.N <= 0) return hipSuccess;
+  const int nblk = ((op.M + 63) / 64) * ((op.N + 63) / 64);
+  switch (out.kind) {
+    case EpiKind::Store:
+      run_f32(op, Epilogue<float, EpiKind::Store>{out}, nblk, s);
+      break;
+    case EpiKind::StoreF32:
+      run_f32(op, Epilogue<float, EpiKind::StoreF32>{out}, nblk, s);
+      break;
+    case EpiKind::XProj:
+      run_f32(op, Epilogue<float, EpiKind::XProj>{out}, nblk, s);
+      break;
+    default:
+      run_f32(op, Epilogue<float, EpiKind::Softplus>{out}, nblk, s);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hymba

@@ -1,0 +1,549 @@
+// C ABI of libhymba: argument validation, workspace layout and the launch sequence of
+// the Hymba hybrid-head layer (prefill and decode).  The method's steps follow the
+// design formulation of "Hymba: A Hybrid-head Architecture for Small Language Models"
+// (outta.ai summary): meta-prefixed in_proj, attention heads and SSM heads on the same
+// split, normalised + beta-scaled fusion, out_proj.
+#include "../../include/hymba.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace hymba;
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+hymba_status fail_hip(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return HYMBA_ERR_HIP;
+}
+
+// ----------------------------------------------------------------- stage timers
+struct StageTimer {
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+};
+bool g_timer_on = false;
+StageTimer g_timers[HYMBA_NUM_STAGES];
+constexpr int kMaxTimedLaunches = 4096;
+
+struct TimerScope {
+  StageTimer* t = nullptr;
+  hipStream_t s;
+  int idx = -1;
+  TimerScope(int stage, hipStream_t stream) : s(stream) {
+    if (!g_timer_on) return;
+    t = &g_timers[stage];
+    if (t->used >= kMaxTimedLaunches) {
+      t = nullptr;
+      return;
+    }
+    if (t->used == (int)t->start.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) {
+        t = nullptr;
+        return;
+      }
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        t = nullptr;
+        return;
+      }
+      t->start.push_back(a);
+      t->stop.push_back(b);
+    }
+    idx = t->used++;
+    (void)hipEventRecord(t->start[idx], s);
+  }
+  ~TimerScope() {
+    if (t != nullptr && idx >= 0) (void)hipEventRecord(t->stop[idx], s);
+  }
+};
+
+#define HYMBA_LAUNCH(stage, expr)            \
+  do {                                       \
+    TimerScope ts_((stage), stream);         \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return fail_hip(e_); \
+  } while (0)
+
+// ----------------------------------------------------------------- shapes
+struct Shape {
+  int d, Hq, Hkv, dh, Di, N, R, M, W, share, es;
+  bool bf16;
+  int64_t qw, kvw, n_in, fw, xs_col, g_col, k_col, v_col;
+  float scale;
+};
+
+bool is_pow2_in(int v, int lo, int hi) {
+  if (v < lo || v > hi) return false;
+  return (v & (v - 1)) == 0;
+}
+
+hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
+  if (desc == nullptr) return HYMBA_ERR_INVALID_ARG;
+  const hymba_layer_desc& d = *desc;
+  if (d.d_model <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 ||
+      d.d_inner <= 0 || d.d_state <= 0 || d.dt_rank <= 0 || d.n_meta < 0 || d.window < 0)
+    return HYMBA_ERR_INVALID_ARG;
+  if (d.kv_share != 0 && d.kv_share != 1) return HYMBA_ERR_INVALID_ARG;
+  if (d.dtype != HYMBA_DTYPE_F32 && d.dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
+  if (!(d.rms_eps >= 0.f) || !std::isfinite(d.rms_eps)) return HYMBA_ERR_INVALID_ARG;
+  if (!(d.softmax_scale >= 0.f) || !std::isfinite(d.softmax_scale)) return HYMBA_ERR_INVALID_ARG;
+  if (d.n_q_heads % d.n_kv_heads != 0) return HYMBA_ERR_INVALID_ARG;
+  const bool bf16 = d.dtype == HYMBA_DTYPE_BF16;
+  // kernels: 16-byte row chunks, 4-column epilogue groups, <= 16 q heads per kv head
+  if (d.d_model % 8 || d.d_inner % 8 || d.dt_rank % 8 || d.head_dim % 8)
+    return HYMBA_ERR_UNSUPPORTED;
+  if (d.n_q_heads / d.n_kv_heads > 16) return HYMBA_ERR_UNSUPPORTED;
+  if (bf16 ? (d.head_dim != 64 && d.head_dim != 128)
+           : (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128))
+    return HYMBA_ERR_UNSUPPORTED;
+  if (!is_pow2_in(d.d_state, 4, 128)) return HYMBA_ERR_UNSUPPORTED;
+  s.d = d.d_model;
+  s.Hq = d.n_q_heads;
+  s.Hkv = d.n_kv_heads;
+  s.dh = d.head_dim;
+  s.Di = d.d_inner;
+  s.N = d.d_state;
+  s.R = d.dt_rank;
+  s.M = d.n_meta;
+  s.W = d.window;
+  s.share = d.kv_share;
+  s.bf16 = bf16;
+  s.es = bf16 ? 2 : 4;
+  s.qw = (int64_t)s.Hq * s.dh;
+  s.kvw = (int64_t)s.Hkv * s.dh;
+  s.k_col = s.qw;
+  s.v_col = s.qw + s.kvw;
+  s.xs_col = s.qw + (s.share ? 0 : 2 * s.kvw);
+  s.g_col = s.xs_col + s.Di;
+  s.n_in = s.g_col + s.Di;
+  s.fw = s.qw + s.Di;
+  s.scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / std::sqrt((float)s.dh);
+  if (s.n_in > (1 << 30) || s.fw > (1 << 30)) return HYMBA_ERR_UNSUPPORTED;
+  return HYMBA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Carve {
+  size_t z, delta, bc, dt, f, part, total;
+};
+
+constexpr int kDecodeKeysPerSplit = 256;
+
+int decode_nsplit(const Shape& s, int span_max) {
+  return (s.M + span_max + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
+}
+
+// rows = meta rows + batch * tokens (prefill) or batch (decode).
+Carve carve(const Shape& s, int64_t rows, int batch, int nsplit) {
+  Carve c{};
+  size_t off = 0;
+  c.z = off;
+  off = align_up(off + (size_t)rows * s.n_in * s.es);
+  c.delta = off;
+  off = align_up(off + (size_t)rows * s.R * s.es);
+  c.bc = off;
+  off = align_up(off + (size_t)rows * 2 * s.N * 4);
+  c.dt = off;
+  off = align_up(off + (size_t)rows * s.Di * 4);
+  c.f = off;
+  off = align_up(off + (size_t)rows * s.fw * s.es);
+  c.part = off;
+  off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 2) * 4);
+  c.total = off;
+  return c;
+}
+
+bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15) != 0; }
+
+template <typename... P>
+bool any_misaligned(P... ptrs) {
+  return (misaligned((const void*)ptrs) || ...);
+}
+
+hymba_status check_weights(const hymba_layer_weights* w) {
+  if (w == nullptr || !w->w_in || !w->w_x || !w->w_dt || !w->w_out || !w->dt_bias || !w->A ||
+      !w->D || !w->beta_attn || !w->beta_ssm)
+    return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(w->w_in, w->w_x, w->w_dt, w->w_out, w->dt_bias, w->A, w->D, w->beta_attn,
+                     w->beta_ssm))
+    return HYMBA_ERR_ALIGNMENT;
+  return HYMBA_OK;
+}
+
+char* ws_ptr(void* ws, size_t off) { return (char*)ws + off; }
+
+}  // namespace
+
+// ===================================================================== ABI
+
+extern "C" {
+
+int32_t hymba_abi_version(void) { return HYMBA_ABI_VERSION; }
+
+int32_t hymba_last_hip_error(void) { return g_last_hip_error; }
+
+const char* hymba_status_str(hymba_status s) {
+  switch (s) {
+    case HYMBA_OK: return "ok";
+    case HYMBA_ERR_INVALID_ARG: return "invalid argument";
+    case HYMBA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case HYMBA_ERR_WORKSPACE: return "workspace missing or too small";
+    case HYMBA_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case HYMBA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t hymba_layer_workspace_bytes(const hymba_layer_desc* desc, int32_t batch, int32_t seq_len,
+                                   int32_t mode) {
+  Shape s;
+  if (make_shape(desc, s) != HYMBA_OK || batch < 0 || seq_len < 0) return 0;
+  if (mode == 0) {
+    const int64_t rows = (int64_t)s.M + (int64_t)batch * seq_len;
+    return carve(s, rows, 0, 0).total;
+  }
+  if (mode == 1) {
+    // seq_len carries the ring capacity (slots) for decode.
+    const int span_max = s.W > 0 ? std::min(s.W, seq_len) : seq_len;
+    return carve(s, batch, batch, decode_nsplit(s, span_max)).total;
+  }
+  return 0;
+}
+
+hymba_status hymba_timer_enable(int32_t on) {
+  g_timer_on = on != 0;
+  return HYMBA_OK;
+}
+
+hymba_status hymba_timer_read(int32_t stage, double* total_ms, int32_t* launches) {
+  if (stage < 0 || stage >= HYMBA_NUM_STAGES || total_ms == nullptr || launches == nullptr)
+    return HYMBA_ERR_INVALID_ARG;
+  StageTimer& t = g_timers[stage];
+  double sum = 0.0;
+  for (int i = 0; i < t.used; ++i) {
+    hipError_t e = hipEventSynchronize(t.stop[i]);
+    if (e != hipSuccess) return fail_hip(e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+    if (e != hipSuccess) return fail_hip(e);
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = t.used;
+  t.used = 0;
+  return HYMBA_OK;
+}
+
+hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer_weights* w,
+                                 const void* meta, const void* x, int32_t batch,
+                                 int32_t seq_len, const hymba_kv* kv_in, hymba_kv* kv_out,
+                                 hymba_ssm_state* state_out, void* y, void* y_meta,
+                                 void* workspace, size_t workspace_bytes, void* stream_) {
+  Shape s;
+  hymba_status st = make_shape(desc, s);
+  if (st != HYMBA_OK) return st;
+  if ((st = check_weights(w)) != HYMBA_OK) return st;
+  if (batch < 0 || seq_len < 0) return HYMBA_ERR_INVALID_ARG;
+  const int B = batch, L = seq_len, M = s.M;
+  const int64_t BL = (int64_t)B * L;
+  const int64_t rows = M + BL;
+  if (rows > (int64_t)1 << 31 || BL > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  if (M > 0 && meta == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (BL > 0 && (x == nullptr || y == nullptr)) return HYMBA_ERR_INVALID_ARG;
+  if (s.share) {
+    if (kv_in == nullptr || kv_out != nullptr) return HYMBA_ERR_INVALID_ARG;
+    if (kv_in->k == nullptr || kv_in->v == nullptr || kv_in->slots < L || kv_in->slots <= 0)
+      return HYMBA_ERR_INVALID_ARG;
+    if (M > 0 && (kv_in->k_meta == nullptr || kv_in->v_meta == nullptr))
+      return HYMBA_ERR_INVALID_ARG;
+    if (any_misaligned(kv_in->k, kv_in->v, kv_in->k_meta, kv_in->v_meta))
+      return HYMBA_ERR_ALIGNMENT;
+  } else {
+    if (kv_in != nullptr) return HYMBA_ERR_INVALID_ARG;
+    if (kv_out != nullptr) {
+      if (kv_out->slots <= 0 || kv_out->k == nullptr || kv_out->v == nullptr)
+        return HYMBA_ERR_INVALID_ARG;
+      if (M > 0 && (kv_out->k_meta == nullptr || kv_out->v_meta == nullptr))
+        return HYMBA_ERR_INVALID_ARG;
+      if (any_misaligned(kv_out->k, kv_out->v, kv_out->k_meta, kv_out->v_meta))
+        return HYMBA_ERR_ALIGNMENT;
+    }
+  }
+  if (state_out != nullptr) {
+    if (state_out->h == nullptr) return HYMBA_ERR_INVALID_ARG;
+    if (any_misaligned(state_out->h, state_out->pos)) return HYMBA_ERR_ALIGNMENT;
+  }
+  if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
+  const Carve cv = carve(s, rows, 0, 0);
+  if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_;
+  if (rows == 0) return HYMBA_OK;
+
+  char* z = ws_ptr(workspace, cv.z);
+  char* delta = ws_ptr(workspace, cv.delta);
+  float* bc = (float*)ws_ptr(workspace, cv.bc);
+  float* dt = (float*)ws_ptr(workspace, cv.dt);
+  char* f = ws_ptr(workspace, cv.f);
+  const bool b16 = s.bf16;
+  auto gemm = [&](const GemmOperands& op, const GemmOutput& out, GemmShape shape) {
+    return b16 ? launch_gemm_bf16(op, out, shape, stream) : launch_gemm_f32(op, out, stream);
+  };
+
+  // 1. in_proj over [meta; X] (meta rows once).
+  {
+    GemmOperands op{meta, s.d, x, s.d, M, w->w_in, s.d, (int)rows, (int)s.n_in, s.d};
+    GemmOutput out{EpiKind::Store, z, s.n_in, z + (size_t)M * s.n_in * s.es, s.n_in, M, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out, GemmShape::Large));
+  }
+  // 2. producer cache.
+  if (!s.share && kv_out != nullptr) {
+    HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE,
+                 launch_kv_write_prefill(b16, z, s.n_in, (int)s.k_col, (int)s.v_col, kv_out->k_meta,
+                                         kv_out->v_meta, kv_out->k, kv_out->v, kv_out->slots, M, L,
+                                         B, s.Hkv, s.dh, stream));
+  }
+  // 3. attention heads -> F[:, :qw].
+  {
+    AttnParams ap{};
+    ap.q = z;
+    ap.q_row_stride = s.n_in;
+    if (s.share) {
+      ap.k_meta = kv_in->k_meta;
+      ap.v_meta = kv_in->v_meta;
+      ap.meta_head_stride = (int64_t)M * s.dh;
+      ap.meta_row_stride = s.dh;
+      ap.k_seq = kv_in->k;
+      ap.v_seq = kv_in->v;
+      ap.seq_batch_stride = (int64_t)s.Hkv * kv_in->slots * s.dh;
+      ap.seq_head_stride = (int64_t)kv_in->slots * s.dh;
+      ap.seq_row_stride = s.dh;
+      ap.seq_slots = kv_in->slots;
+    } else {
+      ap.k_meta = z + s.k_col * s.es;
+      ap.v_meta = z + s.v_col * s.es;
+      ap.meta_head_stride = s.dh;
+      ap.meta_row_stride = s.n_in;
+      ap.k_seq = z + ((size_t)M * s.n_in + s.k_col) * s.es;
+      ap.v_seq = z + ((size_t)M * s.n_in + s.v_col) * s.es;
+      ap.seq_batch_stride = (int64_t)L * s.n_in;
+      ap.seq_head_stride = s.dh;
+      ap.seq_row_stride = s.n_in;
+      ap.seq_slots = L > 0 ? L : 1;
+    }
+    ap.o = f;
+    ap.o_row_stride = s.fw;
+    ap.n_meta = M;
+    ap.L = L;
+    ap.B = B;
+    ap.Hq = s.Hq;
+    ap.Hkv = s.Hkv;
+    ap.head_dim = s.dh;
+    ap.window = s.W;
+    ap.scale = s.scale;
+    HYMBA_LAUNCH(HYMBA_STAGE_ATTN, b16 ? launch_attention_prefill_bf16(ap, stream)
+                                       : launch_attention_prefill_f32(ap, stream));
+  }
+  // 4. x_proj: [delta | B | C] = Xs W_x^T.
+  {
+    GemmOperands op{z + s.xs_col * s.es, s.n_in, nullptr, 0, (int)rows, w->w_x, s.Di, (int)rows,
+                    s.R + 2 * s.N, s.Di};
+    GemmOutput out{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out, GemmShape::Narrow));
+  }
+  // 5. dt_proj + softplus.
+  {
+    GemmOperands op{delta, s.R, nullptr, 0, (int)rows, w->w_dt, s.R, (int)rows, s.Di, s.R};
+    GemmOutput out{EpiKind::Softplus, dt, s.Di, nullptr, 0, 0, 0, w->dt_bias};
+    HYMBA_LAUNCH(HYMBA_STAGE_DTPROJ, gemm(op, out, GemmShape::Narrow));
+  }
+  // 6. selective scan + gate -> F[:, qw:].
+  {
+    ScanParams sp{};
+    sp.z = z;
+    sp.z_stride = s.n_in;
+    sp.xs_col = (int)s.xs_col;
+    sp.g_col = (int)s.g_col;
+    sp.dt = dt;
+    sp.bc = bc;
+    sp.A = w->A;
+    sp.D = w->D;
+    sp.y = f + s.qw * s.es;
+    sp.y_stride = s.fw;
+    sp.h_out = state_out ? state_out->h : nullptr;
+    sp.n_meta = M;
+    sp.L = L;
+    sp.B = B;
+    sp.Di = s.Di;
+    sp.N = s.N;
+    if (B == 0) {  // meta rows only: run them as one sequence of length 0
+      sp.B = 1;
+      sp.h_out = nullptr;
+    }
+    HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill(b16, sp, stream));
+  }
+  // 7. RMSNorm + beta + average, in place.
+  HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
+                                                  w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
+  // 8. out_proj: meta rows -> y_meta, sequence rows -> y.
+  {
+    GemmOperands op{f, s.fw, nullptr, 0, (int)rows, w->w_out, s.fw, (int)rows, s.d, (int)s.fw};
+    GemmOutput out{EpiKind::Store, y_meta, s.d, y, s.d, M, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out, GemmShape::Large));
+  }
+  if (state_out != nullptr && state_out->pos != nullptr && B > 0) {
+    HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE, launch_fill_i32(state_out->pos, L, B, stream));
+  }
+  return HYMBA_OK;
+}
+
+hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_weights* w,
+                                const void* x, int32_t batch, hymba_kv* kv,
+                                hymba_ssm_state* state, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream_) {
+  Shape s;
+  hymba_status st = make_shape(desc, s);
+  if (st != HYMBA_OK) return st;
+  if ((st = check_weights(w)) != HYMBA_OK) return st;
+  if (batch < 0) return HYMBA_ERR_INVALID_ARG;
+  const int B = batch, M = s.M;
+  if (kv == nullptr || state == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (kv->slots <= 0 || kv->k == nullptr || kv->v == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (M > 0 && (kv->k_meta == nullptr || kv->v_meta == nullptr)) return HYMBA_ERR_INVALID_ARG;
+  if (s.W > 0 && kv->slots < s.W) return HYMBA_ERR_INVALID_ARG;
+  if (state->h == nullptr || state->pos == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (B > 0 && (x == nullptr || y == nullptr)) return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(x, y, kv->k, kv->v, kv->k_meta, kv->v_meta, state->h, state->pos, workspace))
+    return HYMBA_ERR_ALIGNMENT;
+  const int span_max = s.W > 0 ? s.W : kv->slots;
+  const int nsplit = decode_nsplit(s, span_max);
+  const Carve cv = carve(s, B, B, nsplit);
+  if (B > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_;
+  if (B == 0) return HYMBA_OK;
+
+  char* z = ws_ptr(workspace, cv.z);
+  char* delta = ws_ptr(workspace, cv.delta);
+  float* bc = (float*)ws_ptr(workspace, cv.bc);
+  float* dt = (float*)ws_ptr(workspace, cv.dt);
+  char* f = ws_ptr(workspace, cv.f);
+  float* part = (float*)ws_ptr(workspace, cv.part);
+  const bool b16 = s.bf16;
+  auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
+    return b16 ? launch_gemm_bf16(op, out, GemmShape::Skinny, stream)
+               : launch_gemm_f32(op, out, stream);
+  };
+
+  {
+    GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
+    GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, B, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out));
+  }
+  if (!s.share) {
+    HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE,
+                 launch_kv_write_decode(b16, z, s.n_in, (int)s.k_col, (int)s.v_col, kv->k, kv->v,
+                                        kv->slots, state->pos, B, s.Hkv, s.dh, stream));
+  }
+  {
+    AttnDecodeParams ap{};
+    ap.q = z;
+    ap.q_row_stride = s.n_in;
+    ap.k_meta = kv->k_meta;
+    ap.v_meta = kv->v_meta;
+    ap.k = kv->k;
+    ap.v = kv->v;
+    ap.slots = kv->slots;
+    ap.pos = state->pos;
+    ap.part = part;
+    ap.nsplit = nsplit;
+    ap.keys_per_split = kDecodeKeysPerSplit;
+    ap.n_meta = M;
+    ap.B = B;
+    ap.Hq = s.Hq;
+    ap.Hkv = s.Hkv;
+    ap.head_dim = s.dh;
+    ap.span_max = span_max;
+    ap.scale = s.scale;
+    HYMBA_LAUNCH(HYMBA_STAGE_ATTN, launch_attention_decode(b16, ap, stream));
+  }
+  {
+    GemmOperands op{z + s.xs_col * s.es, s.n_in, nullptr, 0, B, w->w_x, s.Di, B, s.R + 2 * s.N,
+                    s.Di};
+    GemmOutput out{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out));
+  }
+  {
+    GemmOperands op{delta, s.R, nullptr, 0, B, w->w_dt, s.R, B, s.Di, s.R};
+    GemmOutput out{EpiKind::Softplus, dt, s.Di, nullptr, 0, 0, 0, w->dt_bias};
+    HYMBA_LAUNCH(HYMBA_STAGE_DTPROJ, gemm(op, out));
+  }
+  {
+    SsmStepParams sp{};
+    sp.z = z;
+    sp.z_stride = s.n_in;
+    sp.xs_col = (int)s.xs_col;
+    sp.g_col = (int)s.g_col;
+    sp.dt = dt;
+    sp.bc = bc;
+    sp.A = w->A;
+    sp.D = w->D;
+    sp.h = state->h;
+    sp.y = f + s.qw * s.es;
+    sp.y_stride = s.fw;
+    sp.pos = state->pos;
+    sp.B = B;
+    sp.Di = s.Di;
+    sp.N = s.N;
+    HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_ssm_step(b16, sp, stream));
+  }
+  HYMBA_LAUNCH(HYMBA_STAGE_NORM,
+               launch_decode_combine_norm(b16, part, nsplit, f, s.fw, B, s.Hq, s.dh, s.Di,
+                                          w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
+  {
+    GemmOperands op{f, s.fw, nullptr, 0, B, w->w_out, s.fw, B, s.d, (int)s.fw};
+    GemmOutput out{EpiKind::Store, y, s.d, nullptr, 0, B, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out));
+  }
+  return HYMBA_OK;
+}
+
+hymba_status hymba_op_gemm(int32_t dtype, const void* a, int64_t lda, const void* b, int64_t ldb,
+                           void* c, int64_t ldc, int32_t c_dtype, int32_t m, int32_t n, int32_t k,
+                           void* stream) {
+  if (dtype != HYMBA_DTYPE_F32 && dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
+  if (c_dtype != HYMBA_DTYPE_F32 && c_dtype != dtype) return HYMBA_ERR_INVALID_ARG;
+  if (m < 0 || n < 0 || k < 0 || lda < k || ldb < k || ldc < n) return HYMBA_ERR_INVALID_ARG;
+  if ((int64_t)m * n > 0 && (a == nullptr || b == nullptr || c == nullptr))
+    return HYMBA_ERR_INVALID_ARG;
+  if (k % 8 || lda % 8 || ldb % 8 || ldc % 4) return HYMBA_ERR_UNSUPPORTED;
+  if (any_misaligned(a, b, c)) return HYMBA_ERR_ALIGNMENT;
+  if ((int64_t)m * n == 0) return HYMBA_OK;
+  GemmOperands op{a, lda, nullptr, 0, m, b, ldb, m, n, k};
+  GemmOutput out{c_dtype == dtype ? EpiKind::Store : EpiKind::StoreF32, c, ldc, nullptr, 0, m, 0,
+                 nullptr};
+  hipError_t e = dtype == HYMBA_DTYPE_BF16
+                     ? launch_gemm_bf16(op, out, GemmShape::Large, (hipStream_t)stream)
+                     : launch_gemm_f32(op, out, (hipStream_t)stream);
+  return e == hipSuccess ? HYMBA_OK : fail_hip(e);
+}
+
+hymba_status hymba_op_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes % 16) return HYMBA_ERR_UNSUPPORTED;
+  if (bytes > 0 && (src == nullptr || dst == nullptr)) return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(src, dst)) return HYMBA_ERR_ALIGNMENT;
+  hipError_t e = launch_copy(src, dst, bytes, (hipStream_t)stream);
+  return e == hipSuccess ? HYMBA_OK : fail_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Host-side launchers of the gfx950 kernels (internal to libhymba).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hymba {
+
+// ----------------------------------------------------------------- GEMM
+// C[M, N] = A[M, K] * B[N, K]^T.  A's rows come from two sources: rows < a_split
+// from a0 (stride lda0), the rest from a1 (stride lda1).  Element type of A and B is
+// `bf16` (MFMA) or fp32 (VALU), per the launcher.
+struct GemmOperands {
+  const void* a0;
+  int64_t lda0;
+  const void* a1;
+  int64_t lda1;
+  int a_split;
+  const void* b;
+  int64_t ldb;
+  int M, N, K;
+};
+
+enum class EpiKind { Store, StoreF32, XProj, Softplus };
+
+// Output description for the epilogues.
+//  Store:    rows < c_split -> c0 (stride ldc0, skipped if c0 == nullptr), others ->
+//            c1 (stride ldc1); storage type = the input type.
+//  StoreF32: fp32 rows into c0 (stride ldc0).
+//  XProj:    columns < split_col -> c0 (storage type, stride ldc0), columns >= split_col
+//            -> c1 fp32 (stride ldc1, column - split_col).
+//  Softplus: fp32 c0[m, n] = softplus(acc + bias[n]).
+struct GemmOutput {
+  EpiKind kind;
+  void* c0;
+  int64_t ldc0;
+  void* c1;
+  int64_t ldc1;
+  int c_split;
+  int split_col;
+  const float* bias;
+};
+
+enum class GemmShape { Large, Narrow, Skinny };
+
+hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmShape shape,
+                            hipStream_t s);
+hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStream_t s);
+
+// ----------------------------------------------------------------- attention
+// Keys/values at X~ position j of sequence b: j < n_meta from the meta arrays
+// (meta + g*meta_head_stride + j*meta_row_stride), otherwise from the sequence
+// arrays (seq + b*seq_batch_stride + g*seq_head_stride + ((j - n_meta) % seq_slots) *
+// seq_row_stride).  Queries: row r of q (stride q_row_stride); r < n_meta is a meta
+// row (shared), otherwise sequence b = (r - n_meta) / L at X-position (r - n_meta) % L.
+struct AttnParams {
+  const void* q;
+  int64_t q_row_stride;
+  const void* k_meta;
+  const void* v_meta;
+  int64_t meta_head_stride, meta_row_stride;
+  const void* k_seq;
+  const void* v_seq;
+  int64_t seq_batch_stride, seq_head_stride, seq_row_stride;
+  int seq_slots;
+  void* o;
+  int64_t o_row_stride;
+  int n_meta, L, B, Hq, Hkv, head_dim, window;
+  float scale;
+};
+hipError_t launch_attention_prefill_bf16(const AttnParams& p, hipStream_t s);
+hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s);
+
+// Decode: one query per sequence at X-position pos[b]; keys = meta + the
+// min(pos+1, span_max) most recent ring positions.  Partial results per split go to
+// part (fp32): [B, Hq, nsplit, head_dim + 2] holding (o[head_dim], m, l).
+struct AttnDecodeParams {
+  const void* q;  // row b at q + b*q_row_stride (+ h*head_dim)
+  int64_t q_row_stride;
+  const void* k_meta;
+  const void* v_meta;  // [Hkv, M, dh]
+  const void* k;
+  const void* v;  // [B, Hkv, S, dh]
+  int slots;
+  const int32_t* pos;
+  float* part;
+  int nsplit, keys_per_split;
+  int n_meta, B, Hq, Hkv, head_dim, span_max;
+  float scale;
+};
+hipError_t launch_attention_decode(bool bf16, const AttnDecodeParams& p, hipStream_t s);
+
+// ----------------------------------------------------------------- scan
+struct ScanParams {
+  const void* z;       // in_proj output, rows as for attention queries
+  int64_t z_stride;
+  int xs_col, g_col;   // column offsets of Xs and G in z
+  const float* dt;     // [rows, Di]
+  const float* bc;     // [rows, 2N] (B then C)
+  const float* A;      // [Di, N]
+  const float* D;      // [Di]
+  void* y;             // gated output, row stride y_stride (storage type)
+  int64_t y_stride;
+  float* h_out;        // [B, Di, N] or nullptr
+  int n_meta, L, B, Di, N;
+};
+hipError_t launch_scan_prefill(bool bf16, const ScanParams& p, hipStream_t s);
+
+// Decode: one step per sequence, h updated in place, pos[b] += 1 when pos != nullptr.
+struct SsmStepParams {
+  const void* z;
+  int64_t z_stride;
+  int xs_col, g_col;
+  const float* dt;  // [B, Di]
+  const float* bc;  // [B, 2N]
+  const float* A;
+  const float* D;
+  float* h;         // [B, Di, N]
+  void* y;          // row b at y + b*y_stride
+  int64_t y_stride;
+  int32_t* pos;
+  int B, Di, N;
+};
+hipError_t launch_ssm_step(bool bf16, const SsmStepParams& p, hipStream_t s);
+
+// ----------------------------------------------------------------- fusion
+// F[r, :] = 0.5 * [beta_a * rms(F[r, :wa]) ; beta_s * rms(F[r, wa:wa+ws])], in place.
+hipError_t launch_fuse_norm(bool bf16, void* f, int64_t f_stride, int rows, int wa, int ws,
+                            const float* beta_a, const float* beta_s, float eps,
+                            hipStream_t s);
+// Decode: merge the split-attention partials into O (rounded to the storage type),
+// write it to F[b, :wa], then normalise F[b] as above.
+hipError_t launch_decode_combine_norm(bool bf16, const float* part, int nsplit, void* f,
+                                      int64_t f_stride, int B, int Hq, int head_dim, int ws,
+                                      const float* beta_a, const float* beta_s, float eps,
+                                      hipStream_t s);
+
+// ----------------------------------------------------------------- cache / misc
+// Prefill: copy K/V columns of z into the cache (meta rows -> k_meta/v_meta, the last
+// min(L, slots) positions of every sequence -> ring slot p % slots).
+hipError_t launch_kv_write_prefill(bool bf16, const void* z, int64_t z_stride, int k_col,
+                                   int v_col, void* k_meta, void* v_meta, void* k, void* v,
+                                   int slots, int n_meta, int L, int B, int Hkv,
+                                   int head_dim, hipStream_t s);
+// Decode: write row b's K/V at slot pos[b] % slots.
+hipError_t launch_kv_write_decode(bool bf16, const void* z, int64_t z_stride, int k_col,
+                                  int v_col, void* k, void* v, int slots,
+                                  const int32_t* pos, int B, int Hkv, int head_dim,
+                                  hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int n, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace hymba

@@ -1,0 +1,284 @@
+// Fusion epilogue, cache writes and small utility kernels of the hybrid-head layer.
+//
+// Fusion source: "Hymba: A Hybrid-head Architecture for Small Language Models"
+// (outta.ai summary), Design formulation, total fusion equation (each branch
+// normalised, rescaled by a learnable vector, then combined before out_proj) and the
+// Chinese summary's 核心架构 / 实现细节 (RMSNorm per branch, 0.5 average).  The
+// branches have different widths, so F = 0.5 [beta_a rms(O) ; beta_s rms(Y_ssm)] is
+// the concatenation that out_proj consumes.
+#include "common.h"
+#include "kernels.h"
+
+namespace hymba {
+
+namespace {
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float v[8]) {
+    const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float v[8]) {
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (bf16)v[e];
+    *(bf16x8*)p = x;
+  }
+};
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[8]) {
+    const floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[8]) {
+    *(floatx4*)p = floatx4{v[0], v[1], v[2], v[3]};
+    *(floatx4*)(p + 4) = floatx4{v[4], v[5], v[6], v[7]};
+  }
+};
+
+// Block-wide sums of two values (256 threads).
+__device__ __forceinline__ void block_sum2(float& a, float& b) {
+  __shared__ float ra[4], rb[4];
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) {
+    ra[w] = a;
+    rb[w] = b;
+  }
+  __syncthreads();
+  a = ra[0] + ra[1] + ra[2] + ra[3];
+  b = rb[0] + rb[1] + rb[2] + rb[3];
+  __syncthreads();
+}
+
+// Normalise one row of F in place: [0, wa) by the attention rms, [wa, wa + ws) by the
+// SSM rms.  wa and ws are multiples of 8.
+template <typename T>
+__device__ __forceinline__ void norm_row(T* f, int wa, int ws, const float* ba, const float* bs,
+                                         float eps) {
+  float sa = 0.f, ss = 0.f;
+  for (int i = threadIdx.x * 8; i < wa + ws; i += 256 * 8) {
+    float v[8];
+    Vec8<T>::load(f + i, v);
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q = fmaf(v[e], v[e], q);
+    if (i < wa)
+      sa += q;
+    else
+      ss += q;
+  }
+  block_sum2(sa, ss);
+  const float ia = 0.5f * rsqrtf(sa / (float)wa + eps);
+  const float is = 0.5f * rsqrtf(ss / (float)ws + eps);
+  for (int i = threadIdx.x * 8; i < wa + ws; i += 256 * 8) {
+    float v[8];
+    Vec8<T>::load(f + i, v);
+    const bool att = i < wa;
+    const float* beta = att ? ba + i : bs + (i - wa);
+    const float sc = att ? ia : is;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * sc * beta[e];
+    Vec8<T>::store(f + i, v);
+  }
+}
+
+}  // namespace
+
+template <typename T>
+__global__ __launch_bounds__(256) void fuse_norm_kernel(T* f, int64_t stride, int wa, int ws,
+                                                        const float* ba, const float* bs, float eps) {
+  norm_row<T>(f + (int64_t)blockIdx.x * stride, wa, ws, ba, bs, eps);
+}
+
+hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int wa, int ws,
+                            const float* beta_a, const float* beta_s, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (bf16_)
+    fuse_norm_kernel<bf16><<<dim3(rows), dim3(256), 0, s>>>((bf16*)f, f_stride, wa, ws, beta_a,
+                                                            beta_s, eps);
+  else
+    fuse_norm_kernel<float><<<dim3(rows), dim3(256), 0, s>>>((float*)f, f_stride, wa, ws, beta_a,
+                                                             beta_s, eps);
+  return hipGetLastError();
+}
+
+// Decode: merge split partials (o, m, l) of every q head of sequence b into O, round it
+// to the storage type (as the prefill path stores O), then normalise the row.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_combine_norm_kernel(const float* part, int nsplit,
+                                                                  T* f, int64_t stride, int Hq,
+                                                                  int dh, int ws, const float* ba,
+                                                                  const float* bs, float eps) {
+  const int b = blockIdx.x;
+  T* row = f + (int64_t)b * stride;
+  const int wa = Hq * dh;
+  for (int e = threadIdx.x; e < wa; e += 256) {
+    const int h = e / dh, d = e % dh;
+    const float* ph = part + ((int64_t)b * Hq + h) * nsplit * (dh + 2);
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, ph[s * (dh + 2) + dh]);
+    float lsum = 0.f, o = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float m = ph[s * (dh + 2) + dh];
+      if (m == -INFINITY) continue;
+      const float w = __expf(m - mx);
+      lsum = fmaf(ph[s * (dh + 2) + dh + 1], w, lsum);
+      o = fmaf(ph[s * (dh + 2) + d], w, o);
+    }
+    row[e] = from_f32<T>(o / lsum);
+  }
+  __syncthreads();
+  norm_row<T>(row, wa, ws, ba, bs, eps);
+}
+
+hipError_t launch_decode_combine_norm(bool bf16_, const float* part, int nsplit, void* f,
+                                      int64_t f_stride, int B, int Hq, int head_dim, int ws,
+                                      const float* beta_a, const float* beta_s, float eps,
+                                      hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (bf16_)
+    decode_combine_norm_kernel<bf16><<<dim3(B), dim3(256), 0, s>>>(
+        part, nsplit, (bf16*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+  else
+    decode_combine_norm_kernel<float><<<dim3(B), dim3(256), 0, s>>>(
+        part, nsplit, (float*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- cache writes
+// One thread per 16-byte chunk.  Chunk index space: [meta rows | B * n_last rows] x
+// Hkv x (head_dim * sizeof(T) / 16) x {K, V}.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_write_prefill_kernel(const T* z, int64_t zs, int k_col,
+                                                               int v_col, T* k_meta, T* v_meta,
+                                                               T* k, T* v, int slots, int n_meta,
+                                                               int L, int B, int Hkv, int dh,
+                                                               int n_last) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int cpr = dh / EPC;
+  const int64_t total = (int64_t)(n_meta + (int64_t)B * n_last) * Hkv * cpr * 2;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  int64_t r = gid;
+  const int which = (int)(r % 2);
+  r /= 2;
+  const int dc = (int)(r % cpr);
+  r /= cpr;
+  const int g = (int)(r % Hkv);
+  r /= Hkv;
+  const int64_t rr = r;  // row in [meta | B * n_last]
+  int64_t zrow;
+  T* dst;
+  if (rr < n_meta) {
+    zrow = rr;
+    dst = (which ? v_meta : k_meta) + ((int64_t)g * n_meta + rr) * dh;
+  } else {
+    const int64_t q = rr - n_meta;
+    const int b = (int)(q / n_last);
+    const int p = L - n_last + (int)(q % n_last);
+    zrow = n_meta + (int64_t)b * L + p;
+    dst = (which ? v : k) + (((int64_t)b * Hkv + g) * slots + (p % slots)) * dh;
+  }
+  const T* src = z + zrow * zs + (which ? v_col : k_col) + g * dh + dc * EPC;
+  *(u32x4*)(dst + dc * EPC) = *(const u32x4*)src;
+}
+
+hipError_t launch_kv_write_prefill(bool bf16_, const void* z, int64_t z_stride, int k_col,
+                                   int v_col, void* k_meta, void* v_meta, void* k, void* v,
+                                   int slots, int n_meta, int L, int B, int Hkv, int head_dim,
+                                   hipStream_t s) {
+  const int n_last = L < slots ? L : slots;
+  const int esz = bf16_ ? 2 : 4;
+  const int64_t total = (int64_t)(n_meta + (int64_t)B * n_last) * Hkv * (head_dim * esz / 16) * 2;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (bf16_)
+    kv_write_prefill_kernel<bf16><<<dim3(blocks), dim3(256), 0, s>>>(
+        (const bf16*)z, z_stride, k_col, v_col, (bf16*)k_meta, (bf16*)v_meta, (bf16*)k, (bf16*)v,
+        slots, n_meta, L, B, Hkv, head_dim, n_last);
+  else
+    kv_write_prefill_kernel<float><<<dim3(blocks), dim3(256), 0, s>>>(
+        (const float*)z, z_stride, k_col, v_col, (float*)k_meta, (float*)v_meta, (float*)k,
+        (float*)v, slots, n_meta, L, B, Hkv, head_dim, n_last);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void kv_write_decode_kernel(const T* z, int64_t zs, int k_col,
+                                                              int v_col, T* k, T* v, int slots,
+                                                              const int32_t* pos, int B, int Hkv,
+                                                              int dh) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int cpr = dh / EPC;
+  const int64_t total = (int64_t)B * Hkv * cpr * 2;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  int64_t r = gid;
+  const int which = (int)(r % 2);
+  r /= 2;
+  const int dc = (int)(r % cpr);
+  r /= cpr;
+  const int g = (int)(r % Hkv);
+  const int b = (int)(r / Hkv);
+  const int slot = max(pos[b], 0) % slots;
+  const T* src = z + (int64_t)b * zs + (which ? v_col : k_col) + g * dh + dc * EPC;
+  T* dst = (which ? v : k) + (((int64_t)b * Hkv + g) * slots + slot) * dh + dc * EPC;
+  *(u32x4*)dst = *(const u32x4*)src;
+}
+
+hipError_t launch_kv_write_decode(bool bf16_, const void* z, int64_t z_stride, int k_col,
+                                  int v_col, void* k, void* v, int slots, const int32_t* pos,
+                                  int B, int Hkv, int head_dim, hipStream_t s) {
+  const int esz = bf16_ ? 2 : 4;
+  const int64_t total = (int64_t)B * Hkv * (head_dim * esz / 16) * 2;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (bf16_)
+    kv_write_decode_kernel<bf16><<<dim3(blocks), dim3(256), 0, s>>>(
+        (const bf16*)z, z_stride, k_col, v_col, (bf16*)k, (bf16*)v, slots, pos, B, Hkv, head_dim);
+  else
+    kv_write_decode_kernel<float><<<dim3(blocks), dim3(256), 0, s>>>(
+        (const float*)z, z_stride, k_col, v_col, (float*)k, (float*)v, slots, pos, B, Hkv,
+        head_dim);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- utilities
+__global__ void fill_i32_kernel(int32_t* p, int32_t value, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  fill_i32_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(p, value, n);
+  return hipGetLastError();
+}
+
+// Plain copy, 16 bytes per lane, grid-stride.  Used to calibrate HBM traffic counters.
+__global__ __launch_bounds__(256) void copy16_kernel(const u32x4* src, u32x4* dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  copy16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>((const u32x4*)src, (u32x4*)dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace hymba

@@ -1,0 +1,242 @@
+// SSM heads of the hybrid-head layer: Mamba selective scan with a diagonal A per
+// channel, the D skip term and the SiLU output gate.
+//
+// Source: "Hymba: A Hybrid-head Architecture for Small Language Models" (outta.ai
+// summary), Design formulation: the SSM mixing coefficient
+// alpha_{i,j} = C_i (prod_{k=j+1..i} exp(A dt_k)) B_j dt_j and the gated head output
+// Y_ssm = G * (alpha-mixed SSM input).  In recurrent form, per channel c and state n:
+//   h_t[c,n] = exp(dt_t[c] A[c,n]) h_{t-1}[c,n] + dt_t[c] x_t[c] B_t[n]
+//   y_t[c]   = sum_n C_t[n] h_t[c,n] + D[c] x_t[c];      out = y * SiLU(G)
+// h = 0 before the first meta token.
+//
+// Prefill: a workgroup owns (sequence, block of channels); each lane keeps NS states
+// of one channel in fp32 registers and walks the sequence in order.  Inputs for a
+// chunk of TC tokens (x, G, dt of the block's channels and the shared B, C rows) are
+// staged in LDS with coalesced loads; the per-token sum over states is a DPP
+// butterfly across the channel's lanes.  A is pre-scaled by log2(e) so the decay is
+// one v_exp_f32.  Every sequence replays the (batch-shared) meta prefix; only
+// sequence 0 stores the meta rows.
+#include "common.h"
+#include "kernels.h"
+
+namespace hymba {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over groups of LPC consecutive lanes (LPC a power of two <= 64); every lane of
+// the group receives the total.
+template <int LPC>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPC >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (LPC >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (LPC >= 8) v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (LPC >= 16) v += dpp<0x140>(v); // row_mirror
+  if constexpr (LPC >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPC >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ int64_t seq_row(int t, int b, int n_meta, int L) {
+  return t < n_meta ? (int64_t)t : (int64_t)n_meta + (int64_t)b * L + (t - n_meta);
+}
+
+}  // namespace
+
+template <typename T, int NS, int LPC>
+__global__ __launch_bounds__(256) void scan_prefill_kernel(ScanParams p) {
+  constexpr int N = NS * LPC;
+  constexpr int CB = 256 / LPC;  // channels per workgroup
+  constexpr int TC = 32;         // tokens per staged chunk
+  __shared__ float dt_s[TC][CB];
+  __shared__ float b_s[TC][N];
+  __shared__ float c_s[TC][N];
+  __shared__ T x_s[TC][CB];
+  __shared__ T g_s[TC][CB];
+  __shared__ T y_s[TC][CB];
+
+  const int tid = threadIdx.x;
+  const int cl = tid / LPC, sg = tid % LPC;
+  const int c0 = blockIdx.x * CB;
+  const int b = blockIdx.y;
+  const int c = c0 + cl;
+  const bool cok = c < p.Di;
+
+  float A2[NS], h[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    A2[k] = cok ? p.A[(int64_t)c * N + sg * NS + k] * kLog2e : 0.f;
+    h[k] = 0.f;
+  }
+  const float Dc = cok ? p.D[c] : 0.f;
+  const T* z = (const T*)p.z;
+  T* yout = (T*)p.y;
+  const int total = p.n_meta + p.L;
+
+  for (int t0 = 0; t0 < total; t0 += TC) {
+    const int tn = min(TC, total - t0);
+    for (int e = tid; e < tn * CB; e += 256) {
+      const int tt = e / CB, cc = e % CB, ch = c0 + cc;
+      const int64_t row = seq_row(t0 + tt, b, p.n_meta, p.L);
+      if (ch < p.Di) {
+        dt_s[tt][cc] = p.dt[row * p.Di + ch];
+        x_s[tt][cc] = z[row * p.z_stride + p.xs_col + ch];
+        g_s[tt][cc] = z[row * p.z_stride + p.g_col + ch];
+      } else {
+        dt_s[tt][cc] = 0.f;
+        x_s[tt][cc] = from_f32<T>(0.f);
+        g_s[tt][cc] = from_f32<T>(0.f);
+      }
+    }
+    for (int e = tid; e < tn * 2 * N; e += 256) {
+      const int tt = e / (2 * N), j = e % (2 * N);
+      const int64_t row = seq_row(t0 + tt, b, p.n_meta, p.L);
+      const float v = p.bc[row * 2 * N + j];
+      if (j < N)
+        b_s[tt][j] = v;
+      else
+        c_s[tt][j - N] = v;
+    }
+    __syncthreads();
+
+    for (int tt = 0; tt < tn; ++tt) {
+      const float dtv = dt_s[tt][cl];
+      const float xv = to_f32(x_s[tt][cl]);
+      const float dx = dtv * xv;
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int n = sg * NS + k;
+        const float a = __builtin_amdgcn_exp2f(dtv * A2[k]);
+        h[k] = fmaf(a, h[k], dx * b_s[tt][n]);
+        acc = fmaf(h[k], c_s[tt][n], acc);
+      }
+      acc = group_sum<LPC>(acc);
+      if (sg == 0) {
+        const float yv = fmaf(Dc, xv, acc);
+        y_s[tt][cl] = from_f32<T>(yv * silu_f(to_f32(g_s[tt][cl])));
+      }
+    }
+    __syncthreads();
+
+    for (int e = tid; e < tn * CB; e += 256) {
+      const int tt = e / CB, cc = e % CB, ch = c0 + cc;
+      const int t = t0 + tt;
+      if (ch < p.Di && (t >= p.n_meta || b == 0))
+        yout[seq_row(t, b, p.n_meta, p.L) * p.y_stride + ch] = y_s[tt][cc];
+    }
+    // the next chunk's staging writes only after every lane passed this chunk's
+    // compute (barrier above); y_s is rewritten only after the next barrier.
+  }
+
+  if (p.h_out != nullptr && cok) {
+    float* dst = p.h_out + ((int64_t)b * p.Di + c) * N + sg * NS;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) dst[k] = h[k];
+  }
+}
+
+template <typename T, int NS, int LPC>
+static hipError_t run_scan(const ScanParams& p, hipStream_t s) {
+  constexpr int CB = 256 / LPC;
+  dim3 grid((p.Di + CB - 1) / CB, p.B);
+  scan_prefill_kernel<T, NS, LPC><<<grid, dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t scan_dispatch(const ScanParams& p, hipStream_t s) {
+  switch (p.N) {
+    case 4: return run_scan<T, 4, 1>(p, s);
+    case 8: return run_scan<T, 4, 2>(p, s);
+    case 16: return run_scan<T, 4, 4>(p, s);
+    case 32: return run_scan<T, 4, 8>(p, s);
+    case 64: return run_scan<T, 8, 8>(p, s);
+    case 128: return run_scan<T, 8, 16>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_prefill(bool bf16_, const ScanParams& p, hipStream_t s) {
+  if (p.B == 0 || p.Di == 0 || p.n_meta + p.L == 0) return hipSuccess;
+  return bf16_ ? scan_dispatch<bf16>(p, s) : scan_dispatch<float>(p, s);
+}
+
+// --------------------------------------------------------------------- decode step
+// Thread per (sequence, channel, group of 4 states); h is read and written once as a
+// float4 per thread.  The thread of state group 0 of channel 0 advances pos[b] after
+// every kernel that reads it has been enqueued before this one.
+template <typename T, int LPC>
+__global__ __launch_bounds__(256) void ssm_step_kernel(SsmStepParams p) {
+  constexpr int NS = 4;
+  constexpr int N = NS * LPC;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int sg = (int)(gid % LPC);
+  const int64_t bc_ = gid / LPC;
+  const int c = (int)(bc_ % p.Di);
+  const int b = (int)(bc_ / p.Di);
+  const bool ok = b < p.B;
+  const int bb = ok ? b : 0;
+  const T* z = (const T*)p.z + (int64_t)bb * p.z_stride;
+  const float xv = to_f32(z[p.xs_col + c]);
+  const float gv = to_f32(z[p.g_col + c]);
+  const float dtv = p.dt[(int64_t)bb * p.Di + c];
+  const float* bcr = p.bc + (int64_t)bb * 2 * N;
+  float* hp = p.h + ((int64_t)bb * p.Di + c) * N + sg * NS;
+  const floatx4 hv = *(const floatx4*)hp;
+  const floatx4 av = *(const floatx4*)(p.A + (int64_t)c * N + sg * NS);
+  const float dx = dtv * xv;
+  float acc = 0.f;
+  floatx4 hn;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int n = sg * NS + k;
+    const float a = __builtin_amdgcn_exp2f(dtv * av[k] * kLog2e);
+    hn[k] = fmaf(a, hv[k], dx * bcr[n]);
+    acc = fmaf(hn[k], bcr[N + n], acc);
+  }
+  acc = group_sum<LPC>(acc);
+  if (!ok) return;
+  *(floatx4*)hp = hn;
+  if (sg == 0) {
+    const float yv = fmaf(p.D[c], xv, acc);
+    ((T*)p.y)[(int64_t)b * p.y_stride + c] = from_f32<T>(yv * silu_f(gv));
+    if (c == 0 && p.pos != nullptr) p.pos[b] += 1;
+  }
+}
+
+template <typename T, int LPC>
+static hipError_t run_step(const SsmStepParams& p, hipStream_t s) {
+  const int64_t threads = (int64_t)p.B * p.Di * LPC;
+  const int64_t blocks = (threads + 255) / 256;
+  ssm_step_kernel<T, LPC><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t step_dispatch(const SsmStepParams& p, hipStream_t s) {
+  switch (p.N) {
+    case 4: return run_step<T, 1>(p, s);
+    case 8: return run_step<T, 2>(p, s);
+    case 16: return run_step<T, 4>(p, s);
+    case 32: return run_step<T, 8>(p, s);
+    case 64: return run_step<T, 16>(p, s);
+    case 128: return run_step<T, 32>(p, s);
+    case 256: return run_step<T, 64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_ssm_step(bool bf16_, const SsmStepParams& p, hipStream_t s) {
+  if (p.B == 0 || p.Di == 0) return hipSuccess;
+  return bf16_ ? step_dispatch<bf16>(p, s) : step_dispatch<float>(p, s);
+}
+
+}  // namespace hymba

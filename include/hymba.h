@@ -1,0 +1,207 @@
+/*
+ * hymba.h -- C ABI of libhymba: the forward pass of the Hymba fused hybrid-head
+ * layer on one AMD Instinct MI355X (gfx950), for prefill and single-token decode.
+ *
+ * The layer (source: "Hymba: A Hybrid-head Architecture for Small Language Models",
+ * reader's summary on blog.outta.ai, section "A Fused Hybrid Head Module / Design
+ * formulation"):
+ *   X~ = [meta; X]                 meta tokens prefixed to every sequence
+ *   Z  = X~ W_in^T  split by columns into [Q | K | V | Xs | G]
+ *   attention heads:  O = softmax(s Q K^T + mask) V    (GQA, causal, optional
+ *                     sliding window; meta keys always visible)
+ *   SSM heads (Mamba selective scan, diagonal A):
+ *       [delta | B | C] = Xs W_x^T,  dt = softplus(delta W_dt^T + dt_bias)
+ *       h_t = exp(dt_t * A) * h_{t-1} + (dt_t * x_t) B_t,   y_t = h_t C_t + D * x_t
+ *       Y_ssm = y * SiLU(G)
+ *   fusion:  F = 0.5 [beta_attn * rms(O) ; beta_ssm * rms(Y_ssm)]    (total fusion
+ *            equation, with the averaging of the Chinese summary "Hymba ... hybrid
+ *            attention-SSM heads", sections 核心架构 and 实现细节)
+ *   Y = F W_out^T;  y = rows of X, y_meta = rows of the meta tokens.
+ * Readings where the pages are silent: softmax scale 1/sqrt(head_dim), no positional
+ * encoding, a window of W keys counts the query itself, q head h uses kv head
+ * floor(h * Hkv / Hq), RMSNorm over each branch's full width, h = 0 before the first
+ * meta token, only dt_proj has a bias.
+ *
+ * Conventions for every entry point
+ *  - All pointers are DEVICE pointers unless stated otherwise; descriptor and
+ *    weight-table structs themselves live in host memory and are read during the
+ *    call only.
+ *  - The caller owns every buffer.  The library allocates no device memory on these
+ *    paths and keeps no per-call state.
+ *  - Every call is asynchronous and ordered on `stream` (a hipStream_t; NULL is the
+ *    default stream).  No host synchronisation happens inside.
+ *  - Arguments are validated on the host before anything is launched: an error
+ *    return means nothing was enqueued and no output was touched.  No exception or
+ *    abort crosses the ABI.
+ *  - Row-major layouts; weights use the [out, in] convention.
+ *  - Device pointers must be 16-byte aligned (HYMBA_ERR_ALIGNMENT otherwise).
+ *
+ * Precision contract (dtype HYMBA_DTYPE_BF16): weights, meta, X, Z, delta, O, Y_ssm,
+ * F, y, y_meta and the K/V cache are bf16 (round to nearest even where produced);
+ * dt, B, C, A, D, beta, the SSM state h and all accumulation and softmax arithmetic
+ * are fp32.  dtype HYMBA_DTYPE_F32: fp32 storage and arithmetic throughout.
+ */
+#ifndef HYMBA_H
+#define HYMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYMBA_ABI_VERSION 1
+
+typedef enum {
+  HYMBA_DTYPE_F32 = 0,
+  HYMBA_DTYPE_BF16 = 1
+} hymba_dtype;
+
+typedef enum {
+  HYMBA_OK = 0,
+  HYMBA_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size        */
+  HYMBA_ERR_UNSUPPORTED = 2,   /* valid shape with no kernel (e.g. head_dim, d_state) */
+  HYMBA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required          */
+  HYMBA_ERR_ALIGNMENT = 4,     /* a device pointer is not 16-byte aligned             */
+  HYMBA_ERR_HIP = 5            /* a HIP launch failed; see hymba_last_hip_error()     */
+} hymba_status;
+
+/* Layer shape.  Supported: head_dim in {32, 64, 128} (bf16: {64, 128}); d_state a
+ * multiple of 4 up to 256 (bf16 prefill: 16, 32, 64 or 128); d_model, d_inner,
+ * dt_rank, Hq*head_dim multiples of 8; n_q_heads a multiple of n_kv_heads. */
+typedef struct {
+  int32_t d_model;      /* d                                                      */
+  int32_t n_q_heads;    /* Hq                                                     */
+  int32_t n_kv_heads;   /* Hkv (divides Hq)                                       */
+  int32_t head_dim;     /* dh                                                     */
+  int32_t d_inner;      /* Di: SSM channels                                       */
+  int32_t d_state;      /* N: SSM states per channel                              */
+  int32_t dt_rank;      /* R: rank of the dt projection                           */
+  int32_t n_meta;       /* M: meta tokens (>= 0)                                  */
+  int32_t window;       /* 0 = full causal; > 0: a non-meta key is visible if it is
+                           fewer than `window` positions back (the query counts)  */
+  int32_t kv_share;     /* 0 = producer (own K/V columns in w_in);
+                           1 = consumer (no K/V columns; reads the producer's)    */
+  int32_t dtype;        /* hymba_dtype                                            */
+  float rms_eps;        /* RMSNorm epsilon, e.g. 1e-6                             */
+  float softmax_scale;  /* 0 => 1/sqrt(head_dim)                                  */
+} hymba_layer_desc;
+
+/* Weights (device).  n_in = Hq*dh + (kv_share ? 0 : 2*Hkv*dh) + 2*Di; column
+ * blocks of w_in's output in that order: Q, K, V, Xs, G. */
+typedef struct {
+  const void *w_in;       /* [n_in, d]            dtype                          */
+  const void *w_x;        /* [R + 2N, Di]         dtype  (rows: delta, B, C)     */
+  const void *w_dt;       /* [Di, R]              dtype                          */
+  const void *w_out;      /* [d, Hq*dh + Di]      dtype                          */
+  const float *dt_bias;   /* [Di]                                                */
+  const float *A;         /* [Di, N]                                             */
+  const float *D;         /* [Di]                                                */
+  const float *beta_attn; /* [Hq*dh]                                             */
+  const float *beta_ssm;  /* [Di]                                                */
+} hymba_layer_weights;
+
+/* Attention cache (device, dtype).  X-position p of sequence b lives at slot
+ * p % slots of k/v; the M meta entries are batch-shared. */
+typedef struct {
+  void *k_meta;   /* [Hkv, M, dh]            */
+  void *v_meta;   /* [Hkv, M, dh]            */
+  void *k;        /* [B, Hkv, slots, dh]     */
+  void *v;        /* [B, Hkv, slots, dh]     */
+  int32_t slots;  /* ring capacity S (> 0)   */
+} hymba_kv;
+
+/* SSM recurrent state (device). */
+typedef struct {
+  float *h;       /* [B, Di, N] fp32                                   */
+  int32_t *pos;   /* [B] number of X tokens already consumed per sequence */
+} hymba_ssm_state;
+
+/* ---------------------------------------------------------------------------
+ * hymba_layer_prefill: the layer over [meta; X_b] for every sequence b.
+ *   meta      [M, d] dtype (batch-shared; its rows are computed once per call)
+ *   x         [B, L, d] dtype
+ *   kv_in     consumer only (kv_share = 1): the producer's cache holding all L
+ *             positions (slots >= L) and its meta entries; must be NULL otherwise.
+ *   kv_out    producer only, may be NULL: receives the meta K/V and the last
+ *             min(L, slots) positions of every sequence.
+ *   state_out may be NULL: receives h after the last token and pos[b] = L.
+ *   y         [B, L, d] dtype;   y_meta [M, d] dtype or NULL.
+ *   workspace device scratch of at least hymba_layer_workspace_bytes(desc, B, L, 0).
+ * Source: Design formulation (meta prefix, in_proj split, both heads, fusion);
+ * "Cross-layer KV sharing" (consumer reads the producer's K/V); "Combine global and
+ * local attention" (window).
+ * ------------------------------------------------------------------------- */
+hymba_status hymba_layer_prefill(const hymba_layer_desc *desc, const hymba_layer_weights *w,
+                                 const void *meta, const void *x, int32_t batch,
+                                 int32_t seq_len, const hymba_kv *kv_in, hymba_kv *kv_out,
+                                 hymba_ssm_state *state_out, void *y, void *y_meta,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * hymba_layer_decode: one new token per sequence at X-position pos[b].
+ *   x    [B, d] dtype;  y [B, d] dtype.
+ *   kv   producer: writes K/V of the new token at slot pos[b] % slots, then attends;
+ *        consumer: reads the producer's cache (enqueue the producer's decode first).
+ *        Attention covers the M meta entries and the min(pos[b]+1, W) most recent
+ *        positions, W = window (window > 0; requires slots >= window) or
+ *        W = slots (window = 0: equals full causal attention while pos[b] < slots).
+ *   state h is advanced one step in place; pos[b] += 1.
+ * Source: summary sections "Introduction" (attention keeps a KV cache, the SSM a
+ * recurrent state) and "Meta Tokens" (meta entries are a fixed cache prefix).
+ * ------------------------------------------------------------------------- */
+hymba_status hymba_layer_decode(const hymba_layer_desc *desc, const hymba_layer_weights *w,
+                                const void *x, int32_t batch, hymba_kv *kv,
+                                hymba_ssm_state *state, void *y, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for mode 0 (prefill of batch x seq_len) or 1 (decode of batch).
+ * Returns 0 if the descriptor or sizes are invalid. */
+size_t hymba_layer_workspace_bytes(const hymba_layer_desc *desc, int32_t batch,
+                                   int32_t seq_len, int32_t mode);
+
+const char *hymba_status_str(hymba_status s);
+int32_t hymba_abi_version(void);
+/* Last hipError_t seen by a failing call on this thread (0 if none). */
+int32_t hymba_last_hip_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Stage timing.  While enabled, every launch of a stage inside the two layer calls
+ * is bracketed by a pair of HIP events recorded on the call's stream.
+ * hymba_timer_read waits for the recorded events of `stage`, returns the summed
+ * milliseconds and the number of launches, and forgets them.  Host-side state; not
+ * thread-safe.  At most 4096 launches are remembered per stage between reads.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  HYMBA_STAGE_IN_PROJ = 0,   /* in_proj GEMM                                   */
+  HYMBA_STAGE_ATTN = 1,      /* attention (prefill) / split attention (decode) */
+  HYMBA_STAGE_XPROJ = 2,     /* x_proj GEMM: delta, B, C                       */
+  HYMBA_STAGE_DTPROJ = 3,    /* dt_proj GEMM + softplus                        */
+  HYMBA_STAGE_SCAN = 4,      /* selective scan + gate (prefill) / SSM step     */
+  HYMBA_STAGE_NORM = 5,      /* RMSNorm + beta + average                       */
+  HYMBA_STAGE_OUT_PROJ = 6,  /* out_proj GEMM                                  */
+  HYMBA_STAGE_KV_WRITE = 7,  /* cache writes                                   */
+  HYMBA_NUM_STAGES = 8
+} hymba_stage;
+
+hymba_status hymba_timer_enable(int32_t on);
+hymba_status hymba_timer_read(int32_t stage, double *total_ms, int32_t *launches);
+
+/* ---------------------------------------------------------------------------
+ * Single-kernel entry points used by the tests and the bandwidth calibration.
+ * hymba_op_gemm: C[M, N] = A[M, K] B[N, K]^T with fp32 accumulation, on the same
+ *   kernel the layer uses for `dtype` (bf16: MFMA).  lda/ldb/ldc in elements;
+ *   c_dtype is the storage type of C (HYMBA_DTYPE_F32 or the input dtype).
+ * hymba_op_copy: a plain 16-byte-per-lane device copy of `bytes` (multiple of 16).
+ * ------------------------------------------------------------------------- */
+hymba_status hymba_op_gemm(int32_t dtype, const void *a, int64_t lda, const void *b,
+                           int64_t ldb, void *c, int64_t ldc, int32_t c_dtype, int32_t m,
+                           int32_t n, int32_t k, void *stream);
+hymba_status hymba_op_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYMBA_H */

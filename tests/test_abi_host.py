@@ -1,0 +1,139 @@
+"""Host-side checks of libhymba that need no GPU: the library loads, exports every
+symbol include/hymba.h declares, sizes workspaces, and rejects invalid arguments
+before anything is launched (error paths return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_attention_ssm_proj_amd as hy
+from synth import CASES, LayerDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "hymba.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hymba_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hy.LIB_PATH):
+        pytest.skip("libhymba.so is not built")
+    return hy.load_library()
+
+
+def test_header_declares_the_abi():
+    names = header_functions()
+    for n in ("hymba_layer_prefill", "hymba_layer_decode", "hymba_layer_workspace_bytes",
+              "hymba_op_gemm", "hymba_timer_read"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert hy.hymba_abi_version() == 1
+    assert hy.hymba_status_str(0) == "ok"
+    assert hy.hymba_status_str(3).startswith("workspace")
+
+
+def desc_of(k=1, **kw):
+    return hy.LayerDesc.from_dims(CASES[k].dims.replace(**kw))
+
+
+def test_workspace_sizes(lib):
+    d = desc_of(1)
+    rows = 128 + 8 * 2048
+    n_in = 16 * 128 + 2 * 4 * 128 + 2 * 4096
+    got = hy.hymba_layer_workspace_bytes(d, 8, 2048, 0)
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 4096 * 4 + 6144 * 2)
+    assert floor <= got <= floor + 8 * 256
+    assert hy.hymba_layer_workspace_bytes(d, 128, 1024, 1) > 0
+    assert hy.hymba_layer_workspace_bytes(d, -1, 10, 0) == 0
+    assert hy.hymba_layer_workspace_bytes(d, 1, 10, 7) == 0
+    bad = desc_of(1, d_state=24)
+    assert hy.hymba_layer_workspace_bytes(bad, 1, 10, 0) == 0
+
+
+def _weights_struct(addr=4096):
+    return hy.LayerWeights(*[addr + 256 * i for i in range(9)])
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(n_kv_heads=3), 1),          # Hq % Hkv != 0
+    (dict(head_dim=96), 2),           # no kernel for this head_dim
+    (dict(d_state=24), 2),            # state size not a power of two
+    (dict(d_state=256), 2),           # beyond the prefill scan's LDS budget
+    (dict(d_model=100), 2),           # not a multiple of 8
+    (dict(window=-1), 1),
+    (dict(kv_share=2), 1),
+    (dict(rms_eps=float("nan")), 1),
+])
+def test_prefill_rejects_bad_descriptors(lib, change, status):
+    d = desc_of(1, **change)
+    st = hy.hymba_layer_prefill(d, _weights_struct(), 4096, 8192, 1, 4, None, None, None, 12288,
+                                None, 1 << 20, 1 << 40, stream=0, check=False)
+    assert st == status
+
+
+def test_prefill_argument_errors(lib):
+    d = desc_of(1)
+    w = _weights_struct()
+    call = lambda **kw: hy.hymba_layer_prefill(**{**dict(
+        desc=d, weights=w, meta=4096, x=8192, batch=1, seq_len=4, kv_in=None, kv_out=None,
+        state_out=None, y=12288, y_meta=None, workspace=1 << 20, workspace_bytes=1 << 40,
+        stream=0, check=False), **kw})
+    assert call(meta=None) == 1                      # meta tokens but no meta buffer
+    assert call(x=None) == 1
+    assert call(batch=-1) == 1
+    assert call(workspace_bytes=1000) == 3           # too small
+    assert call(workspace=None) == 3
+    assert call(x=8192 + 2) == 4                     # misaligned
+    assert call(weights=hy.LayerWeights(*([4096] * 8 + [None]))) == 1
+    # a producer must not be given a producer's cache
+    assert call(kv_in=hy.KV(4096, 4096, 4096, 4096, 16)) == 1
+    # a consumer needs one holding every position
+    dc = desc_of(1, kv_share=1)
+    assert call(desc=dc) == 1
+    assert call(desc=dc, kv_in=hy.KV(4096, 4096, 4096, 4096, 3)) == 1
+    assert call(desc=dc, kv_in=hy.KV(4096, 4096, 4096, 4096, 4),
+                kv_out=hy.KV(4096, 4096, 4096, 4096, 4)) == 1
+    assert call(kv_out=hy.KV(4096, 4096, 4096, None, 4)) == 1
+    assert call(state_out=hy.SSMState(None, None)) == 1
+    # nothing to do: zero rows is a successful no-op that launches nothing
+    assert hy.hymba_layer_prefill(desc_of(1, n_meta=0), w, None, None, 0, 0, None, None, None,
+                                  None, None, None, 0, stream=0, check=False) == 0
+
+
+def test_decode_argument_errors(lib):
+    d = desc_of(4)
+    w = _weights_struct()
+    kv = hy.KV(4096, 4096, 4096, 4096, 1024)
+    state = hy.SSMState(4096, 4096)
+    call = lambda **kw: hy.hymba_layer_decode(**{**dict(
+        desc=d, weights=w, x=4096, batch=2, kv=kv, state=state, y=4096, workspace=4096,
+        workspace_bytes=1 << 40, stream=0, check=False), **kw})
+    assert call(kv=None) == 1
+    assert call(state=None) == 1
+    assert call(kv=hy.KV(4096, 4096, 4096, 4096, 512)) == 1   # ring shorter than the window
+    assert call(state=hy.SSMState(4096, None)) == 1
+    assert call(workspace_bytes=16) == 3
+    assert call(y=4100) == 4
+    assert call(batch=0) == 0
+
+
+def test_op_gemm_argument_errors(lib):
+    call = lambda **kw: lib.hymba_op_gemm(*[{**dict(
+        dtype=1, a=4096, lda=64, b=4096, ldb=64, c=4096, ldc=64, c_dtype=1, m=4, n=4, k=64,
+        stream=None), **kw}[n] for n in ("dtype", "a", "lda", "b", "ldb", "c", "ldc", "c_dtype",
+                                         "m", "n", "k", "stream")])
+    assert call(dtype=7) == 1
+    assert call(k=60, lda=60, ldb=60) == 2
+    assert call(lda=32) == 1
+    assert call(a=4098) == 4
+    assert call(m=0) == 0
+    assert lib.hymba_op_copy(4096, 8192, 17, None) == 2
