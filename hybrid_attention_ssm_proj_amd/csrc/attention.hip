@@ -376,126 +376,210 @@ hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------- decode
-// Workgroup per (key split, kv head, sequence).  Each thread scores one key against
-// every q head of the group; one wave per head reduces the split's max and sum; the
-// value sum runs with threads over head_dim.  Keys of sequence b in order: M meta
-// entries, then X-positions pos - span + 1 .. pos at ring slot (position % slots),
-// span = min(pos + 1, span_max).
-template <typename T, int DH>
+// Workgroup per (key split, kv head, sequence); 4 waves of 64 keys each.  A key's
+// head_dim values are spread over LPK lanes that each own one 16-byte chunk, so a wave
+// instruction reads KPI whole rows of K (or V) contiguously.  Scores: every lane dots
+// its chunk with the same chunk of each q head (held in registers), then a DPP
+// butterfly over the key's lanes finishes the sums.  Values: each lane accumulates
+// its chunk of O for every head; lanes of different keys are summed at the end.
+// Keys of sequence b in order: M meta entries, then X-positions pos - span + 1 .. pos
+// at ring slot (position % slots), span = min(pos + 1, span_max).
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// Sum over aligned groups of LPK lanes (LPK in {4, 8, 16}), result in every lane.
+template <int LPK>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += dppf<0xB1>(v);                           // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);                           // quad_perm [2,3,0,1]
+  if constexpr (LPK >= 8) v += dppf<0x141>(v);  // row_half_mirror
+  if constexpr (LPK >= 16) v += dppf<0x140>(v); // row_mirror
+  return v;
+}
+
+template <typename T>
+struct Chunk;
+template <>
+struct Chunk<bf16> {
+  static constexpr int E = 8;
+  static __device__ __forceinline__ void cvt(const u32x4& r, float* f) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
+  }
+};
+template <>
+struct Chunk<float> {
+  static constexpr int E = 4;
+  static __device__ __forceinline__ void cvt(const u32x4& r, float* f) {
+    const floatx4 v = __builtin_bit_cast(floatx4, r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = v[e];
+  }
+};
+
+}  // namespace
+
+template <typename T, int DH, int GQ>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
-  constexpr int KPS = 256;  // keys per split (one per thread)
-  __shared__ float qs[16][DH];
-  __shared__ float ss[16][KPS];
-  __shared__ float red[256 / DH][16][DH];
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int gqn = p.Hq / p.Hkv;
-  const int h0 = g * gqn;
+  constexpr int E = Chunk<T>::E;     // elements per 16-byte chunk
+  constexpr int LPK = DH / E;        // lanes per key
+  constexpr int KPI = 64 / LPK;      // keys per wave instruction
+  constexpr int KPS = 256;           // keys per split
+  constexpr int KPW = KPS / 4;       // keys per wave
+  constexpr int NI = KPW / KPI;      // instructions per wave
+  static_assert(LPK >= 4 && LPK <= 16, "lane grouping");
+  __shared__ float s_s[GQ][KPS];
+  __shared__ float mstat[GQ], lstat[GQ];
+  __shared__ float o_s[4][GQ][DH];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h0 = g * GQ;
   const int posb = max(p.pos[b], 0);  // a negative position is treated as 0
   const int span = min(posb + 1, p.span_max);
   const int nkeys = p.n_meta + span;
   const int k0 = split * KPS;
   const int nk = min(KPS, nkeys - k0);  // may be <= 0: empty split
+  const int dc = lane % LPK, kin = lane / LPK;
 
-  for (int e = tid; e < gqn * DH; e += 256) {
-    const int hh = e / DH, d = e % DH;
-    qs[hh][d] = to_f32(((const T*)p.q)[(int64_t)b * p.q_row_stride + (h0 + hh) * DH + d]) * p.scale;
+  float q[GQ][E];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float f[E];
+    Chunk<T>::cvt(*(const u32x4*)((const T*)p.q + (int64_t)b * p.q_row_stride + (h0 + h) * DH + dc * E), f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) q[h][e] = f[e] * p.scale;
   }
-  __syncthreads();
 
-  auto key_row = [&](const T* meta, const T* ring, int idx) -> const T* {
+  auto row_of = [&](const T* meta, const T* ring, int idx) -> const T* {
     if (idx < p.n_meta) return meta + ((int64_t)g * p.n_meta + idx) * DH;
     const int xpos = posb - span + 1 + (idx - p.n_meta);
-    const int slot = xpos % p.slots;
-    return ring + (((int64_t)b * p.Hkv + g) * p.slots + slot) * DH;
+    return ring + (((int64_t)b * p.Hkv + g) * p.slots + (xpos % p.slots)) * DH;
   };
 
-  if (tid < nk) {
-    const T* kr = key_row((const T*)p.k_meta, (const T*)p.k, k0 + tid);
-    float acc[16];
+  // scores
+  u32x4 raw[NI];
 #pragma unroll
-    for (int hh = 0; hh < 16; ++hh) acc[hh] = 0.f;
-    for (int d0 = 0; d0 < DH; d0 += 8) {
-      float kv[8];
-      load8(kr + d0, kv);
+  for (int i = 0; i < NI; ++i) {
+    const int kk = wave * KPW + i * KPI + kin;
+    raw[i] = kk < nk ? *(const u32x4*)(row_of((const T*)p.k_meta, (const T*)p.k, k0 + kk) + dc * E)
+                     : u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+  for (int i = 0; i < NI; ++i) {
+    const int kk = wave * KPW + i * KPI + kin;
+    float kf[E];
+    Chunk<T>::cvt(raw[i], kf);
 #pragma unroll
-        for (int hh = 0; hh < 16; ++hh)
-          if (hh < gqn) acc[hh] = fmaf(qs[hh][d0 + e], kv[e], acc[hh]);
+    for (int h = 0; h < GQ; ++h) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part = fmaf(q[h][e], kf[e], part);
+      part = lane_group_sum<LPK>(part);
+      if (dc == 0) s_s[h][kk] = kk < nk ? part : -INFINITY;
     }
+  }
+  // V loads do not depend on the softmax: issue them before the reduction.
 #pragma unroll
-    for (int hh = 0; hh < 16; ++hh)
-      if (hh < gqn) ss[hh][tid] = acc[hh];
+  for (int i = 0; i < NI; ++i) {
+    const int kk = wave * KPW + i * KPI + kin;
+    raw[i] = kk < nk ? *(const u32x4*)(row_of((const T*)p.v_meta, (const T*)p.v, k0 + kk) + dc * E)
+                     : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
 
-  __shared__ float mstat[16], lstat[16];
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int hh = wave; hh < gqn; hh += 4) {
+  for (int h = wave; h < GQ; h += 4) {
     float mx = -INFINITY;
-    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, ss[hh][k]);
+    for (int k = lane; k < KPS; k += 64) mx = fmaxf(mx, s_s[h][k]);
     mx = wave_max(mx);
+    const float muse = mx == -INFINITY ? 0.f : mx;
     float sum = 0.f;
-    for (int k = lane; k < nk; k += 64) {
-      const float e = __expf(ss[hh][k] - mx);
-      ss[hh][k] = e;
+    for (int k = lane; k < KPS; k += 64) {
+      const float e = __expf(s_s[h][k] - muse);
+      s_s[h][k] = e;
       sum += e;
     }
     sum = wave_sum(sum);
     if (lane == 0) {
-      mstat[hh] = mx;
-      lstat[hh] = sum;
+      mstat[h] = mx;
+      lstat[h] = sum;
     }
   }
   __syncthreads();
 
-  // value sums: thread -> (d, quarter of the split's keys)
-  constexpr int QN = 256 / DH;  // key groups
-  const int d = tid % DH, qg = tid / DH;
-  float o[16];
+  float o[GQ][E];
 #pragma unroll
-  for (int hh = 0; hh < 16; ++hh) o[hh] = 0.f;
-  for (int k = qg; k < nk; k += QN) {
-    const float vv = to_f32(key_row((const T*)p.v_meta, (const T*)p.v, k0 + k)[d]);
+  for (int h = 0; h < GQ; ++h)
 #pragma unroll
-    for (int hh = 0; hh < 16; ++hh)
-      if (hh < gqn) o[hh] = fmaf(ss[hh][k], vv, o[hh]);
+    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int kk = wave * KPW + i * KPI + kin;
+    float vf[E];
+    Chunk<T>::cvt(raw[i], vf);
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float pk = s_s[h][kk];
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h][e] = fmaf(pk, vf[e], o[h][e]);
+    }
   }
+  // sum the KPI key groups of the wave (lanes with the same chunk index)
 #pragma unroll
-  for (int hh = 0; hh < 16; ++hh)
-    if (hh < gqn) red[qg][hh][d] = o[hh];
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float v = o[h][e];
+#pragma unroll
+      for (int off = LPK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      o[h][e] = v;
+    }
+  if (kin == 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) o_s[wave][h][dc * E + e] = o[h][e];
+  }
   __syncthreads();
-  for (int e = tid; e < gqn * DH; e += 256) {
-    const int hh = e / DH, dd = e % DH;
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < QN; ++q) sum += red[q][hh][dd];
-    float* dst = p.part + (((int64_t)b * p.Hq + h0 + hh) * p.nsplit + split) * (DH + 2);
-    dst[dd] = nk > 0 ? sum : 0.f;
-    if (dd == 0) {
-      dst[DH] = nk > 0 ? mstat[hh] : -INFINITY;
-      dst[DH + 1] = nk > 0 ? lstat[hh] : 0.f;
+  for (int i = tid; i < GQ * DH; i += 256) {
+    const int h = i / DH, d = i % DH;
+    const float sum = o_s[0][h][d] + o_s[1][h][d] + o_s[2][h][d] + o_s[3][h][d];
+    float* dst = p.part + (((int64_t)b * p.Hq + h0 + h) * p.nsplit + split) * (DH + 2);
+    dst[d] = nk > 0 ? sum : 0.f;
+    if (d == 0) {
+      dst[DH] = nk > 0 ? mstat[h] : -INFINITY;
+      dst[DH + 1] = nk > 0 ? lstat[h] : 0.f;
     }
   }
 }
 
+template <typename T, int DH>
+static hipError_t run_decode(const AttnDecodeParams& p, hipStream_t s) {
+  dim3 grid(p.nsplit, p.Hkv, p.B);
+  switch (p.Hq / p.Hkv) {
+    case 1: attn_decode_kernel<T, DH, 1><<<grid, dim3(256), 0, s>>>(p); break;
+    case 2: attn_decode_kernel<T, DH, 2><<<grid, dim3(256), 0, s>>>(p); break;
+    case 4: attn_decode_kernel<T, DH, 4><<<grid, dim3(256), 0, s>>>(p); break;
+    case 8: attn_decode_kernel<T, DH, 8><<<grid, dim3(256), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_decode(bool bf16_, const AttnDecodeParams& p, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
-  dim3 grid(p.nsplit, p.Hkv, p.B);
-#define HYMBA_DEC(T, DHV)                                           \
-  do {                                                              \
-    attn_decode_kernel<T, DHV><<<grid, dim3(256), 0, s>>>(p);       \
-    return hipGetLastError();                                       \
-  } while (0)
   if (bf16_) {
-    if (p.head_dim == 128) HYMBA_DEC(bf16, 128);
-    if (p.head_dim == 64) HYMBA_DEC(bf16, 64);
+    if (p.head_dim == 128) return run_decode<bf16, 128>(p, s);
+    if (p.head_dim == 64) return run_decode<bf16, 64>(p, s);
   } else {
-    if (p.head_dim == 128) HYMBA_DEC(float, 128);
-    if (p.head_dim == 64) HYMBA_DEC(float, 64);
-    if (p.head_dim == 32) HYMBA_DEC(float, 32);
+    if (p.head_dim == 64) return run_decode<float, 64>(p, s);
+    if (p.head_dim == 32) return run_decode<float, 32>(p, s);
   }
-#undef HYMBA_DEC
   return hipErrorInvalidValue;
 }
 

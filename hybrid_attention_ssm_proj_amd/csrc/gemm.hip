@@ -227,6 +227,169 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_kernel(GemmOperands g, Epi 
     }
 }
 
+// ------------------------------------------------------------ bf16 MFMA, direct-to-LDS
+// K % 64 == 0.  Tiles of BM x BN x 64 are fetched with global_load_lds_dwordx4 (each
+// wave instruction fills 1 KB of LDS = 8 rows x 64 k), so no VGPR staging and no LDS
+// store instructions.  Row r of a tile keeps its 8 16-byte k-chunks XOR-swizzled by
+// f(r) = (r & 7) ^ ((r >> 3) & 1): the 16 rows an MFMA fragment read touches then hit
+// distinct bank groups for both 16-lane and 8-lane LDS phases.  Two stages live in
+// distinct LDS arrays so the compiler can tell in-flight DMA from fragment reads.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct DlCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * kWave;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA blocks per wave
+  static constexpr int A_INS = BM / 8 / NW;        // 8-row wave instructions per wave
+  static constexpr int B_INS = BN / 8 / NW;
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "loader tiling");
+};
+
+// Swizzle of the 8 16-byte k-chunks of row r: the 16 rows one fragment read touches
+// land in distinct bank groups for both 8-lane and 16-lane LDS phases.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A and column (l % 32) of B,
+// 8 consecutive k each (block l / 32); it receives D[(e/4)*8 + (l/32)*4 + e%4][l % 32],
+// e = 0..15.
+__device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
+                                                 const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// K % 64 == 0.  Two LDS stages of BM x 64 and BN x 64 filled by global_load_lds_dwordx4
+// (one wave instruction = 8 rows x 128 contiguous bytes, the L2-friendliest request
+// pattern measured); the next k-tile streams in while the current one is multiplied.
+// The stages are distinct LDS arrays so in-flight DMA and fragment reads never alias.
+template <typename Cfg, typename Epi>
+__global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) bf16 sA0[Cfg::BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB0[Cfg::BN * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sA1[Cfg::BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB1[Cfg::BN * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  const int nbm = (g.M + Cfg::BM - 1) / Cfg::BM, nbn = (g.N + Cfg::BN - 1) / Cfg::BN;
+  int bm, bn;
+  tile_coords(blockIdx.x, nbm, nbn, 8, bm, bn);
+  const int m0 = bm * Cfg::BM, n0 = bn * Cfg::BN;
+
+  // Loader: wave instruction j fills LDS chunks [(j*NW + wave)*64, +64): rows
+  // (j*NW + wave)*8 + lane/8, slot lane%8 holding k-chunk (lane%8) ^ f(row).  A has a
+  // single source here (a_split >= M); element offsets fit in 32 bits (checked on the
+  // host).  Rows past M / N load a valid row and are never stored.
+  const bf16* A = (const bf16*)g.a0;
+  const bf16* Bm = (const bf16*)g.b;
+  int a_off[Cfg::A_INS], b_off[Cfg::B_INS];
+#pragma unroll
+  for (int j = 0; j < Cfg::A_INS; ++j) {
+    const int r = (j * Cfg::NW + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    a_off[j] = min(m0 + r, g.M - 1) * (int)g.lda0 + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg::B_INS; ++j) {
+    const int r = (j * Cfg::NW + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    b_off[j] = min(n0 + r, g.N - 1) * (int)g.ldb + c * 8;
+  }
+  auto issue = [&](bf16* sa, bf16* sb, int k0) {
+#pragma unroll
+    for (int j = 0; j < Cfg::A_INS; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(A + k0 + a_off[j]),
+                                       (lds_void_t*)(sa + (j * Cfg::NW + wave) * 512), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < Cfg::B_INS; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(Bm + k0 + b_off[j]),
+                                       (lds_void_t*)(sb + (j * Cfg::NW + wave) * 512), 16, 0, 0);
+  };
+
+  floatx16 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Fragment reads: row (l % 32) of a 32-row block (32 rows = 2048 elements), k-chunk
+  // 2*ks + l/32 swizzled by f(l % 16) (block bases are multiples of 16 rows).
+  const int rl = lane & 31;
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    koff[ks] = rl * 64 + (((ks * 2 + (lane >> 5)) ^ swz(lane & 15)) * 8);
+  const int a_row0 = wm * Cfg::TM * 64, b_row0 = wn * Cfg::TN * 64;
+
+  auto compute = [&](const bf16* sa, const bf16* sb) {
+    bf16x8 af[2][Cfg::FM], bfr[2][Cfg::FN];
+    auto load = [&](int buf, int ks) {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+        af[buf][i] = *(const bf16x8*)(sa + a_row0 + i * 2048 + koff[ks]);
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        bfr[buf][j] = *(const bf16x8*)(sb + b_row0 + j * 2048 + koff[ks]);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) load((ks + 1) & 1, ks + 1);
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          acc[i][j] = mfma32x32x16(bfr[ks & 1][j], af[ks & 1][i], acc[i][j]);
+    }
+  };
+
+  // Two k-tiles per trip, one stage each; a single loop exit keeps the accumulators
+  // in place (an odd last tile runs after the loop).
+  const int KT = g.K / 64;
+  issue(sA0, sB0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    issue(sA1, sB1, (kt + 1) * 64);
+    compute(sA0, sB0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (kt + 2 < KT) issue(sA0, sB0, (kt + 2) * 64);
+    compute(sA1, sB1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (kt < KT) compute(sA0, sB0);
+
+  // acc[i][j] holds C^T of the 32 x 32 block: lane -> row rl, columns
+  // (e/4)*8 + (lane/32)*4 + 0..3.
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * Cfg::TM + i * 32 + rl;
+        const int n = n0 + wn * Cfg::TN + j * 32 + q * 8 + (lane >> 5) * 4;
+        const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+        epi(m, n, v, g.M, g.N);
+      }
+}
+
+template <typename Cfg, typename Epi>
+static hipError_t run_bf16_dl(const GemmOperands& op, const Epi& epi, hipStream_t s) {
+  const int nbm = (op.M + Cfg::BM - 1) / Cfg::BM, nbn = (op.N + Cfg::BN - 1) / Cfg::BN;
+  gemm_bf16_dl_kernel<Cfg, Epi><<<dim3(nbm * nbn), dim3(Cfg::NT), 0, s>>>(op, epi);
+  return hipGetLastError();
+}
+
 template <typename Cfg, typename Epi>
 static hipError_t run_bf16(const GemmOperands& op, const Epi& epi, hipStream_t s) {
   const int nbm = (op.M + Cfg::BM - 1) / Cfg::BM, nbn = (op.N + Cfg::BN - 1) / Cfg::BN;
@@ -253,10 +416,19 @@ static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShap
                                 hipStream_t s) {
   switch (shape) {
     case GemmShape::Large:
-      if constexpr (std::is_same_v<Epi, Epilogue<bf16, EpiKind::Store>>)
+      if constexpr (std::is_same_v<Epi, Epilogue<bf16, EpiKind::Store>>) {
+        const bool one_src = op.a_split >= op.M;
+        const bool fits32 = (int64_t)op.M * op.lda0 < (1ll << 31) && (int64_t)op.N * op.ldb < (1ll << 31);
+        if (op.K % 64 == 0 && one_src && fits32) {
+          // 256 x 256 tiles when they fill the chip several times over, else 256 x 128
+          const long t256 = (long)((op.M + 255) / 256) * ((op.N + 255) / 256);
+          if (t256 >= 4 * 256) return run_bf16_dl<DlCfg<256, 256, 2, 2>>(op, epi, s);
+          return run_bf16_dl<DlCfg<256, 128, 2, 2>>(op, epi, s);
+        }
         return run_bf16<CfgLarge>(op, epi, s);
-      else
+      } else {
         return run_bf16<CfgNarrow>(op, epi, s);
+      }
     case GemmShape::Narrow:
       return run_bf16<CfgNarrow>(op, epi, s);
     default:

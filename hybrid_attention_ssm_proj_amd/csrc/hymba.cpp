@@ -102,9 +102,9 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
   // kernels: 16-byte row chunks, 4-column epilogue groups, <= 16 q heads per kv head
   if (d.d_model % 8 || d.d_inner % 8 || d.dt_rank % 8 || d.head_dim % 8)
     return HYMBA_ERR_UNSUPPORTED;
-  if (d.n_q_heads / d.n_kv_heads > 16) return HYMBA_ERR_UNSUPPORTED;
-  if (bf16 ? (d.head_dim != 64 && d.head_dim != 128)
-           : (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128))
+  const int grp = d.n_q_heads / d.n_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return HYMBA_ERR_UNSUPPORTED;
+  if (bf16 ? (d.head_dim != 64 && d.head_dim != 128) : (d.head_dim != 32 && d.head_dim != 64))
     return HYMBA_ERR_UNSUPPORTED;
   if (!is_pow2_in(d.d_state, 4, 128)) return HYMBA_ERR_UNSUPPORTED;
   s.d = d.d_model;
@@ -301,10 +301,16 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     return b16 ? launch_gemm_bf16(op, out, shape, stream) : launch_gemm_f32(op, out, stream);
   };
 
-  // 1. in_proj over [meta; X] (meta rows once).
-  {
-    GemmOperands op{meta, s.d, x, s.d, M, w->w_in, s.d, (int)rows, (int)s.n_in, s.d};
-    GemmOutput out{EpiKind::Store, z, s.n_in, z + (size_t)M * s.n_in * s.es, s.n_in, M, 0, nullptr};
+  // 1. in_proj over [meta; X]: the batch-shared meta rows once, then the X rows.
+  if (M > 0) {
+    GemmOperands op{meta, s.d, nullptr, 0, M, w->w_in, s.d, M, (int)s.n_in, s.d};
+    GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, M, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out, GemmShape::Large));
+  }
+  if (BL > 0) {
+    GemmOperands op{x, s.d, nullptr, 0, (int)BL, w->w_in, s.d, (int)BL, (int)s.n_in, s.d};
+    GemmOutput out{EpiKind::Store, z + (size_t)M * s.n_in * s.es, s.n_in, nullptr, 0, (int)BL, 0,
+                   nullptr};
     HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out, GemmShape::Large));
   }
   // 2. producer cache.

@@ -45,19 +45,23 @@ struct Vec8<float> {
   }
 };
 
-// Block-wide sums of two values (256 threads).
+// Block-wide sums of two values (up to 1024 threads).
 __device__ __forceinline__ void block_sum2(float& a, float& b) {
-  __shared__ float ra[4], rb[4];
+  __shared__ float ra[16], rb[16];
   a = wave_sum(a);
   b = wave_sum(b);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
   if (l == 0) {
     ra[w] = a;
     rb[w] = b;
   }
   __syncthreads();
-  a = ra[0] + ra[1] + ra[2] + ra[3];
-  b = rb[0] + rb[1] + rb[2] + rb[3];
+  a = 0.f;
+  b = 0.f;
+  for (int i = 0; i < nw; ++i) {
+    a += ra[i];
+    b += rb[i];
+  }
   __syncthreads();
 }
 
@@ -67,7 +71,8 @@ template <typename T>
 __device__ __forceinline__ void norm_row(T* f, int wa, int ws, const float* ba, const float* bs,
                                          float eps) {
   float sa = 0.f, ss = 0.f;
-  for (int i = threadIdx.x * 8; i < wa + ws; i += 256 * 8) {
+  const int step = blockDim.x * 8;
+  for (int i = threadIdx.x * 8; i < wa + ws; i += step) {
     float v[8];
     Vec8<T>::load(f + i, v);
     float q = 0.f;
@@ -81,7 +86,7 @@ __device__ __forceinline__ void norm_row(T* f, int wa, int ws, const float* ba, 
   block_sum2(sa, ss);
   const float ia = 0.5f * rsqrtf(sa / (float)wa + eps);
   const float is = 0.5f * rsqrtf(ss / (float)ws + eps);
-  for (int i = threadIdx.x * 8; i < wa + ws; i += 256 * 8) {
+  for (int i = threadIdx.x * 8; i < wa + ws; i += step) {
     float v[8];
     Vec8<T>::load(f + i, v);
     const bool att = i < wa;
@@ -116,14 +121,14 @@ hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int
 // Decode: merge split partials (o, m, l) of every q head of sequence b into O, round it
 // to the storage type (as the prefill path stores O), then normalise the row.
 template <typename T>
-__global__ __launch_bounds__(256) void decode_combine_norm_kernel(const float* part, int nsplit,
+__global__ __launch_bounds__(1024) void decode_combine_norm_kernel(const float* part, int nsplit,
                                                                   T* f, int64_t stride, int Hq,
                                                                   int dh, int ws, const float* ba,
                                                                   const float* bs, float eps) {
   const int b = blockIdx.x;
   T* row = f + (int64_t)b * stride;
   const int wa = Hq * dh;
-  for (int e = threadIdx.x; e < wa; e += 256) {
+  for (int e = threadIdx.x; e < wa; e += blockDim.x) {
     const int h = e / dh, d = e % dh;
     const float* ph = part + ((int64_t)b * Hq + h) * nsplit * (dh + 2);
     float mx = -INFINITY;
@@ -148,10 +153,10 @@ hipError_t launch_decode_combine_norm(bool bf16_, const float* part, int nsplit,
                                       hipStream_t s) {
   if (B == 0) return hipSuccess;
   if (bf16_)
-    decode_combine_norm_kernel<bf16><<<dim3(B), dim3(256), 0, s>>>(
+    decode_combine_norm_kernel<bf16><<<dim3(B), dim3(1024), 0, s>>>(
         part, nsplit, (bf16*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
   else
-    decode_combine_norm_kernel<float><<<dim3(B), dim3(256), 0, s>>>(
+    decode_combine_norm_kernel<float><<<dim3(B), dim3(1024), 0, s>>>(
         part, nsplit, (float*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
   return hipGetLastError();
 }

@@ -67,9 +67,9 @@ typedef enum {
   HYMBA_ERR_HIP = 5            /* a HIP launch failed; see hymba_last_hip_error()     */
 } hymba_status;
 
-/* Layer shape.  Supported: head_dim in {32, 64, 128} (bf16: {64, 128}); d_state a
- * multiple of 4 up to 256 (bf16 prefill: 16, 32, 64 or 128); d_model, d_inner,
- * dt_rank, Hq*head_dim multiples of 8; n_q_heads a multiple of n_kv_heads. */
+/* Layer shape.  Supported: head_dim 64 or 128 (bf16) / 32 or 64 (fp32); d_state a power
+ * of two from 4 to 128; n_q_heads / n_kv_heads in {1, 2, 4, 8}; d_model, d_inner,
+ * dt_rank and head_dim multiples of 8. */
 typedef struct {
   int32_t d_model;      /* d                                                      */
   int32_t n_q_heads;    /* Hq                                                     */
