@@ -44,8 +44,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
-                    help="X tokens of the oracle's CPU sample (one sequence)")
+    ap.add_argument("--cpu-seqs", type=int, default=8,
+                    help="sequences of the prefill workload the CPU oracle runs (8 = all)")
     return ap.parse_args()
 
 
@@ -98,9 +98,27 @@ def traffic_for(kernel_stage):
     return rec["bytes_per_launch"] if h == rec["source_sha"] else None
 
 
-def cpu_baseline(tokens):
-    """The oracle (fp64 numpy) on one sequence of the prefill workload, `tokens` X tokens
-    plus the 128 meta tokens."""
+def stage_pass(hy, torch, step, steps, mask):
+    """Run `steps` steps with the stage timers in `mask` on; per-stage average launch time."""
+    torch.cuda.synchronize()
+    for i in range(len(hy.STAGES)):
+        hy.hymba_timer_read(i)
+    hy.hymba_timer_enable(mask)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    hy.hymba_timer_enable(0)
+    out = {}
+    for i, name in enumerate(hy.STAGES):
+        ms, n = hy.hymba_timer_read(i)
+        if n:
+            out[name] = {"avg_ms": ms / n, "per_step": n // steps}
+    return out
+
+
+def cpu_baseline(seqs):
+    """The oracle (fp64 numpy) on `seqs` sequences of the prefill workload (2048 tokens
+    plus the 128 meta tokens each)."""
     import numpy as np
     import oracle as orc
     from synth import CASES, gen_layer_weights, gen_activations
@@ -112,14 +130,16 @@ def cpu_baseline(tokens):
     case = CASES[1]
     dims = case.dims
     w = gen_layer_weights(dims, case.case_id)
-    _, meta, _, x = gen_activations(dims, case.case_id, 1, tokens)
+    _, meta, _, x = gen_activations(dims, case.case_id, seqs, case.seq_len)
     t0 = time.perf_counter()
     orc.prefill(dims, w, meta, x)
     dt = time.perf_counter() - t0
+    tokens = seqs * case.seq_len
     return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"one sequence of the prefill workload: {tokens} tokens + "
-                      f"{dims.n_meta} meta tokens (fp64 numpy), {dt:.1f} s"}
+            "sample": f"{seqs} of the {case.batch} sequences of the prefill workload "
+                      f"({case.seq_len} tokens + {dims.n_meta} meta tokens each, fp64 numpy), "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -158,41 +178,48 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    hy.hymba_timer_enable(True)
+
+    # 1) stage breakdown: every launch bracketed by HIP events (not the timed pass)
+    stages = stage_pass(hy, torch, step, max(3, args.steps // 2), -1)
+    work = stage_work(dims, B, L)
+    dominant = max((n for n in stages if n in work),
+                   key=lambda n: stages[n]["avg_ms"] * stages[n]["per_step"])
+    dom_idx = hy.STAGES.index(dominant)
+
+    # 2) timed pass: K steps between synchronisations, only the dominant kernel's
+    #    launches bracketed by events (on the stream it runs on)
     for i in range(len(hy.STAGES)):
-        hy.hymba_timer_read(i)  # forget warm-up launches
+        hy.hymba_timer_read(i)
+    hy.hymba_timer_enable(1 << dom_idx)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    hy.hymba_timer_enable(False)
-    stages = {}
-    for i, name in enumerate(hy.STAGES):
-        ms, n = hy.hymba_timer_read(i)
-        if n:
-            stages[name] = {"avg_ms": ms / n, "launches": n}
+    hy.hymba_timer_enable(0)
+    dom_ms, dom_n = hy.hymba_timer_read(dom_idx)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = B * L
     value = tokens / (elapsed / args.steps)
     log(f"[bench] prefill {ms_per_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s")
 
-    work = stage_work(dims, B, L)
     stage_report = {}
     for name, rec in stages.items():
+        entry = {"avg_ms": round(rec["avg_ms"], 4), "launches_per_step": rec["per_step"]}
         if name in work:
             bound, wk = work[name]
-            stage_report[name] = {"avg_ms": round(rec["avg_ms"], 4),
-                                  **roofline_entry(bound, wk, rec["avg_ms"])}
-        else:
-            stage_report[name] = {"avg_ms": round(rec["avg_ms"], 4)}
-    dominant = max((n for n in stage_report if n in work), key=lambda n: stage_report[n]["avg_ms"])
+            entry.update(roofline_entry(bound, wk / rec["per_step"], rec["avg_ms"]))
+        stage_report[name] = entry
     bound, wk = work[dominant]
-    roof = roofline_entry(bound, wk, stages[dominant]["avg_ms"])
+    per_launch = wk / stages[dominant]["per_step"]
+    roof = roofline_entry(bound, per_launch, dom_ms / dom_n)
     roof["kernel"] = dominant
+    roof["avg_launch_ms"] = round(dom_ms / dom_n, 4)
+    roof["work_per_launch"] = per_launch
     roof["traffic"] = traffic_for(dominant)
-    log(f"[bench] stages: " + ", ".join(f"{k} {v['avg_ms']:.3f} ms" for k, v in stage_report.items()))
+    log("[bench] stages: " + ", ".join(f"{k} {v['avg_ms']:.3f} ms x{v['launches_per_step']}"
+                                       for k, v in stage_report.items()))
 
     decode = None
     if not args.no_decode:
@@ -201,7 +228,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
-        cpu = cpu_baseline(args.cpu_tokens)
+        cpu = cpu_baseline(args.cpu_seqs)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -258,23 +285,24 @@ def bench_decode(hy, torch, dev, args):
     for s in range(4):  # warm-up steps advance the state like any other step
         layer.decode(xin[steps + s], kvs, sts, y=yout, stream=stream)
     torch.cuda.synchronize()
-    hy.hymba_timer_enable(True)
-    for i in range(len(hy.STAGES)):
-        hy.hymba_timer_read(i)
+    # breakdown on a copy of the state so the timed span starts from the same place
+    saved = {k: v.clone() for k, v in kv.items()}, h.clone(), pos.clone()
+    it = iter(range(32))
+    st_rec = stage_pass(hy, torch, lambda: layer.decode(xin[next(it)], kvs, sts, y=yout,
+                                                         stream=stream), 32, -1)
+    for k, v in saved[0].items():
+        kv[k].copy_(v)
+    h.copy_(saved[1])
+    pos.copy_(saved[2])
+    del saved
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         layer.decode(xin[s], kvs, sts, y=yout, stream=stream)
     torch.cuda.synchronize()
     span = time.perf_counter() - t0
-    hy.hymba_timer_enable(False)
-    st = {}
-    total_kernel_ms = 0.0
-    for i, name in enumerate(hy.STAGES):
-        ms, n = hy.hymba_timer_read(i)
-        if n:
-            st[name] = round(ms / n * 1e3, 2)  # us per step
-            total_kernel_ms += ms
+    st = {name: {"us": round(r["avg_ms"] * 1e3, 2), "launches_per_step": r["per_step"]}
+          for name, r in st_rec.items()}
     # algorithmic bytes per step: weights, ring K/V read, meta K/V, state read + write
     wbytes = 2 * (dims.n_in * dims.d_model + dims.n_xproj * dims.d_inner +
                   dims.d_inner * dims.dt_rank + dims.d_model * dims.f_width)

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhymba.so
 DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE",
           4: "ERR_ALIGNMENT", 5: "ERR_HIP"}
-STAGES = ["in_proj", "attn", "x_proj", "dt_proj", "scan", "norm", "out_proj", "kv_write"]
+STAGES = ["in_proj", "attn", "x_proj", "dt_proj", "scan", "norm", "out_proj", "kv_write",
+          "meta_in_proj", "misc"]
 
 
 class HymbaError(RuntimeError):
@@ -166,8 +167,13 @@ def hymba_layer_decode(desc, weights, x, batch, kv, state, y, workspace, workspa
     return st
 
 
-def hymba_timer_enable(on: bool) -> None:
-    _check(load_library().hymba_timer_enable(1 if on else 0), "hymba_timer_enable")
+def hymba_timer_enable(stage_mask) -> None:
+    """stage_mask: bit i selects stage i (STAGES order); True = all, False/0 = off."""
+    if stage_mask is True:
+        stage_mask = -1
+    elif stage_mask is False:
+        stage_mask = 0
+    _check(load_library().hymba_timer_enable(int(stage_mask)), "hymba_timer_enable")
 
 
 def hymba_timer_read(stage: int):

@@ -9,6 +9,7 @@
 // issued as (B-tile, A-tile) so each lane ends with 4 consecutive output columns of
 // one row, which the epilogue writes with a single vector store.
 // fp32 path: a plain LDS-tiled VALU GEMM with the same epilogues.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -252,6 +253,14 @@ struct DlCfg {
 // land in distinct bank groups for both 8-lane and 16-lane LDS phases.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+  // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A and column (l % 32) of B,
 // 8 consecutive k each (block l / 32); it receives D[(e/4)*8 + (l/32)*4 + e%4][l % 32],
 // e = 0..15.
@@ -381,6 +390,208 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
                             acc[i][j][4 * q + 3]};
         epi(m, n, v, g.M, g.N);
       }
+}
+
+// ------------------------------------------------------------ bf16 few-row GEMM (decode)
+// Few rows (the decode batch): a workgroup owns a 128 x 64 output tile (all rows of its
+// m-block) and one K slice (blockIdx.y, a multiple of 256).  Four LDS stages of 64-k
+// tiles, three in flight ahead of the one being multiplied, keep the weight stream
+// busy.  The MFMA runs un-swapped, so per accumulator element the 64 lanes cover two
+// rows x 32 consecutive columns.  Epilogues: fp32 atomics into an accumulator (when K
+// is split), or the decode in_proj store: Z in bf16 plus the producer's new K/V row
+// at ring slot pos[b] % slots.
+struct FewRowOut {
+  float* acc;        // atomic mode: [M, ldacc] fp32
+  int64_t ldacc;
+  bf16* z;           // store mode: [M, ldz]
+  int64_t ldz;
+  int k_col, v_col;  // store mode: K / V column ranges (k_col < 0: no ring write)
+  bf16* ring_k;
+  bf16* ring_v;
+  int slots, kvw, head_dim, Hkv;
+  const int32_t* pos;
+};
+
+template <bool ATOMIC>
+__global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, FewRowOut out,
+                                                               int kslice) {
+  constexpr int BM = 128, BN = 64, NW = 4, WN = 2;
+  constexpr int TM = BM / 2, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW, INS = A_INS + B_INS;
+  __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sA2[BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sA3[BM * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB2[BN * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB3[BN * 64];
+  bf16* const sa[4] = {sA0, sA1, sA2, sA3};
+  bf16* const sb[4] = {sB0, sB1, sB2, sB3};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.z * BM;
+  const int kb = blockIdx.y * kslice;
+
+  const bf16* A = (const bf16*)g.a0;
+  const bf16* Bm = (const bf16*)g.b;
+  int a_off[A_INS], b_off[B_INS];
+#pragma unroll
+  for (int j = 0; j < A_INS; ++j) {
+    const int r = (j * NW + wave) * 8 + (lane >> 3);
+    a_off[j] = min(m0 + r, g.M - 1) * (int)g.lda0 + ((lane & 7) ^ swz(r)) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j) {
+    const int r = (j * NW + wave) * 8 + (lane >> 3);
+    b_off[j] = min(n0 + r, g.N - 1) * (int)g.ldb + ((lane & 7) ^ swz(r)) * 8;
+  }
+  auto issue = [&](int st, int k0) {
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(A + k0 + a_off[j]),
+                                       (lds_void_t*)(sa[st] + (j * NW + wave) * 512), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(Bm + k0 + b_off[j]),
+                                       (lds_void_t*)(sb[st] + (j * NW + wave) * 512), 16, 0, 0);
+  };
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int rl = lane & 31;
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    koff[ks] = rl * 64 + (((ks * 2 + (lane >> 5)) ^ swz(lane & 15)) * 8);
+  const int a_row0 = wm * TM * 64, b_row0 = wn * TN * 64;
+  auto compute = [&](int st) {
+    const bf16* a = sa[st];
+    const bf16* b = sb[st];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8*)(a + a_row0 + i * 2048 + koff[ks]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *(const bf16x8*)(b + b_row0 + j * 2048 + koff[ks]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // Step t waits for tile t (up to two later tiles may still be in flight), syncs, refills
+  // the stage tile t-1 used with tile t+3, then multiplies tile t.
+  const int KT = kslice / 64;  // multiple of 4
+  issue(0, kb);
+  issue(1, kb + 64);
+  issue(2, kb + 128);
+  auto step = [&](int t, int st) {
+    const int ahead = min(2, KT - 1 - t);
+    if (ahead == 2)
+      wait_vmcnt<2 * INS>();
+    else if (ahead == 1)
+      wait_vmcnt<INS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 3 < KT) issue((st + 3) & 3, kb + (t + 3) * 64);
+    compute(st);
+  };
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(kt, 0);
+    step(kt + 1, 1);
+    step(kt + 2, 2);
+    step(kt + 3, 3);
+  }
+
+  // acc[i][j] = D of the 32 x 32 block: element e of lane l is row (e/4)*8 + (l/32)*4 + e%4,
+  // column l % 32.
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + j * 32 + rl;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * TM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        if (m >= g.M || n >= g.N) continue;
+        if constexpr (ATOMIC) {
+          unsafeAtomicAdd(out.acc + (int64_t)m * out.ldacc + n, acc[i][j][e]);
+        } else {
+          const bf16 v = (bf16)acc[i][j][e];
+          out.z[(int64_t)m * out.ldz + n] = v;
+          if (out.k_col >= 0) {
+            bf16* ring = nullptr;
+            int rel = 0;
+            if (n >= out.k_col && n < out.k_col + out.kvw) {
+              ring = out.ring_k;
+              rel = n - out.k_col;
+            } else if (n >= out.v_col && n < out.v_col + out.kvw) {
+              ring = out.ring_v;
+              rel = n - out.v_col;
+            }
+            if (ring != nullptr) {
+              const int gh = rel / out.head_dim, d = rel % out.head_dim;
+              const int slot = max(out.pos[m], 0) % out.slots;
+              ring[(((int64_t)m * out.Hkv + gh) * out.slots + slot) * out.head_dim + d] = v;
+            }
+          }
+        }
+      }
+    }
+}
+
+static bool fewrow_ok(const GemmOperands& op) {
+  return op.K % 256 == 0 && op.a_split >= op.M && (int64_t)op.M * op.lda0 < (1ll << 31) &&
+         (int64_t)op.N * op.ldb < (1ll << 31);
+}
+
+hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t ldacc,
+                                   int ksplit, hipStream_t s) {
+  if (op.M <= 0 || op.N <= 0) return hipSuccess;
+  if (!fewrow_ok(op)) return hipErrorInvalidValue;
+  const int units = op.K / 256;
+  ksplit = std::max(1, std::min(ksplit, units));
+  const int kslice = ((units + ksplit - 1) / ksplit) * 256;
+  const int ns = (op.K + kslice - 1) / kslice;
+  FewRowOut out{};
+  out.acc = acc;
+  out.ldacc = ldacc;
+  dim3 grid((op.N + 63) / 64, ns, (op.M + 127) / 128);
+  gemm_bf16_fewrow_kernel<true><<<grid, dim3(256), 0, s>>>(op, out, kslice);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t ldz, int k_col,
+                                      int v_col, void* ring_k, void* ring_v, int slots, int Hkv,
+                                      int head_dim, const int32_t* pos, hipStream_t s) {
+  if (op.M <= 0 || op.N <= 0) return hipSuccess;
+  if (!fewrow_ok(op)) return hipErrorInvalidValue;
+  FewRowOut out{};
+  out.z = (bf16*)z;
+  out.ldz = ldz;
+  out.k_col = k_col;
+  out.v_col = v_col;
+  out.ring_k = (bf16*)ring_k;
+  out.ring_v = (bf16*)ring_v;
+  out.slots = slots;
+  out.kvw = Hkv * head_dim;
+  out.head_dim = head_dim;
+  out.Hkv = Hkv;
+  out.pos = pos;
+  dim3 grid((op.N + 63) / 64, 1, (op.M + 127) / 128);
+  gemm_bf16_fewrow_kernel<false><<<grid, dim3(256), 0, s>>>(op, out, op.K);
+  return hipGetLastError();
 }
 
 template <typename Cfg, typename Epi>

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -30,7 +31,7 @@ struct StageTimer {
   std::vector<hipEvent_t> start, stop;
   int used = 0;
 };
-bool g_timer_on = false;
+uint32_t g_timer_mask = 0;
 StageTimer g_timers[HYMBA_NUM_STAGES];
 constexpr int kMaxTimedLaunches = 4096;
 
@@ -39,7 +40,7 @@ struct TimerScope {
   hipStream_t s;
   int idx = -1;
   TimerScope(int stage, hipStream_t stream) : s(stream) {
-    if (!g_timer_on) return;
+    if (!(g_timer_mask & (1u << stage))) return;
     t = &g_timers[stage];
     if (t->used >= kMaxTimedLaunches) {
       t = nullptr;
@@ -107,6 +108,7 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
   if (bf16 ? (d.head_dim != 64 && d.head_dim != 128) : (d.head_dim != 32 && d.head_dim != 64))
     return HYMBA_ERR_UNSUPPORTED;
   if (!is_pow2_in(d.d_state, 4, 128)) return HYMBA_ERR_UNSUPPORTED;
+  if (d.dt_rank > 512) return HYMBA_ERR_UNSUPPORTED;
   s.d = d.d_model;
   s.Hq = d.n_q_heads;
   s.Hkv = d.n_kv_heads;
@@ -136,7 +138,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-  size_t z, delta, bc, dt, f, part, total;
+  size_t z, delta, bc, dt, f, part, xdbl, yacc, total;
 };
 
 constexpr int kDecodeKeysPerSplit = 256;
@@ -145,8 +147,8 @@ int decode_nsplit(const Shape& s, int span_max) {
   return (s.M + span_max + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
 }
 
-// rows = meta rows + batch * tokens (prefill) or batch (decode).
-Carve carve(const Shape& s, int64_t rows, int batch, int nsplit) {
+// Prefill: rows = meta rows + batch * tokens.
+Carve carve_prefill(const Shape& s, int64_t rows) {
   Carve c{};
   size_t off = 0;
   c.z = off;
@@ -159,10 +161,34 @@ Carve carve(const Shape& s, int64_t rows, int batch, int nsplit) {
   off = align_up(off + (size_t)rows * s.Di * 4);
   c.f = off;
   off = align_up(off + (size_t)rows * s.fw * s.es);
-  c.part = off;
-  off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 2) * 4);
   c.total = off;
   return c;
+}
+
+// Decode: one row per sequence.  The fp32 accumulators of the split-K projections
+// (xdbl, yacc) are contiguous and last, so one fill clears them.
+Carve carve_decode(const Shape& s, int batch, int nsplit) {
+  Carve c{};
+  size_t off = 0;
+  c.z = off;
+  off = align_up(off + (size_t)batch * s.n_in * s.es);
+  c.f = off;
+  off = align_up(off + (size_t)batch * s.fw * s.es);
+  c.part = off;
+  off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 2) * 4);
+  c.xdbl = off;
+  off = align_up(off + (size_t)batch * (s.R + 2 * s.N) * 4);
+  c.yacc = off;
+  off = align_up(off + (size_t)batch * s.d * 4);
+  c.total = off;
+  return c;
+}
+
+// K slices for a split-K projection so that the grid holds ~1 workgroup per CU.
+int splitk_factor(int M, int N, int K) {
+  const int tiles = ((N + 63) / 64) * ((M + 127) / 128);
+  const int want = (256 + tiles - 1) / tiles;
+  return std::max(1, std::min(want, K / 256));
 }
 
 bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15) != 0; }
@@ -212,18 +238,18 @@ size_t hymba_layer_workspace_bytes(const hymba_layer_desc* desc, int32_t batch, 
   if (make_shape(desc, s) != HYMBA_OK || batch < 0 || seq_len < 0) return 0;
   if (mode == 0) {
     const int64_t rows = (int64_t)s.M + (int64_t)batch * seq_len;
-    return carve(s, rows, 0, 0).total;
+    return carve_prefill(s, rows).total;
   }
   if (mode == 1) {
     // seq_len carries the ring capacity (slots) for decode.
     const int span_max = s.W > 0 ? std::min(s.W, seq_len) : seq_len;
-    return carve(s, batch, batch, decode_nsplit(s, span_max)).total;
+    return carve_decode(s, batch, decode_nsplit(s, span_max)).total;
   }
   return 0;
 }
 
-hymba_status hymba_timer_enable(int32_t on) {
-  g_timer_on = on != 0;
+hymba_status hymba_timer_enable(int32_t stage_mask) {
+  g_timer_mask = (uint32_t)stage_mask & ((1u << HYMBA_NUM_STAGES) - 1);
   return HYMBA_OK;
 }
 
@@ -286,7 +312,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     if (any_misaligned(state_out->h, state_out->pos)) return HYMBA_ERR_ALIGNMENT;
   }
   if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
-  const Carve cv = carve(s, rows, 0, 0);
+  const Carve cv = carve_prefill(s, rows);
   if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_;
   if (rows == 0) return HYMBA_OK;
@@ -305,7 +331,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   if (M > 0) {
     GemmOperands op{meta, s.d, nullptr, 0, M, w->w_in, s.d, M, (int)s.n_in, s.d};
     GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, M, 0, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out, GemmShape::Large));
+    HYMBA_LAUNCH(HYMBA_STAGE_META, gemm(op, out, GemmShape::Large));
   }
   if (BL > 0) {
     GemmOperands op{x, s.d, nullptr, 0, (int)BL, w->w_in, s.d, (int)BL, (int)s.n_in, s.d};
@@ -409,7 +435,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out, GemmShape::Large));
   }
   if (state_out != nullptr && state_out->pos != nullptr && B > 0) {
-    HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE, launch_fill_i32(state_out->pos, L, B, stream));
+    HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_fill_i32(state_out->pos, L, B, stream));
   }
   return HYMBA_OK;
 }
@@ -434,32 +460,45 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     return HYMBA_ERR_ALIGNMENT;
   const int span_max = s.W > 0 ? s.W : kv->slots;
   const int nsplit = decode_nsplit(s, span_max);
-  const Carve cv = carve(s, B, B, nsplit);
+  const Carve cv = carve_decode(s, B, nsplit);
   if (B > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_;
   if (B == 0) return HYMBA_OK;
 
   char* z = ws_ptr(workspace, cv.z);
-  char* delta = ws_ptr(workspace, cv.delta);
-  float* bc = (float*)ws_ptr(workspace, cv.bc);
-  float* dt = (float*)ws_ptr(workspace, cv.dt);
   char* f = ws_ptr(workspace, cv.f);
   float* part = (float*)ws_ptr(workspace, cv.part);
+  float* xdbl = (float*)ws_ptr(workspace, cv.xdbl);
+  float* yacc = (float*)ws_ptr(workspace, cv.yacc);
   const bool b16 = s.bf16;
+  const int nx = s.R + 2 * s.N;
+
+  // in_proj.  bf16 with K % 64 == 0 everywhere: split-K into fp32 accumulators, then
+  // rounded to Z, the producer's new K/V row landing in the ring in the same pass.
+  // Otherwise the tiled GEMM writes Z directly and a copy kernel fills the ring.
+  const bool splitk = b16 && s.d % 256 == 0 && s.Di % 256 == 0 && s.fw % 256 == 0;
   auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
     return b16 ? launch_gemm_bf16(op, out, GemmShape::Skinny, stream)
                : launch_gemm_f32(op, out, stream);
   };
-
-  {
+  if (splitk) {
+    // clears the x_proj / out_proj accumulators (contiguous after zacc)
+    HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_zero_f32(xdbl, (int64_t)(cv.total - cv.xdbl) / 4,
+                                                   stream));
+    GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
+    HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ,
+                 launch_gemm_bf16_decode_in(op, z, s.n_in, s.share ? -1 : (int)s.k_col,
+                                            (int)s.v_col, kv->k, kv->v, kv->slots, s.Hkv, s.dh,
+                                            state->pos, stream));
+  } else {
     GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
     GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, B, 0, nullptr};
     HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out));
-  }
-  if (!s.share) {
-    HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE,
-                 launch_kv_write_decode(b16, z, s.n_in, (int)s.k_col, (int)s.v_col, kv->k, kv->v,
-                                        kv->slots, state->pos, B, s.Hkv, s.dh, stream));
+    if (!s.share) {
+      HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE,
+                   launch_kv_write_decode(b16, z, s.n_in, (int)s.k_col, (int)s.v_col, kv->k,
+                                          kv->v, kv->slots, state->pos, B, s.Hkv, s.dh, stream));
+    }
   }
   {
     AttnDecodeParams ap{};
@@ -483,25 +522,27 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     ap.scale = s.scale;
     HYMBA_LAUNCH(HYMBA_STAGE_ATTN, launch_attention_decode(b16, ap, stream));
   }
+  // x_proj -> xdbl [B, R + 2N] fp32 (delta, B, C).
   {
-    GemmOperands op{z + s.xs_col * s.es, s.n_in, nullptr, 0, B, w->w_x, s.Di, B, s.R + 2 * s.N,
-                    s.Di};
-    GemmOutput out{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out));
+    GemmOperands op{z + s.xs_col * s.es, s.n_in, nullptr, 0, B, w->w_x, s.Di, B, nx, s.Di};
+    if (splitk) {
+      HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, launch_gemm_bf16_splitk(op, xdbl, nx,
+                                                              splitk_factor(B, nx, s.Di), stream));
+    } else {
+      GemmOutput out{EpiKind::StoreF32, xdbl, nx, nullptr, 0, 0, 0, nullptr};
+      HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out));
+    }
   }
-  {
-    GemmOperands op{delta, s.R, nullptr, 0, B, w->w_dt, s.R, B, s.Di, s.R};
-    GemmOutput out{EpiKind::Softplus, dt, s.Di, nullptr, 0, 0, 0, w->dt_bias};
-    HYMBA_LAUNCH(HYMBA_STAGE_DTPROJ, gemm(op, out));
-  }
+  // dt_proj + softplus + one scan step + gate (h in place, pos += 1).
   {
     SsmStepParams sp{};
     sp.z = z;
     sp.z_stride = s.n_in;
     sp.xs_col = (int)s.xs_col;
     sp.g_col = (int)s.g_col;
-    sp.dt = dt;
-    sp.bc = bc;
+    sp.xdbl = xdbl;
+    sp.w_dt = w->w_dt;
+    sp.dt_bias = w->dt_bias;
     sp.A = w->A;
     sp.D = w->D;
     sp.h = state->h;
@@ -511,6 +552,7 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     sp.B = B;
     sp.Di = s.Di;
     sp.N = s.N;
+    sp.R = s.R;
     HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_ssm_step(b16, sp, stream));
   }
   HYMBA_LAUNCH(HYMBA_STAGE_NORM,
@@ -518,8 +560,15 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
                                           w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
   {
     GemmOperands op{f, s.fw, nullptr, 0, B, w->w_out, s.fw, B, s.d, (int)s.fw};
-    GemmOutput out{EpiKind::Store, y, s.d, nullptr, 0, B, 0, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out));
+    if (splitk) {
+      HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ,
+                   launch_gemm_bf16_splitk(op, yacc, s.d, splitk_factor(B, s.d, (int)s.fw),
+                                           stream));
+      HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_store_rows(true, yacc, y, B, s.d, stream));
+    } else {
+      GemmOutput out{EpiKind::Store, y, s.d, nullptr, 0, B, 0, nullptr};
+      HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out));
+    }
   }
   return HYMBA_OK;
 }

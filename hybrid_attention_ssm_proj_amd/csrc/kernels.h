@@ -46,6 +46,16 @@ enum class GemmShape { Large, Narrow, Skinny };
 hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmShape shape,
                             hipStream_t s);
 hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStream_t s);
+// Few-row (decode) GEMMs, K % 256 == 0, single-source A.
+// acc[M, N] (fp32, row stride ldacc) += A B^T, K split into up to `ksplit` slices that
+// run as separate workgroups and meet through atomics.
+hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t ldacc, int ksplit,
+                                   hipStream_t s);
+// Z = bf16(A B^T) (row stride ldz); with k_col >= 0 the K / V columns of row b are also
+// written to ring slot pos[b] % slots of ring_k / ring_v ([B, Hkv, slots, head_dim]).
+hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t ldz, int k_col,
+                                      int v_col, void* ring_k, void* ring_v, int slots, int Hkv,
+                                      int head_dim, const int32_t* pos, hipStream_t s);
 
 // ----------------------------------------------------------------- attention
 // Keys/values at X~ position j of sequence b: j < n_meta from the meta arrays
@@ -107,19 +117,23 @@ struct ScanParams {
 hipError_t launch_scan_prefill(bool bf16, const ScanParams& p, hipStream_t s);
 
 // Decode: one step per sequence, h updated in place, pos[b] += 1 when pos != nullptr.
+// dt is computed in place from the x_proj output: dt = softplus(delta W_dt^T + b) with
+// delta = xdbl[b, :R] (rounded to bf16 first when round_delta), B = xdbl[b, R:R+N],
+// C = xdbl[b, R+N:R+2N].
 struct SsmStepParams {
   const void* z;
   int64_t z_stride;
   int xs_col, g_col;
-  const float* dt;  // [B, Di]
-  const float* bc;  // [B, 2N]
+  const float* xdbl;    // [B, R + 2N] fp32
+  const void* w_dt;     // [Di, R] storage type
+  const float* dt_bias; // [Di]
   const float* A;
   const float* D;
-  float* h;         // [B, Di, N]
-  void* y;          // row b at y + b*y_stride
+  float* h;             // [B, Di, N]
+  void* y;              // row b at y + b*y_stride
   int64_t y_stride;
   int32_t* pos;
-  int B, Di, N;
+  int B, Di, N, R;
 };
 hipError_t launch_ssm_step(bool bf16, const SsmStepParams& p, hipStream_t s);
 
@@ -148,6 +162,10 @@ hipError_t launch_kv_write_decode(bool bf16, const void* z, int64_t z_stride, in
                                   const int32_t* pos, int B, int Hkv, int head_dim,
                                   hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int n, hipStream_t s);
+// Zero `n` floats (n % 4 == 0, 16-byte aligned).
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// y[B, d] (storage type, row stride y_stride) = acc[B, d] fp32.
+hipError_t launch_store_rows(bool bf16, const float* acc, void* y, int B, int d, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 }  // namespace hymba

@@ -6,6 +6,8 @@
 // Chinese summary's 核心架构 / 实现细节 (RMSNorm per branch, 0.5 average).  The
 // branches have different widths, so F = 0.5 [beta_a rms(O) ; beta_s rms(Y_ssm)] is
 // the concatenation that out_proj consumes.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -268,6 +270,39 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t value, int n) {
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   fill_i32_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(p, value, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(floatx4* p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  zero_f32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>((floatx4*)p, n4);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void store_rows_kernel(const float* acc, T* y, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const floatx4 a = *(const floatx4*)(acc + i);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[i + e] = from_f32<T>(a[e]);
+}
+
+hipError_t launch_store_rows(bool bf16_, const float* acc, void* y, int B, int d, hipStream_t s) {
+  const int64_t n = (int64_t)B * d;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
+  if (bf16_)
+    store_rows_kernel<bf16><<<dim3(blocks), dim3(256), 0, s>>>(acc, (bf16*)y, n);
+  else
+    store_rows_kernel<float><<<dim3(blocks), dim3(256), 0, s>>>(acc, (float*)y, n);
   return hipGetLastError();
 }
 

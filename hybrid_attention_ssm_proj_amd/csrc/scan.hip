@@ -44,6 +44,20 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ void load8v(const bf16* p, float out[8]) {
+  const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8v(const float* p, float out[8]) {
+  const floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    out[e] = a[e];
+    out[4 + e] = b[e];
+  }
+}
+
 __device__ __forceinline__ int64_t seq_row(int t, int b, int n_meta, int L) {
   return t < n_meta ? (int64_t)t : (int64_t)n_meta + (int64_t)b * L + (t - n_meta);
 }
@@ -170,53 +184,84 @@ hipError_t launch_scan_prefill(bool bf16_, const ScanParams& p, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------- decode step
-// Thread per (sequence, channel, group of 4 states); h is read and written once as a
-// float4 per thread.  The thread of state group 0 of channel 0 advances pos[b] after
-// every kernel that reads it has been enqueued before this one.
-template <typename T, int LPC>
+// Workgroup per (block of channels, group of SB sequences); thread per (channel, group
+// of 4 states).  The lanes of a channel share the dt projection
+// dt = softplus(delta . W_dt[c] + b[c]) (delta rounded to the storage type, as the
+// prefill path stores it): each lane streams its slice of W_dt[c] once and accumulates
+// it against the SB sequences' deltas staged in LDS.  Then every sequence advances its
+// states (h read and written once as a float4 per thread).  The thread of state group
+// 0 of channel 0 advances pos[b]: every kernel that reads pos precedes this one.
+template <typename T, int LPC, int SB>
 __global__ __launch_bounds__(256) void ssm_step_kernel(SsmStepParams p) {
   constexpr int NS = 4;
   constexpr int N = NS * LPC;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int sg = (int)(gid % LPC);
-  const int64_t bc_ = gid / LPC;
-  const int c = (int)(bc_ % p.Di);
-  const int b = (int)(bc_ / p.Di);
-  const bool ok = b < p.B;
-  const int bb = ok ? b : 0;
-  const T* z = (const T*)p.z + (int64_t)bb * p.z_stride;
-  const float xv = to_f32(z[p.xs_col + c]);
-  const float gv = to_f32(z[p.g_col + c]);
-  const float dtv = p.dt[(int64_t)bb * p.Di + c];
-  const float* bcr = p.bc + (int64_t)bb * 2 * N;
-  float* hp = p.h + ((int64_t)bb * p.Di + c) * N + sg * NS;
-  const floatx4 hv = *(const floatx4*)hp;
-  const floatx4 av = *(const floatx4*)(p.A + (int64_t)c * N + sg * NS);
-  const float dx = dtv * xv;
-  float acc = 0.f;
-  floatx4 hn;
-#pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    const int n = sg * NS + k;
-    const float a = __builtin_amdgcn_exp2f(dtv * av[k] * kLog2e);
-    hn[k] = fmaf(a, hv[k], dx * bcr[n]);
-    acc = fmaf(hn[k], bcr[N + n], acc);
+  constexpr int CB = 256 / LPC;
+  __shared__ float dl_s[SB][512];  // dt_rank <= 512, checked on the host
+  const int tid = threadIdx.x, sg = tid % LPC;
+  const int c_raw = blockIdx.x * CB + tid / LPC;
+  const bool cok = c_raw < p.Di;
+  const int c = cok ? c_raw : 0;
+  const int b0 = blockIdx.y * SB;
+  const int nb = min(SB, p.B - b0);
+  const int xw = p.R + 2 * N;
+  for (int i = tid; i < SB * p.R; i += 256) {
+    const int bb = i / p.R, r = i % p.R;
+    dl_s[bb][r] = bb < nb ? to_f32(from_f32<T>(p.xdbl[(int64_t)(b0 + bb) * xw + r])) : 0.f;
   }
-  acc = group_sum<LPC>(acc);
-  if (!ok) return;
-  *(floatx4*)hp = hn;
-  if (sg == 0) {
-    const float yv = fmaf(p.D[c], xv, acc);
-    ((T*)p.y)[(int64_t)b * p.y_stride + c] = from_f32<T>(yv * silu_f(gv));
-    if (c == 0 && p.pos != nullptr) p.pos[b] += 1;
+  __syncthreads();
+
+  float part[SB];
+#pragma unroll
+  for (int bb = 0; bb < SB; ++bb) part[bb] = 0.f;
+  const T* wrow = (const T*)p.w_dt + (int64_t)c * p.R;
+  for (int r0 = sg * 8; r0 < p.R; r0 += LPC * 8) {
+    float wv[8];
+    load8v(wrow + r0, wv);
+#pragma unroll
+    for (int bb = 0; bb < SB; ++bb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[bb] = fmaf(dl_s[bb][r0 + e], wv[e], part[bb]);
+  }
+
+  const floatx4 av = *(const floatx4*)(p.A + (int64_t)c * N + sg * NS);
+  const float Dc = p.D[c], bias = p.dt_bias[c];
+#pragma unroll
+  for (int bb = 0; bb < SB; ++bb) {
+    if (bb >= nb) break;  // uniform across the workgroup
+    const int b = b0 + bb;
+    const float dtv = softplus_f(group_sum<LPC>(part[bb]) + bias);
+    const T* z = (const T*)p.z + (int64_t)b * p.z_stride;
+    const float xv = to_f32(z[p.xs_col + c]);
+    const float gv = to_f32(z[p.g_col + c]);
+    const float* xr = p.xdbl + (int64_t)b * xw;
+    float* hp = p.h + ((int64_t)b * p.Di + c) * N + sg * NS;
+    const floatx4 hv = *(const floatx4*)hp;
+    const float dx = dtv * xv;
+    float acc = 0.f;
+    floatx4 hn;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int n = sg * NS + k;
+      const float a = __builtin_amdgcn_exp2f(dtv * av[k] * kLog2e);
+      hn[k] = fmaf(a, hv[k], dx * xr[p.R + n]);
+      acc = fmaf(hn[k], xr[p.R + N + n], acc);
+    }
+    acc = group_sum<LPC>(acc);
+    if (!cok) continue;
+    *(floatx4*)hp = hn;
+    if (sg == 0) {
+      const float yv = fmaf(Dc, xv, acc);
+      ((T*)p.y)[(int64_t)b * p.y_stride + c] = from_f32<T>(yv * silu_f(gv));
+      if (c == 0 && p.pos != nullptr) p.pos[b] += 1;
+    }
   }
 }
 
 template <typename T, int LPC>
 static hipError_t run_step(const SsmStepParams& p, hipStream_t s) {
-  const int64_t threads = (int64_t)p.B * p.Di * LPC;
-  const int64_t blocks = (threads + 255) / 256;
-  ssm_step_kernel<T, LPC><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p);
+  constexpr int SB = 8;
+  const int blocks = (p.Di * LPC + 255) / 256;
+  ssm_step_kernel<T, LPC, SB><<<dim3(blocks, (p.B + SB - 1) / SB), dim3(256), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ typedef enum {
 
 /* Layer shape.  Supported: head_dim 64 or 128 (bf16) / 32 or 64 (fp32); d_state a power
  * of two from 4 to 128; n_q_heads / n_kv_heads in {1, 2, 4, 8}; d_model, d_inner,
- * dt_rank and head_dim multiples of 8. */
+ * dt_rank and head_dim multiples of 8; dt_rank <= 512. */
 typedef struct {
   int32_t d_model;      /* d                                                      */
   int32_t n_q_heads;    /* Hq                                                     */
@@ -167,25 +167,28 @@ int32_t hymba_abi_version(void);
 int32_t hymba_last_hip_error(void);
 
 /* ---------------------------------------------------------------------------
- * Stage timing.  While enabled, every launch of a stage inside the two layer calls
- * is bracketed by a pair of HIP events recorded on the call's stream.
- * hymba_timer_read waits for the recorded events of `stage`, returns the summed
- * milliseconds and the number of launches, and forgets them.  Host-side state; not
- * thread-safe.  At most 4096 launches are remembered per stage between reads.
+ * Stage timing.  hymba_timer_enable(mask) selects stages by bit (1 << stage; -1 = all,
+ * 0 = off).  Every launch of a selected stage inside the two layer calls is then
+ * bracketed by a pair of HIP events recorded on the call's stream.  hymba_timer_read
+ * waits for the recorded events of `stage`, returns the summed milliseconds and the
+ * number of launches, and forgets them.  Host-side state; not thread-safe.  At most
+ * 4096 launches are remembered per stage between reads.
  * ------------------------------------------------------------------------- */
 typedef enum {
-  HYMBA_STAGE_IN_PROJ = 0,   /* in_proj GEMM                                   */
-  HYMBA_STAGE_ATTN = 1,      /* attention (prefill) / split attention (decode) */
-  HYMBA_STAGE_XPROJ = 2,     /* x_proj GEMM: delta, B, C                       */
-  HYMBA_STAGE_DTPROJ = 3,    /* dt_proj GEMM + softplus                        */
-  HYMBA_STAGE_SCAN = 4,      /* selective scan + gate (prefill) / SSM step     */
-  HYMBA_STAGE_NORM = 5,      /* RMSNorm + beta + average                       */
-  HYMBA_STAGE_OUT_PROJ = 6,  /* out_proj GEMM                                  */
-  HYMBA_STAGE_KV_WRITE = 7,  /* cache writes                                   */
-  HYMBA_NUM_STAGES = 8
+  HYMBA_STAGE_IN_PROJ = 0,   /* in_proj GEMM over the X rows (decode: all rows)    */
+  HYMBA_STAGE_ATTN = 1,      /* attention (prefill) / split attention (decode)   */
+  HYMBA_STAGE_XPROJ = 2,     /* x_proj GEMM: delta, B, C                         */
+  HYMBA_STAGE_DTPROJ = 3,    /* dt_proj GEMM + softplus (prefill)                */
+  HYMBA_STAGE_SCAN = 4,      /* selective scan + gate (prefill) / SSM step       */
+  HYMBA_STAGE_NORM = 5,      /* RMSNorm + beta + average                         */
+  HYMBA_STAGE_OUT_PROJ = 6,  /* out_proj GEMM                                    */
+  HYMBA_STAGE_KV_WRITE = 7,  /* cache writes                                     */
+  HYMBA_STAGE_META = 8,      /* in_proj GEMM over the batch-shared meta rows     */
+  HYMBA_STAGE_MISC = 9,      /* accumulator clears, format conversions, pos fill */
+  HYMBA_NUM_STAGES = 10
 } hymba_stage;
 
-hymba_status hymba_timer_enable(int32_t on);
+hymba_status hymba_timer_enable(int32_t stage_mask);
 hymba_status hymba_timer_read(int32_t stage, double *total_ms, int32_t *launches);
 
 /* ---------------------------------------------------------------------------
