@@ -36,6 +36,16 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then
+// s_barrier.  __syncthreads(), and any release fence covering LDS, also drains every
+// outstanding vector-memory operation including global_load_lds DMA (vmcnt(0)), which
+// would empty a prefetch pipeline at every barrier.  Code reading DMA'd data waits for
+// it explicitly (s_waitcnt vmcnt(N)) before calling this.  The memory clobber keeps
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

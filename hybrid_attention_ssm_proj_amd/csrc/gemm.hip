@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
       wait_vmcnt<INS>();
     else
       wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();  // keeps the younger tiles in flight
     if (t + 3 < KT) issue((st + 3) & 3, kb + (t + 3) * 64);
     compute(st);
   };

@@ -147,7 +147,10 @@ int decode_nsplit(const Shape& s, int span_max) {
   return (s.M + span_max + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
 }
 
-// Prefill: rows = meta rows + batch * tokens.
+bool fused_dt(const Shape& s) { return s.bf16 && scan_fused_supported(s.N, s.R, s.Di); }
+
+// Prefill: rows = meta rows + batch * tokens.  dt is materialised only when the scan
+// does not compute it in place.
 Carve carve_prefill(const Shape& s, int64_t rows) {
   Carve c{};
   size_t off = 0;
@@ -158,7 +161,7 @@ Carve carve_prefill(const Shape& s, int64_t rows) {
   c.bc = off;
   off = align_up(off + (size_t)rows * 2 * s.N * 4);
   c.dt = off;
-  off = align_up(off + (size_t)rows * s.Di * 4);
+  if (!fused_dt(s)) off = align_up(off + (size_t)rows * s.Di * 4);
   c.f = off;
   off = align_up(off + (size_t)rows * s.fw * s.es);
   c.total = off;
@@ -394,8 +397,9 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     GemmOutput out{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
     HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out, GemmShape::Narrow));
   }
-  // 5. dt_proj + softplus.
-  {
+  // 5. dt_proj + softplus (unless the scan computes it in place).
+  const bool fuse = fused_dt(s);
+  if (!fuse) {
     GemmOperands op{delta, s.R, nullptr, 0, (int)rows, w->w_dt, s.R, (int)rows, s.Di, s.R};
     GemmOutput out{EpiKind::Softplus, dt, s.Di, nullptr, 0, 0, 0, w->dt_bias};
     HYMBA_LAUNCH(HYMBA_STAGE_DTPROJ, gemm(op, out, GemmShape::Narrow));
@@ -423,7 +427,12 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
       sp.B = 1;
       sp.h_out = nullptr;
     }
-    HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill(b16, sp, stream));
+    if (fuse) {
+      HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill_fused(sp, delta, w->w_dt, w->dt_bias,
+                                                               s.R, stream));
+    } else {
+      HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill(b16, sp, stream));
+    }
   }
   // 7. RMSNorm + beta + average, in place.
   HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,

@@ -115,6 +115,11 @@ struct ScanParams {
   int n_meta, L, B, Di, N;
 };
 hipError_t launch_scan_prefill(bool bf16, const ScanParams& p, hipStream_t s);
+// bf16 prefill scan with the dt projection fused in (ScanParams::dt unused): dt =
+// softplus(delta W_dt^T + dt_bias) with delta [rows, R] bf16, W_dt [Di, R] bf16.
+bool scan_fused_supported(int N, int R, int Di);
+hipError_t launch_scan_prefill_fused(const ScanParams& p, const void* delta, const void* w_dt,
+                                     const float* dt_bias, int R, hipStream_t s);
 
 // Decode: one step per sequence, h updated in place, pos[b] += 1 when pos != nullptr.
 // dt is computed in place from the x_proj output: dt = softplus(delta W_dt^T + b) with

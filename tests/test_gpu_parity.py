@@ -136,6 +136,23 @@ def test_small_bf16_prefill_state_sizes(d_state):
     check_prefill(dims, g, ref, TOL_BF16, TOL_H)
 
 
+@pytest.mark.parametrize("d_state,dt_rank,L,M,B", [
+    (16, 128, 77, 16, 2),    # ragged last chunk, meta prefix inside the first chunk
+    (128, 64, 45, 40, 1),    # meta prefix spanning two chunks
+    (32, 64, 64, 8, 3),      # exact chunk multiple
+    (64, 128, 100, 0, 2),    # no meta tokens
+])
+def test_small_bf16_prefill_fused_dt_scan(d_state, dt_rank, L, M, B):
+    """Shapes whose dt projection runs inside the scan kernel (dt_rank 64 or 128)."""
+    dims = small_dims(d_state=d_state, dt_rank=dt_rank, n_meta=M, window=30, d_inner=512)
+    cid = 75 + d_state + dt_rank + M
+    w = gen_layer_weights(dims, cid)
+    meta_t, meta, x_t, x = gen_activations(dims, cid, B, L)
+    ref = orc.prefill(dims, w, meta, x, contract=True)
+    g = gpu_prefill(dims, w, meta_t, x_t)
+    check_prefill(dims, g, ref, TOL_BF16, TOL_H)
+
+
 def test_small_bf16_kv_share_pair():
     """Producer then consumer; the consumer reads the producer's cache, takes the
     producer's y as its X and y_meta as its meta rows.
