@@ -45,6 +45,40 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Transpose-reduction over groups of LPC lanes: lane j of a group holds partials
+// v[0..LPC) for LPC tokens; afterwards it holds the group's total for token j.  Each
+// stage halves the list: the lane keeps the half matching its bit and adds what its
+// partner (lane ^ 2^s) sends for that half.
+template <int LPC>
+__device__ __forceinline__ float transpose_reduce(float (&v)[LPC], int sg) {
+  if constexpr (LPC == 1) {
+    return v[0];
+  } else {
+    int n = LPC;
+#pragma unroll
+    for (int st = 0; (1 << st) < LPC; ++st) {
+      const bool bit = (sg >> st) & 1;
+#pragma unroll
+      for (int i = 0; i < LPC / 2; ++i) {
+        if (2 * i + 1 < n) {
+          const float keep = bit ? v[2 * i + 1] : v[2 * i];
+          const float send = bit ? v[2 * i] : v[2 * i + 1];
+          float recv;
+          if ((1 << st) == 1)
+            recv = dpp<0xB1>(send);
+          else if ((1 << st) == 2)
+            recv = dpp<0x4E>(send);
+          else
+            recv = __shfl_xor(send, 1 << st, 64);
+          v[i] = keep + recv;
+        }
+      }
+      n >>= 1;
+    }
+    return v[0];
+  }
+}
+
 __device__ __forceinline__ int64_t seq_row(int t, int b, int n_meta, int L) {
   return t < n_meta ? (int64_t)t : (int64_t)n_meta + (int64_t)b * L + (t - n_meta);
 }
@@ -185,39 +219,54 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ch = rbk * 16 + (lane >> 4) * 4 + i;
-        dt_s[tt * C::DTP + ch] = softplus_f(acc[i] + bias_s[ch]);
+        dt_s[tt * C::DTP + ch] = tt < tn ? softplus_f(acc[i] + bias_s[ch]) : 0.f;
       }
     }
     for (int e = tid; e < C::XE; e += 256) gate_s[e] = silu_f((float)gs(cur)[e]);
     lds_barrier();  // the next chunk's loads stay in flight
 
+    // Tokens in groups of LPC: all LDS reads of a group are issued before its state
+    // updates; the transpose-reduction then leaves lane sg with the full state sum of
+    // token g0 + sg, so every lane finishes one token's output.  Tokens past the chunk
+    // have dt = 0 and leave h unchanged.
     const bf16* xc = xs(cur);
     const float* bcc = bcs(cur);
-    for (int tt = 0; tt < tn; ++tt) {
-      const float dtv = dt_s[tt * C::DTP + cl];
-      const float xv = (float)xc[tt * CB + cl];
-      const float* brow = bcc + tt * 2 * N + sg * NS;
-      float bv[NS], cv[NS];
+    for (int g0 = 0; g0 < tn; g0 += LPC) {
+      float dtv[LPC], xv[LPC], bv[LPC][NS], cv[LPC][NS];
 #pragma unroll
-      for (int k4 = 0; k4 < NS; k4 += 4) {
-        const floatx4 b4 = *(const floatx4*)(brow + k4);
-        const floatx4 c4 = *(const floatx4*)(brow + N + k4);
+      for (int u = 0; u < LPC; ++u) {
+        const int tt = g0 + u;
+        dtv[u] = dt_s[tt * C::DTP + cl];
+        xv[u] = (float)xc[tt * CB + cl];
+        const float* brow = bcc + tt * 2 * N + sg * NS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bv[k4 + e] = b4[e];
-          cv[k4 + e] = c4[e];
+        for (int k4 = 0; k4 < NS; k4 += 4) {
+          const floatx4 b4 = *(const floatx4*)(brow + k4);
+          const floatx4 c4 = *(const floatx4*)(brow + N + k4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bv[u][k4 + e] = b4[e];
+            cv[u][k4 + e] = c4[e];
+          }
         }
       }
-      const float dx = dtv * xv;
-      float acc = 0.f;
+      float part[LPC];
 #pragma unroll
-      for (int kk = 0; kk < NS; ++kk) {
-        const float a = __builtin_amdgcn_exp2f(dtv * A2[kk]);
-        h[kk] = fmaf(a, h[kk], dx * bv[kk]);
-        acc = fmaf(h[kk], cv[kk], acc);
+      for (int u = 0; u < LPC; ++u) {
+        const float dx = dtv[u] * xv[u];
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NS; ++kk) {
+          const float a = __builtin_amdgcn_exp2f(dtv[u] * A2[kk]);
+          h[kk] = fmaf(a, h[kk], dx * bv[u][kk]);
+          acc = fmaf(h[kk], cv[u][kk], acc);
+        }
+        part[u] = acc;
       }
-      acc = group_sum<LPC>(acc);
-      if (sg == 0) y_s[tt * CB + cl] = (bf16)(fmaf(Dc, xv, acc) * gate_s[tt * CB + cl]);
+      const float tot = transpose_reduce<LPC>(part, sg);
+      const int tt = g0 + sg;
+      const float xt = (float)xc[tt * CB + cl];
+      y_s[tt * CB + cl] = (bf16)(fmaf(Dc, xt, tot) * gate_s[tt * CB + cl]);
     }
     lds_barrier();
 
