@@ -149,7 +149,10 @@ def attention(Q, K, V, qpos, kpos, n_meta: int, window: int, scale: float,
     [HYMBA-SUM] Design formulation, attention-head equation (an input-dependent
     mixing matrix over tokens); GQA from [HYMBA-ZH] 跨层KV缓存共享.
     Query rows are independent, so they are processed `q_block` at a time only to
-    bound memory.
+    bound memory; each block scores only the keys that the visibility rule can admit
+    for some query of the block (meta keys and keys inside the block's causal/window
+    span).  Every excluded key is masked for every query of the block, so its softmax
+    weight is exactly zero either way: the result is the same definition.
     """
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
@@ -159,19 +162,22 @@ def attention(Q, K, V, qpos, kpos, n_meta: int, window: int, scale: float,
     O = np.zeros((Tq, Hq, V.shape[2]))
     probs = np.zeros((Hq, Tq, K.shape[0])) if return_probs else None
     qpos = np.asarray(qpos)
+    kpos = np.asarray(kpos)
     for q0 in range(0, Tq, q_block):
         q1 = min(Tq, q0 + q_block)
-        mask = visible(qpos[q0:q1], kpos, n_meta, window)
+        block_vis = visible(qpos[q0:q1], kpos, n_meta, window).any(axis=0)
+        keys = np.nonzero(block_vis)[0]
+        mask = visible(qpos[q0:q1], kpos[keys], n_meta, window)
         for h in range(Hq):
             g = (h * Hkv) // Hq
-            S = scale * (Q[q0:q1, h, :] @ K[:, g, :].T)
+            S = scale * (Q[q0:q1, h, :] @ K[keys, g, :].T)
             S = np.where(mask, S, -np.inf)
             m = S.max(axis=1, keepdims=True)
             P = np.exp(S - m)
             P /= P.sum(axis=1, keepdims=True)
-            O[q0:q1, h, :] = P @ V[:, g, :]
+            O[q0:q1, h, :] = P @ V[keys, g, :]
             if return_probs:
-                probs[h, q0:q1] = P
+                probs[h, q0:q1, keys] = P
     if return_probs:
         return O, probs
     return O
