@@ -177,7 +177,7 @@ def attention(Q, K, V, qpos, kpos, n_meta: int, window: int, scale: float,
             P /= P.sum(axis=1, keepdims=True)
             O[q0:q1, h, :] = P @ V[keys, g, :]
             if return_probs:
-                probs[h, q0:q1, keys] = P
+                probs[h, q0:q1][:, keys] = P
     if return_probs:
         return O, probs
     return O
