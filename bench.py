@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the prefill workload the CPU oracle runs (8 = all)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the prefill pass, copy BYTES once with the library's copy "
+                         "kernel (the known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -59,7 +62,9 @@ def stage_work(dims, B, L):
     pairs_meta = M * (M + 1) // 2
     attn_flops = 4 * dims.head_dim * dims.n_q_heads * (B * pairs_seq + pairs_meta)
     return {
-        "in_proj": ("mfma", 2.0 * rows * dims.n_in * d),
+        # the meta rows are projected once, by their own launch
+        "meta_in_proj": ("mfma", 2.0 * M * dims.n_in * d),
+        "in_proj": ("mfma", 2.0 * B * L * dims.n_in * d),
         "attn": ("mfma", float(attn_flops)),
         "x_proj": ("mfma", 2.0 * rows * dims.n_xproj * Di),
         "dt_proj": ("mfma", 2.0 * rows * Di * R),
@@ -93,9 +98,10 @@ def traffic_for(kernel_stage):
         return None
     if not rec:
         return None
-    src = os.path.join(ROOT, "hybrid_attention_ssm_proj_amd", "csrc", rec["source"])
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return rec["bytes_per_launch"] if h == rec["source_sha"] else None
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        h.update(open(os.path.join(ROOT, "hybrid_attention_ssm_proj_amd", "csrc", name), "rb").read())
+    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha"] else None
 
 
 def stage_pass(hy, torch, step, steps, mask):
@@ -221,6 +227,16 @@ def main():
     log("[bench] stages: " + ", ".join(f"{k} {v['avg_ms']:.3f} ms x{v['launches_per_step']}"
                                        for k, v in stage_report.items()))
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        hy.hymba_op_copy(src, dst, n, stream=stream)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes")
+        del src, dst
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(hy, torch, dev, args)
@@ -287,9 +303,10 @@ def bench_decode(hy, torch, dev, args):
     torch.cuda.synchronize()
     # breakdown on a copy of the state so the timed span starts from the same place
     saved = {k: v.clone() for k, v in kv.items()}, h.clone(), pos.clone()
-    it = iter(range(32))
+    n_break = min(32, steps)
+    it = iter(range(n_break))
     st_rec = stage_pass(hy, torch, lambda: layer.decode(xin[next(it)], kvs, sts, y=yout,
-                                                         stream=stream), 32, -1)
+                                                         stream=stream), n_break, -1)
     for k, v in saved[0].items():
         kv[k].copy_(v)
     h.copy_(saved[1])

@@ -50,8 +50,15 @@ def test_workspace_sizes(lib):
     rows = 128 + 8 * 2048
     n_in = 16 * 128 + 2 * 4 * 128 + 2 * 4096
     got = hy.hymba_layer_workspace_bytes(d, 8, 2048, 0)
-    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 4096 * 4 + 6144 * 2)
+    # Z, delta (bf16), B|C (fp32), F (bf16); this shape computes dt inside the scan
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2)
     assert floor <= got <= floor + 8 * 256
+    # fp32 layers keep a separate fp32 dt buffer
+    d0 = desc_of(0)
+    rows0 = 8 + 64
+    floor0 = rows0 * 4 * (4 * 32 + 2 * 2 * 32 + 2 * 256 + 8 + 32 + 256 + 128 + 256)
+    got0 = hy.hymba_layer_workspace_bytes(d0, 1, 64, 0)
+    assert floor0 <= got0 <= floor0 + 8 * 256
     assert hy.hymba_layer_workspace_bytes(d, 128, 1024, 1) > 0
     assert hy.hymba_layer_workspace_bytes(d, -1, 10, 0) == 0
     assert hy.hymba_layer_workspace_bytes(d, 1, 10, 7) == 0
