@@ -482,9 +482,10 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   const bool b16 = s.bf16;
   const int nx = s.R + 2 * s.N;
 
-  // in_proj.  bf16 with K % 64 == 0 everywhere: split-K into fp32 accumulators, then
-  // rounded to Z, the producer's new K/V row landing in the ring in the same pass.
-  // Otherwise the tiled GEMM writes Z directly and a copy kernel fills the ring.
+  // in_proj.  bf16 with every K a multiple of 256: the few-row GEMM writes Z and the
+  // producer's new K/V row into its ring slot in the same pass, and x_proj / out_proj
+  // run split-K into fp32 accumulators.  Otherwise the tiled GEMM writes Z directly and
+  // a copy kernel fills the ring.
   const bool splitk = b16 && s.d % 256 == 0 && s.Di % 256 == 0 && s.fw % 256 == 0;
   auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
     return b16 ? launch_gemm_bf16(op, out, GemmShape::Skinny, stream)
