@@ -68,8 +68,9 @@ def stage_work(dims, B, L):
         "attn": ("mfma", float(attn_flops)),
         "x_proj": ("mfma", 2.0 * rows * dims.n_xproj * Di),
         "dt_proj": ("mfma", 2.0 * rows * Di * R),
-        # bytes: x, G (bf16), dt (fp32), y (bf16) per (row, channel); B, C per row; h once
-        "scan": ("hbm", float(rows * (Di * 10 + 8 * N) + B * Di * N * 4)),
+        # bytes: x, G, y (bf16) per (row, channel), delta (bf16) and B, C (fp32) per row,
+        # h once; dt is computed in the scan and never stored
+        "scan": ("hbm", float(rows * (Di * 6 + 2 * R + 8 * N) + B * Di * N * 4)),
         # bytes: read O and Y_ssm, write F (bf16)
         "norm": ("hbm", float(rows * (qw + Di) * 2 * 2)),
         "out_proj": ("mfma", 2.0 * rows * dims.f_width * d),

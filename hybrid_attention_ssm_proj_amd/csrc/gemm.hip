@@ -233,8 +233,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_kernel(GemmOperands g, Epi 
 // wave instruction fills 1 KB of LDS = 8 rows x 64 k), so no VGPR staging and no LDS
 // store instructions.  Row r of a tile keeps its 8 16-byte k-chunks XOR-swizzled by
 // f(r) = (r & 7) ^ ((r >> 3) & 1): the 16 rows an MFMA fragment read touches then hit
-// distinct bank groups for both 16-lane and 8-lane LDS phases.  Two stages live in
-// distinct LDS arrays so the compiler can tell in-flight DMA from fragment reads.
+// distinct bank groups for both 16-lane and 8-lane LDS phases.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
@@ -269,10 +268,24 @@ __device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8& a, const bf16x8& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// K % 64 == 0.  Two LDS stages of BM x 64 and BN x 64 filled by global_load_lds_dwordx4
-// (one wave instruction = 8 rows x 128 contiguous bytes, the L2-friendliest request
-// pattern measured); the next k-tile streams in while the current one is multiplied.
-// The stages are distinct LDS arrays so in-flight DMA and fragment reads never alias.
+// global_load_lds_dwordx4 of one 16-byte chunk per lane into the wave's 1 KB LDS block
+// at `lptr`, issued from inline asm.  The compiler does not see this LDS write, so it
+// adds no conservative vmcnt waits in front of LDS reads of the other stage (it cannot
+// separate the two stages once a transfer is in flight across the loop back-edge).
+// Every consumer waits explicitly (wait_vmcnt) and then passes a workgroup barrier.
+// The instruction has no VGPR result; its address operands are read at issue.
+__device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lptr) {
+  const uint32_t l = (uint32_t)(uintptr_t)lptr;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(gptr) : "memory", "m0");
+}
+
+// K % 64 == 0.  Two LDS stages of BM x 64 and BN x 64.  Per k-tile t: fragments of
+// k-substeps 1..3 are read one substep ahead of the MFMAs; before the last substep's
+// MFMAs every wave waits for tile t+1 to land, passes a barrier (after which nobody
+// reads tile t's stage), refills that stage with tile t+2 and reads tile t+1's first
+// fragments, so the barrier, the DMA issue and the LDS latency hide behind the last
+// 16 MFMAs of the tile.  Each transfer has one full k-tile of MFMA work to land.
 template <typename Cfg, typename Epi>
 __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, Epi epi) {
   __shared__ __attribute__((aligned(1024))) bf16 sA0[Cfg::BM * 64];
@@ -310,12 +323,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
   auto issue = [&](bf16* sa, bf16* sb, int k0) {
 #pragma unroll
     for (int j = 0; j < Cfg::A_INS; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(A + k0 + a_off[j]),
-                                       (lds_void_t*)(sa + (j * Cfg::NW + wave) * 512), 16, 0, 0);
+      dma16(A + k0 + a_off[j], (lds_void_t*)(sa + (j * Cfg::NW + wave) * 512));
 #pragma unroll
     for (int j = 0; j < Cfg::B_INS; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(Bm + k0 + b_off[j]),
-                                       (lds_void_t*)(sb + (j * Cfg::NW + wave) * 512), 16, 0, 0);
+      dma16(Bm + k0 + b_off[j], (lds_void_t*)(sb + (j * Cfg::NW + wave) * 512));
   };
 
   floatx16 acc[Cfg::FM][Cfg::FN];
@@ -334,47 +345,67 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
   for (int ks = 0; ks < 4; ++ks)
     koff[ks] = rl * 64 + (((ks * 2 + (lane >> 5)) ^ swz(lane & 15)) * 8);
   const int a_row0 = wm * Cfg::TM * 64, b_row0 = wn * Cfg::TN * 64;
-
-  auto compute = [&](const bf16* sa, const bf16* sb) {
-    bf16x8 af[2][Cfg::FM], bfr[2][Cfg::FN];
-    auto load = [&](int buf, int ks) {
+  bf16x8 af[2][Cfg::FM], bfr[2][Cfg::FN];
+  auto load = [&](const bf16* sa, const bf16* sb, int buf, int ks) {
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-        af[buf][i] = *(const bf16x8*)(sa + a_row0 + i * 2048 + koff[ks]);
+    for (int i = 0; i < Cfg::FM; ++i)
+      af[buf][i] = *(const bf16x8*)(sa + a_row0 + i * 2048 + koff[ks]);
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+      bfr[buf][j] = *(const bf16x8*)(sb + b_row0 + j * 2048 + koff[ks]);
+  };
+  auto mm = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
-        bfr[buf][j] = *(const bf16x8*)(sb + b_row0 + j * 2048 + koff[ks]);
-    };
-    load(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) load((ks + 1) & 1, ks + 1);
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          acc[i][j] = mfma32x32x16(bfr[ks & 1][j], af[ks & 1][i], acc[i][j]);
-    }
+        acc[i][j] = mfma32x32x16(bfr[buf][j], af[buf][i], acc[i][j]);
   };
 
-  // Two k-tiles per trip, one stage each; a single loop exit keeps the accumulators
-  // in place (an odd last tile runs after the loop).
   const int KT = g.K / 64;
   issue(sA0, sB0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    issue(sA1, sB1, (kt + 1) * 64);
-    compute(sA0, sB0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (kt + 2 < KT) issue(sA0, sB0, (kt + 2) * 64);
-    compute(sA1, sB1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+  wait_vmcnt<0>();
+  lds_barrier();
+  if (KT > 1) issue(sA1, sB1, 64);
+  load(sA0, sB0, 0, 0);
+  // Two k-tiles per trip (stage 0, then stage 1); a single loop exit keeps the
+  // accumulators in place, an odd last tile runs after the loop.
+  int t = 0;
+  for (; t + 1 < KT; t += 2) {
+    load(sA0, sB0, 1, 1);
+    mm(0);
+    load(sA0, sB0, 0, 2);
+    mm(1);
+    load(sA0, sB0, 1, 3);
+    mm(0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 2 < KT) issue(sA0, sB0, (t + 2) * 64);
+    load(sA1, sB1, 0, 0);
+    mm(1);
+    load(sA1, sB1, 1, 1);
+    mm(0);
+    load(sA1, sB1, 0, 2);
+    mm(1);
+    load(sA1, sB1, 1, 3);
+    mm(0);
+    if (t + 2 < KT) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (t + 3 < KT) issue(sA1, sB1, (t + 3) * 64);
+      load(sA0, sB0, 0, 0);
+    }
+    mm(1);
   }
-  if (kt < KT) compute(sA0, sB0);
+  if (t < KT) {
+    load(sA0, sB0, 1, 1);
+    mm(0);
+    load(sA0, sB0, 0, 2);
+    mm(1);
+    load(sA0, sB0, 1, 3);
+    mm(0);
+    mm(1);
+  }
 
   // acc[i][j] holds C^T of the 32 x 32 block: lane -> row rl, columns
   // (e/4)*8 + (lane/32)*4 + 0..3.
@@ -634,7 +665,7 @@ static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShap
           // 256 x 256 tiles when they fill the chip several times over, else 256 x 128
           const long t256 = (long)((op.M + 255) / 256) * ((op.N + 255) / 256);
           if (t256 >= 4 * 256) return run_bf16_dl<DlCfg<256, 256, 2, 2>>(op, epi, s);
-          return run_bf16_dl<DlCfg<256, 128, 2, 2>>(op, epi, s);
+          return run_bf16_dl<DlCfg<256, 128, 2, 4>>(op, epi, s);
         }
         return run_bf16<CfgLarge>(op, epi, s);
       } else {
