@@ -424,15 +424,15 @@ struct Chunk<float> {
 
 }  // namespace
 
-template <typename T, int DH, int GQ>
+template <typename T, int DH, int GQ, int KPS>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
   constexpr int E = Chunk<T>::E;     // elements per 16-byte chunk
   constexpr int LPK = DH / E;        // lanes per key
   constexpr int KPI = 64 / LPK;      // keys per wave instruction
-  constexpr int KPS = 256;           // keys per split
   constexpr int KPW = KPS / 4;       // keys per wave
   constexpr int NI = KPW / KPI;      // instructions per wave
   static_assert(LPK >= 4 && LPK <= 16, "lane grouping");
+  static_assert(KPS % (4 * KPI) == 0 && KPS % 64 == 0, "keys per split");
   __shared__ float s_s[GQ][KPS];
   __shared__ float mstat[GQ], lstat[GQ];
   __shared__ float o_s[4][GQ][DH];
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
   for (int i = tid; i < GQ * DH; i += 256) {
     const int h = i / DH, d = i % DH;
     const float sum = o_s[0][h][d] + o_s[1][h][d] + o_s[2][h][d] + o_s[3][h][d];
-    float* dst = p.part + (((int64_t)b * p.Hq + h0 + h) * p.nsplit + split) * (DH + 2);
+    float* dst = p.part + (((int64_t)b * p.Hq + h0 + h) * p.nsplit + split) * (DH + 4);
     dst[d] = nk > 0 ? sum : 0.f;
     if (d == 0) {
       dst[DH] = nk > 0 ? mstat[h] : -INFINITY;
@@ -558,17 +558,27 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
   }
 }
 
-template <typename T, int DH>
-static hipError_t run_decode(const AttnDecodeParams& p, hipStream_t s) {
+template <typename T, int DH, int KPS>
+static hipError_t run_decode_kps(const AttnDecodeParams& p, hipStream_t s) {
   dim3 grid(p.nsplit, p.Hkv, p.B);
   switch (p.Hq / p.Hkv) {
-    case 1: attn_decode_kernel<T, DH, 1><<<grid, dim3(256), 0, s>>>(p); break;
-    case 2: attn_decode_kernel<T, DH, 2><<<grid, dim3(256), 0, s>>>(p); break;
-    case 4: attn_decode_kernel<T, DH, 4><<<grid, dim3(256), 0, s>>>(p); break;
-    case 8: attn_decode_kernel<T, DH, 8><<<grid, dim3(256), 0, s>>>(p); break;
+    case 1: attn_decode_kernel<T, DH, 1, KPS><<<grid, dim3(256), 0, s>>>(p); break;
+    case 2: attn_decode_kernel<T, DH, 2, KPS><<<grid, dim3(256), 0, s>>>(p); break;
+    case 4: attn_decode_kernel<T, DH, 4, KPS><<<grid, dim3(256), 0, s>>>(p); break;
+    case 8: attn_decode_kernel<T, DH, 8, KPS><<<grid, dim3(256), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T, int DH>
+static hipError_t run_decode(const AttnDecodeParams& p, hipStream_t s) {
+  switch (p.keys_per_split) {
+    case 128: return run_decode_kps<T, DH, 128>(p, s);
+    case 192: return run_decode_kps<T, DH, 192>(p, s);
+    case 256: return run_decode_kps<T, DH, 256>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attention_decode(bool bf16_, const AttnDecodeParams& p, hipStream_t s) {

@@ -441,6 +441,8 @@ struct FewRowOut {
   bf16* ring_v;
   int slots, kvw, head_dim, Hkv;
   const int32_t* pos;
+  floatx4* zero;     // store mode: accumulators cleared by the grid (zero_n4 vectors)
+  int64_t zero_n4;
 };
 
 template <bool ATOMIC>
@@ -466,6 +468,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
   const int wm = wave / WN, wn = wave % WN;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.z * BM;
   const int kb = blockIdx.y * kslice;
+  if constexpr (!ATOMIC) {
+    const int64_t nblk = (int64_t)gridDim.x * gridDim.z;
+    for (int64_t i = (blockIdx.z * (int64_t)gridDim.x + blockIdx.x) * 256 + tid; i < out.zero_n4;
+         i += nblk * 256)
+      out.zero[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const bf16* A = (const bf16*)g.a0;
   const bf16* Bm = (const bf16*)g.b;
@@ -483,12 +491,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
   auto issue = [&](int st, int k0) {
 #pragma unroll
     for (int j = 0; j < A_INS; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(A + k0 + a_off[j]),
-                                       (lds_void_t*)(sa[st] + (j * NW + wave) * 512), 16, 0, 0);
+      dma16(A + k0 + a_off[j], (lds_void_t*)(sa[st] + (j * NW + wave) * 512));
 #pragma unroll
     for (int j = 0; j < B_INS; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(Bm + k0 + b_off[j]),
-                                       (lds_void_t*)(sb[st] + (j * NW + wave) * 512), 16, 0, 0);
+      dma16(Bm + k0 + b_off[j], (lds_void_t*)(sb[st] + (j * NW + wave) * 512));
   };
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -506,17 +512,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
   auto compute = [&](int st) {
     const bf16* a = sa[st];
     const bf16* b = sb[st];
+    bf16x8 af[2][FM], bfr[2][FN];
+    auto frag = [&](int buf, int ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[buf][i] = *(const bf16x8*)(a + a_row0 + i * 2048 + koff[ks]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[buf][j] = *(const bf16x8*)(b + b_row0 + j * 2048 + koff[ks]);
+    };
+    frag(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8*)(a + a_row0 + i * 2048 + koff[ks]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *(const bf16x8*)(b + b_row0 + j * 2048 + koff[ks]);
+      if (ks + 1 < 4) frag((ks + 1) & 1, ks + 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = mfma32x32x16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j]);
     }
   };
 
@@ -605,10 +616,13 @@ hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t l
 
 hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t ldz, int k_col,
                                       int v_col, void* ring_k, void* ring_v, int slots, int Hkv,
-                                      int head_dim, const int32_t* pos, hipStream_t s) {
+                                      int head_dim, const int32_t* pos, float* zero,
+                                      int64_t zero_n, hipStream_t s) {
   if (op.M <= 0 || op.N <= 0) return hipSuccess;
-  if (!fewrow_ok(op)) return hipErrorInvalidValue;
+  if (!fewrow_ok(op) || zero_n % 4 != 0 || ((uintptr_t)zero & 15)) return hipErrorInvalidValue;
   FewRowOut out{};
+  out.zero = (floatx4*)zero;
+  out.zero_n4 = zero_n / 4;
   out.z = (bf16*)z;
   out.ldz = ldz;
   out.k_col = k_col;

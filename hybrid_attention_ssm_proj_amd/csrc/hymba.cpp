@@ -141,10 +141,18 @@ struct Carve {
   size_t z, delta, bc, dt, f, part, xdbl, yacc, total;
 };
 
-constexpr int kDecodeKeysPerSplit = 256;
 
+// Keys per decode-attention split: the largest of 256 / 192 / 128 that tiles the
+// longest key list (meta + window) without a partly empty last split, else 256.
+int decode_kps(const Shape& s, int span_max) {
+  const int n = s.M + span_max;
+  for (int k : {256, 192, 128})
+    if (n % k == 0) return k;
+  return 256;
+}
 int decode_nsplit(const Shape& s, int span_max) {
-  return (s.M + span_max + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
+  const int k = decode_kps(s, span_max);
+  return (s.M + span_max + k - 1) / k;
 }
 
 bool fused_dt(const Shape& s) { return s.bf16 && scan_fused_supported(s.N, s.R, s.Di); }
@@ -178,7 +186,7 @@ Carve carve_decode(const Shape& s, int batch, int nsplit) {
   c.f = off;
   off = align_up(off + (size_t)batch * s.fw * s.es);
   c.part = off;
-  off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 2) * 4);
+  off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 4) * 4);
   c.xdbl = off;
   off = align_up(off + (size_t)batch * (s.R + 2 * s.N) * 4);
   c.yacc = off;
@@ -492,14 +500,13 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
                : launch_gemm_f32(op, out, stream);
   };
   if (splitk) {
-    // clears the x_proj / out_proj accumulators (contiguous after zacc)
-    HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_zero_f32(xdbl, (int64_t)(cv.total - cv.xdbl) / 4,
-                                                   stream));
+    // the same launch clears the x_proj / out_proj accumulators (contiguous, last)
     GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
     HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ,
                  launch_gemm_bf16_decode_in(op, z, s.n_in, s.share ? -1 : (int)s.k_col,
                                             (int)s.v_col, kv->k, kv->v, kv->slots, s.Hkv, s.dh,
-                                            state->pos, stream));
+                                            state->pos, xdbl, (int64_t)(cv.total - cv.xdbl) / 4,
+                                            stream));
   } else {
     GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
     GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, B, 0, nullptr};
@@ -522,7 +529,7 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     ap.pos = state->pos;
     ap.part = part;
     ap.nsplit = nsplit;
-    ap.keys_per_split = kDecodeKeysPerSplit;
+    ap.keys_per_split = decode_kps(s, span_max);
     ap.n_meta = M;
     ap.B = B;
     ap.Hq = s.Hq;

@@ -53,9 +53,12 @@ hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t l
                                    hipStream_t s);
 // Z = bf16(A B^T) (row stride ldz); with k_col >= 0 the K / V columns of row b are also
 // written to ring slot pos[b] % slots of ring_k / ring_v ([B, Hkv, slots, head_dim]).
+// Also clears `zero_n` floats at `zero` (16-byte aligned, zero_n % 4 == 0): the split-K
+// accumulators the later decode projections add into.
 hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t ldz, int k_col,
                                       int v_col, void* ring_k, void* ring_v, int slots, int Hkv,
-                                      int head_dim, const int32_t* pos, hipStream_t s);
+                                      int head_dim, const int32_t* pos, float* zero,
+                                      int64_t zero_n, hipStream_t s);
 
 // ----------------------------------------------------------------- attention
 // Keys/values at X~ position j of sequence b: j < n_meta from the meta arrays
@@ -83,7 +86,8 @@ hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s);
 
 // Decode: one query per sequence at X-position pos[b]; keys = meta + the
 // min(pos+1, span_max) most recent ring positions.  Partial results per split go to
-// part (fp32): [B, Hq, nsplit, head_dim + 2] holding (o[head_dim], m, l).
+// part (fp32): [B, Hq, nsplit, head_dim + 4] holding (o[head_dim], m, l, 2 pad) so every
+// split record starts 16-byte aligned.
 struct AttnDecodeParams {
   const void* q;  // row b at q + b*q_row_stride (+ h*head_dim)
   int64_t q_row_stride;

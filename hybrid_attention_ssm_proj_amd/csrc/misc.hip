@@ -120,30 +120,147 @@ hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int
   return hipGetLastError();
 }
 
-// Decode: merge split partials (o, m, l) of every q head of sequence b into O, round it
-// to the storage type (as the prefill path stores O), then normalise the row.
+// Decode: merge the split partials (o, m, l) of every q head of sequence b into O,
+// round O to the storage type (as the prefill path stores O), then normalise the row
+// with the SSM half that the SSM step already wrote.  One block of 256 threads per
+// sequence; each thread owns up to kCombineChunks 8-element chunks of the row and keeps
+// them in registers between the two block sums and the scaled store.
+constexpr int kCombineChunks = 4;
+
 template <typename T>
-__global__ __launch_bounds__(1024) void decode_combine_norm_kernel(const float* part, int nsplit,
-                                                                  T* f, int64_t stride, int Hq,
-                                                                  int dh, int ws, const float* ba,
-                                                                  const float* bs, float eps) {
+__device__ __forceinline__ void combine_chunk(const float* ph, int nsplit, int rec, int d0,
+                                              float v[8]) {
+  float mx = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, ph[sp * rec + rec - 4]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* r = ph + sp * rec;
+    const float m = r[rec - 4];
+    if (m == -INFINITY) continue;  // empty split
+    const float w = __expf(m - mx);
+    lsum = fmaf(r[rec - 3], w, lsum);
+    const floatx4 a = *(const floatx4*)(r + d0), c = *(const floatx4*)(r + d0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = fmaf(a[e], w, v[e]);
+      v[4 + e] = fmaf(c[e], w, v[4 + e]);
+    }
+  }
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = to_f32(from_f32<T>(v[e] * inv));
+}
+
+// Same merge for at most S splits: every load is issued before the first use, so the
+// chunk costs one memory round trip.
+template <typename T, int S>
+__device__ __forceinline__ void combine_chunk_fixed(const float* ph, int nsplit, int rec, int d0,
+                                                    float v[8]) {
+  float m[S], l[S];
+  floatx4 a[S], c[S];
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    if (sp < nsplit) {
+      const float* r = ph + sp * rec;
+      const floatx4 ml = *(const floatx4*)(r + rec - 4);
+      m[sp] = ml[0];
+      l[sp] = ml[1];
+      a[sp] = *(const floatx4*)(r + d0);
+      c[sp] = *(const floatx4*)(r + d0 + 4);
+    } else {
+      m[sp] = -INFINITY;
+      l[sp] = 0.f;
+      a[sp] = c[sp] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, m[sp]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = m[sp] == -INFINITY ? 0.f : __expf(m[sp] - mx);  // empty split: 0
+    lsum = fmaf(l[sp], w, lsum);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = fmaf(a[sp][e], w, v[e]);
+      v[4 + e] = fmaf(c[sp][e], w, v[4 + e]);
+    }
+  }
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = to_f32(from_f32<T>(v[e] * inv));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_combine_norm_kernel(const float* part, int nsplit,
+                                                                 T* f, int64_t stride, int Hq,
+                                                                 int dh, int ws, const float* ba,
+                                                                 const float* bs, float eps) {
   const int b = blockIdx.x;
   T* row = f + (int64_t)b * stride;
-  const int wa = Hq * dh;
-  for (int e = threadIdx.x; e < wa; e += blockDim.x) {
-    const int h = e / dh, d = e % dh;
-    const float* ph = part + ((int64_t)b * Hq + h) * nsplit * (dh + 2);
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, ph[s * (dh + 2) + dh]);
-    float lsum = 0.f, o = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float m = ph[s * (dh + 2) + dh];
-      if (m == -INFINITY) continue;
-      const float w = __expf(m - mx);
-      lsum = fmaf(ph[s * (dh + 2) + dh + 1], w, lsum);
-      o = fmaf(ph[s * (dh + 2) + d], w, o);
+  const int wa = Hq * dh, nch = (wa + ws) / 8, rec = dh + 4;
+  float v[kCombineChunks][8];
+  float sa = 0.f, ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kCombineChunks; ++c) {
+    const int ch = threadIdx.x + c * 256;
+    if (ch >= nch) break;
+    const int i = ch * 8;
+    if (i < wa) {
+      const int h = i / dh;
+      const float* ph = part + ((int64_t)b * Hq + h) * nsplit * rec;
+      if (nsplit <= 8)
+        combine_chunk_fixed<T, 8>(ph, nsplit, rec, i - h * dh, v[c]);
+      else
+        combine_chunk<T>(ph, nsplit, rec, i - h * dh, v[c]);
+    } else {
+      Vec8<T>::load(row + i, v[c]);
     }
-    row[e] = from_f32<T>(o / lsum);
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q = fmaf(v[c][e], v[c][e], q);
+    if (i < wa)
+      sa += q;
+    else
+      ss += q;
+  }
+  block_sum2(sa, ss);
+  const float ia = 0.5f * rsqrtf(sa / (float)wa + eps);
+  const float is = 0.5f * rsqrtf(ss / (float)ws + eps);
+#pragma unroll
+  for (int c = 0; c < kCombineChunks; ++c) {
+    const int ch = threadIdx.x + c * 256;
+    if (ch >= nch) break;
+    const int i = ch * 8;
+    const bool att = i < wa;
+    const float* beta = att ? ba + i : bs + (i - wa);
+    const float sc = att ? ia : is;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[c][e] = v[c][e] * sc * beta[e];
+    Vec8<T>::store(row + i, v[c]);
+  }
+}
+
+// Rows wider than 256 x kCombineChunks x 8 elements: merge into F first (same thread
+// layout as the norm pass reads it back), then normalise in place.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_combine_wide_kernel(const float* part, int nsplit,
+                                                                 T* f, int64_t stride, int Hq,
+                                                                 int dh, int ws, const float* ba,
+                                                                 const float* bs, float eps) {
+  const int b = blockIdx.x;
+  T* row = f + (int64_t)b * stride;
+  const int wa = Hq * dh, rec = dh + 4;
+  for (int i = threadIdx.x * 8; i < wa; i += 256 * 8) {
+    const int h = i / dh;
+    float v[8];
+    combine_chunk<T>(part + ((int64_t)b * Hq + h) * nsplit * rec, nsplit, rec, i - h * dh, v);
+    Vec8<T>::store(row + i, v);
   }
   __syncthreads();
   norm_row<T>(row, wa, ws, ba, bs, eps);
@@ -154,12 +271,22 @@ hipError_t launch_decode_combine_norm(bool bf16_, const float* part, int nsplit,
                                       const float* beta_a, const float* beta_s, float eps,
                                       hipStream_t s) {
   if (B == 0) return hipSuccess;
-  if (bf16_)
-    decode_combine_norm_kernel<bf16><<<dim3(B), dim3(1024), 0, s>>>(
-        part, nsplit, (bf16*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
-  else
-    decode_combine_norm_kernel<float><<<dim3(B), dim3(1024), 0, s>>>(
-        part, nsplit, (float*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+  const bool narrow = Hq * head_dim + ws <= 256 * kCombineChunks * 8;
+  if (bf16_) {
+    if (narrow)
+      decode_combine_norm_kernel<bf16><<<dim3(B), dim3(256), 0, s>>>(
+          part, nsplit, (bf16*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+    else
+      decode_combine_wide_kernel<bf16><<<dim3(B), dim3(256), 0, s>>>(
+          part, nsplit, (bf16*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+  } else {
+    if (narrow)
+      decode_combine_norm_kernel<float><<<dim3(B), dim3(256), 0, s>>>(
+          part, nsplit, (float*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+    else
+      decode_combine_wide_kernel<float><<<dim3(B), dim3(256), 0, s>>>(
+          part, nsplit, (float*)f, f_stride, Hq, head_dim, ws, beta_a, beta_s, eps);
+  }
   return hipGetLastError();
 }
 

@@ -58,6 +58,31 @@ __device__ __forceinline__ void load8v(const float* p, float out[8]) {
   }
 }
 
+// 8 consecutive elements held in their storage type until used, so that a load can
+// stay in flight past later loads.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *(const bf16x8*)p; }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+  }
+  __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+};
+template <>
+struct Raw8<float> {
+  floatx4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *(const floatx4*)p;
+    b = *(const floatx4*)(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = floatx4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
 __device__ __forceinline__ int64_t seq_row(int t, int b, int n_meta, int L) {
   return t < n_meta ? (int64_t)t : (int64_t)n_meta + (int64_t)b * L + (t - n_meta);
 }
@@ -185,12 +210,14 @@ hipError_t launch_scan_prefill(bool bf16_, const ScanParams& p, hipStream_t s) {
 
 // --------------------------------------------------------------------- decode step
 // Workgroup per (block of channels, group of SB sequences); thread per (channel, group
-// of 4 states).  The lanes of a channel share the dt projection
+// of 4 states).  Every per-sequence operand that does not depend on dt (the state h as
+// one float4 per thread, x, G, and the thread's 4 entries of B and C) is loaded first,
+// so its latency overlaps the dt projection.  The lanes of a channel share
 // dt = softplus(delta . W_dt[c] + b[c]) (delta rounded to the storage type, as the
 // prefill path stores it): each lane streams its slice of W_dt[c] once and accumulates
 // it against the SB sequences' deltas staged in LDS.  Then every sequence advances its
-// states (h read and written once as a float4 per thread).  The thread of state group
-// 0 of channel 0 advances pos[b]: every kernel that reads pos precedes this one.
+// states.  The thread of state group 0 of channel 0 advances pos[b]: every kernel that
+// reads pos precedes this one.
 template <typename T, int LPC, int SB>
 __global__ __launch_bounds__(256) void ssm_step_kernel(SsmStepParams p) {
   constexpr int NS = 4;
@@ -204,54 +231,91 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(SsmStepParams p) {
   const int b0 = blockIdx.y * SB;
   const int nb = min(SB, p.B - b0);
   const int xw = p.R + 2 * N;
-  for (int i = tid; i < SB * p.R; i += 256) {
-    const int bb = i / p.R, r = i % p.R;
-    dl_s[bb][r] = bb < nb ? to_f32(from_f32<T>(p.xdbl[(int64_t)(b0 + bb) * xw + r])) : 0.f;
+
+  floatx4 hv[SB], bv[SB], cv[SB];
+  float xv[SB], gv[SB];
+#pragma unroll
+  for (int bb = 0; bb < SB; ++bb) {
+    const int b = b0 + min(bb, nb - 1);  // rows past the batch re-read the last one
+    const T* z = (const T*)p.z + (int64_t)b * p.z_stride;
+    const float* xr = p.xdbl + (int64_t)b * xw + p.R + sg * NS;
+    hv[bb] = *(const floatx4*)(p.h + ((int64_t)b * p.Di + c) * N + sg * NS);
+    bv[bb] = *(const floatx4*)xr;
+    cv[bb] = *(const floatx4*)(xr + N);
+    xv[bb] = to_f32(z[p.xs_col + c]);
+    gv[bb] = to_f32(z[p.g_col + c]);
+  }
+  const floatx4 av = *(const floatx4*)(p.A + (int64_t)c * N + sg * NS);
+  const float Dc = p.D[c], bias = p.dt_bias[c];
+
+  // This thread's first 4 slices of W_dt[c] (the whole row for R <= 4 * LPC * 8), also
+  // loaded before anything waits.
+  constexpr int RSTEP = LPC * 8;
+  const T* wrow = (const T*)p.w_dt + (int64_t)c * p.R;
+  Raw8<T> wv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (sg * 8 + u * RSTEP < p.R)
+      wv[u].load(wrow + sg * 8 + u * RSTEP);
+    else
+      wv[u].zero();
+  }
+  // Stage the SB deltas, 4 loads in flight per thread per round.
+  for (int i0 = tid; i0 < SB * p.R; i0 += 4 * 256) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256, bb = i / p.R, r = i % p.R;
+      v[u] = (i < SB * p.R && bb < nb) ? p.xdbl[(int64_t)(b0 + bb) * xw + r] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      if (i < SB * p.R) dl_s[i / p.R][i % p.R] = to_f32(from_f32<T>(v[u]));
+    }
   }
   __syncthreads();
-
   float part[SB];
 #pragma unroll
   for (int bb = 0; bb < SB; ++bb) part[bb] = 0.f;
-  const T* wrow = (const T*)p.w_dt + (int64_t)c * p.R;
-  for (int r0 = sg * 8; r0 < p.R; r0 += LPC * 8) {
-    float wv[8];
-    load8v(wrow + r0, wv);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r0 = sg * 8 + u * RSTEP;
+    if (r0 >= p.R) break;
 #pragma unroll
     for (int bb = 0; bb < SB; ++bb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[bb] = fmaf(dl_s[bb][r0 + e], wv[e], part[bb]);
+      for (int e = 0; e < 8; ++e) part[bb] = fmaf(dl_s[bb][r0 + e], wv[u][e], part[bb]);
+  }
+  for (int r0 = sg * 8 + 4 * RSTEP; r0 < p.R; r0 += RSTEP) {  // R > 4 * LPC * 8 only
+    float w1[8];
+    load8v(wrow + r0, w1);
+#pragma unroll
+    for (int bb = 0; bb < SB; ++bb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[bb] = fmaf(dl_s[bb][r0 + e], w1[e], part[bb]);
   }
 
-  const floatx4 av = *(const floatx4*)(p.A + (int64_t)c * N + sg * NS);
-  const float Dc = p.D[c], bias = p.dt_bias[c];
 #pragma unroll
   for (int bb = 0; bb < SB; ++bb) {
     if (bb >= nb) break;  // uniform across the workgroup
     const int b = b0 + bb;
     const float dtv = softplus_f(group_sum<LPC>(part[bb]) + bias);
-    const T* z = (const T*)p.z + (int64_t)b * p.z_stride;
-    const float xv = to_f32(z[p.xs_col + c]);
-    const float gv = to_f32(z[p.g_col + c]);
-    const float* xr = p.xdbl + (int64_t)b * xw;
-    float* hp = p.h + ((int64_t)b * p.Di + c) * N + sg * NS;
-    const floatx4 hv = *(const floatx4*)hp;
-    const float dx = dtv * xv;
+    const float dx = dtv * xv[bb];
     float acc = 0.f;
     floatx4 hn;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const int n = sg * NS + k;
       const float a = __builtin_amdgcn_exp2f(dtv * av[k] * kLog2e);
-      hn[k] = fmaf(a, hv[k], dx * xr[p.R + n]);
-      acc = fmaf(hn[k], xr[p.R + N + n], acc);
+      hn[k] = fmaf(a, hv[bb][k], dx * bv[bb][k]);
+      acc = fmaf(hn[k], cv[bb][k], acc);
     }
     acc = group_sum<LPC>(acc);
     if (!cok) continue;
-    *(floatx4*)hp = hn;
+    *(floatx4*)(p.h + ((int64_t)b * p.Di + c) * N + sg * NS) = hn;
     if (sg == 0) {
-      const float yv = fmaf(Dc, xv, acc);
-      ((T*)p.y)[(int64_t)b * p.y_stride + c] = from_f32<T>(yv * silu_f(gv));
+      const float yv = fmaf(Dc, xv[bb], acc);
+      ((T*)p.y)[(int64_t)b * p.y_stride + c] = from_f32<T>(yv * silu_f(gv[bb]));
       if (c == 0 && p.pos != nullptr) p.pos[b] += 1;
     }
   }
@@ -259,7 +323,9 @@ __global__ __launch_bounds__(256) void ssm_step_kernel(SsmStepParams p) {
 
 template <typename T, int LPC>
 static hipError_t run_step(const SsmStepParams& p, hipStream_t s) {
-  constexpr int SB = 8;
+  // Two sequences per workgroup: the most workgroups (and the fewest registers) for
+  // the state stream; the W_dt slice is re-read from L2 by each sequence pair.
+  constexpr int SB = 2;
   const int blocks = (p.Di * LPC + 255) / 256;
   ssm_step_kernel<T, LPC, SB><<<dim3(blocks, (p.B + SB - 1) / SB), dim3(256), 0, s>>>(p);
   return hipGetLastError();
