@@ -18,6 +18,8 @@
 // block (outside the meta prefix and the window) are skipped.
 #include <float.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -558,6 +560,219 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeParams p) {
   }
 }
 
+// Stream mode (bf16): one workgroup per (sequence, kv head) walks the whole key list in
+// chunks of CK keys per wave (waves take chunks round-robin), optionally double-buffered
+// in registers so the next chunk's K and V are in flight while the current one is
+// scored and accumulated.  Each wave keeps an online softmax (running max m, sum l and O,
+// rescaled when m grows; the max is shared by the wave's lanes so lane groups can be
+// summed at the end); the four waves are merged through LDS and O is stored, rounded to
+// bf16, straight into its row.  Used when sequences x kv heads fill the chip.
+// The arithmetic is packed: q.k is accumulated with v_dot2_f32_bf16 on the stored bf16
+// pairs (no unpacking of K), and P V pairs the keys of two consecutive instructions
+// (same lane, same head_dim chunk): (p_i, p_j) . (v_i[d], v_j[d]) per d, with P rounded
+// to bf16 as the prefill kernel rounds it for its MFMA.
+namespace {
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ bf16x2_t as_bf2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(a), as_bf2(b), c, false);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const bf16x2_t v{(bf16)lo, (bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+}  // namespace
+
+template <int DH, int GQ, int NW, int NI, bool DB>
+__global__ __launch_bounds__(NW * 64) void attn_decode_stream_kernel(AttnDecodeParams p) {
+  constexpr int LPK = DH / 8;      // lanes per key (one 16-byte chunk each)
+  constexpr int KPI = 64 / LPK;    // keys per wave instruction
+  constexpr int CK = NI * KPI;     // keys per chunk (NI wave instructions, K and V each)
+  static_assert(NI % 2 == 0, "instructions are paired for P V");
+  __shared__ float red_m[NW][GQ], red_l[NW][GQ];
+  __shared__ float red_o[NW][GQ][DH];
+
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h0 = g * GQ;
+  const int posb = max(p.pos[b], 0);
+  const int span = min(posb + 1, p.span_max);
+  const int nkeys = p.n_meta + span;
+  const int nchunks = (nkeys + CK - 1) / CK;
+  const int dc = lane % LPK, kin = lane / LPK;
+  const float sl2 = p.scale * 1.4426950408889634f;  // scores in log2 units
+
+  u32x4 q[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+    q[h] = *(const u32x4*)((const bf16*)p.q + (int64_t)b * p.q_row_stride + (h0 + h) * DH + dc * 8);
+  // Key idx < n_meta is meta row idx; key idx >= n_meta is X-position
+  // posb - span + 1 + (idx - n_meta) at ring slot (position % slots).  Within a chunk the
+  // ring slot advances by KPI per instruction with one wrap (slots >= KPI, checked on the
+  // host); keys past the end read ring slot 0 and are masked.
+  const int64_t ring_off = ((int64_t)b * p.Hkv + g) * p.slots * DH + dc * 8;
+  const int64_t meta_off = (int64_t)g * p.n_meta * DH + dc * 8;
+  const bf16* km = (const bf16*)p.k_meta + meta_off;
+  const bf16* vm = (const bf16*)p.v_meta + meta_off;
+  const bf16* kg = (const bf16*)p.k + ring_off;
+  const bf16* vg = (const bf16*)p.v + ring_off;
+  const int xpos0 = posb - span + 1 - p.n_meta;  // X-position of key idx = xpos0 + idx
+  auto fetch = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], int j) {
+    const int idx0 = j * CK + kin;
+    int slot = (xpos0 + idx0) % p.slots;
+    if (slot < 0) slot += p.slots;  // meta keys: slot unused
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = idx0 + i * KPI;
+      const bool meta = idx < p.n_meta;
+      const int ro = idx < nkeys ? slot * DH : 0;
+      kr[i] = *(const u32x4*)(meta ? km + idx * DH : kg + ro);
+      vr[i] = *(const u32x4*)(meta ? vm + idx * DH : vg + ro);
+      slot += KPI;
+      if (slot >= p.slots) slot -= p.slots;
+    }
+  };
+
+  float m[GQ], l[GQ], o[GQ][8];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  }
+  auto consume = [&](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], int j) {
+    float sc[NI][GQ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool valid = j * CK + i * KPI + kin < nkeys;
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        float d = dot2(q[h][0], kr[i][0], 0.f);
+        d = dot2(q[h][1], kr[i][1], d);
+        d = dot2(q[h][2], kr[i][2], d);
+        d = dot2(q[h][3], kr[i][3], d);
+        d = lane_group_sum<LPK>(d);
+        sc[i][h] = valid ? d * sl2 : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float cm = sc[0][h];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) cm = fmaxf(cm, sc[i][h]);
+#pragma unroll
+      for (int off = LPK; off < 64; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 64));
+      const float mn = fmaxf(m[h], cm);  // finite: every chunk holds a valid key
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+      m[h] = mn;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; i += 2) {
+      // (v_i[d], v_{i+1}[d]) pairs: low halves for even d, high halves for odd d
+      uint32_t vp[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vp[2 * w] = __builtin_amdgcn_perm(vr[i + 1][w], vr[i][w], 0x05040100u);
+        vp[2 * w + 1] = __builtin_amdgcn_perm(vr[i + 1][w], vr[i][w], 0x07060302u);
+      }
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        const float pa = __builtin_amdgcn_exp2f(sc[i][h] - m[h]);
+        const float pb = __builtin_amdgcn_exp2f(sc[i + 1][h] - m[h]);
+        l[h] += pa + pb;
+        const uint32_t pp = pack_bf2(pa, pb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = dot2(pp, vp[e], o[h][e]);
+      }
+    }
+  };
+
+  if constexpr (DB) {  // two register buffers: the next chunk loads during this one
+    u32x4 k0[NI], v0[NI], k1[NI], v1[NI];
+    int j = wave;
+    if (j < nchunks) fetch(k0, v0, j);
+    for (; j < nchunks; j += 2 * NW) {
+      if (j + NW < nchunks) fetch(k1, v1, j + NW);
+      consume(k0, v0, j);
+      if (j + NW >= nchunks) break;
+      if (j + 2 * NW < nchunks) fetch(k0, v0, j + 2 * NW);
+      consume(k1, v1, j + NW);
+    }
+  } else {  // one buffer; the other waves of the SIMD cover the latency
+    u32x4 k0[NI], v0[NI];
+    for (int j = wave; j < nchunks; j += NW) {
+      fetch(k0, v0, j);
+      consume(k0, v0, j);
+    }
+  }
+
+  // lane groups of the wave (same chunk index dc) share m: sum l and O over them
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) l[h] += __shfl_xor(l[h], off, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[h][e];
+#pragma unroll
+      for (int off = LPK; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      o[h][e] = v;
+    }
+  }
+  if (kin == 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[wave][h][dc * 8 + e] = o[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      red_m[wave][h] = m[h];
+      red_l[wave][h] = l[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < GQ * DH; i += NW * 64) {
+    const int h = i / DH, d = i % DH;
+    float mx = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red_m[w][h]);
+    float ls = 0.f, os = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = red_m[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[w][h] - mx);
+      ls = fmaf(red_l[w][h], wt, ls);
+      os = fmaf(red_o[w][h][d], wt, os);
+    }
+    ((bf16*)p.o)[(int64_t)b * p.o_stride + (h0 + h) * DH + d] = (bf16)(os / ls);
+  }
+}
+
+template <int DH, int NW, int NI, bool DB>
+static hipError_t run_decode_stream(const AttnDecodeParams& p, hipStream_t s) {
+  dim3 grid(p.Hkv, p.B);
+  switch (p.Hq / p.Hkv) {
+    case 1: attn_decode_stream_kernel<DH, 1, NW, NI, DB><<<grid, dim3(NW * 64), 0, s>>>(p); break;
+    case 2: attn_decode_stream_kernel<DH, 2, NW, NI, DB><<<grid, dim3(NW * 64), 0, s>>>(p); break;
+    case 4: attn_decode_stream_kernel<DH, 4, NW, NI, DB><<<grid, dim3(NW * 64), 0, s>>>(p); break;
+    case 8: attn_decode_stream_kernel<DH, 8, NW, NI, DB><<<grid, dim3(NW * 64), 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+// Four waves, 6-instruction chunks, one register buffer (measured fastest on the
+// 128-sequence, 4-kv-head, 1152-key case; a second buffer costs more in occupancy than
+// it gains in overlap).
+template <int DH>
+static hipError_t run_decode_stream(const AttnDecodeParams& p, hipStream_t s) {
+  return run_decode_stream<DH, 4, 6, false>(p, s);
+}
+
 template <typename T, int DH, int KPS>
 static hipError_t run_decode_kps(const AttnDecodeParams& p, hipStream_t s) {
   dim3 grid(p.nsplit, p.Hkv, p.B);
@@ -573,6 +788,10 @@ static hipError_t run_decode_kps(const AttnDecodeParams& p, hipStream_t s) {
 
 template <typename T, int DH>
 static hipError_t run_decode(const AttnDecodeParams& p, hipStream_t s) {
+  if (p.o != nullptr) {
+    if constexpr (std::is_same_v<T, bf16>) return run_decode_stream<DH>(p, s);
+    return hipErrorInvalidValue;  // stream mode is bf16 only
+  }
   switch (p.keys_per_split) {
     case 128: return run_decode_kps<T, DH, 128>(p, s);
     case 192: return run_decode_kps<T, DH, 192>(p, s);

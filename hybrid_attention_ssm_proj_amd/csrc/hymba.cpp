@@ -489,6 +489,9 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   float* yacc = (float*)ws_ptr(workspace, cv.yacc);
   const bool b16 = s.bf16;
   const int nx = s.R + 2 * s.N;
+  // Attention (bf16): one workgroup per (sequence, kv head) streaming all keys once the
+  // pairs fill the chip (256 CUs), else key splits merged by the combine kernel.
+  const bool stream_attn = b16 && (int64_t)B * s.Hkv >= 256 && kv->slots >= 64;
 
   // in_proj.  bf16 with every K a multiple of 256: the few-row GEMM writes Z and the
   // producer's new K/V row into its ring slot in the same pass, and x_proj / out_proj
@@ -537,6 +540,10 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     ap.head_dim = s.dh;
     ap.span_max = span_max;
     ap.scale = s.scale;
+    if (stream_attn) {  // O straight into F; no split partials
+      ap.o = f;
+      ap.o_stride = s.fw;
+    }
     HYMBA_LAUNCH(HYMBA_STAGE_ATTN, launch_attention_decode(b16, ap, stream));
   }
   // x_proj -> xdbl [B, R + 2N] fp32 (delta, B, C).
@@ -572,9 +579,15 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     sp.R = s.R;
     HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_ssm_step(b16, sp, stream));
   }
-  HYMBA_LAUNCH(HYMBA_STAGE_NORM,
-               launch_decode_combine_norm(b16, part, nsplit, f, s.fw, B, s.Hq, s.dh, s.Di,
-                                          w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
+  if (stream_attn) {
+    HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, B, (int)s.qw, s.Di,
+                                                    w->beta_attn, w->beta_ssm, desc->rms_eps,
+                                                    stream));
+  } else {
+    HYMBA_LAUNCH(HYMBA_STAGE_NORM,
+                 launch_decode_combine_norm(b16, part, nsplit, f, s.fw, B, s.Hq, s.dh, s.Di,
+                                            w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
+  }
   {
     GemmOperands op{f, s.fw, nullptr, 0, B, w->w_out, s.fw, B, s.d, (int)s.fw};
     if (splitk) {

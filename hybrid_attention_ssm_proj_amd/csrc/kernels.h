@@ -97,8 +97,10 @@ struct AttnDecodeParams {
   const void* v;  // [B, Hkv, S, dh]
   int slots;
   const int32_t* pos;
-  float* part;
+  float* part;     // split mode: partials (see above)
   int nsplit, keys_per_split;
+  void* o;         // stream mode (o != nullptr): O rows at o + b*o_stride, storage type
+  int64_t o_stride;
   int n_meta, B, Hq, Hkv, head_dim, span_max;
   float scale;
 };
