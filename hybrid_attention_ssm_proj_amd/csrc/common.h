@@ -57,10 +57,24 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+
+// softplus(z) = log(1 + e^z) on the hardware base-2 exp / log: e^z = 2^(z log2 e), and
+// log1p(t) in the compensated form log(u) * t / (u - 1) with u = fl(1 + t), which cancels
+// the rounding of 1 + t (Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", Theorem 4); u == 1 means log1p(t) = t to fp32 precision.
+// Above 20, log(1 + e^z) - z = log1p(e^-z) < 2.1e-9 and z is returned.
 __device__ __forceinline__ float softplus_f(float z) {
-  // log(1 + e^z); above 20 the correction e^-z is below fp32 resolution of z.
-  return z > 20.f ? z : log1pf(__expf(z));
+  const float t = __builtin_amdgcn_exp2f(z * kLog2eF);
+  const float u = 1.f + t;
+  const float d = u - 1.f;
+  const float r = d == 0.f ? t : __builtin_amdgcn_logf(u) * kLn2F * (t * __builtin_amdgcn_rcpf(d));
+  return z > 20.f ? z : r;
 }
-__device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) with the hardware reciprocal (1 ulp).
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2eF));
+}
 
 }  // namespace hymba
