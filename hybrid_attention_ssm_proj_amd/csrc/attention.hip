@@ -215,33 +215,47 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnParams p,
     }
 
     const int a = t * Cfg::KT;
+    // The mask is needed only where some (query, key) pair of the wave is hidden: the
+    // diagonal tile and the window's lower edge.  Wave-uniform.
+    const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
+    const bool full = a + Cfg::KT - 1 <= i_lo &&
+                      (p.window <= 0 || a + Cfg::KT <= p.n_meta ||
+                       i_hi - max(a, p.n_meta) < p.window);
     bf16x8 pf[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int i = wp0 + qt * 16 + (lane & 15);
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = a + kt * 16 + (lane >> 4) * 4 + r;
-          const float s = key_visible(i, j, p.n_meta, p.window) ? sacc[kt][qt][r] : -INFINITY;
-          sacc[kt][qt][r] = s;
-          mx = fmaxf(mx, s);
-        }
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = a + kt * 16 + (lane >> 4) * 4 + r;
+            const float s = key_visible(i, j, p.n_meta, p.window) ? sacc[kt][qt][r] : -INFINITY;
+            sacc[kt][qt][r] = s;
+            mx = fmaxf(mx, s);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(mrow[qt], mx);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);
       mrow[qt] = mnew;
+      const float mc2 = muse * c2;
       float ls = 0.f;
       float pv[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(sacc[kt][qt][r] * c2 - muse * c2);
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][r], c2, -mc2));
           pv[kt][r] = e;
           ls += e;
         }
