@@ -53,6 +53,12 @@ template <int LPC>
 __device__ __forceinline__ float transpose_reduce(float (&v)[LPC], int sg) {
   if constexpr (LPC == 1) {
     return v[0];
+  } else if constexpr (LPC == 4) {
+    // written out: two lane-bit selects per stage, masks computed once
+    const bool b0 = sg & 1, b1 = sg & 2;
+    const float q0 = (b0 ? v[1] : v[0]) + dpp<0xB1>(b0 ? v[0] : v[1]);
+    const float q1 = (b0 ? v[3] : v[2]) + dpp<0xB1>(b0 ? v[2] : v[3]);
+    return (b1 ? q1 : q0) + dpp<0x4E>(b1 ? q0 : q1);
   } else {
     int n = LPC;
 #pragma unroll
