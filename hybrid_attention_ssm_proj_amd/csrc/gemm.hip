@@ -354,12 +354,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
     for (int j = 0; j < Cfg::FN; ++j)
       bfr[buf][j] = *(const bf16x8*)(sb + b_row0 + j * 2048 + koff[ks]);
   };
+  // MFMAs of one k-substep; the fragment reads of the next substep (issued just before)
+  // are interleaved one after each of the first MFMAs instead of being bunched ahead
+  // of waits the scheduler would otherwise place between single MFMAs.
   auto mm = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
         acc[i][j] = mfma32x32x16(bfr[buf][j], af[buf][i], acc[i][j]);
+#pragma unroll
+    for (int q = 0; q < Cfg::FM + Cfg::FN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, Cfg::FM * Cfg::FN - Cfg::FM - Cfg::FN, 0);
   };
 
   const int KT = g.K / 64;
@@ -676,9 +685,10 @@ static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShap
         const bool one_src = op.a_split >= op.M;
         const bool fits32 = (int64_t)op.M * op.lda0 < (1ll << 31) && (int64_t)op.N * op.ldb < (1ll << 31);
         if (op.K % 64 == 0 && one_src && fits32) {
-          // 256 x 256 tiles when they fill the chip several times over, else 256 x 128
+          // 256 x 256 tiles on 8 waves (2 x 4 of 128 x 64) once they fill the chip,
+          // else 256 x 128 tiles
           const long t256 = (long)((op.M + 255) / 256) * ((op.N + 255) / 256);
-          if (t256 >= 4 * 256) return run_bf16_dl<DlCfg<256, 256, 2, 2>>(op, epi, s);
+          if (t256 >= 256) return run_bf16_dl<DlCfg<256, 256, 2, 4>>(op, epi, s);
           return run_bf16_dl<DlCfg<256, 128, 2, 4>>(op, epi, s);
         }
         return run_bf16<CfgLarge>(op, epi, s);
