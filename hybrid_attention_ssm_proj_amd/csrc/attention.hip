@@ -340,6 +340,331 @@ hipError_t launch_attention_prefill_bf16(const AttnParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------- bf16 prefill, direct-to-LDS tiles
+// V^T staging: the P V product needs, per lane, 8 consecutive keys of one head_dim
+// column (the k operand of the MFMA), while V is stored key-major.  A small kernel
+// writes V^T per (sequence, kv head): vt[b][g][d][slot] over the meta-prefixed key axis
+// (tpad = keys rounded up to 64, zero past the end), keys permuted inside each 32-key
+// block to the slot order of the S^T accumulators (vt_slot).  Then both the K tile
+// (64 keys x head_dim, key-major) and the V^T tile (head_dim x 64 slots) move straight
+// from global memory into LDS with global_load_lds_dwordx4 (no register staging, no
+// scattered LDS stores), NS stages deep.
+namespace {
+__device__ __forceinline__ int slot_key(int s) {  // inverse of vt_slot within 64
+  const int blk = s >> 5, q = (s & 31) >> 3, i = s & 7;
+  return blk * 32 + (i < 4 ? q * 4 + i : 16 + q * 4 + (i - 4));
+}
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lptr) {
+  // global_load_lds_dwordx4 from inline asm: no VGPR result; the consumer waits
+  // explicitly (vmcnt) and then passes a workgroup barrier.
+  const uint32_t l = (uint32_t)(uintptr_t)lptr;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(gptr) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+}  // namespace
+
+template <int DH>
+__global__ __launch_bounds__(256) void vt_build_kernel(AttnParams p, bf16* vt, int tpad) {
+  __shared__ bf16 vs[64][DH + 8];
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int total = p.n_meta + p.L;
+  constexpr int CPR = DH / 8;
+  for (int q = tid; q < 64 * CPR; q += 256) {
+    const int k = q / CPR, c = q % CPR, j = t * 64 + k;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (j < total) v = *(const u32x4*)(key_ptr((const bf16*)p.v_meta, (const bf16*)p.v_seq, p, b, g, j) + c * 8);
+    *(u32x4*)(&vs[k][c * 8]) = v;
+  }
+  __syncthreads();
+  bf16* dst = vt + ((int64_t)b * p.Hkv + g) * DH * tpad + t * 64;
+  for (int q = tid; q < DH * 8; q += 256) {
+    const int d = q / 8, c = q % 8;
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = vs[slot_key(c * 8 + i)][d];
+    *(bf16x8*)(dst + (int64_t)d * tpad + c * 8) = o;
+  }
+}
+
+template <int DH, int NW, int NS>
+__global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kernel(
+    AttnParams p, const bf16* __restrict__ vt, int tpad, int gq, int qb, int nblk_seq) {
+  constexpr int KT = 64;
+  constexpr int KB = KT * DH;            // elements of a K tile and of a V^T tile
+  constexpr int INS = DH / 8 / NW;       // 1 KB DMA wave instructions per wave, per matrix
+  static_assert(INS >= 1 && NS >= 2 && NS <= 3, "tile loader");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * 2 * KB];
+  auto kst = [&](int st) { return smem + st * 2 * KB; };
+  auto vst = [&](int st) { return smem + st * 2 * KB + KB; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  int b, p0, plim;
+  if (bid < p.B * nblk_seq) {
+    b = bid % p.B;
+    const int qi = nblk_seq - 1 - bid / p.B;  // longest blocks first
+    p0 = p.n_meta + qi * qb;
+    plim = p.n_meta + min(p.L, (qi + 1) * qb);
+  } else {
+    b = 0;
+    const int mi = bid - p.B * nblk_seq;
+    p0 = mi * qb;
+    plim = min(p.n_meta, (mi + 1) * qb);
+  }
+  const int h0 = blockIdx.y * gq;
+  const int h = h0 + (wave % gq);
+  const int g = (h0 * p.Hkv) / p.Hq;
+  const int wp0 = p0 + (wave / gq) * 32;
+
+  const bf16* qbase = (const bf16*)p.q;
+  const bf16* km = (const bf16*)p.k_meta;
+  const bf16* ks_ = (const bf16*)p.k_seq;
+  const bf16* vtb = vt + ((int64_t)b * p.Hkv + g) * DH * tpad;
+
+  bf16x8 qf[2][DH / 32];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int pos = wp0 + qt * 16 + (lane & 15);
+    const bool ok = pos < plim;
+    const bf16* src = qbase + pos_row(ok ? pos : 0, b, p.n_meta, p.L) * p.q_row_stride + h * DH +
+                      (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) {
+      u32x4 v = ok ? *(const u32x4*)(src + ks * 32) : u32x4{0, 0, 0, 0};
+      qf[qt][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  floatx4 oacc[DH / 16][2];
+#pragma unroll
+  for (int i = 0; i < DH / 16; ++i) oacc[i][0] = oacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+
+  const int meta_end = min(p.n_meta, plim);
+  const int wlo = p.window > 0 ? max(p.n_meta, p0 - p.window + 1) : p.n_meta;
+  const int ntile = (plim + KT - 1) / KT;
+  auto tile_needed = [&](int t) {
+    const int a = t * KT, e = a + KT;
+    return a < meta_end || (e > wlo && a < plim);
+  };
+  auto next_tile = [&](int t) {
+    ++t;
+    while (t < ntile && !tile_needed(t)) ++t;
+    return t;
+  };
+
+  // DMA of tile t into stage st.  K: 1 KB block (j*NW + wave) of the tile holds rows
+  // of 256 B (DH 128: 4 rows) or 128 B (DH 64: 8 rows), each row's 16-byte chunks
+  // XOR-permuted (chunk ^ (row & 15), resp. chunk ^ swz8(row)).  V^T rows are 128 B
+  // (64 slots), chunk ^ swz8(row).  Keys past the visible end read the last one (masked).
+  auto issue = [&](int st, int t) {
+    const int a = t * KT;
+#pragma unroll
+    for (int j = 0; j < INS; ++j) {
+      const int blk = j * NW + wave;
+      int row, gch;
+      if constexpr (DH == 128) {
+        row = blk * 4 + (lane >> 4);
+        gch = (lane & 15) ^ (row & 15);
+      } else {
+        row = blk * 8 + (lane >> 3);
+        gch = (lane & 7) ^ swz8(row);
+      }
+      const int key = min(a + row, plim - 1);
+      dma16(key_ptr(km, ks_, p, b, g, key) + gch * 8, (lds_void_t*)(kst(st) + blk * 512));
+      const int vr = blk * 8 + (lane >> 3);
+      const int vch = (lane & 7) ^ swz8(vr);
+      dma16(vtb + (int64_t)vr * tpad + a + vch * 8, (lds_void_t*)(vst(st) + blk * 512));
+    }
+  };
+
+  const float c2 = p.scale * kLog2e;
+  int t = tile_needed(0) ? 0 : next_tile(0);
+  int tq[NS];  // tiles issued into the stages after the current one
+  int st = 0;
+  if (t < ntile) issue(0, t);
+  tq[0] = t < ntile ? next_tile(t) : ntile;
+  if (tq[0] < ntile) issue(1, tq[0]);
+  if constexpr (NS == 3) {
+    tq[1] = tq[0] < ntile ? next_tile(tq[0]) : ntile;
+    if (tq[1] < ntile) issue(2, tq[1]);
+    if (tq[1] < ntile) wait_vm<4 * INS>();
+    else if (tq[0] < ntile) wait_vm<2 * INS>();
+    else wait_vm<0>();
+  } else {
+    if (tq[0] < ntile) wait_vm<2 * INS>();
+    else wait_vm<0>();
+  }
+  lds_barrier();
+
+  while (t < ntile) {
+    const bf16* kt_ = kst(st);
+    const bf16* vt_ = vst(st);
+    floatx4 sacc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sacc[i][0] = sacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int row = kt * 16 + (lane & 15), c = ks * 4 + (lane >> 4);
+        const int sw = DH == 128 ? (c ^ (row & 15)) : (c ^ swz8(row));
+        const bf16x8 kf = *(const bf16x8*)(kt_ + row * DH + sw * 8);
+        sacc[kt][0] = mfma16x16x32(kf, qf[0][ks], sacc[kt][0]);
+        sacc[kt][1] = mfma16x16x32(kf, qf[1][ks], sacc[kt][1]);
+      }
+    }
+
+    const int a = t * KT;
+    const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
+    const bool full = a + KT - 1 <= i_lo &&
+                      (p.window <= 0 || a + KT <= p.n_meta || i_hi - max(a, p.n_meta) < p.window);
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int i = wp0 + qt * 16 + (lane & 15);
+      float mx = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = a + kt * 16 + (lane >> 4) * 4 + r;
+            const float sv = key_visible(i, j, p.n_meta, p.window) ? sacc[kt][qt][r] : -INFINITY;
+            sacc[kt][qt][r] = sv;
+            mx = fmaxf(mx, sv);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrow[qt], mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);
+      mrow[qt] = mnew;
+      const float mc2 = muse * c2;
+      float ls = 0.f;
+      float pv[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][r], c2, -mc2));
+          pv[kt][r] = e;
+          ls += e;
+        }
+      lrow[qt] = lrow[qt] * alpha + ls;
+#pragma unroll
+      for (int d = 0; d < DH / 16; ++d) oacc[d][qt] *= alpha;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f[r] = (bf16)pv[2 * k2][r];
+          f[4 + r] = (bf16)pv[2 * k2 + 1][r];
+        }
+        pf[k2][qt] = f;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int row = d * 16 + (lane & 15), c = k2 * 4 + (lane >> 4);
+        const bf16x8 vf = *(const bf16x8*)(vt_ + row * 64 + ((c ^ swz8(row)) * 8));
+        oacc[d][0] = mfma16x16x32(vf, pf[k2][0], oacc[d][0]);
+        oacc[d][1] = mfma16x16x32(vf, pf[k2][1], oacc[d][1]);
+      }
+
+    // hand-over: the next tile has landed (one more may stay in flight), every wave is
+    // done with this stage, which then takes the tile after the ones in flight
+    const int tn = tq[0];
+    if (tn >= ntile) break;
+    if constexpr (NS == 3) {
+      if (tq[1] < ntile) wait_vm<2 * INS>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    const int tlast = NS == 3 ? tq[1] : tq[0];
+    const int tnew = tlast < ntile ? next_tile(tlast) : ntile;
+    if (tnew < ntile) issue(st, tnew);
+    if constexpr (NS == 3) {
+      tq[0] = tq[1];
+      tq[1] = tnew;
+    } else {
+      tq[0] = tnew;
+    }
+    st = st + 1 == NS ? 0 : st + 1;
+    t = tn;
+  }
+
+  bf16* obase = (bf16*)p.o;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = lrow[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int pos = wp0 + qt * 16 + (lane & 15);
+    if (pos >= plim) continue;
+    bf16* dst = obase + pos_row(pos, b, p.n_meta, p.L) * p.o_row_stride + h * DH + (lane >> 4) * 4;
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d) {
+      bf16x4 o;
+      o[0] = (bf16)(oacc[d][qt][0] * inv);
+      o[1] = (bf16)(oacc[d][qt][1] * inv);
+      o[2] = (bf16)(oacc[d][qt][2] * inv);
+      o[3] = (bf16)(oacc[d][qt][3] * inv);
+      *(bf16x4*)(dst + d * 16) = o;
+    }
+  }
+}
+
+template <int DH, int NW, int NS>
+static hipError_t run_attn_dl(const AttnParams& p, void* vt, hipStream_t s) {
+  const int total = p.n_meta + p.L;
+  const int tpad = (total + 63) / 64 * 64;
+  const int vb = (p.B > 0 ? p.B : 1);
+  vt_build_kernel<DH><<<dim3(tpad / 64, p.Hkv, vb), dim3(256), 0, s>>>(p, (bf16*)vt, tpad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grp = p.Hq / p.Hkv;
+  const int gq = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
+  const int qb = 32 * (NW / gq);
+  const int nblk_seq = (p.L + qb - 1) / qb;
+  const int nblk_meta = (p.n_meta + qb - 1) / qb;
+  const int nx = p.B * nblk_seq + nblk_meta;
+  if (nx == 0) return hipSuccess;
+  attn_prefill_dl_kernel<DH, NW, NS><<<dim3(nx, p.Hq / gq), dim3(NW * 64), 0, s>>>(
+      p, (const bf16*)vt, tpad, gq, qb, nblk_seq);
+  return hipGetLastError();
+}
+
+size_t attention_vt_bytes(int n_meta, int L, int B, int Hkv, int head_dim) {
+  const int64_t tpad = (int64_t)(n_meta + L + 63) / 64 * 64;
+  return (size_t)(B > 0 ? B : 1) * Hkv * head_dim * tpad * 2;
+}
+
+hipError_t launch_attention_prefill_bf16_dl(const AttnParams& p, void* vt, hipStream_t s) {
+  if (p.head_dim == 128) return run_attn_dl<128, 8, 3>(p, vt, s);
+  if (p.head_dim == 64) return run_attn_dl<64, 8, 3>(p, vt, s);
+  return hipErrorInvalidValue;
+}
+
 // --------------------------------------------------------------------- fp32 prefill
 // One wave per (query row, q head); lanes cover head_dim (<= 128).  Plain online
 // softmax over the visible keys.

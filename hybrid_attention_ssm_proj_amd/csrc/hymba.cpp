@@ -138,7 +138,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-  size_t z, delta, bc, dt, f, part, xdbl, yacc, total;
+  size_t z, delta, bc, dt, f, vt, part, xdbl, yacc, total;
 };
 
 
@@ -159,7 +159,7 @@ bool fused_dt(const Shape& s) { return s.bf16 && scan_fused_supported(s.N, s.R, 
 
 // Prefill: rows = meta rows + batch * tokens.  dt is materialised only when the scan
 // does not compute it in place.
-Carve carve_prefill(const Shape& s, int64_t rows) {
+Carve carve_prefill(const Shape& s, int64_t rows, int B, int L) {
   Carve c{};
   size_t off = 0;
   c.z = off;
@@ -172,6 +172,8 @@ Carve carve_prefill(const Shape& s, int64_t rows) {
   if (!fused_dt(s)) off = align_up(off + (size_t)rows * s.Di * 4);
   c.f = off;
   off = align_up(off + (size_t)rows * s.fw * s.es);
+  c.vt = off;  // bf16 attention: V^T staging
+  if (s.bf16) off = align_up(off + attention_vt_bytes(s.M, L, B, s.Hkv, s.dh));
   c.total = off;
   return c;
 }
@@ -249,7 +251,7 @@ size_t hymba_layer_workspace_bytes(const hymba_layer_desc* desc, int32_t batch, 
   if (make_shape(desc, s) != HYMBA_OK || batch < 0 || seq_len < 0) return 0;
   if (mode == 0) {
     const int64_t rows = (int64_t)s.M + (int64_t)batch * seq_len;
-    return carve_prefill(s, rows).total;
+    return carve_prefill(s, rows, batch, seq_len).total;
   }
   if (mode == 1) {
     // seq_len carries the ring capacity (slots) for decode.
@@ -323,7 +325,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     if (any_misaligned(state_out->h, state_out->pos)) return HYMBA_ERR_ALIGNMENT;
   }
   if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
-  const Carve cv = carve_prefill(s, rows);
+  const Carve cv = carve_prefill(s, rows, B, L);
   if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_;
   if (rows == 0) return HYMBA_OK;
@@ -395,8 +397,9 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     ap.head_dim = s.dh;
     ap.window = s.W;
     ap.scale = s.scale;
-    HYMBA_LAUNCH(HYMBA_STAGE_ATTN, b16 ? launch_attention_prefill_bf16(ap, stream)
-                                       : launch_attention_prefill_f32(ap, stream));
+    HYMBA_LAUNCH(HYMBA_STAGE_ATTN,
+                 b16 ? launch_attention_prefill_bf16_dl(ap, ws_ptr(workspace, cv.vt), stream)
+                     : launch_attention_prefill_f32(ap, stream));
   }
   // 4. x_proj: [delta | B | C] = Xs W_x^T.
   {

@@ -83,6 +83,10 @@ struct AttnParams {
 };
 hipError_t launch_attention_prefill_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s);
+// bf16 prefill with direct-to-LDS K / V^T tiles; `vt` is scratch of
+// attention_vt_bytes(...) bytes (16-byte aligned) that receives V^T first.
+size_t attention_vt_bytes(int n_meta, int L, int B, int Hkv, int head_dim);
+hipError_t launch_attention_prefill_bf16_dl(const AttnParams& p, void* vt, hipStream_t s);
 
 // Decode: one query per sequence at X-position pos[b]; keys = meta + the
 // min(pos+1, span_max) most recent ring positions.  Partial results per split go to

@@ -50,8 +50,10 @@ def test_workspace_sizes(lib):
     rows = 128 + 8 * 2048
     n_in = 16 * 128 + 2 * 4 * 128 + 2 * 4096
     got = hy.hymba_layer_workspace_bytes(d, 8, 2048, 0)
-    # Z, delta (bf16), B|C (fp32), F (bf16); this shape computes dt inside the scan
-    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2)
+    # Z, delta (bf16), B|C (fp32), F (bf16); this shape computes dt inside the scan;
+    # plus V^T staging for attention: B x Hkv x head_dim x (keys rounded up to 64), bf16
+    vt = 8 * 4 * 128 * ((128 + 2048 + 63) // 64 * 64) * 2
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt
     assert floor <= got <= floor + 8 * 256
     # fp32 layers keep a separate fp32 dt buffer
     d0 = desc_of(0)
