@@ -28,6 +28,7 @@ namespace hymba {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.f;  // lazy-rescaling headroom (log2 units)
 
 // X~ position -> row of the query / Z arrays.
 __device__ __forceinline__ int64_t pos_row(int pos, int b, int n_meta, int L) {
@@ -425,8 +426,11 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   const int wp0 = p0 + (wave / gq) * 32;
 
   const bf16* qbase = (const bf16*)p.q;
-  const bf16* km = (const bf16*)p.k_meta;
-  const bf16* ks_ = (const bf16*)p.k_seq;
+  // K rows of this (sequence, kv head): meta key j at kmeta + j*meta_row_stride, key
+  // j >= n_meta at kseq + (j - n_meta)*seq_row_stride (prefill sources hold every
+  // position: seq_slots >= L, so no ring wrap).
+  const bf16* kmeta = (const bf16*)p.k_meta + g * p.meta_head_stride;
+  const bf16* kseq = (const bf16*)p.k_seq + (int64_t)b * p.seq_batch_stride + g * p.seq_head_stride;
   const bf16* vtb = vt + ((int64_t)b * p.Hkv + g) * DH * tpad;
 
   bf16x8 qf[2][DH / 32];
@@ -478,7 +482,9 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
         gch = (lane & 7) ^ swz8(row);
       }
       const int key = min(a + row, plim - 1);
-      dma16(key_ptr(km, ks_, p, b, g, key) + gch * 8, (lds_void_t*)(kst(st) + blk * 512));
+      const bf16* krow = key < p.n_meta ? kmeta + (int64_t)key * p.meta_row_stride
+                                        : kseq + (int64_t)(key - p.n_meta) * p.seq_row_stride;
+      dma16(krow + gch * 8, (lds_void_t*)(kst(st) + blk * 512));
       const int vr = blk * 8 + (lane >> 3);
       const int vch = (lane & 7) ^ swz8(vr);
       dma16(vtb + (int64_t)vr * tpad + a + vch * 8, (lds_void_t*)(vst(st) + blk * 512));
@@ -526,7 +532,12 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
     const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
     const bool full = a + KT - 1 <= i_lo &&
                       (p.window <= 0 || a + KT <= p.n_meta || i_hi - max(a, p.n_meta) < p.window);
-    bf16x8 pf[2][2];
+    // Row maxima of the tile (masked where needed), then lazy rescaling: the running
+    // max m moves only when some row's tile max exceeds it by more than kLazyLog2 in
+    // log2 units (wave-uniform decision), so O and l are rescaled rarely and every
+    // exp2 argument stays <= kLazyLog2 (P <= 2^kLazyLog2, exact in the fp32 sums and
+    // in bf16 for the MFMA).  O / l is unchanged by the choice of m.
+    float tmax[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int i = wp0 + qt * 16 + (lane & 15);
@@ -548,12 +559,25 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
           }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);
-      mrow[qt] = mnew;
-      const float mc2 = muse * c2;
+      tmax[qt] = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    const float thr = kLazyLog2 / c2;
+    if (__builtin_amdgcn_ballot_w64(tmax[0] > mrow[0] + thr || tmax[1] > mrow[1] + thr)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mnew = fmaxf(mrow[qt], tmax[qt]);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);  // 0 from -inf
+        mrow[qt] = mnew;
+        lrow[qt] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DH / 16; ++d) oacc[d][qt] *= alpha;
+      }
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mc2 = (mrow[qt] == -INFINITY ? 0.f : mrow[qt]) * c2;
       float ls = 0.f;
       float pv[4][4];
 #pragma unroll
@@ -564,9 +588,7 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
           pv[kt][r] = e;
           ls += e;
         }
-      lrow[qt] = lrow[qt] * alpha + ls;
-#pragma unroll
-      for (int d = 0; d < DH / 16; ++d) oacc[d][qt] *= alpha;
+      lrow[qt] += ls;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 f;
