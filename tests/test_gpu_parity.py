@@ -210,6 +210,36 @@ def test_small_bf16_decode_ring_wrap():
     assert np.all(st["pos"].cpu().numpy() == L + steps)
 
 
+@pytest.mark.parametrize("head_dim,n_kv", [(128, 2), (64, 4)])
+def test_bf16_decode_streaming_attention(head_dim, n_kv):
+    """Batches whose sequences x kv heads fill the chip (>= 256) take the decode
+    attention that streams every key of a (sequence, kv head) in one workgroup; the
+    96-slot ring wraps during the steps."""
+    dims = small_dims(window=96, head_dim=head_dim, n_kv_heads=n_kv)
+    B, L, S, steps = 256 // n_kv, 90, 96, 10
+    w = gen_layer_weights(dims, 84)
+    meta_t, meta, x_t, x = gen_activations(dims, 84, B, L + steps)
+    ref = orc.prefill(dims, w, meta, x[:, :L], contract=True, ring_slots=S)
+    layer = make_layer(dims, w)
+    to_dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(DEV)
+    kv = {k: to_dev(ref[k], torch.bfloat16) for k in ("k_meta", "v_meta", "k", "v")}
+    st = {"h": to_dev(ref["h"], torch.float32),
+          "pos": torch.full((B,), L, dtype=torch.int32, device=DEV)}
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    xb = x_t.to(DEV)
+    for s in range(steps):
+        y = layer.decode(xb[:, L + s].contiguous(), kv_struct(kv), state_struct(st))
+        o = orc.decode_step(dims, w, x[:, L + s], ref["k_meta"], ref["v_meta"], o["k"], o["v"],
+                            o["h"], o["pos"], contract=True)
+        torch.cuda.synchronize()
+        e = rel_err(to_np(y), o["y"])
+        assert e < TOL_BF16, (s, e)
+    print("last step y err", f"{e:.2e}")
+    assert rel_err(to_np(st["h"]), o["h"]) < TOL_H
+    assert rel_err(to_np(kv["k"]), o["k"]) < TOL_BF16
+    assert np.all(st["pos"].cpu().numpy() == L + steps)
+
+
 def test_gemm_op_bf16_ragged():
     import hybrid_attention_ssm_proj_amd as hy
     g = np.random.default_rng(5)
