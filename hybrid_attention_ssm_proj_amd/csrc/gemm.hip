@@ -454,10 +454,10 @@ struct FewRowOut {
   int64_t zero_n4;
 };
 
-template <bool ATOMIC>
+template <bool ATOMIC, int BM>
 __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, FewRowOut out,
                                                                int kslice) {
-  constexpr int BM = 128, BN = 64, NW = 4, WN = 2;
+  constexpr int BN = 64, NW = 4, WN = 2;
   constexpr int TM = BM / 2, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW, INS = A_INS + B_INS;
@@ -619,7 +619,7 @@ hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t l
   out.acc = acc;
   out.ldacc = ldacc;
   dim3 grid((op.N + 63) / 64, ns, (op.M + 127) / 128);
-  gemm_bf16_fewrow_kernel<true><<<grid, dim3(256), 0, s>>>(op, out, kslice);
+  gemm_bf16_fewrow_kernel<true, 128><<<grid, dim3(256), 0, s>>>(op, out, kslice);
   return hipGetLastError();
 }
 
@@ -643,8 +643,10 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
   out.head_dim = head_dim;
   out.Hkv = Hkv;
   out.pos = pos;
-  dim3 grid((op.N + 63) / 64, 1, (op.M + 127) / 128);
-  gemm_bf16_fewrow_kernel<false><<<grid, dim3(256), 0, s>>>(op, out, op.K);
+  // 64-row blocks: twice the workgroups of one 128-row block per column tile (the
+  // weight slice is then read by two workgroups, mostly from L2)
+  dim3 grid((op.N + 63) / 64, 1, (op.M + 63) / 64);
+  gemm_bf16_fewrow_kernel<false, 64><<<grid, dim3(256), 0, s>>>(op, out, op.K);
   return hipGetLastError();
 }
 
