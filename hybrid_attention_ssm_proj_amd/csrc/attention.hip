@@ -9,13 +9,13 @@
 // (j < M or window == 0 or i - j < window); scale 1/sqrt(head_dim) unless given.
 //
 // Prefill (bf16): flash-style, one workgroup per (query block, kv head, head
-// subgroup).  Its 4 waves each own 32 query rows of one q head; all share the K/V
-// tiles of their kv head staged in LDS.  The waves compute S^T = K Q^T with
+// subgroup).  Its waves each own 32 query rows of one q head; all share the K/V tiles
+// of their kv head staged in LDS.  The waves compute S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16, so the softmax statistics of a query live in one lane
-// column, and O^T = V^T P^T takes P^T straight from the S^T accumulators (the
-// 32-key k-order of the second MFMA is permuted to match them; V is stored
-// transposed and permuted the same way).  Key tiles that hold no visible key for the
-// block (outside the meta prefix and the window) are skipped.
+// column, and O^T = V^T P^T takes P^T straight from the S^T accumulators (the 32-key
+// k-order of the second MFMA is permuted to match them; V is staged transposed and
+// permuted the same way).  Key tiles that hold no visible key for the block (outside
+// the meta prefix and the window) are skipped.
 #include <float.h>
 
 #include <type_traits>
@@ -44,314 +44,27 @@ __device__ __forceinline__ const T* key_ptr(const T* meta, const T* seq, const A
          (int64_t)slot * p.seq_row_stride;
 }
 
-__device__ __forceinline__ void load8(const bf16* p, float out[8]) {
-  const bf16x8 v = *(const bf16x8*)p;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
-}
-__device__ __forceinline__ void load8(const float* p, float out[8]) {
-  const floatx4 a = *(const floatx4*)p, b = *(const floatx4*)(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    out[e] = a[e];
-    out[4 + e] = b[e];
-  }
-}
-
 __device__ __forceinline__ bool key_visible(int i, int j, int n_meta, int window) {
   return j <= i && (j < n_meta || window <= 0 || i - j < window);
 }
 
-template <int DH>
-struct AttnCfg {
-  static constexpr int KT = 64;            // keys per tile
-  static constexpr int KLDS = DH + 8;      // K row pitch (bf16)
-  static constexpr int VLDS = KT + 8;      // V^T row pitch (bf16)
-  static constexpr int KE = KT * KLDS;
-  static constexpr int VE = DH * VLDS;
-  static constexpr int CPR = DH / 8;       // 16-byte chunks per key row
-  static constexpr int CH = KT * CPR / 256;
-  static constexpr size_t SMEM = (size_t)2 * (KE + VE) * sizeof(bf16);
-};
-
-// slot of key k (0..63) inside the V^T tile; see the file comment.
-__device__ __forceinline__ int vt_slot(int k) {
-  const int blk = k >> 5, kk = k & 31;
-  return blk * 32 + ((kk & 15) >> 2) * 8 + (kk & 3) + ((kk >> 4) << 2);
-}
-
 }  // namespace
-
-template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnParams p, int gq, int qb,
-                                                                   int nblk_seq) {
-  using Cfg = AttnCfg<DH>;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16* Ks = (bf16*)smem_raw;            // [2][KT][KLDS]
-  bf16* Vt = Ks + 2 * Cfg::KE;           // [2][DH][VLDS]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bid = blockIdx.x;
-  int b, p0, plim;
-  if (bid < p.B * nblk_seq) {
-    b = bid % p.B;
-    const int qi = nblk_seq - 1 - bid / p.B;  // longest blocks first
-    p0 = p.n_meta + qi * qb;
-    plim = p.n_meta + min(p.L, (qi + 1) * qb);
-  } else {
-    b = 0;
-    const int mi = bid - p.B * nblk_seq;
-    p0 = mi * qb;
-    plim = min(p.n_meta, (mi + 1) * qb);
-  }
-  const int h0 = blockIdx.y * gq;
-  const int h = h0 + (wave % gq);
-  const int g = (h0 * p.Hkv) / p.Hq;
-  const int wp0 = p0 + (wave / gq) * 32;
-
-  const bf16* qbase = (const bf16*)p.q;
-  const bf16* km = (const bf16*)p.k_meta;
-  const bf16* vm = (const bf16*)p.v_meta;
-  const bf16* ks_ = (const bf16*)p.k_seq;
-  const bf16* vs_ = (const bf16*)p.v_seq;
-
-  // Q fragments: B operand of S^T = K Q^T.
-  bf16x8 qf[2][DH / 32];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int pos = wp0 + qt * 16 + (lane & 15);
-    const bool ok = pos < plim;
-    const bf16* src = qbase + pos_row(ok ? pos : 0, b, p.n_meta, p.L) * p.q_row_stride + h * DH +
-                      (lane >> 4) * 8;
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) {
-      u32x4 v = ok ? *(const u32x4*)(src + ks * 32) : u32x4{0, 0, 0, 0};
-      qf[qt][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  floatx4 oacc[DH / 16][2];
-#pragma unroll
-  for (int i = 0; i < DH / 16; ++i) oacc[i][0] = oacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
-
-  // Visible key range of the block: [0, meta_end) and [wlo, plim).
-  const int meta_end = min(p.n_meta, plim);
-  const int wlo = p.window > 0 ? max(p.n_meta, p0 - p.window + 1) : p.n_meta;
-  const int ntile = (plim + Cfg::KT - 1) / Cfg::KT;
-  auto tile_needed = [&](int t) {
-    const int a = t * Cfg::KT, e = a + Cfg::KT;
-    return a < meta_end || (e > wlo && a < plim);
-  };
-  auto next_tile = [&](int t) {
-    ++t;
-    while (t < ntile && !tile_needed(t)) ++t;
-    return t;
-  };
-
-  // Loader: K rows contiguous (4 keys x 256 B per wave instruction); V as 16 keys x
-  // 64 B per wave instruction, scattered transposed into V^T.
-  u32x4 rk[Cfg::CH], rv[Cfg::CH];
-  auto gload = [&](int t) {
-    const int a = t * Cfg::KT;
-#pragma unroll
-    for (int c = 0; c < Cfg::CH; ++c) {
-      const int q = tid + c * 256;
-      const int kk = q / Cfg::CPR, dc = q % Cfg::CPR;
-      const int j = a + kk;
-      rk[c] = (j < plim) ? *(const u32x4*)(key_ptr(km, ks_, p, b, g, j) + dc * 8)
-                         : u32x4{0, 0, 0, 0};
-      const int combo = c * 4 + wave;
-      const int vk = (combo % 4) * 16 + (lane & 15);
-      const int vdc = (combo / 4) * 4 + (lane >> 4);
-      const int jv = a + vk;
-      rv[c] = (jv < plim) ? *(const u32x4*)(key_ptr(vm, vs_, p, b, g, jv) + vdc * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto sstore = [&](int buf) {
-    bf16* kd = Ks + buf * Cfg::KE;
-    bf16* vd = Vt + buf * Cfg::VE;
-#pragma unroll
-    for (int c = 0; c < Cfg::CH; ++c) {
-      const int q = tid + c * 256;
-      const int kk = q / Cfg::CPR, dc = q % Cfg::CPR;
-      *(u32x4*)(kd + kk * Cfg::KLDS + dc * 8) = rk[c];
-      const int combo = c * 4 + wave;
-      const int vk = (combo % 4) * 16 + (lane & 15);
-      const int vdc = (combo / 4) * 4 + (lane >> 4);
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, rv[c]);
-      const int slot = vt_slot(vk);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vd[(vdc * 8 + e) * Cfg::VLDS + slot] = vv[e];
-    }
-  };
-
-  const float c2 = p.scale * kLog2e;
-  int t = tile_needed(0) ? 0 : next_tile(0);
-  if (t < ntile) {
-    gload(t);
-    sstore(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (t < ntile) {
-    const int tn = next_tile(t);
-    if (tn < ntile) gload(tn);
-    const bf16* kt_ = Ks + buf * Cfg::KE;
-    const bf16* vt_ = Vt + buf * Cfg::VE;
-
-    floatx4 sacc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sacc[i][0] = sacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 kf =
-            *(const bf16x8*)(kt_ + (kt * 16 + (lane & 15)) * Cfg::KLDS + ks * 32 + (lane >> 4) * 8);
-        sacc[kt][0] = mfma16x16x32(kf, qf[0][ks], sacc[kt][0]);
-        sacc[kt][1] = mfma16x16x32(kf, qf[1][ks], sacc[kt][1]);
-      }
-    }
-
-    const int a = t * Cfg::KT;
-    // The mask is needed only where some (query, key) pair of the wave is hidden: the
-    // diagonal tile and the window's lower edge.  Wave-uniform.
-    const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
-    const bool full = a + Cfg::KT - 1 <= i_lo &&
-                      (p.window <= 0 || a + Cfg::KT <= p.n_meta ||
-                       i_hi - max(a, p.n_meta) < p.window);
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int i = wp0 + qt * 16 + (lane & 15);
-      float mx = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = a + kt * 16 + (lane >> 4) * 4 + r;
-            const float s = key_visible(i, j, p.n_meta, p.window) ? sacc[kt][qt][r] : -INFINITY;
-            sacc[kt][qt][r] = s;
-            mx = fmaxf(mx, s);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);
-      mrow[qt] = mnew;
-      const float mc2 = muse * c2;
-      float ls = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][r], c2, -mc2));
-          pv[kt][r] = e;
-          ls += e;
-        }
-      lrow[qt] = lrow[qt] * alpha + ls;
-#pragma unroll
-      for (int d = 0; d < DH / 16; ++d) oacc[d][qt] *= alpha;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f[r] = (bf16)pv[2 * k2][r];
-          f[4 + r] = (bf16)pv[2 * k2 + 1][r];
-        }
-        pf[k2][qt] = f;
-      }
-    }
-
-#pragma unroll
-    for (int d = 0; d < DH / 16; ++d)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 vf =
-            *(const bf16x8*)(vt_ + (d * 16 + (lane & 15)) * Cfg::VLDS + k2 * 32 + (lane >> 4) * 8);
-        oacc[d][0] = mfma16x16x32(vf, pf[k2][0], oacc[d][0]);
-        oacc[d][1] = mfma16x16x32(vf, pf[k2][1], oacc[d][1]);
-      }
-
-    if (tn < ntile) sstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    t = tn;
-  }
-
-  bf16* obase = (bf16*)p.o;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = lrow[qt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int pos = wp0 + qt * 16 + (lane & 15);
-    if (pos >= plim) continue;
-    bf16* dst = obase + pos_row(pos, b, p.n_meta, p.L) * p.o_row_stride + h * DH + (lane >> 4) * 4;
-#pragma unroll
-    for (int d = 0; d < DH / 16; ++d) {
-      bf16x4 o;
-      o[0] = (bf16)(oacc[d][qt][0] * inv);
-      o[1] = (bf16)(oacc[d][qt][1] * inv);
-      o[2] = (bf16)(oacc[d][qt][2] * inv);
-      o[3] = (bf16)(oacc[d][qt][3] * inv);
-      *(bf16x4*)(dst + d * 16) = o;
-    }
-  }
-}
-
-template <int DH>
-static hipError_t run_attn_bf16(const AttnParams& p, hipStream_t s) {
-  using Cfg = AttnCfg<DH>;
-  const int grp = p.Hq / p.Hkv;
-  const int gq = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);  // heads per workgroup, one kv head
-  const int qb = 32 * (4 / gq);
-  const int nblk_seq = (p.L + qb - 1) / qb;
-  const int nblk_meta = (p.n_meta + qb - 1) / qb;
-  const int nx = p.B * nblk_seq + nblk_meta;
-  if (nx == 0) return hipSuccess;
-  auto kern = attn_prefill_bf16_kernel<DH>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  kern<<<dim3(nx, p.Hq / gq), dim3(256), Cfg::SMEM, s>>>(p, gq, qb, nblk_seq);
-  return hipGetLastError();
-}
-
-hipError_t launch_attention_prefill_bf16(const AttnParams& p, hipStream_t s) {
-  if (p.head_dim == 128) return run_attn_bf16<128>(p, s);
-  if (p.head_dim == 64) return run_attn_bf16<64>(p, s);
-  return hipErrorInvalidValue;
-}
 
 // ------------------------------------------------- bf16 prefill, direct-to-LDS tiles
 // V^T staging: the P V product needs, per lane, 8 consecutive keys of one head_dim
 // column (the k operand of the MFMA), while V is stored key-major.  A small kernel
 // writes V^T per (sequence, kv head): vt[b][g][d][slot] over the meta-prefixed key axis
 // (tpad = keys rounded up to 64, zero past the end), keys permuted inside each 32-key
-// block to the slot order of the S^T accumulators (vt_slot).  Then both the K tile
+// block to the slot order of the S^T accumulators (slot_key).  Then both the K tile
 // (64 keys x head_dim, key-major) and the V^T tile (head_dim x 64 slots) move straight
 // from global memory into LDS with global_load_lds_dwordx4 (no register staging, no
 // scattered LDS stores), NS stages deep.
 namespace {
-__device__ __forceinline__ int slot_key(int s) {  // inverse of vt_slot within 64
+// Slot order of V^T inside a 64-key tile: the P^T operand a lane builds from its S^T
+// accumulators holds, for k-block q = lane / 16 of 32-key half blk, the keys
+// blk*32 + 4q + (0..3) and blk*32 + 16 + 4q + (0..3); V^T slots blk*32 + 8q + (0..7)
+// hold the same keys in the same order.  slot_key maps a slot to its key.
+__device__ __forceinline__ int slot_key(int s) {
   const int blk = s >> 5, q = (s & 31) >> 3, i = s & 7;
   return blk * 32 + (i < 4 ? q * 4 + i : 16 + q * 4 + (i - 4));
 }

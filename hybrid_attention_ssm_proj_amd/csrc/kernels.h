@@ -81,7 +81,6 @@ struct AttnParams {
   int n_meta, L, B, Hq, Hkv, head_dim, window;
   float scale;
 };
-hipError_t launch_attention_prefill_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s);
 // bf16 prefill with direct-to-LDS K / V^T tiles; `vt` is scratch of
 // attention_vt_bytes(...) bytes (16-byte aligned) that receives V^T first.
