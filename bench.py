@@ -62,8 +62,9 @@ def stage_work(dims, B, L):
     pairs_meta = M * (M + 1) // 2
     attn_flops = 4 * dims.head_dim * dims.n_q_heads * (B * pairs_seq + pairs_meta)
     return {
-        # the meta rows are projected once, by their own launch
-        "meta_in_proj": ("mfma", 2.0 * M * dims.n_in * d),
+        # the batch-shared meta rows go through in_proj and out_proj in launches of
+        # their own (two per step)
+        "meta": ("mfma", 2.0 * M * (dims.n_in + dims.f_width) * d),
         "in_proj": ("mfma", 2.0 * B * L * dims.n_in * d),
         "attn": ("mfma", float(attn_flops)),
         "x_proj": ("mfma", 2.0 * rows * dims.n_xproj * Di),
@@ -73,7 +74,7 @@ def stage_work(dims, B, L):
         "scan": ("hbm", float(rows * (Di * 6 + 2 * R + 8 * N) + B * Di * N * 4)),
         # bytes: read O and Y_ssm, write F (bf16)
         "norm": ("hbm", float(rows * (qw + Di) * 2 * 2)),
-        "out_proj": ("mfma", 2.0 * rows * dims.f_width * d),
+        "out_proj": ("mfma", 2.0 * B * L * dims.f_width * d),
     }
 
 

@@ -24,7 +24,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE",
           4: "ERR_ALIGNMENT", 5: "ERR_HIP"}
 STAGES = ["in_proj", "attn", "x_proj", "dt_proj", "scan", "norm", "out_proj", "kv_write",
-          "meta_in_proj", "misc"]
+          "meta", "misc"]
 
 
 class HymbaError(RuntimeError):

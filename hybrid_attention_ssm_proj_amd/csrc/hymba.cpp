@@ -138,7 +138,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-  size_t z, delta, bc, dt, f, vt, part, xdbl, yacc, total;
+  size_t z, delta, bc, dt, f, vt, macc, part, xdbl, yacc, total;
 };
 
 
@@ -174,6 +174,8 @@ Carve carve_prefill(const Shape& s, int64_t rows, int B, int L) {
   off = align_up(off + (size_t)rows * s.fw * s.es);
   c.vt = off;  // bf16 attention: V^T staging
   if (s.bf16) off = align_up(off + attention_vt_bytes(s.M, L, B, s.Hkv, s.dh));
+  c.macc = off;  // bf16: fp32 accumulator of the split-K out_proj over the meta rows
+  if (s.bf16) off = align_up(off + (size_t)s.M * s.d * 4);
   c.total = off;
   return c;
 }
@@ -341,10 +343,19 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   };
 
   // 1. in_proj over [meta; X]: the batch-shared meta rows once, then the X rows.
+  // The meta rows are few: the few-row kernel (64-row blocks, every column tile its own
+  // workgroup) fills the chip better than 256-row tiles.
+  const bool few_meta = b16 && s.d % 256 == 0 && s.fw % 256 == 0;
   if (M > 0) {
     GemmOperands op{meta, s.d, nullptr, 0, M, w->w_in, s.d, M, (int)s.n_in, s.d};
-    GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, M, 0, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_META, gemm(op, out, GemmShape::Large));
+    if (few_meta) {
+      HYMBA_LAUNCH(HYMBA_STAGE_META,
+                   launch_gemm_bf16_decode_in(op, z, s.n_in, -1, -1, nullptr, nullptr, 1, s.Hkv,
+                                              s.dh, nullptr, nullptr, 0, stream));
+    } else {
+      GemmOutput out{EpiKind::Store, z, s.n_in, nullptr, 0, M, 0, nullptr};
+      HYMBA_LAUNCH(HYMBA_STAGE_META, gemm(op, out, GemmShape::Large));
+    }
   }
   if (BL > 0) {
     GemmOperands op{x, s.d, nullptr, 0, (int)BL, w->w_in, s.d, (int)BL, (int)s.n_in, s.d};
@@ -448,11 +459,28 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   // 7. RMSNorm + beta + average, in place.
   HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
                                                   w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
-  // 8. out_proj: meta rows -> y_meta, sequence rows -> y.
-  {
-    GemmOperands op{f, s.fw, nullptr, 0, (int)rows, w->w_out, s.fw, (int)rows, s.d, (int)s.fw};
-    GemmOutput out{EpiKind::Store, y_meta, s.d, y, s.d, M, 0, nullptr};
+  // 8. out_proj: sequence rows -> y, then the batch-shared meta rows -> y_meta.  Two
+  // launches keep the large one on whole 256-row tiles (B*L rows), so it runs as an
+  // exact number of rounds over the CUs.
+  if (BL > 0) {
+    GemmOperands op{f + (size_t)M * s.fw * s.es, s.fw, nullptr, 0, (int)BL, w->w_out, s.fw,
+                    (int)BL, s.d, (int)s.fw};
+    GemmOutput out{EpiKind::Store, y, s.d, nullptr, 0, (int)BL, 0, nullptr};
     HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out, GemmShape::Large));
+  }
+  if (M > 0 && y_meta != nullptr) {
+    GemmOperands op{f, s.fw, nullptr, 0, M, w->w_out, s.fw, M, s.d, (int)s.fw};
+    if (few_meta) {  // K is long: split it into fp32 atomics, then round to bf16
+      float* macc = (float*)ws_ptr(workspace, cv.macc);
+      HYMBA_LAUNCH(HYMBA_STAGE_META, launch_zero_f32(macc, (int64_t)M * s.d, stream));
+      HYMBA_LAUNCH(HYMBA_STAGE_META,
+                   launch_gemm_bf16_splitk(op, macc, s.d, splitk_factor(M, s.d, (int)s.fw),
+                                           stream));
+      HYMBA_LAUNCH(HYMBA_STAGE_META, launch_store_rows(true, macc, y_meta, M, s.d, stream));
+    } else {
+      GemmOutput out{EpiKind::Store, y_meta, s.d, nullptr, 0, M, 0, nullptr};
+      HYMBA_LAUNCH(HYMBA_STAGE_META, gemm(op, out, GemmShape::Large));
+    }
   }
   if (state_out != nullptr && state_out->pos != nullptr && B > 0) {
     HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_fill_i32(state_out->pos, L, B, stream));

@@ -183,7 +183,7 @@ typedef enum {
   HYMBA_STAGE_NORM = 5,      /* RMSNorm + beta + average                         */
   HYMBA_STAGE_OUT_PROJ = 6,  /* out_proj GEMM                                    */
   HYMBA_STAGE_KV_WRITE = 7,  /* cache writes                                     */
-  HYMBA_STAGE_META = 8,      /* in_proj GEMM over the batch-shared meta rows     */
+  HYMBA_STAGE_META = 8,      /* in_proj and out_proj GEMMs over the meta rows   */
   HYMBA_STAGE_MISC = 9,      /* accumulator clears, format conversions, pos fill */
   HYMBA_NUM_STAGES = 10
 } hymba_stage;
