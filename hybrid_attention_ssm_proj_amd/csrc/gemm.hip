@@ -86,6 +86,34 @@ struct Epilogue {
       store4<float>(p, w, valid, ((uintptr_t)p & 15) == 0);
     }
   }
+  // Unchecked path for a whole tile: rows [m0, m1) inside one destination that is
+  // written with 16-byte stores (Store epilogue only; the caller checks the bounds).
+  __device__ __forceinline__ bool tile_fast(int m0, int m1) const {
+    if constexpr (K == EpiKind::Store) {
+      const bool first = m1 <= o.c_split;
+      if (!first && m0 < o.c_split) return false;
+      const T* base = (const T*)(first ? o.c0 : o.c1);
+      const int64_t ld = first ? o.ldc0 : o.ldc1;
+      return base != nullptr && ld % 8 == 0 && ((uintptr_t)base & 15) == 0;
+    } else {
+      return false;
+    }
+  }
+  // Output (m, n..n+7) = lo[0..3], hi[0..3]; valid after tile_fast() returned true.
+  __device__ __forceinline__ void store8(int m, int n, const float lo[4], const float hi[4]) const {
+    if constexpr (K == EpiKind::Store) {
+      const bool first = m < o.c_split;
+      T* p = (T*)(first ? o.c0 : o.c1) + (int64_t)(first ? m : m - o.c_split) *
+                                             (first ? o.ldc0 : o.ldc1) + n;
+      bf16x8 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w[r] = (bf16)lo[r];
+        w[4 + r] = (bf16)hi[r];
+      }
+      *(bf16x8*)p = w;
+    }
+  }
 };
 
 // --------------------------------------------------------------------- tile order
@@ -418,6 +446,34 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
 
   // acc[i][j] holds C^T of the 32 x 32 block: lane -> row rl, columns
   // (e/4)*8 + (lane/32)*4 + 0..3.
+  if (m0 + Cfg::BM <= g.M && n0 + Cfg::BN <= g.N && epi.tile_fast(m0, m0 + Cfg::BM)) {
+    // Interior tile: v_permlane32_swap exchanges lanes 32..63 of its first operand with
+    // lanes 0..31 of its second, so after swapping the column groups 2p (e = 8p..8p+3)
+    // and 2p+1 (e = 8p+4..8p+7) lane l < 32 holds columns 16p + 0..7 of row l and lane
+    // l + 32 holds columns 16p + 8..15: one 16-byte store each.
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          float lo[4], hi[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // (vector elements are copied to scalars first: a bit cast applied to the
+            // subscript itself reads element 0)
+            const float x0 = acc[i][j][8 * pp + r], x1 = acc[i][j][8 * pp + 4 + r];
+            const auto sw = __builtin_amdgcn_permlane32_swap(
+                __builtin_bit_cast(unsigned, x0), __builtin_bit_cast(unsigned, x1), false, false);
+            lo[r] = __builtin_bit_cast(float, (unsigned)sw[0]);
+            hi[r] = __builtin_bit_cast(float, (unsigned)sw[1]);
+          }
+          const int m = m0 + wm * Cfg::TM + i * 32 + rl;
+          const int n = n0 + wn * Cfg::TN + j * 32 + pp * 16 + (lane >> 5) * 8;
+          epi.store8(m, n, lo, hi);
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll

@@ -231,19 +231,23 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
     for (int e = tid; e < C::XE; e += 256) gate_s[e] = silu_f((float)gs(cur)[e]);
     lds_barrier();  // the next chunk's loads stay in flight
 
-    // Tokens in groups of LPC: all LDS reads of a group are issued before its state
-    // updates; the transpose-reduction then leaves lane sg with the full state sum of
-    // token g0 + sg, so every lane finishes one token's output.  Tokens past the chunk
-    // have dt = 0 and leave h unchanged.
+    // Tokens in groups of LPC.  With few states per lane group (LPC * NS <= 16) the LDS
+    // reads of group i + 1 are issued before the state updates of group i (two register
+    // sets), so their latency hides behind the exponentials, and all TC tokens run:
+    // tokens past the chunk have dt = 0, which leaves h unchanged (exp2(0) = 1 and a zero
+    // input term), and their outputs are never stored.  Larger groups read just in time.
+    // The transpose-reduction leaves lane sg with the full state sum of token g0 + sg, so
+    // every lane finishes one token's output.
     const bf16* xc = xs(cur);
     const float* bcc = bcs(cur);
-    for (int g0 = 0; g0 < tn; g0 += LPC) {
-      float dtv[LPC], xv[LPC], bv[LPC][NS], cv[LPC][NS];
+    constexpr bool kPipe = LPC * NS <= 16;
+    float dtv[2][LPC], xv[2][LPC], bv[2][LPC][NS], cv[2][LPC][NS];
+    auto fetch = [&](int slot, int g0) {
 #pragma unroll
       for (int u = 0; u < LPC; ++u) {
         const int tt = g0 + u;
-        dtv[u] = dt_s[tt * C::DTP + cl];
-        xv[u] = (float)xc[tt * CB + cl];
+        dtv[slot][u] = dt_s[tt * C::DTP + cl];
+        xv[slot][u] = (float)xc[tt * CB + cl];
         const float* brow = bcc + tt * 2 * N + sg * NS;
 #pragma unroll
         for (int k4 = 0; k4 < NS; k4 += 4) {
@@ -251,21 +255,23 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
           const floatx4 c4 = *(const floatx4*)(brow + N + k4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            bv[u][k4 + e] = b4[e];
-            cv[u][k4 + e] = c4[e];
+            bv[slot][u][k4 + e] = b4[e];
+            cv[slot][u][k4 + e] = c4[e];
           }
         }
       }
+    };
+    auto group = [&](int sl, int g0) {
       float part[LPC];
 #pragma unroll
       for (int u = 0; u < LPC; ++u) {
-        const float dx = dtv[u] * xv[u];
+        const float dx = dtv[sl][u] * xv[sl][u];
         float acc = 0.f;
 #pragma unroll
         for (int kk = 0; kk < NS; ++kk) {
-          const float a = __builtin_amdgcn_exp2f(dtv[u] * A2[kk]);
-          h[kk] = fmaf(a, h[kk], dx * bv[u][kk]);
-          acc = fmaf(h[kk], cv[u][kk], acc);
+          const float a = __builtin_amdgcn_exp2f(dtv[sl][u] * A2[kk]);
+          h[kk] = fmaf(a, h[kk], dx * bv[sl][u][kk]);
+          acc = fmaf(h[kk], cv[sl][u][kk], acc);
         }
         part[u] = acc;
       }
@@ -273,6 +279,52 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
       const int tt = g0 + sg;
       const float xt = (float)xc[tt * CB + cl];
       y_s[tt * CB + cl] = (bf16)(fmaf(Dc, xt, tot) * gate_s[tt * CB + cl]);
+    };
+    if constexpr (kPipe) {
+      fetch(0, 0);
+#pragma unroll
+      for (int gi = 0; gi < TC / LPC; ++gi) {
+        if (gi + 1 < TC / LPC) fetch((gi & 1) ^ 1, (gi + 1) * LPC);
+        group(gi & 1, gi * LPC);
+      }
+    } else {
+      for (int g0 = 0; g0 < tn; g0 += LPC) {
+        float dtw[LPC], xw[LPC], bw[LPC][NS], cw[LPC][NS];
+#pragma unroll
+        for (int u = 0; u < LPC; ++u) {
+          const int tt = g0 + u;
+          dtw[u] = dt_s[tt * C::DTP + cl];
+          xw[u] = (float)xc[tt * CB + cl];
+          const float* brow = bcc + tt * 2 * N + sg * NS;
+#pragma unroll
+          for (int k4 = 0; k4 < NS; k4 += 4) {
+            const floatx4 b4 = *(const floatx4*)(brow + k4);
+            const floatx4 c4 = *(const floatx4*)(brow + N + k4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bw[u][k4 + e] = b4[e];
+              cw[u][k4 + e] = c4[e];
+            }
+          }
+        }
+        float part[LPC];
+#pragma unroll
+        for (int u = 0; u < LPC; ++u) {
+          const float dx = dtw[u] * xw[u];
+          float acc = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < NS; ++kk) {
+            const float a = __builtin_amdgcn_exp2f(dtw[u] * A2[kk]);
+            h[kk] = fmaf(a, h[kk], dx * bw[u][kk]);
+            acc = fmaf(h[kk], cw[u][kk], acc);
+          }
+          part[u] = acc;
+        }
+        const float tot = transpose_reduce<LPC>(part, sg);
+        const int tt = g0 + sg;
+        const float xt = (float)xc[tt * CB + cl];
+        y_s[tt * CB + cl] = (bf16)(fmaf(Dc, xt, tot) * gate_s[tt * CB + cl]);
+      }
     }
     lds_barrier();
 
