@@ -44,9 +44,6 @@ __device__ __forceinline__ const T* key_ptr(const T* meta, const T* seq, const A
          (int64_t)slot * p.seq_row_stride;
 }
 
-__device__ __forceinline__ bool key_visible(int i, int j, int n_meta, int window) {
-  return j <= i && (j < n_meta || window <= 0 || i - j < window);
-}
 
 }  // namespace
 
@@ -69,6 +66,20 @@ __device__ __forceinline__ int slot_key(int s) {
   return blk * 32 + (i < 4 ? q * 4 + i : 16 + q * 4 + (i - 4));
 }
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48: v_permlane16_swap exchanges the odd
+// 16-lane rows of its first operand with the even rows of its second, v_permlane32_swap
+// the upper half of the first with the lower half of the second; with both operands a
+// copy of x, the two results hold the butterfly partners.
+__device__ __forceinline__ float max_over_key_lanes(float x) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+  const float y = fmaxf(__builtin_bit_cast(float, (unsigned)s16[0]),
+                        __builtin_bit_cast(float, (unsigned)s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, y),
+                                                    __builtin_bit_cast(unsigned, y), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)s32[0]),
+               __builtin_bit_cast(float, (unsigned)s32[1]));
+}
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lptr) {
   // global_load_lds_dwordx4 from inline asm: no VGPR result; the consumer waits
@@ -162,7 +173,11 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   floatx4 oacc[DH / 16][2];
 #pragma unroll
   for (int i = 0; i < DH / 16; ++i) oacc[i][0] = oacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY};
+  floatx4 lacc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
 
   const int meta_end = min(p.n_meta, plim);
   const int wlo = p.window > 0 ? max(p.n_meta, p0 - p.window + 1) : p.n_meta;
@@ -245,34 +260,47 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
     const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
     const bool full = a + KT - 1 <= i_lo &&
                       (p.window <= 0 || a + KT <= p.n_meta || i_hi - max(a, p.n_meta) < p.window);
-    // Row maxima of the tile (masked where needed), then lazy rescaling: the running
-    // max m moves only when some row's tile max exceeds it by more than kLazyLog2 in
-    // log2 units (wave-uniform decision), so O and l are rescaled rarely and every
-    // exp2 argument stays <= kLazyLog2 (P <= 2^kLazyLog2, exact in the fp32 sums and
-    // in bf16 for the MFMA).  O / l is unchanged by the choice of m.
+    if (!full) {
+      // Mask S^T[key j][query i] to -inf where j is not visible.  Lane holds keys
+      // j = a + c + 4 (lane / 16) with c = 16 kt + r, so each condition is one compare of
+      // the constant c with a per-lane threshold: j <= i <=> c <= lim; j < n_meta <=>
+      // c < mlim; i - j < window <=> c > lim - window.
+      const int lq = (lane >> 4) * 4;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int lim = wp0 + qt * 16 + (lane & 15) - a - lq;
+        if (p.window <= 0) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (kt * 16 + r > lim) sacc[kt][qt][r] = -INFINITY;
+        } else {
+          const int mlim = p.n_meta - a - lq, wlim = lim - p.window;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int c = kt * 16 + r;
+              if (c > lim || (c >= mlim && c <= wlim)) sacc[kt][qt][r] = -INFINITY;
+            }
+        }
+      }
+    }
+    // Row maxima of the tile, then lazy rescaling: the running max m moves only when
+    // some row's tile max exceeds it by more than kLazyLog2 in log2 units (wave-uniform
+    // decision), so O and l are rescaled rarely and every exp2 argument stays <=
+    // kLazyLog2 (P <= 2^kLazyLog2, exact in the fp32 sums and in bf16 for the MFMA).
+    // O / l is unchanged by the choice of m.
     float tmax[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const int i = wp0 + qt * 16 + (lane & 15);
-      float mx = -INFINITY;
-      if (full) {
+      float mx = sacc[0][qt][0];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = a + kt * 16 + (lane >> 4) * 4 + r;
-            const float sv = key_visible(i, j, p.n_meta, p.window) ? sacc[kt][qt][r] : -INFINITY;
-            sacc[kt][qt][r] = sv;
-            mx = fmaxf(mx, sv);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      tmax[qt] = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+      tmax[qt] = max_over_key_lanes(mx);
     }
     const float thr = kLazyLog2 / c2;
     if (__builtin_amdgcn_ballot_w64(tmax[0] > mrow[0] + thr || tmax[1] > mrow[1] + thr)) {
@@ -282,35 +310,28 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
         const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);  // 0 from -inf
         mrow[qt] = mnew;
-        lrow[qt] *= alpha;
+        lacc[qt] *= alpha;
 #pragma unroll
         for (int d = 0; d < DH / 16; ++d) oacc[d][qt] *= alpha;
       }
     }
+    // P^T in bf16 (the B operand of both MFMAs below); the row sums l come from the same
+    // rounded P through an MFMA with an all-ones A operand (every output row of it is
+    // the column sum, so each lane ends with the full sum of its query).
     bf16x8 pf[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const float mc2 = (mrow[qt] == -INFINITY ? 0.f : mrow[qt]) * c2;
-      float ls = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][r], c2, -mc2));
-          pv[kt][r] = e;
-          ls += e;
-        }
-      lrow[qt] += ls;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          f[r] = (bf16)pv[2 * k2][r];
-          f[4 + r] = (bf16)pv[2 * k2 + 1][r];
+          f[r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * k2][qt][r], c2, -mc2));
+          f[4 + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * k2 + 1][qt][r], c2, -mc2));
         }
         pf[k2][qt] = f;
+        lacc[qt] = mfma16x16x32(ones, f, lacc[qt]);
       }
     }
 #pragma unroll
@@ -350,9 +371,7 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   bf16* obase = (bf16*)p.o;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    float l = lrow[qt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lacc[qt][0];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int pos = wp0 + qt * 16 + (lane & 15);
     if (pos >= plim) continue;
