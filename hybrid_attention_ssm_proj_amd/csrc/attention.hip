@@ -241,20 +241,42 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   while (t < ntile) {
     const bf16* kt_ = kst(st);
     const bf16* vt_ = vst(st);
-    floatx4 sacc[4][2];
+    // All K fragments of the tile are read first; the V^T fragments (independent of S)
+    // are read between the S MFMAs, so their latency hides behind the MFMAs and the
+    // softmax instead of stalling the P V product.
+    bf16x8 kf[DH / 32][4], vf[DH / 16][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sacc[i][0] = sacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) {
+    for (int ks = 0; ks < DH / 32; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int row = kt * 16 + (lane & 15), c = ks * 4 + (lane >> 4);
         const int sw = DH == 128 ? (c ^ (row & 15)) : (c ^ swz8(row));
-        const bf16x8 kf = *(const bf16x8*)(kt_ + row * DH + sw * 8);
-        sacc[kt][0] = mfma16x16x32(kf, qf[0][ks], sacc[kt][0]);
-        sacc[kt][1] = mfma16x16x32(kf, qf[1][ks], sacc[kt][1]);
+        kf[ks][kt] = *(const bf16x8*)(kt_ + row * DH + sw * 8);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    floatx4 sacc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sacc[i][0] = sacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sacc[kt][0] = mfma16x16x32(kf[ks][kt], qf[0][ks], sacc[kt][0]);
+        sacc[kt][1] = mfma16x16x32(kf[ks][kt], qf[1][ks], sacc[kt][1]);
+      }
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int row = d * 16 + (lane & 15), c = k2 * 4 + (lane >> 4);
+        vf[d][k2] = *(const bf16x8*)(vt_ + row * 64 + ((c ^ swz8(row)) * 8));
+      }
+#pragma unroll
+    for (int q = 0; q < DH / 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     const int a = t * KT;
     const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
@@ -338,10 +360,8 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
     for (int d = 0; d < DH / 16; ++d)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const int row = d * 16 + (lane & 15), c = k2 * 4 + (lane >> 4);
-        const bf16x8 vf = *(const bf16x8*)(vt_ + row * 64 + ((c ^ swz8(row)) * 8));
-        oacc[d][0] = mfma16x16x32(vf, pf[k2][0], oacc[d][0]);
-        oacc[d][1] = mfma16x16x32(vf, pf[k2][1], oacc[d][1]);
+        oacc[d][0] = mfma16x16x32(vf[d][k2], pf[k2][0], oacc[d][0]);
+        oacc[d][1] = mfma16x16x32(vf[d][k2], pf[k2][1], oacc[d][1]);
       }
 
     // hand-over: the next tile has landed (one more may stay in flight), every wave is
