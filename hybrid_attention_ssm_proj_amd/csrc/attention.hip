@@ -66,6 +66,16 @@ __device__ __forceinline__ int slot_key(int s) {
   return blk * 32 + (i < 4 ? q * 4 + i : 16 + q * 4 + (i - 4));
 }
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (same butterflies as below).
+__device__ __forceinline__ float sum_over_key_lanes(float x) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+  const float y = __builtin_bit_cast(float, (unsigned)s16[0]) +
+                  __builtin_bit_cast(float, (unsigned)s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, y),
+                                                    __builtin_bit_cast(unsigned, y), false, false);
+  return __builtin_bit_cast(float, (unsigned)s32[0]) + __builtin_bit_cast(float, (unsigned)s32[1]);
+}
 // Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48: v_permlane16_swap exchanges the odd
 // 16-lane rows of its first operand with the even rows of its second, v_permlane32_swap
 // the upper half of the first with the lower half of the second; with both operands a
@@ -388,22 +398,51 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
     t = tn;
   }
 
+  // O^T layout: lane holds head_dim entries d*16 + 4*(lane/16) + r of query lane % 16.
+  // With p.ssp, O is rounded to bf16 first (as stored O would be); the row's sum of its
+  // squares over this head (the 4 lanes of a query) goes to ssp[h, row] and beta * O is
+  // stored.
   bf16* obase = (bf16*)p.o;
+  const float* bh = p.beta != nullptr ? p.beta + h * DH + (lane >> 4) * 4 : nullptr;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const float l = lacc[qt][0];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int pos = wp0 + qt * 16 + (lane & 15);
+    float o[DH / 16][4];
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[d][r] = oacc[d][qt][r] * inv;
+    const int64_t row = pos_row(pos < plim ? pos : 0, b, p.n_meta, p.L);
+    if (p.ssp != nullptr) {
+      float q = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH / 16; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o[d][r] = (float)(bf16)o[d][r];
+          q = fmaf(o[d][r], o[d][r], q);
+        }
+      q = sum_over_key_lanes(q);
+      if (pos < plim && lane < 16) p.ssp[h * p.ssp_ld + row] = q;
+#pragma unroll
+      for (int d = 0; d < DH / 16; ++d) {
+        const floatx4 bv = *(const floatx4*)(bh + d * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[d][r] *= bv[r];
+      }
+    }
     if (pos >= plim) continue;
-    bf16* dst = obase + pos_row(pos, b, p.n_meta, p.L) * p.o_row_stride + h * DH + (lane >> 4) * 4;
+    bf16* dst = obase + row * p.o_row_stride + h * DH + (lane >> 4) * 4;
 #pragma unroll
     for (int d = 0; d < DH / 16; ++d) {
-      bf16x4 o;
-      o[0] = (bf16)(oacc[d][qt][0] * inv);
-      o[1] = (bf16)(oacc[d][qt][1] * inv);
-      o[2] = (bf16)(oacc[d][qt][2] * inv);
-      o[3] = (bf16)(oacc[d][qt][3] * inv);
-      *(bf16x4*)(dst + d * 16) = o;
+      bf16x4 ov;
+      ov[0] = (bf16)o[d][0];
+      ov[1] = (bf16)o[d][1];
+      ov[2] = (bf16)o[d][2];
+      ov[3] = (bf16)o[d][3];
+      *(bf16x4*)(dst + d * 16) = ov;
     }
   }
 }

@@ -314,8 +314,9 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lptr) {
 // reads tile t's stage), refills that stage with tile t+2 and reads tile t+1's first
 // fragments, so the barrier, the DMA issue and the LDS latency hide behind the last
 // 16 MFMAs of the tile.  Each transfer has one full k-tile of MFMA work to land.
-template <typename Cfg, typename Epi>
-__global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, Epi epi) {
+template <typename Cfg, typename Epi, bool RS = false>
+__global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, Epi epi,
+                                                               RowScale rs) {
   __shared__ __attribute__((aligned(1024))) bf16 sA0[Cfg::BM * 64];
   __shared__ __attribute__((aligned(1024))) bf16 sB0[Cfg::BN * 64];
   __shared__ __attribute__((aligned(1024))) bf16 sA1[Cfg::BM * 64];
@@ -399,6 +400,30 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
     __builtin_amdgcn_sched_group_barrier(0x008, Cfg::FM * Cfg::FN - Cfg::FM - Cfg::FN, 0);
   };
 
+  // Row scaling (RS): every accumulator of lane row i belongs to output row
+  // m0 + wm*TM + i*32 + rl.  After the first segment's k-tiles the accumulators take the
+  // factor ratio fa / fs, at the end fs.
+  float ratio[Cfg::FM], fin[Cfg::FM];
+  int ks_t = -1;
+  if constexpr (RS) {
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int m = min(m0 + wm * Cfg::TM + i * 32 + rl, g.M - 1);
+      const float fa = rs.fac[2 * (int64_t)m], fs = rs.fac[2 * (int64_t)m + 1];
+      ratio[i] = fa / fs;
+      fin[i] = fs;
+    }
+    ks_t = rs.k_split / 64;
+  }
+  auto scale_rows = [&](const float (&f)[Cfg::FM]) {
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= f[i];
+  };
+
   const int KT = g.K / 64;
   issue(sA0, sB0, 0);
   wait_vmcnt<0>();
@@ -433,6 +458,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
       load(sA0, sB0, 0, 0);
     }
     mm(1);
+    if constexpr (RS) {
+      if (t + 2 == ks_t) scale_rows(ratio);  // first segment complete (ks_t is even)
+    }
   }
   if (t < KT) {
     load(sA0, sB0, 1, 1);
@@ -444,6 +472,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
     mm(1);
   }
 
+  if constexpr (RS) scale_rows(fin);
   // acc[i][j] holds C^T of the 32 x 32 block: lane -> row rl, columns
   // (e/4)*8 + (lane/32)*4 + 0..3.
   if (m0 + Cfg::BM <= g.M && n0 + Cfg::BN <= g.N && epi.tile_fast(m0, m0 + Cfg::BM)) {
@@ -706,10 +735,11 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
   return hipGetLastError();
 }
 
-template <typename Cfg, typename Epi>
-static hipError_t run_bf16_dl(const GemmOperands& op, const Epi& epi, hipStream_t s) {
+template <typename Cfg, typename Epi, bool RS = false>
+static hipError_t run_bf16_dl(const GemmOperands& op, const Epi& epi, hipStream_t s,
+                              const RowScale& rs = RowScale{}) {
   const int nbm = (op.M + Cfg::BM - 1) / Cfg::BM, nbn = (op.N + Cfg::BN - 1) / Cfg::BN;
-  gemm_bf16_dl_kernel<Cfg, Epi><<<dim3(nbm * nbn), dim3(Cfg::NT), 0, s>>>(op, epi);
+  gemm_bf16_dl_kernel<Cfg, Epi, RS><<<dim3(nbm * nbn), dim3(Cfg::NT), 0, s>>>(op, epi, rs);
   return hipGetLastError();
 }
 
@@ -758,6 +788,23 @@ static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShap
     default:
       return run_bf16<CfgSkinny>(op, epi, s);
   }
+}
+
+bool gemm_bf16_rowscaled_ok(const GemmOperands& op, int k_split) {
+  return op.K % 128 == 0 && k_split % 128 == 0 && k_split > 0 && k_split < op.K &&
+         op.a_split >= op.M && (int64_t)op.M * op.lda0 < (1ll << 31) &&
+         (int64_t)op.N * op.ldb < (1ll << 31);
+}
+
+hipError_t launch_gemm_bf16_rowscaled(const GemmOperands& op, const GemmOutput& out,
+                                      const RowScale& rs, hipStream_t s) {
+  if (op.M <= 0 || op.N <= 0) return hipSuccess;
+  if (out.kind != EpiKind::Store || !gemm_bf16_rowscaled_ok(op, rs.k_split) || rs.fac == nullptr)
+    return hipErrorInvalidValue;
+  const Epilogue<bf16, EpiKind::Store> epi{out};
+  const long t256 = (long)((op.M + 255) / 256) * ((op.N + 255) / 256);
+  if (t256 >= 256) return run_bf16_dl<DlCfg<256, 256, 2, 4>, decltype(epi), true>(op, epi, s, rs);
+  return run_bf16_dl<DlCfg<256, 128, 2, 4>, decltype(epi), true>(op, epi, s, rs);
 }
 
 hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmShape shape,

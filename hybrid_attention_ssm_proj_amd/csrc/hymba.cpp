@@ -138,7 +138,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-  size_t z, delta, bc, dt, f, vt, macc, part, xdbl, yacc, total;
+  size_t z, delta, bc, dt, f, vt, macc, ssp, fac, part, xdbl, yacc, total;
 };
 
 
@@ -176,6 +176,11 @@ Carve carve_prefill(const Shape& s, int64_t rows, int B, int L) {
   if (s.bf16) off = align_up(off + attention_vt_bytes(s.M, L, B, s.Hkv, s.dh));
   c.macc = off;  // bf16: fp32 accumulator of the split-K out_proj over the meta rows
   if (s.bf16) off = align_up(off + (size_t)s.M * s.d * 4);
+  c.ssp = off;   // bf16 + fused scan: per-row partial sums of squares of the branches
+  if (s.bf16 && fused_dt(s))
+    off = align_up(off + (size_t)rows * (s.Hq + scan_channel_blocks(s.N, s.Di)) * 4);
+  c.fac = off;   // and the two row factors derived from them
+  if (s.bf16 && fused_dt(s)) off = align_up(off + (size_t)rows * 2 * 4);
   c.total = off;
   return c;
 }
@@ -342,10 +347,25 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     return b16 ? launch_gemm_bf16(op, out, shape, stream) : launch_gemm_f32(op, out, stream);
   };
 
+  // The RMS norms of the two branches are applied inside out_proj (bf16, fused scan):
+  // attention and the scan store beta * O and beta * Y_ssm plus partial sums of squares
+  // (per head, per channel block); a small kernel turns them into two factors per row,
+  // and out_proj scales the two K segments of F by them.  This drops the separate pass
+  // that rewrote F.
+  const bool few_meta = b16 && s.d % 256 == 0 && s.fw % 256 == 0;
+  const GemmOperands op_out{f + (size_t)M * s.fw * s.es, s.fw, nullptr, 0, (int)BL, w->w_out,
+                            s.fw, (int)BL, s.d, (int)s.fw};
+  const bool defer_norm = b16 && fused_dt(s) && s.qw % 128 == 0 &&
+                          (BL == 0 || gemm_bf16_rowscaled_ok(op_out, (int)s.qw)) &&
+                          !any_misaligned(w->beta_attn, w->beta_ssm);
+  const int n_sblk = defer_norm ? scan_channel_blocks(s.N, s.Di) : 0;
+  const int64_t ssp_ld = rows;  // partial column i of row r at ssp[i * rows + r]
+  float* ssp = defer_norm ? (float*)ws_ptr(workspace, cv.ssp) : nullptr;
+  float* fac = defer_norm ? (float*)ws_ptr(workspace, cv.fac) : nullptr;
+
   // 1. in_proj over [meta; X]: the batch-shared meta rows once, then the X rows.
   // The meta rows are few: the few-row kernel (64-row blocks, every column tile its own
   // workgroup) fills the chip better than 256-row tiles.
-  const bool few_meta = b16 && s.d % 256 == 0 && s.fw % 256 == 0;
   if (M > 0) {
     GemmOperands op{meta, s.d, nullptr, 0, M, w->w_in, s.d, M, (int)s.n_in, s.d};
     if (few_meta) {
@@ -408,6 +428,9 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     ap.head_dim = s.dh;
     ap.window = s.W;
     ap.scale = s.scale;
+    ap.ssp = ssp;
+    ap.ssp_ld = ssp_ld;
+    ap.beta = w->beta_attn;
     HYMBA_LAUNCH(HYMBA_STAGE_ATTN,
                  b16 ? launch_attention_prefill_bf16_dl(ap, ws_ptr(workspace, cv.vt), stream)
                      : launch_attention_prefill_f32(ap, stream));
@@ -445,6 +468,10 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     sp.B = B;
     sp.Di = s.Di;
     sp.N = s.N;
+    sp.ssp = ssp;
+    sp.ssp_ld = ssp_ld;
+    sp.ssp_col0 = s.Hq;
+    sp.beta = w->beta_ssm;
     if (B == 0) {  // meta rows only: run them as one sequence of length 0
       sp.B = 1;
       sp.h_out = nullptr;
@@ -456,17 +483,29 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
       HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill(b16, sp, stream));
     }
   }
-  // 7. RMSNorm + beta + average, in place.
-  HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
-                                                  w->beta_attn, w->beta_ssm, desc->rms_eps, stream));
+  // 7. RMSNorm + beta + average: in place, or as row factors for out_proj (the meta
+  // rows, projected by the split-K kernel, are scaled in place by the same launch).
+  if (defer_norm) {
+    HYMBA_LAUNCH(HYMBA_STAGE_NORM,
+                 launch_row_factors(ssp, ssp_ld, s.Hq, n_sblk, (int)rows, (int)s.qw, s.Di,
+                                    desc->rms_eps, fac, f, s.fw,
+                                    y_meta != nullptr ? M : 0, stream));
+  } else {
+    HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
+                                                    w->beta_attn, w->beta_ssm, desc->rms_eps,
+                                                    stream));
+  }
+  const RowScale rs_seq{fac != nullptr ? fac + 2 * (int64_t)M : nullptr, (int)s.qw};
   // 8. out_proj: sequence rows -> y, then the batch-shared meta rows -> y_meta.  Two
   // launches keep the large one on whole 256-row tiles (B*L rows), so it runs as an
   // exact number of rounds over the CUs.
   if (BL > 0) {
-    GemmOperands op{f + (size_t)M * s.fw * s.es, s.fw, nullptr, 0, (int)BL, w->w_out, s.fw,
-                    (int)BL, s.d, (int)s.fw};
     GemmOutput out{EpiKind::Store, y, s.d, nullptr, 0, (int)BL, 0, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out, GemmShape::Large));
+    if (defer_norm) {
+      HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, launch_gemm_bf16_rowscaled(op_out, out, rs_seq, stream));
+    } else {
+      HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op_out, out, GemmShape::Large));
+    }
   }
   if (M > 0 && y_meta != nullptr) {
     GemmOperands op{f, s.fw, nullptr, 0, M, w->w_out, s.fw, M, s.d, (int)s.fw};

@@ -43,6 +43,13 @@ struct GemmOutput {
 
 enum class GemmShape { Large, Narrow, Skinny };
 
+// Row scaling of a product whose K range splits in two segments (the attention and SSM
+// halves of F): out[m, n] = fac[2m] * sum_{k < k_split} A B^T + fac[2m+1] * sum_{k >= k_split}.
+struct RowScale {
+  const float* fac;
+  int k_split;
+};
+
 hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmShape shape,
                             hipStream_t s);
 hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStream_t s);
@@ -51,6 +58,12 @@ hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStr
 // run as separate workgroups and meet through atomics.
 hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t ldacc, int ksplit,
                                    hipStream_t s);
+// bf16 C = row-scaled A B^T (see RowScale) with the plain store epilogue; K and k_split
+// multiples of 128, 0 < k_split < K.  Returns hipErrorInvalidValue when the operands do
+// not suit the 256-wide tile kernel (check with gemm_bf16_rowscaled_ok first).
+bool gemm_bf16_rowscaled_ok(const GemmOperands& op, int k_split);
+hipError_t launch_gemm_bf16_rowscaled(const GemmOperands& op, const GemmOutput& out,
+                                      const RowScale& rs, hipStream_t s);
 // Z = bf16(A B^T) (row stride ldz); with k_col >= 0 the K / V columns of row b are also
 // written to ring slot pos[b] % slots of ring_k / ring_v ([B, Hkv, slots, head_dim]).
 // Also clears `zero_n` floats at `zero` (16-byte aligned, zero_n % 4 == 0): the split-K
@@ -80,6 +93,11 @@ struct AttnParams {
   int64_t o_row_stride;
   int n_meta, L, B, Hq, Hkv, head_dim, window;
   float scale;
+  // bf16 prefill only: with ssp != nullptr the kernel writes beta[h*head_dim + d] * O
+  // and the row's sum of O^2 over head h to ssp[h * ssp_ld + row] (row as for q).
+  float* ssp;
+  int64_t ssp_ld;
+  const float* beta;
 };
 hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s);
 // bf16 prefill with direct-to-LDS K / V^T tiles; `vt` is scratch of
@@ -122,11 +140,19 @@ struct ScanParams {
   int64_t y_stride;
   float* h_out;        // [B, Di, N] or nullptr
   int n_meta, L, B, Di, N;
+  // fused bf16 scan only: with ssp != nullptr the kernel writes beta[c] * y and the
+  // row's sum of y^2 over the workgroup's channel block j to ssp[(ssp_col0 + j) * ssp_ld
+  // + row] (scan_channel_blocks() blocks)
+  float* ssp;
+  int64_t ssp_ld;
+  int ssp_col0;
+  const float* beta;
 };
 hipError_t launch_scan_prefill(bool bf16, const ScanParams& p, hipStream_t s);
 // bf16 prefill scan with the dt projection fused in (ScanParams::dt unused): dt =
 // softplus(delta W_dt^T + dt_bias) with delta [rows, R] bf16, W_dt [Di, R] bf16.
 bool scan_fused_supported(int N, int R, int Di);
+int scan_channel_blocks(int N, int Di);
 hipError_t launch_scan_prefill_fused(const ScanParams& p, const void* delta, const void* w_dt,
                                      const float* dt_bias, int R, hipStream_t s);
 
@@ -156,6 +182,14 @@ hipError_t launch_ssm_step(bool bf16, const SsmStepParams& p, hipStream_t s);
 hipError_t launch_fuse_norm(bool bf16, void* f, int64_t f_stride, int rows, int wa, int ws,
                             const float* beta_a, const float* beta_s, float eps,
                             hipStream_t s);
+// Row factors of the deferred branch norms: for every row, fa = 0.5 / sqrt(sum of the
+// na partials ssp[0:na, row] / wa + eps) and fs likewise over ssp[na:na+ns, row] / ws
+// (partial i of row r at ssp[i * ssp_ld + r]); fac[2*row] = fa, fac[2*row+1] = fs.
+// Rows < scale_rows of f (storage bf16, row stride f_stride) are scaled in place:
+// columns < wa by fa, the rest by fs.
+hipError_t launch_row_factors(const float* ssp, int64_t ssp_ld, int na, int ns, int rows,
+                              int wa, int ws, float eps, float* fac, void* f, int64_t f_stride,
+                              int scale_rows, hipStream_t s);
 // Decode: merge the split-attention partials into O (rounded to the storage type),
 // write it to F[b, :wa], then normalise F[b] as above.
 hipError_t launch_decode_combine_norm(bool bf16, const float* part, int nsplit, void* f,

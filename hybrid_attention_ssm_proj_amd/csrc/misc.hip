@@ -120,6 +120,70 @@ hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int
   return hipGetLastError();
 }
 
+// Row factors of the deferred branch norms.  Blocks [0, nfac) take 256 rows each, one
+// row per thread (consecutive threads read consecutive rows of each partial column);
+// blocks from nfac on scale one of the first scale_rows rows of F in place, recomputing
+// that row's two factors from its partials.
+// Sum of n partials r[0], r[ld], ...: eight independent loads in flight at a time.
+__device__ __forceinline__ float col_sum(const float* r, int64_t ld, int n) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = r[(i + u) * ld];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += v[u];
+  }
+  for (; i < n; ++i) acc[0] += r[i * ld];
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+__device__ __forceinline__ void row_sums(const float* r, int64_t ld, int na, int ns, float& sa,
+                                         float& ss) {
+  sa = col_sum(r, ld, na);
+  ss = col_sum(r + na * ld, ld, ns);
+}
+
+__global__ __launch_bounds__(256) void row_factors_kernel(const float* ssp, int64_t ld, int na,
+                                                          int ns, int rows, int wa, int ws,
+                                                          float eps, float* fac, bf16* f,
+                                                          int64_t f_stride, int nfac) {
+  if ((int)blockIdx.x < nfac) {
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    float sa, ss;
+    row_sums(ssp + row, ld, na, ns, sa, ss);
+    fac[2 * (int64_t)row] = 0.5f * rsqrtf(sa / (float)wa + eps);
+    fac[2 * (int64_t)row + 1] = 0.5f * rsqrtf(ss / (float)ws + eps);
+    return;
+  }
+  const int row = blockIdx.x - nfac;
+  float sa, ss;
+  row_sums(ssp + row, ld, na, ns, sa, ss);
+  const float fa = 0.5f * rsqrtf(sa / (float)wa + eps);
+  const float fs = 0.5f * rsqrtf(ss / (float)ws + eps);
+  bf16* fr = f + row * f_stride;
+  for (int i = threadIdx.x * 8; i < wa + ws; i += 256 * 8) {
+    float v[8];
+    Vec8<bf16>::load(fr + i, v);
+    const float sc = i < wa ? fa : fs;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= sc;
+    Vec8<bf16>::store(fr + i, v);
+  }
+}
+
+hipError_t launch_row_factors(const float* ssp, int64_t ssp_ld, int na, int ns, int rows,
+                              int wa, int ws, float eps, float* fac, void* f, int64_t f_stride,
+                              int scale_rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (wa % 8 || ws % 8 || scale_rows > rows) return hipErrorInvalidValue;
+  const int nfac = (rows + 255) / 256;
+  row_factors_kernel<<<dim3(nfac + scale_rows), dim3(256), 0, s>>>(
+      ssp, ssp_ld, na, ns, rows, wa, ws, eps, fac, (bf16*)f, f_stride, nfac);
+  return hipGetLastError();
+}
+
 // Decode: merge the split partials (o, m, l) of every q head of sequence b into O,
 // round O to the storage type (as the prefill path stores O), then normalise the row
 // with the SSM half that the SSM step already wrote.  One block of 256 threads per

@@ -155,6 +155,11 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
     h[k] = 0.f;
   }
   const float Dc = p.D[c];
+  float beta8[8];
+  static_assert(256 % (CB / 8) == 0, "store-phase channel group is fixed per thread");
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    beta8[e] = p.beta != nullptr ? p.beta[c0 + (tid % (CB / 8)) * 8 + e] : 1.f;
   for (int i = tid; i < CB; i += 256) bias_s[i] = dt_bias[c0 + i];
 
   // Stage chunk `t0` into buffer `buf`.  Slot q of an array is written by lane q % 64
@@ -328,12 +333,29 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
     }
     lds_barrier();
 
+    // Store: thread q takes 8 channels of one token (8 consecutive lanes per token).  With
+    // p.ssp the token row's sum of y^2 (of the rounded y, as a norm reading stored Y_ssm
+    // sees it) over the workgroup's channels goes to ssp[ssp_col0 + blockIdx.x, row] and
+    // beta * y is stored.
     for (int q = tid; q < C::X_SLOTS; q += 256) {
       const int tt = q / (CB / 8), j16 = q % (CB / 8);
       const int t = t0 + tt;
-      if (tt < tn && (t >= p.n_meta || b == 0))
-        *(u32x4*)(yout + seq_row(t, b, p.n_meta, p.L) * p.y_stride + c0 + j16 * 8) =
-            *(const u32x4*)(y_s + q * 8);
+      const bool keep = tt < tn && (t >= p.n_meta || b == 0);
+      const int64_t row = seq_row(min(t, total - 1), b, p.n_meta, p.L);
+      bf16x8 o = *(const bf16x8*)(y_s + q * 8);
+      if (p.ssp != nullptr) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (float)o[e];
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq = fmaf(v[e], v[e], sq);
+        sq = group_sum<CB / 8>(sq);
+        if (keep && j16 == 0) p.ssp[(p.ssp_col0 + blockIdx.x) * p.ssp_ld + row] = sq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)(v[e] * beta8[e]);
+      }
+      if (keep) *(bf16x8*)(yout + row * p.y_stride + c0 + j16 * 8) = o;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA for the next chunk has landed
     lds_barrier();
@@ -366,6 +388,12 @@ static hipError_t fused_by_state(const ScanParams& p, const void* delta, const v
     case 128: return run_fused<8, 16, R>(p, delta, w_dt, bias, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+int scan_channel_blocks(int N, int Di) {
+  // channels per workgroup: 256 / LPC with LPC = 4, 8, 8, 16 for N = 16, 32, 64, 128
+  const int cb = N == 16 ? 64 : (N == 128 ? 16 : 32);
+  return Di / cb;
 }
 
 bool scan_fused_supported(int N, int R, int Di) {

@@ -40,8 +40,11 @@ before the first meta token; RMSNorm over each branch's full width; the two bran
 of unequal width are concatenated and projected by one W_out (equal to averaging the
 two projected branches); only dt_proj has a bias.
 
-`contract=True` rounds to bf16 (round-to-nearest-even) exactly where the bf16 GPU
-path stores bf16: Z, delta, O, Y_ssm and F.  Everything else stays fp64.
+`contract=True` rounds to bf16 (round-to-nearest-even) where the bf16 GPU path
+rounds to bf16: Z, delta, O, Y_ssm and F.  Everything else stays fp64.  (The GPU's
+bf16 prefill rounds beta * O and beta * Y_ssm in place of F and applies the two
+per-row norm factors in fp32 inside out_proj: one rounding of a different product, well
+inside the bf16 parity tolerance.)
 
 Parity pins: every function here is pinned by tests that do not retype it (closed
 forms, brute force, library special cases, invariants).  The conventions above that

@@ -54,7 +54,10 @@ def test_workspace_sizes(lib):
     # plus V^T staging for attention: B x Hkv x head_dim x (keys rounded up to 64), bf16
     vt = 8 * 4 * 128 * ((128 + 2048 + 63) // 64 * 64) * 2
     macc = 128 * 2048 * 4  # fp32 accumulator of the meta-row out_proj
-    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc
+    # per-row partial sums of squares (16 heads + 64 scan channel blocks) and the two
+    # row factors of the branch norms, all fp32
+    ss = rows * (16 + 64) * 4 + rows * 2 * 4
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss
     assert floor <= got <= floor + 8 * 256
     # fp32 layers keep a separate fp32 dt buffer
     d0 = desc_of(0)
