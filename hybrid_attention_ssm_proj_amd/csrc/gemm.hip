@@ -783,8 +783,13 @@ static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShap
       } else {
         return run_bf16<CfgNarrow>(op, epi, s);
       }
-    case GemmShape::Narrow:
+    case GemmShape::Narrow: {
+      // few output columns (x_proj: 160): 128 x 64 tiles moved by DMA, 4 waves of 64 x 32
+      const bool one_src = op.a_split >= op.M;
+      const bool fits32 = (int64_t)op.M * op.lda0 < (1ll << 31) && (int64_t)op.N * op.ldb < (1ll << 31);
+      if (op.K % 64 == 0 && one_src && fits32) return run_bf16_dl<DlCfg<128, 64, 2, 2>>(op, epi, s);
       return run_bf16<CfgNarrow>(op, epi, s);
+    }
     default:
       return run_bf16<CfgSkinny>(op, epi, s);
   }
