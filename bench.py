@@ -30,6 +30,9 @@ METRIC = "hybrid-layer prefill tokens/s + decode tokens/s on 1 MI355X; % MFMA/HB
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_VALU_TFLOPS = 157.3       # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
+# v_exp_f32 throughput measured on MI355X with a one-off probe (independent exp2 chains):
+# about 8.4 cycles per wave64 instruction at 2.4 GHz on each of 1024 SIMDs
+PEAK_EXP_TPS = 18.7            # 10^12 exponentials per second
 
 
 def log(*a):
@@ -52,6 +55,19 @@ def parse():
     return ap.parse_args()
 
 
+def scan_channels(N):
+    """Channels per workgroup of the fused bf16 scan (4, 8, 8, 16 lanes per channel)."""
+    return 64 if N == 16 else (16 if N == 128 else 32)
+
+
+def deferred_norm(dims):
+    """The library applies the branch norms inside out_proj for bf16 layers whose scan
+    has the fused dt projection (dt_rank 64 or 128, d_state 16..128)."""
+    return (dims.dtype == "bf16" and dims.dt_rank in (64, 128) and
+            dims.d_state in (16, 32, 64, 128) and dims.d_inner % scan_channels(dims.d_state) == 0
+            and dims.q_width % 128 == 0)
+
+
 def stage_work(dims, B, L):
     """Algorithmic work per prefill launch of each stage (flops or bytes)."""
     M, d, Di, N, R = dims.n_meta, dims.d_model, dims.d_inner, dims.d_state, dims.dt_rank
@@ -72,8 +88,13 @@ def stage_work(dims, B, L):
         # bytes: x, G, y (bf16) per (row, channel), delta (bf16) and B, C (fp32) per row,
         # h once; dt is computed in the scan and never stored
         "scan": ("hbm", float(rows * (Di * 6 + 2 * R + 8 * N) + B * Di * N * 4)),
-        # bytes: read O and Y_ssm, write F (bf16)
-        "norm": ("hbm", float(rows * (qw + Di) * 2 * 2)),
+        # bytes: bf16 prefill with the fused scan derives two factors per row from the
+        # partial sums of squares (read), writes them, and rescales the meta rows of F in
+        # place (out_proj applies the factors); otherwise the pass reads O and Y_ssm and
+        # writes F
+        "norm": ("hbm", float(rows * (dims.n_q_heads + Di // scan_channels(N)) * 4 + rows * 8 +
+                              M * (qw + Di) * 2 * 2) if deferred_norm(dims) else
+                 float(rows * (qw + Di) * 2 * 2)),
         "out_proj": ("mfma", 2.0 * B * L * dims.f_width * d),
     }
 
@@ -218,6 +239,12 @@ def main():
         if name in work:
             bound, wk = work[name]
             entry.update(roofline_entry(bound, wk / rec["per_step"], rec["avg_ms"]))
+        if name == "scan":
+            # exponentials rows * Di * N against the v_exp_f32 rate measured on this chip
+            exps = (dims.n_meta + B * L) * dims.d_inner * dims.d_state
+            rate = exps / (rec["avg_ms"] * 1e-3)
+            entry["exp"] = {"achieved": round(rate / 1e12, 3), "peak": PEAK_EXP_TPS,
+                            "unit": "Texp/s", "frac": round(rate / 1e12 / PEAK_EXP_TPS, 4)}
         stage_report[name] = entry
     bound, wk = work[dominant]
     per_launch = wk / stages[dominant]["per_step"]

@@ -92,6 +92,12 @@ def load_library() -> ctypes.CDLL:
         "hymba_timer_read": (I32, [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
         "hymba_op_gemm": (I32, [I32, P, I64, P, I64, P, I64, I32, I32, I32, I32, P]),
         "hymba_op_copy": (I32, [P, P, SZ, P]),
+        "hymba_op_attn_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "hymba_op_attn": (I32, [I32, P, I64, P, P, I64, P, I64, I32, I32, I32, I32, I32, I32,
+                                I32, ctypes.c_float, P, SZ, P]),
+        "hymba_op_scan_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32, I32]),
+        "hymba_op_scan": (I32, [I32, P, I64, I32, I32, P, P, P, P, P, P, P, I64, P, I32, I32, I32,
+                                I32, I32, I32, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -192,6 +198,41 @@ def hymba_op_gemm(dtype, a, lda, b, ldb, c, ldc, c_dtype, m, n, k, stream=None) 
 def hymba_op_copy(src, dst, nbytes, stream=None) -> None:
     _check(load_library().hymba_op_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
            "hymba_op_copy")
+
+
+def hymba_op_attn_workspace_bytes(dtype, n_meta, seq_len, batch, n_kv_heads, head_dim) -> int:
+    return load_library().hymba_op_attn_workspace_bytes(dtype, n_meta, seq_len, batch,
+                                                        n_kv_heads, head_dim)
+
+
+def hymba_op_attn(dtype, q, q_ld, k, v, kv_ld, o, o_ld, n_meta, seq_len, batch, n_q_heads,
+                  n_kv_heads, head_dim, window, scale, workspace, workspace_bytes, stream=None,
+                  check=True) -> int:
+    st = load_library().hymba_op_attn(dtype, _ptr(q), q_ld, _ptr(k), _ptr(v), kv_ld, _ptr(o),
+                                      o_ld, n_meta, seq_len, batch, n_q_heads, n_kv_heads,
+                                      head_dim, window, scale, _ptr(workspace), workspace_bytes,
+                                      _stream(stream))
+    if check:
+        _check(st, "hymba_op_attn")
+    return st
+
+
+def hymba_op_scan_workspace_bytes(dtype, n_meta, seq_len, batch, d_inner, d_state,
+                                  dt_rank) -> int:
+    return load_library().hymba_op_scan_workspace_bytes(dtype, n_meta, seq_len, batch, d_inner,
+                                                        d_state, dt_rank)
+
+
+def hymba_op_scan(dtype, z, z_ld, xs_col, g_col, delta, bc, w_dt, dt_bias, A, D, y, y_ld, h_out,
+                  n_meta, seq_len, batch, d_inner, d_state, dt_rank, workspace, workspace_bytes,
+                  stream=None, check=True) -> int:
+    st = load_library().hymba_op_scan(dtype, _ptr(z), z_ld, xs_col, g_col, _ptr(delta), _ptr(bc),
+                                      _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(y), y_ld,
+                                      _ptr(h_out), n_meta, seq_len, batch, d_inner, d_state,
+                                      dt_rank, _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "hymba_op_scan")
+    return st
 
 
 # ----------------------------------------------------------------- convenience

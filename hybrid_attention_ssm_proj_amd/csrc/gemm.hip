@@ -86,23 +86,26 @@ struct Epilogue {
       store4<float>(p, w, valid, ((uintptr_t)p & 15) == 0);
     }
   }
-  // Unchecked path for a whole tile: rows [m0, m1) inside one destination that is
-  // written with 16-byte stores (Store epilogue only; the caller checks the bounds).
-  __device__ __forceinline__ bool tile_fast(int m0, int m1) const {
+  // Unchecked path for a whole tile: rows [m0, m1) x columns [n0, n1) inside one
+  // destination of the storage type, written with 16-byte stores (Store; XProj when the
+  // tile lies in the delta columns).  The caller checks the bounds.
+  __device__ __forceinline__ bool tile_fast(int m0, int m1, int n0, int n1) const {
     if constexpr (K == EpiKind::Store) {
       const bool first = m1 <= o.c_split;
       if (!first && m0 < o.c_split) return false;
       const T* base = (const T*)(first ? o.c0 : o.c1);
       const int64_t ld = first ? o.ldc0 : o.ldc1;
       return base != nullptr && ld % 8 == 0 && ((uintptr_t)base & 15) == 0;
+    } else if constexpr (K == EpiKind::XProj) {
+      return n1 <= o.split_col && o.ldc0 % 8 == 0 && ((uintptr_t)o.c0 & 15) == 0;
     } else {
       return false;
     }
   }
   // Output (m, n..n+7) = lo[0..3], hi[0..3]; valid after tile_fast() returned true.
   __device__ __forceinline__ void store8(int m, int n, const float lo[4], const float hi[4]) const {
-    if constexpr (K == EpiKind::Store) {
-      const bool first = m < o.c_split;
+    if constexpr (K == EpiKind::Store || K == EpiKind::XProj) {
+      const bool first = K == EpiKind::XProj || m < o.c_split;
       T* p = (T*)(first ? o.c0 : o.c1) + (int64_t)(first ? m : m - o.c_split) *
                                              (first ? o.ldc0 : o.ldc1) + n;
       bf16x8 w;
@@ -475,7 +478,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
   if constexpr (RS) scale_rows(fin);
   // acc[i][j] holds C^T of the 32 x 32 block: lane -> row rl, columns
   // (e/4)*8 + (lane/32)*4 + 0..3.
-  if (m0 + Cfg::BM <= g.M && n0 + Cfg::BN <= g.N && epi.tile_fast(m0, m0 + Cfg::BM)) {
+  if (m0 + Cfg::BM <= g.M && n0 + Cfg::BN <= g.N &&
+      epi.tile_fast(m0, m0 + Cfg::BM, n0, n0 + Cfg::BN)) {
     // Interior tile: v_permlane32_swap exchanges lanes 32..63 of its first operand with
     // lanes 0..31 of its second, so after swapping the column groups 2p (e = 8p..8p+3)
     // and 2p+1 (e = 8p+4..8p+7) lane l < 32 holds columns 16p + 0..7 of row l and lane

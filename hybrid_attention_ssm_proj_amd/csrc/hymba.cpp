@@ -693,6 +693,131 @@ hymba_status hymba_op_gemm(int32_t dtype, const void* a, int64_t lda, const void
   return e == hipSuccess ? HYMBA_OK : fail_hip(e);
 }
 
+size_t hymba_op_attn_workspace_bytes(int32_t dtype, int32_t n_meta, int32_t seq_len,
+                                     int32_t batch, int32_t n_kv_heads, int32_t head_dim) {
+  if (n_meta < 0 || seq_len < 0 || batch < 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
+  if (dtype != HYMBA_DTYPE_BF16) return 0;
+  return attention_vt_bytes(n_meta, seq_len, batch, n_kv_heads, head_dim);
+}
+
+hymba_status hymba_op_attn(int32_t dtype, const void* q, int64_t q_ld, const void* k,
+                           const void* v, int64_t kv_ld, void* o, int64_t o_ld, int32_t n_meta,
+                           int32_t seq_len, int32_t batch, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t window, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != HYMBA_DTYPE_F32 && dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
+  if (n_meta < 0 || seq_len < 0 || batch < 0 || window < 0 || n_q_heads <= 0 ||
+      n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+    return HYMBA_ERR_INVALID_ARG;
+  const bool b16 = dtype == HYMBA_DTYPE_BF16;
+  if (b16 ? (head_dim != 64 && head_dim != 128) : (head_dim != 32 && head_dim != 64))
+    return HYMBA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)n_meta + (int64_t)batch * seq_len;
+  if (rows > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  if (q_ld < (int64_t)n_q_heads * head_dim || kv_ld < (int64_t)n_kv_heads * head_dim ||
+      o_ld < (int64_t)n_q_heads * head_dim)
+    return HYMBA_ERR_INVALID_ARG;
+  if (q_ld % 8 || kv_ld % 8 || o_ld % 8) return HYMBA_ERR_UNSUPPORTED;
+  if (rows == 0) return HYMBA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(q, k, v, o, workspace)) return HYMBA_ERR_ALIGNMENT;
+  const size_t need = hymba_op_attn_workspace_bytes(dtype, n_meta, seq_len, batch, n_kv_heads,
+                                                    head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HYMBA_ERR_WORKSPACE;
+  const size_t es = b16 ? 2 : 4;
+  AttnParams ap{};
+  ap.q = q;
+  ap.q_row_stride = q_ld;
+  ap.k_meta = k;
+  ap.v_meta = v;
+  ap.meta_head_stride = head_dim;
+  ap.meta_row_stride = kv_ld;
+  ap.k_seq = (const char*)k + (size_t)n_meta * kv_ld * es;
+  ap.v_seq = (const char*)v + (size_t)n_meta * kv_ld * es;
+  ap.seq_batch_stride = (int64_t)seq_len * kv_ld;
+  ap.seq_head_stride = head_dim;
+  ap.seq_row_stride = kv_ld;
+  ap.seq_slots = seq_len > 0 ? seq_len : 1;
+  ap.o = o;
+  ap.o_row_stride = o_ld;
+  ap.n_meta = n_meta;
+  ap.L = seq_len;
+  ap.B = batch;
+  ap.Hq = n_q_heads;
+  ap.Hkv = n_kv_heads;
+  ap.head_dim = head_dim;
+  ap.window = window;
+  ap.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)head_dim);
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = b16 ? launch_attention_prefill_bf16_dl(ap, workspace, st)
+                           : launch_attention_prefill_f32(ap, st);
+  return e == hipSuccess ? HYMBA_OK : fail_hip(e);
+}
+
+size_t hymba_op_scan_workspace_bytes(int32_t dtype, int32_t n_meta, int32_t seq_len,
+                                     int32_t batch, int32_t d_inner, int32_t d_state,
+                                     int32_t dt_rank) {
+  if (n_meta < 0 || seq_len < 0 || batch < 0 || d_inner <= 0) return 0;
+  const int64_t rows = (int64_t)n_meta + (int64_t)batch * seq_len;
+  if (dtype == HYMBA_DTYPE_BF16 && scan_fused_supported(d_state, dt_rank, d_inner)) return 0;
+  return (size_t)rows * d_inner * 4;
+}
+
+hymba_status hymba_op_scan(int32_t dtype, const void* z, int64_t z_ld, int32_t xs_col,
+                           int32_t g_col, const void* delta, const float* bc, const void* w_dt,
+                           const float* dt_bias, const float* A, const float* D, void* y,
+                           int64_t y_ld, float* h_out, int32_t n_meta, int32_t seq_len,
+                           int32_t batch, int32_t d_inner, int32_t d_state, int32_t dt_rank,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != HYMBA_DTYPE_F32 && dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
+  if (n_meta < 0 || seq_len < 0 || batch < 0 || d_inner <= 0 || dt_rank <= 0 || xs_col < 0 ||
+      g_col < 0 || xs_col + d_inner > z_ld || g_col + d_inner > z_ld || y_ld < d_inner)
+    return HYMBA_ERR_INVALID_ARG;
+  if (d_state < 4 || d_state > 128 || (d_state & (d_state - 1)) || d_inner % 8 || dt_rank % 8 ||
+      dt_rank > 512 || z_ld % 8 || xs_col % 8 || g_col % 8 || y_ld % 8)
+    return HYMBA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)n_meta + (int64_t)batch * seq_len;
+  if (rows > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  if (rows == 0 || batch == 0) return HYMBA_OK;
+  if (z == nullptr || delta == nullptr || bc == nullptr || w_dt == nullptr || dt_bias == nullptr ||
+      A == nullptr || D == nullptr || y == nullptr)
+    return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(z, delta, bc, w_dt, y, h_out, workspace)) return HYMBA_ERR_ALIGNMENT;
+  const size_t need = hymba_op_scan_workspace_bytes(dtype, n_meta, seq_len, batch, d_inner,
+                                                    d_state, dt_rank);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HYMBA_ERR_WORKSPACE;
+  const bool b16 = dtype == HYMBA_DTYPE_BF16;
+  hipStream_t st = (hipStream_t)stream;
+  ScanParams sp{};
+  sp.z = z;
+  sp.z_stride = z_ld;
+  sp.xs_col = xs_col;
+  sp.g_col = g_col;
+  sp.dt = (const float*)workspace;
+  sp.bc = bc;
+  sp.A = A;
+  sp.D = D;
+  sp.y = y;
+  sp.y_stride = y_ld;
+  sp.h_out = h_out;
+  sp.n_meta = n_meta;
+  sp.L = seq_len;
+  sp.B = batch;
+  sp.Di = d_inner;
+  sp.N = d_state;
+  hipError_t e;
+  if (need == 0) {
+    e = launch_scan_prefill_fused(sp, delta, w_dt, dt_bias, dt_rank, st);
+  } else {
+    GemmOperands op{delta, dt_rank, nullptr, 0, (int)rows, w_dt, dt_rank, (int)rows, d_inner,
+                    dt_rank};
+    GemmOutput out{EpiKind::Softplus, workspace, d_inner, nullptr, 0, 0, 0, dt_bias};
+    e = b16 ? launch_gemm_bf16(op, out, GemmShape::Narrow, st) : launch_gemm_f32(op, out, st);
+    if (e == hipSuccess) e = launch_scan_prefill(b16, sp, st);
+  }
+  return e == hipSuccess ? HYMBA_OK : fail_hip(e);
+}
+
 hymba_status hymba_op_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes % 16) return HYMBA_ERR_UNSUPPORTED;
   if (bytes > 0 && (src == nullptr || dst == nullptr)) return HYMBA_ERR_INVALID_ARG;

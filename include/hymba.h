@@ -203,6 +203,56 @@ hymba_status hymba_op_gemm(int32_t dtype, const void *a, int64_t lda, const void
                            int32_t n, int32_t k, void *stream);
 hymba_status hymba_op_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * hymba_op_attn: the attention heads alone (step a4), on the kernels the layer uses.
+ * Source: Design formulation, attention-head equation (softmax(Q K^T) mixing over the
+ * meta-prefixed tokens); "Meta Tokens" (meta keys always visible); "Combine global and
+ * local attention" (window); GQA grouping from the KV-sharing section.
+ *   Rows: the n_meta batch-shared meta rows, then batch * seq_len sequence rows (row
+ *   n_meta + b*seq_len + j is X-position j of sequence b).
+ *   q [rows, row stride q_ld], head h at columns h*head_dim ..; k, v [rows, kv_ld],
+ *   kv head g at columns g*head_dim ..; o [rows, o_ld] receives O (head h at
+ *   h*head_dim), all `dtype`.  Key j is visible to query i iff j <= i and (j < n_meta
+ *   or window == 0 or i - j < window); q head h reads kv head h*Hkv/Hq.
+ *   scale: 0 => 1/sqrt(head_dim).  Strides in elements, multiples of 8; pointers
+ *   16-byte aligned.  bf16: head_dim 64 or 128; fp32: 32 or 64.
+ *   workspace: device scratch of hymba_op_attn_workspace_bytes(...) bytes (V^T staging
+ *   for bf16; may be NULL when that is 0).  Errors as for the layer calls.
+ * ------------------------------------------------------------------------- */
+size_t hymba_op_attn_workspace_bytes(int32_t dtype, int32_t n_meta, int32_t seq_len,
+                                     int32_t batch, int32_t n_kv_heads, int32_t head_dim);
+hymba_status hymba_op_attn(int32_t dtype, const void *q, int64_t q_ld, const void *k,
+                           const void *v, int64_t kv_ld, void *o, int64_t o_ld, int32_t n_meta,
+                           int32_t seq_len, int32_t batch, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t window, float scale,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * hymba_op_scan: the SSM heads alone (steps a3's dt projection and a5), on the kernels
+ * the layer uses.  Source: Design formulation, SSM-head mixing coefficients and the
+ * gated output Y_ssm = G * SSM(X); dt = softplus(delta W_dt^T + b) (Mamba).
+ *   Rows as for hymba_op_attn.  z [rows, z_ld] dtype holds the SSM input x at columns
+ *   xs_col .. xs_col + d_inner and G at g_col .. g_col + d_inner; delta [rows, dt_rank]
+ *   dtype (dense); bc [rows, 2*d_state] fp32 (B then C); w_dt [d_inner, dt_rank] dtype;
+ *   dt_bias [d_inner], A [d_inner, d_state], D [d_inner] fp32.
+ *   Every sequence starts from h = 0 and runs over the meta rows, then its own rows:
+ *     dt = softplus(delta W_dt^T + dt_bias); h = exp(dt A) h + dt x B; y = C.h + D x;
+ *   y [rows, y_ld] (dtype) receives y * SiLU(G) (meta rows from sequence 0);
+ *   h_out [batch, d_inner, d_state] fp32 (may be NULL) the final states.
+ *   workspace: hymba_op_scan_workspace_bytes(...) bytes (fp32 dt when the shape has no
+ *   fused kernel; may be NULL when that is 0).  Errors as for the layer calls.
+ * ------------------------------------------------------------------------- */
+size_t hymba_op_scan_workspace_bytes(int32_t dtype, int32_t n_meta, int32_t seq_len,
+                                     int32_t batch, int32_t d_inner, int32_t d_state,
+                                     int32_t dt_rank);
+hymba_status hymba_op_scan(int32_t dtype, const void *z, int64_t z_ld, int32_t xs_col,
+                           int32_t g_col, const void *delta, const float *bc,
+                           const void *w_dt, const float *dt_bias, const float *A,
+                           const float *D, void *y, int64_t y_ld, float *h_out,
+                           int32_t n_meta, int32_t seq_len, int32_t batch, int32_t d_inner,
+                           int32_t d_state, int32_t dt_rank, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -150,3 +150,39 @@ def test_op_gemm_argument_errors(lib):
     assert call(a=4098) == 4
     assert call(m=0) == 0
     assert lib.hymba_op_copy(4096, 8192, 17, None) == 2
+
+
+def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
+    """Validation of the single-step entry points returns a status and launches nothing
+    (every case below fails before the first HIP call, so this runs without a GPU)."""
+    bf, f32 = hy.DTYPE_BF16, hy.DTYPE_F32
+    p = 4096  # a 16-byte aligned stand-in address; nothing is dereferenced
+    attn = lambda **kw: hy.hymba_op_attn(**{**dict(
+        dtype=bf, q=p, q_ld=1024, k=p, v=p, kv_ld=256, o=p, o_ld=1024, n_meta=8, seq_len=64,
+        batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, window=0, scale=0.0, workspace=p,
+        workspace_bytes=0), **kw}, stream=0, check=False)
+    assert attn(dtype=7) == 1
+    assert attn(n_q_heads=6, n_kv_heads=4) == 1          # Hq % Hkv != 0
+    assert attn(head_dim=96, q_ld=768, o_ld=768, kv_ld=192) == 2
+    assert attn(dtype=f32, head_dim=128) == 2             # fp32 kernels: 32 or 64
+    assert attn(q_ld=1000) == 1                           # stride below the heads' width
+    assert attn(q=p + 8) == 4
+    assert attn(q=None) == 1
+    assert attn(workspace_bytes=0) == 3                   # V^T staging needed for bf16
+    assert attn(seq_len=0, n_meta=0) == 0                 # nothing to do
+    need = hy.hymba_op_attn_workspace_bytes(bf, 8, 64, 2, 2, 128)
+    assert need == 2 * 2 * 128 * 128 * 2                  # B x Hkv x dh x keys rounded to 64
+    assert hy.hymba_op_attn_workspace_bytes(f32, 8, 64, 2, 2, 64) == 0
+    scan = lambda **kw: hy.hymba_op_scan(**{**dict(
+        dtype=bf, z=p, z_ld=1024, xs_col=0, g_col=512, delta=p, bc=p, w_dt=p, dt_bias=p, A=p,
+        D=p, y=p, y_ld=512, h_out=None, n_meta=8, seq_len=64, batch=2, d_inner=512, d_state=16,
+        dt_rank=64, workspace=None, workspace_bytes=0), **kw}, stream=0, check=False)
+    assert scan(dtype=3) == 1
+    assert scan(d_state=24) == 2
+    assert scan(g_col=600) == 1                           # G columns past the row
+    assert scan(delta=None) == 1
+    assert scan(y=p + 4) == 4
+    assert scan(dt_rank=16) == 3                          # unfused: needs the fp32 dt buffer
+    assert scan(batch=0, n_meta=0) == 0
+    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64) == 0
+    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 16) == (8 + 128) * 512 * 4

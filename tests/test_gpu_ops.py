@@ -1,0 +1,104 @@
+"""GPU parity of the single-step entry points hymba_op_attn and hymba_op_scan (called
+through the C ABI) against the oracle's attention and selective-scan functions on the
+same seeded inputs.
+
+Tolerances (relative to the tensor's max magnitude) as for the layer: fp32 1e-4; bf16
+outputs 2e-2; the fp32 SSM state 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_attention_ssm_proj_amd as hy
+import oracle as orc
+from synth import BF16, F32, rng, to_storage
+from tests.gpu_util import DEV, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+DT = {F32: hy.DTYPE_F32, BF16: hy.DTYPE_BF16}
+TOL = {F32: 1e-4, BF16: 2e-2}
+
+
+def _normal(g, shape, std=1.0):
+    return (g.standard_normal(size=shape) * std).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,dh,M,L,B,window", [
+    (BF16, 8, 2, 128, 16, 96, 2, 0),
+    (BF16, 8, 2, 128, 16, 160, 2, 48),
+    (BF16, 4, 2, 64, 8, 72, 3, 0),
+    (BF16, 4, 4, 64, 0, 130, 1, 32),
+    (F32, 4, 2, 32, 8, 64, 2, 0),
+    (F32, 2, 1, 64, 4, 40, 1, 16),
+])
+def test_op_attn_matches_oracle(dtype, Hq, Hkv, dh, M, L, B, window):
+    g = rng(40 + Hq + dh + window, 1)
+    rows = M + B * L
+    q_t, q = to_storage(_normal(g, (rows, Hq * dh)), dtype)
+    k_t, k = to_storage(_normal(g, (rows, Hkv * dh)), dtype)
+    v_t, v = to_storage(_normal(g, (rows, Hkv * dh)), dtype)
+    code = DT[dtype]
+    o = torch.zeros(rows, Hq * dh, dtype=q_t.dtype, device=DEV)
+    ws_n = hy.hymba_op_attn_workspace_bytes(code, M, L, B, Hkv, dh)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=DEV)
+    hy.hymba_op_attn(code, q_t.to(DEV), Hq * dh, k_t.to(DEV), v_t.to(DEV), Hkv * dh, o, Hq * dh,
+                     M, L, B, Hq, Hkv, dh, window, 0.0, ws, ws.numel())
+    torch.cuda.synchronize()
+    got = to_np(o)
+    ref = np.zeros((rows, Hq * dh))
+    pos = np.arange(M + L)
+    for b in range(B):
+        idx = np.concatenate([np.arange(M), M + b * L + np.arange(L)]).astype(np.int64)
+        O = orc.attention(q[idx].reshape(-1, Hq, dh), k[idx].reshape(-1, Hkv, dh),
+                          v[idx].reshape(-1, Hkv, dh), pos, pos, M, window, dh ** -0.5)
+        ref[idx] = O.reshape(-1, Hq * dh)
+    err = rel_err(got, ref)
+    print(f"op_attn err {err:.2e}")
+    assert err < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,Di,N,R,M,L,B", [
+    (BF16, 256, 16, 64, 16, 100, 2),   # fused dt projection + scan
+    (BF16, 128, 32, 128, 8, 70, 1),    # fused, 8 lanes per channel
+    (BF16, 128, 16, 16, 8, 64, 2),     # dt_rank outside the fused set: dt GEMM, then scan
+    (F32, 64, 16, 16, 4, 48, 2),
+])
+def test_op_scan_matches_oracle(dtype, Di, N, R, M, L, B):
+    g = rng(60 + Di + N + R, 2)
+    rows = M + B * L
+    zld = 2 * Di + 16
+    zt, z = to_storage(_normal(g, (rows, zld)), dtype)
+    dlt_t, dlt = to_storage(_normal(g, (rows, R), 0.5), dtype)
+    bc = _normal(g, (rows, 2 * N))
+    wdt_t, wdt = to_storage(_normal(g, (Di, R), 0.1), dtype)
+    bias = g.uniform(-4, -2, Di).astype(np.float32)
+    A = (-np.exp(g.uniform(0, 2, (Di, N)))).astype(np.float32)
+    D = _normal(g, (Di,))
+    xs_col, g_col = 8, 8 + Di
+    code = DT[dtype]
+    y = torch.zeros(rows, Di, dtype=zt.dtype, device=DEV)
+    h = torch.zeros(B, Di, N, dtype=torch.float32, device=DEV)
+    ws_n = hy.hymba_op_scan_workspace_bytes(code, M, L, B, Di, N, R)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=DEV)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    hy.hymba_op_scan(code, zt.to(DEV), zld, xs_col, g_col, dlt_t.to(DEV), dev(bc), wdt_t.to(DEV),
+                     dev(bias), dev(A), dev(D), y, Di, h, M, L, B, Di, N, R, ws, ws.numel())
+    torch.cuda.synchronize()
+    dt = orc.softplus(dlt.astype(np.float64) @ wdt.astype(np.float64).T + bias)
+    ref_y = np.zeros((rows, Di))
+    ref_h = np.zeros((B, Di, N))
+    for b in range(B):
+        idx = np.concatenate([np.arange(M), M + b * L + np.arange(L)]).astype(np.int64)
+        yy, hT = orc.selective_scan(z[idx, xs_col:xs_col + Di], dt[idx], A, bc[idx, :N],
+                                    bc[idx, N:], D)
+        out = orc.gate(yy, z[idx, g_col:g_col + Di])
+        if b == 0:
+            ref_y[idx] = out
+        else:
+            ref_y[idx[M:]] = out[M:]
+        ref_h[b] = hT
+    ey, eh = rel_err(to_np(y), ref_y), rel_err(to_np(h), ref_h)
+    print(f"op_scan y err {ey:.2e} h err {eh:.2e}")
+    assert ey < TOL[dtype]
+    assert eh < (1e-3 if dtype == BF16 else 1e-4)
