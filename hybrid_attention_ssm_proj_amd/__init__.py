@@ -12,6 +12,9 @@ import os
 from typing import Optional
 
 __all__ = [
+    "MetaCache", "hymba_layer_meta_cache_build", "hymba_layer_prefill_cached",
+    "hymba_op_attn", "hymba_op_attn_workspace_bytes", "hymba_op_scan",
+    "hymba_op_scan_workspace_bytes",
     "HymbaError", "LayerDesc", "LayerWeights", "KV", "SSMState", "load_library",
     "hymba_layer_prefill", "hymba_layer_decode", "hymba_layer_workspace_bytes",
     "hymba_status_str", "hymba_abi_version", "hymba_last_hip_error", "hymba_timer_enable",
@@ -65,6 +68,11 @@ class SSMState(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
 
 
+class MetaCache(ctypes.Structure):
+    _fields_ = [("k_meta", ctypes.c_void_p), ("v_meta", ctypes.c_void_p), ("h", ctypes.c_void_p),
+                ("y_meta", ctypes.c_void_p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -85,6 +93,13 @@ def load_library() -> ctypes.CDLL:
                                      I32, ctypes.POINTER(KV), ctypes.POINTER(SSMState), P, P, SZ,
                                      P]),
         "hymba_layer_workspace_bytes": (SZ, [ctypes.POINTER(LayerDesc), I32, I32, I32]),
+        "hymba_layer_meta_cache_build": (I32, [ctypes.POINTER(LayerDesc),
+                                               ctypes.POINTER(LayerWeights), P, ctypes.POINTER(KV),
+                                               ctypes.POINTER(MetaCache), P, SZ, P]),
+        "hymba_layer_prefill_cached": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                             ctypes.POINTER(MetaCache), P, I32, I32,
+                                             ctypes.POINTER(KV), ctypes.POINTER(KV),
+                                             ctypes.POINTER(SSMState), P, P, SZ, P]),
         "hymba_status_str": (ctypes.c_char_p, [I32]),
         "hymba_abi_version": (I32, []),
         "hymba_last_hip_error": (I32, []),
@@ -170,6 +185,27 @@ def hymba_layer_decode(desc, weights, x, batch, kv, state, y, workspace, workspa
         _ptr(workspace), workspace_bytes, _stream(stream))
     if check:
         _check(st, "hymba_layer_decode")
+    return st
+
+
+def hymba_layer_meta_cache_build(desc, weights, meta, kv_in, cache, workspace, workspace_bytes,
+                                 stream=None, check=True) -> int:
+    st = load_library().hymba_layer_meta_cache_build(
+        ctypes.byref(desc), ctypes.byref(weights), _ptr(meta), _ref(kv_in), ctypes.byref(cache),
+        _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "hymba_layer_meta_cache_build")
+    return st
+
+
+def hymba_layer_prefill_cached(desc, weights, cache, x, batch, seq_len, kv_in, kv_out, state_out,
+                               y, workspace, workspace_bytes, stream=None, check=True) -> int:
+    st = load_library().hymba_layer_prefill_cached(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(cache), _ptr(x), batch, seq_len,
+        _ref(kv_in), _ref(kv_out), _ref(state_out), _ptr(y), _ptr(workspace), workspace_bytes,
+        _stream(stream))
+    if check:
+        _check(st, "hymba_layer_prefill_cached")
     return st
 
 
@@ -272,6 +308,39 @@ class HymbaLayer:
         hymba_layer_prefill(self.desc, self.weights, meta, x, B, L, kv_in, kv_out, state_out, y,
                             y_meta, ws, ws.numel(), stream)
         return y, y_meta
+
+    def build_meta_cache(self, meta, kv_in: Optional[KV] = None, stream=None):
+        """The layer over its meta tokens alone, once per weight set.  Returns (dict of
+        device tensors, MetaCache struct pointing at them)."""
+        import torch
+        dm = self.dims
+        M = dm.n_meta
+        t = {"h": torch.zeros(dm.d_inner, dm.d_state, dtype=torch.float32, device=self.device),
+             "y_meta": torch.empty(max(M, 1), dm.d_model, dtype=self.store, device=self.device)}
+        if not dm.kv_share:
+            for n in ("k_meta", "v_meta"):
+                t[n] = torch.zeros(dm.n_kv_heads, max(M, 1), dm.head_dim, dtype=self.store,
+                                   device=self.device)
+        cache = MetaCache(_ptr(t.get("k_meta")), _ptr(t.get("v_meta")), _ptr(t["h"]),
+                          _ptr(t["y_meta"]))
+        nb = hymba_layer_workspace_bytes(self.desc, 0, 0, 0)
+        ws = self.workspace(nb)
+        hymba_layer_meta_cache_build(self.desc, self.weights, meta, kv_in, cache, ws, ws.numel(),
+                                     stream)
+        return t, cache
+
+    def prefill_cached(self, cache: "MetaCache", x, kv_in: Optional[KV] = None,
+                       kv_out: Optional[KV] = None, state_out: Optional[SSMState] = None, y=None,
+                       stream=None):
+        import torch
+        B, L = x.shape[0], x.shape[1]
+        if y is None:
+            y = torch.empty(B, L, self.dims.d_model, dtype=self.store, device=self.device)
+        nb = hymba_layer_workspace_bytes(self.desc, B, L, 2)
+        ws = self.workspace(nb)
+        hymba_layer_prefill_cached(self.desc, self.weights, cache, x, B, L, kv_in, kv_out,
+                                   state_out, y, ws, ws.numel(), stream)
+        return y
 
     def decode(self, x, kv: KV, state: SSMState, y=None, stream=None):
         import torch

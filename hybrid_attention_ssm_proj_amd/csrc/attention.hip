@@ -31,8 +31,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;  // lazy-rescaling headroom (log2 units)
 
 // X~ position -> row of the query / Z arrays.
-__device__ __forceinline__ int64_t pos_row(int pos, int b, int n_meta, int L) {
-  return pos < n_meta ? (int64_t)pos : (int64_t)n_meta + (int64_t)b * L + (pos - n_meta);
+__device__ __forceinline__ int64_t q_row(const AttnParams& p, int pos, int b) {
+  return pos < p.n_meta ? (int64_t)pos
+                        : (int64_t)p.meta_rows + (int64_t)b * p.L + (pos - p.n_meta);
 }
 
 template <typename T>
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   for (int qt = 0; qt < 2; ++qt) {
     const int pos = wp0 + qt * 16 + (lane & 15);
     const bool ok = pos < plim;
-    const bf16* src = qbase + pos_row(ok ? pos : 0, b, p.n_meta, p.L) * p.q_row_stride + h * DH +
+    const bf16* src = qbase + q_row(p, ok ? pos : p0, b) * p.q_row_stride + h * DH +
                       (lane >> 4) * 8;
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
     for (int d = 0; d < DH / 16; ++d)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[d][r] = oacc[d][qt][r] * inv;
-    const int64_t row = pos_row(pos < plim ? pos : 0, b, p.n_meta, p.L);
+    const int64_t row = q_row(p, pos < plim ? pos : p0, b);
     if (p.ssp != nullptr) {
       float q = 0.f;
 #pragma unroll
@@ -459,7 +460,7 @@ static hipError_t run_attn_dl(const AttnParams& p, void* vt, hipStream_t s) {
   const int gq = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
   const int qb = 32 * (NW / gq);
   const int nblk_seq = (p.L + qb - 1) / qb;
-  const int nblk_meta = (p.n_meta + qb - 1) / qb;
+  const int nblk_meta = p.meta_rows > 0 ? (p.n_meta + qb - 1) / qb : 0;
   const int nx = p.B * nblk_seq + nblk_meta;
   if (nx == 0) return hipSuccess;
   attn_prefill_dl_kernel<DH, NW, NS><<<dim3(nx, p.Hq / gq), dim3(NW * 64), 0, s>>>(
@@ -485,12 +486,12 @@ template <typename T>
 __global__ __launch_bounds__(64) void attn_prefill_simple_kernel(AttnParams p) {
   const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   int b, i;
-  if (r < p.n_meta) {
+  if (r < p.meta_rows) {
     b = 0;
     i = r;
   } else {
-    b = (r - p.n_meta) / p.L;
-    i = p.n_meta + (r - p.n_meta) % p.L;
+    b = (r - p.meta_rows) / p.L;
+    i = p.n_meta + (r - p.meta_rows) % p.L;
   }
   const int g = (h * p.Hkv) / p.Hq;
   const int dh = p.head_dim;
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(64) void attn_prefill_simple_kernel(AttnParams p) {
 }
 
 hipError_t launch_attention_prefill_f32(const AttnParams& p, hipStream_t s) {
-  const int rows = p.n_meta + p.B * p.L;
+  const int rows = p.meta_rows + p.B * p.L;
   if (rows == 0) return hipSuccess;
   attn_prefill_simple_kernel<float><<<dim3(rows, p.Hq), dim3(64), 0, s>>>(p);
   return hipGetLastError();

@@ -159,7 +159,7 @@ bool fused_dt(const Shape& s) { return s.bf16 && scan_fused_supported(s.N, s.R, 
 
 // Prefill: rows = meta rows + batch * tokens.  dt is materialised only when the scan
 // does not compute it in place.
-Carve carve_prefill(const Shape& s, int64_t rows, int B, int L) {
+Carve carve_prefill(const Shape& s, int64_t rows, int B, int L, bool cached = false) {
   Carve c{};
   size_t off = 0;
   c.z = off;
@@ -175,7 +175,7 @@ Carve carve_prefill(const Shape& s, int64_t rows, int B, int L) {
   c.vt = off;  // bf16 attention: V^T staging
   if (s.bf16) off = align_up(off + attention_vt_bytes(s.M, L, B, s.Hkv, s.dh));
   c.macc = off;  // bf16: fp32 accumulator of the split-K out_proj over the meta rows
-  if (s.bf16) off = align_up(off + (size_t)s.M * s.d * 4);
+  if (s.bf16 && !cached) off = align_up(off + (size_t)s.M * s.d * 4);
   c.ssp = off;   // bf16 + fused scan: per-row partial sums of squares of the branches
   if (s.bf16 && fused_dt(s))
     off = align_up(off + (size_t)rows * (s.Hq + scan_channel_blocks(s.N, s.Di)) * 4);
@@ -260,6 +260,9 @@ size_t hymba_layer_workspace_bytes(const hymba_layer_desc* desc, int32_t batch, 
     const int64_t rows = (int64_t)s.M + (int64_t)batch * seq_len;
     return carve_prefill(s, rows, batch, seq_len).total;
   }
+  if (mode == 2) {  // prefill from a meta-prefix cache: the meta rows are not recomputed
+    return carve_prefill(s, (int64_t)batch * seq_len, batch, seq_len, true).total;
+  }
   if (mode == 1) {
     // seq_len carries the ring capacity (slots) for decode.
     const int span_max = s.W > 0 ? std::min(s.W, seq_len) : seq_len;
@@ -292,21 +295,38 @@ hymba_status hymba_timer_read(int32_t stage, double* total_ms, int32_t* launches
   return HYMBA_OK;
 }
 
-hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer_weights* w,
-                                 const void* meta, const void* x, int32_t batch,
-                                 int32_t seq_len, const hymba_kv* kv_in, hymba_kv* kv_out,
-                                 hymba_ssm_state* state_out, void* y, void* y_meta,
-                                 void* workspace, size_t workspace_bytes, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// The prefill pass.  Three uses: the plain call (meta rows computed with the batch),
+// the meta-cache build (batch 0: meta rows only; h_meta_out receives the state after
+// them), and the cached call (cache != nullptr: the meta rows are not recomputed; their
+// K/V and the post-meta state come from the cache).  Mr = meta rows held in Z and F.
+hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weights* w,
+                          const void* meta, const void* x, int32_t batch, int32_t seq_len,
+                          const hymba_kv* kv_in, hymba_kv* kv_out, hymba_ssm_state* state_out,
+                          void* y, void* y_meta, const hymba_meta_cache* cache,
+                          float* h_meta_out, void* workspace, size_t workspace_bytes,
+                          void* stream_) {
   Shape s;
   hymba_status st = make_shape(desc, s);
   if (st != HYMBA_OK) return st;
   if ((st = check_weights(w)) != HYMBA_OK) return st;
   if (batch < 0 || seq_len < 0) return HYMBA_ERR_INVALID_ARG;
-  const int B = batch, L = seq_len, M = s.M;
+  const bool cached = cache != nullptr;
+  const int B = batch, L = seq_len, M = s.M, Mr = cached ? 0 : s.M;
   const int64_t BL = (int64_t)B * L;
-  const int64_t rows = M + BL;
+  const int64_t rows = Mr + BL;
   if (rows > (int64_t)1 << 31 || BL > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
-  if (M > 0 && meta == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (Mr > 0 && meta == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (h_meta_out != nullptr && BL != 0) return HYMBA_ERR_INVALID_ARG;
+  if (cached) {
+    if (M > 0 && cache->h == nullptr) return HYMBA_ERR_INVALID_ARG;
+    if (!s.share && M > 0 && (cache->k_meta == nullptr || cache->v_meta == nullptr))
+      return HYMBA_ERR_INVALID_ARG;
+    if (any_misaligned(cache->k_meta, cache->v_meta, cache->h)) return HYMBA_ERR_ALIGNMENT;
+  }
   if (BL > 0 && (x == nullptr || y == nullptr)) return HYMBA_ERR_INVALID_ARG;
   if (s.share) {
     if (kv_in == nullptr || kv_out != nullptr) return HYMBA_ERR_INVALID_ARG;
@@ -321,7 +341,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     if (kv_out != nullptr) {
       if (kv_out->slots <= 0 || kv_out->k == nullptr || kv_out->v == nullptr)
         return HYMBA_ERR_INVALID_ARG;
-      if (M > 0 && (kv_out->k_meta == nullptr || kv_out->v_meta == nullptr))
+      if (Mr > 0 && (kv_out->k_meta == nullptr || kv_out->v_meta == nullptr))
         return HYMBA_ERR_INVALID_ARG;
       if (any_misaligned(kv_out->k, kv_out->v, kv_out->k_meta, kv_out->v_meta))
         return HYMBA_ERR_ALIGNMENT;
@@ -332,9 +352,11 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     if (any_misaligned(state_out->h, state_out->pos)) return HYMBA_ERR_ALIGNMENT;
   }
   if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
-  const Carve cv = carve_prefill(s, rows, B, L);
+  const Carve cv = carve_prefill(s, rows, B, L, cached);
   if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_;
+  if (h_meta_out != nullptr && M == 0)  // no meta tokens: the post-meta state is zero
+    HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_zero_f32(h_meta_out, (int64_t)s.Di * s.N, stream));
   if (rows == 0) return HYMBA_OK;
 
   char* z = ws_ptr(workspace, cv.z);
@@ -353,7 +375,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   // and out_proj scales the two K segments of F by them.  This drops the separate pass
   // that rewrote F.
   const bool few_meta = b16 && s.d % 256 == 0 && s.fw % 256 == 0;
-  const GemmOperands op_out{f + (size_t)M * s.fw * s.es, s.fw, nullptr, 0, (int)BL, w->w_out,
+  const GemmOperands op_out{f + (size_t)Mr * s.fw * s.es, s.fw, nullptr, 0, (int)BL, w->w_out,
                             s.fw, (int)BL, s.d, (int)s.fw};
   const bool defer_norm = b16 && fused_dt(s) && s.qw % 128 == 0 &&
                           (BL == 0 || gemm_bf16_rowscaled_ok(op_out, (int)s.qw)) &&
@@ -366,7 +388,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   // 1. in_proj over [meta; X]: the batch-shared meta rows once, then the X rows.
   // The meta rows are few: the few-row kernel (64-row blocks, every column tile its own
   // workgroup) fills the chip better than 256-row tiles.
-  if (M > 0) {
+  if (Mr > 0) {
     GemmOperands op{meta, s.d, nullptr, 0, M, w->w_in, s.d, M, (int)s.n_in, s.d};
     if (few_meta) {
       HYMBA_LAUNCH(HYMBA_STAGE_META,
@@ -379,7 +401,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   }
   if (BL > 0) {
     GemmOperands op{x, s.d, nullptr, 0, (int)BL, w->w_in, s.d, (int)BL, (int)s.n_in, s.d};
-    GemmOutput out{EpiKind::Store, z + (size_t)M * s.n_in * s.es, s.n_in, nullptr, 0, (int)BL, 0,
+    GemmOutput out{EpiKind::Store, z + (size_t)Mr * s.n_in * s.es, s.n_in, nullptr, 0, (int)BL, 0,
                    nullptr};
     HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ, gemm(op, out, GemmShape::Large));
   }
@@ -387,8 +409,8 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
   if (!s.share && kv_out != nullptr) {
     HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE,
                  launch_kv_write_prefill(b16, z, s.n_in, (int)s.k_col, (int)s.v_col, kv_out->k_meta,
-                                         kv_out->v_meta, kv_out->k, kv_out->v, kv_out->slots, M, L,
-                                         B, s.Hkv, s.dh, stream));
+                                         kv_out->v_meta, kv_out->k, kv_out->v, kv_out->slots, Mr,
+                                         L, B, s.Hkv, s.dh, stream));
   }
   // 3. attention heads -> F[:, :qw].
   {
@@ -407,12 +429,19 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
       ap.seq_row_stride = s.dh;
       ap.seq_slots = kv_in->slots;
     } else {
-      ap.k_meta = z + s.k_col * s.es;
-      ap.v_meta = z + s.v_col * s.es;
-      ap.meta_head_stride = s.dh;
-      ap.meta_row_stride = s.n_in;
-      ap.k_seq = z + ((size_t)M * s.n_in + s.k_col) * s.es;
-      ap.v_seq = z + ((size_t)M * s.n_in + s.v_col) * s.es;
+      if (cached) {  // meta K/V from the cache, [Hkv, M, dh]
+        ap.k_meta = cache->k_meta;
+        ap.v_meta = cache->v_meta;
+        ap.meta_head_stride = (int64_t)M * s.dh;
+        ap.meta_row_stride = s.dh;
+      } else {
+        ap.k_meta = z + s.k_col * s.es;
+        ap.v_meta = z + s.v_col * s.es;
+        ap.meta_head_stride = s.dh;
+        ap.meta_row_stride = s.n_in;
+      }
+      ap.k_seq = z + ((size_t)Mr * s.n_in + s.k_col) * s.es;
+      ap.v_seq = z + ((size_t)Mr * s.n_in + s.v_col) * s.es;
       ap.seq_batch_stride = (int64_t)L * s.n_in;
       ap.seq_head_stride = s.dh;
       ap.seq_row_stride = s.n_in;
@@ -421,6 +450,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     ap.o = f;
     ap.o_row_stride = s.fw;
     ap.n_meta = M;
+    ap.meta_rows = Mr;
     ap.L = L;
     ap.B = B;
     ap.Hq = s.Hq;
@@ -463,7 +493,8 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     sp.y = f + s.qw * s.es;
     sp.y_stride = s.fw;
     sp.h_out = state_out ? state_out->h : nullptr;
-    sp.n_meta = M;
+    sp.h0 = cached ? cache->h : nullptr;
+    sp.n_meta = Mr;
     sp.L = L;
     sp.B = B;
     sp.Di = s.Di;
@@ -474,7 +505,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     sp.beta = w->beta_ssm;
     if (B == 0) {  // meta rows only: run them as one sequence of length 0
       sp.B = 1;
-      sp.h_out = nullptr;
+      sp.h_out = h_meta_out;
     }
     if (fuse) {
       HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill_fused(sp, delta, w->w_dt, w->dt_bias,
@@ -489,13 +520,13 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     HYMBA_LAUNCH(HYMBA_STAGE_NORM,
                  launch_row_factors(ssp, ssp_ld, s.Hq, n_sblk, (int)rows, (int)s.qw, s.Di,
                                     desc->rms_eps, fac, f, s.fw,
-                                    y_meta != nullptr ? M : 0, stream));
+                                    y_meta != nullptr ? Mr : 0, stream));
   } else {
     HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
                                                     w->beta_attn, w->beta_ssm, desc->rms_eps,
                                                     stream));
   }
-  const RowScale rs_seq{fac != nullptr ? fac + 2 * (int64_t)M : nullptr, (int)s.qw};
+  const RowScale rs_seq{fac != nullptr ? fac + 2 * (int64_t)Mr : nullptr, (int)s.qw};
   // 8. out_proj: sequence rows -> y, then the batch-shared meta rows -> y_meta.  Two
   // launches keep the large one on whole 256-row tiles (B*L rows), so it runs as an
   // exact number of rounds over the CUs.
@@ -507,7 +538,7 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
       HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op_out, out, GemmShape::Large));
     }
   }
-  if (M > 0 && y_meta != nullptr) {
+  if (Mr > 0 && y_meta != nullptr) {
     GemmOperands op{f, s.fw, nullptr, 0, M, w->w_out, s.fw, M, s.d, (int)s.fw};
     if (few_meta) {  // K is long: split it into fp32 atomics, then round to bf16
       float* macc = (float*)ws_ptr(workspace, cv.macc);
@@ -525,6 +556,56 @@ hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer
     HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_fill_i32(state_out->pos, L, B, stream));
   }
   return HYMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hymba_status hymba_layer_prefill(const hymba_layer_desc* desc, const hymba_layer_weights* w,
+                                 const void* meta, const void* x, int32_t batch,
+                                 int32_t seq_len, const hymba_kv* kv_in, hymba_kv* kv_out,
+                                 hymba_ssm_state* state_out, void* y, void* y_meta,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(desc, w, meta, x, batch, seq_len, kv_in, kv_out, state_out, y, y_meta,
+                      nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+hymba_status hymba_layer_meta_cache_build(const hymba_layer_desc* desc,
+                                          const hymba_layer_weights* w, const void* meta,
+                                          const hymba_kv* kv_in, hymba_meta_cache* cache,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (desc == nullptr || cache == nullptr || cache->h == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (desc->kv_share) {
+    // the consumer's meta keys are the producer's: kv_in holds them
+    if (kv_in == nullptr) return HYMBA_ERR_INVALID_ARG;
+    hymba_kv src = *kv_in;
+    if (src.k == nullptr || src.v == nullptr) {  // no sequence positions are read
+      src.k = src.k_meta;
+      src.v = src.v_meta;
+    }
+    if (src.slots <= 0) src.slots = 1;
+    return prefill_impl(desc, w, meta, nullptr, 0, 0, &src, nullptr, nullptr, nullptr,
+                        cache->y_meta, nullptr, cache->h, workspace, workspace_bytes, stream);
+  }
+  if (kv_in != nullptr) return HYMBA_ERR_INVALID_ARG;
+  // producer: the meta K/V go to the cache (no sequence slots are written at batch 0)
+  hymba_kv out{cache->k_meta, cache->v_meta, cache->k_meta, cache->v_meta, 1};
+  return prefill_impl(desc, w, meta, nullptr, 0, 0, nullptr,
+                      desc->n_meta > 0 ? &out : nullptr, nullptr, nullptr, cache->y_meta,
+                      nullptr, cache->h, workspace, workspace_bytes, stream);
+}
+
+hymba_status hymba_layer_prefill_cached(const hymba_layer_desc* desc,
+                                        const hymba_layer_weights* w,
+                                        const hymba_meta_cache* cache, const void* x,
+                                        int32_t batch, int32_t seq_len, const hymba_kv* kv_in,
+                                        hymba_kv* kv_out, hymba_ssm_state* state_out, void* y,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache == nullptr) return HYMBA_ERR_INVALID_ARG;
+  return prefill_impl(desc, w, nullptr, x, batch, seq_len, kv_in, kv_out, state_out, y, nullptr,
+                      cache, nullptr, workspace, workspace_bytes, stream);
 }
 
 hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_weights* w,
@@ -741,6 +822,7 @@ hymba_status hymba_op_attn(int32_t dtype, const void* q, int64_t q_ld, const voi
   ap.o = o;
   ap.o_row_stride = o_ld;
   ap.n_meta = n_meta;
+  ap.meta_rows = n_meta;
   ap.L = seq_len;
   ap.B = batch;
   ap.Hq = n_q_heads;

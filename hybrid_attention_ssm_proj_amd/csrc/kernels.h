@@ -77,8 +77,10 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
 // Keys/values at X~ position j of sequence b: j < n_meta from the meta arrays
 // (meta + g*meta_head_stride + j*meta_row_stride), otherwise from the sequence
 // arrays (seq + b*seq_batch_stride + g*seq_head_stride + ((j - n_meta) % seq_slots) *
-// seq_row_stride).  Queries: row r of q (stride q_row_stride); r < n_meta is a meta
-// row (shared), otherwise sequence b = (r - n_meta) / L at X-position (r - n_meta) % L.
+// seq_row_stride).  Queries and outputs: row r of q / o; the first meta_rows rows are
+// the meta queries (meta_rows = n_meta, or 0 when the meta rows are cached and not
+// recomputed), then sequence b = (r - meta_rows) / L at X-position
+// n_meta + (r - meta_rows) % L.
 struct AttnParams {
   const void* q;
   int64_t q_row_stride;
@@ -93,6 +95,7 @@ struct AttnParams {
   int64_t o_row_stride;
   int n_meta, L, B, Hq, Hkv, head_dim, window;
   float scale;
+  int meta_rows;
   // bf16 prefill only: with ssp != nullptr the kernel writes beta[h*head_dim + d] * O
   // and the row's sum of O^2 over head h to ssp[h * ssp_ld + row] (row as for q).
   float* ssp;
@@ -139,6 +142,7 @@ struct ScanParams {
   void* y;             // gated output, row stride y_stride (storage type)
   int64_t y_stride;
   float* h_out;        // [B, Di, N] or nullptr
+  const float* h0;     // [Di, N] initial state of every sequence, or nullptr (zero)
   int n_meta, L, B, Di, N;
   // fused bf16 scan only: with ssp != nullptr the kernel writes beta[c] * y and the
   // row's sum of y^2 over the workgroup's channel block j to ssp[(ssp_col0 + j) * ssp_ld

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void scan_prefill_kernel(ScanParams p) {
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     A2[k] = cok ? p.A[(int64_t)c * N + sg * NS + k] * kLog2e : 0.f;
-    h[k] = 0.f;
+    h[k] = (cok && p.h0 != nullptr) ? p.h0[(int64_t)c * N + sg * NS + k] : 0.f;
   }
   const float Dc = cok ? p.D[c] : 0.f;
   const T* z = (const T*)p.z;

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(ScanParams p, const bf1
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     A2[k] = p.A[(int64_t)c * N + sg * NS + k] * kLog2e;
-    h[k] = 0.f;
+    h[k] = p.h0 != nullptr ? p.h0[(int64_t)c * N + sg * NS + k] : 0.f;
   }
   const float Dc = p.D[c];
   float beta8[8];

@@ -156,7 +156,51 @@ hymba_status hymba_layer_decode(const hymba_layer_desc *desc, const hymba_layer_
                                 hymba_ssm_state *state, void *y, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
-/* Workspace bytes for mode 0 (prefill of batch x seq_len) or 1 (decode of batch).
+/* ---------------------------------------------------------------------------
+ * Meta-prefix cache: what a layer computes over its M meta tokens alone.  The meta
+ * tokens are fixed at inference and act as a learned initialisation of the KV cache and
+ * of the SSM state ("Meta Tokens"), so these values do not depend on X and can be built
+ * once per weight set:
+ *   k_meta, v_meta  [Hkv, M, dh] dtype: the meta keys and values (producer layers;
+ *                   NULL for a consumer, whose meta keys are its producer's);
+ *   h               [Di, N] fp32: the SSM state after the meta tokens;
+ *   y_meta          [M, d] dtype: the layer's output rows of the meta tokens (NULL:
+ *                   not produced).
+ * Owned by the caller (device memory).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  void *k_meta;
+  void *v_meta;
+  float *h;
+  void *y_meta;
+} hymba_meta_cache;
+
+/* hymba_layer_meta_cache_build: fills *cache from meta [M, d] (dtype).  A consumer
+ * (kv_share = 1) passes its producer's cache in kv_in (only k_meta / v_meta are read);
+ * a producer passes kv_in = NULL.  workspace: hymba_layer_workspace_bytes(desc, 0, 0, 0).
+ * Source: "Meta Tokens" (learned cache initialisation); Design formulation. */
+hymba_status hymba_layer_meta_cache_build(const hymba_layer_desc *desc,
+                                          const hymba_layer_weights *w, const void *meta,
+                                          const hymba_kv *kv_in, hymba_meta_cache *cache,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *stream);
+
+/* hymba_layer_prefill_cached: hymba_layer_prefill over X with the meta rows taken from
+ * a built cache instead of being recomputed: attention reads the meta K/V from the cache
+ * (a consumer: from kv_in as usual), every sequence's scan starts from cache->h, and no
+ * y_meta is produced.  kv_out (producer, may be NULL) receives only the sequence
+ * positions; a later decode reads the meta K/V through kv->k_meta = cache->k_meta.
+ * workspace: hymba_layer_workspace_bytes(desc, B, L, 2).  Results equal those of
+ * hymba_layer_prefill on the same meta tokens. */
+hymba_status hymba_layer_prefill_cached(const hymba_layer_desc *desc,
+                                        const hymba_layer_weights *w,
+                                        const hymba_meta_cache *cache, const void *x,
+                                        int32_t batch, int32_t seq_len, const hymba_kv *kv_in,
+                                        hymba_kv *kv_out, hymba_ssm_state *state_out, void *y,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for mode 0 (prefill of batch x seq_len), 1 (decode of batch; seq_len
+ * carries the ring capacity) or 2 (prefill_cached of batch x seq_len).
  * Returns 0 if the descriptor or sizes are invalid. */
 size_t hymba_layer_workspace_bytes(const hymba_layer_desc *desc, int32_t batch,
                                    int32_t seq_len, int32_t mode);
