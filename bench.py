@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 16-layer partial-SWA vs all-global stack comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the prefill workload the CPU oracle runs (8 = all)")
@@ -294,6 +296,10 @@ def main():
     if not args.no_decode:
         decode = bench_decode(hy, torch, dev, args)
 
+    stack = None
+    if not args.no_stack:
+        stack = bench_stack(hy, torch, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
@@ -311,9 +317,75 @@ def main():
         "cpu_baseline": cpu,
         "decode": decode,
         "prefill_meta_cached": cached,
+        "stack": stack,
         "stages": stage_report,
     }
     print(json.dumps(out), flush=True)
+
+
+def device_weights(torch, dims, seed, dev):
+    """Synthetic weights of one layer drawn on the device (the distributions of the
+    seeded CPU generator: W ~ N(0, 0.02), dt_bias ~ U[-4, -2], A = -exp(U[0, 2]),
+    D ~ N(0, 1), beta = 1), for stacks too large to draw on the host quickly."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+    n = lambda *sh, std=0.02: (torch.randn(*sh, generator=g, device=dev) * std)
+    u = lambda lo, hi, *sh: torch.rand(*sh, generator=g, device=dev) * (hi - lo) + lo
+    Di, N, R = dims.d_inner, dims.d_state, dims.dt_rank
+    return {"w_in": n(dims.n_in, dims.d_model).to(bf), "w_x": n(R + 2 * N, Di).to(bf),
+            "w_dt": n(Di, R).to(bf), "w_out": n(dims.d_model, dims.f_width).to(bf),
+            "dt_bias": u(-4, -2, Di), "A": -torch.exp(u(0, 2, Di, N)),
+            "D": n(Di, std=1.0), "beta_attn": torch.ones(dims.q_width, device=dev),
+            "beta_ssm": torch.ones(Di, device=dev)}
+
+
+def bench_stack(hy, torch, dev, n_layers=16, B=1, L=8192, W=1024, dsteps=16, steps=3):
+    """The partial sliding-window schedule with KV-sharing pairs (global attention at the
+    first, middle and last layers) against an all-global stack of the same depth: prefill
+    tokens/s, decode tokens/s and the K/V bytes kept for decode."""
+    from hybrid_attention_ssm_proj_amd.stack import HymbaStack
+    from synth import CASES
+    dims = CASES[1].dims
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    meta = torch.randn(dims.n_meta, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    x = torch.randn(B, L + dsteps, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    xp = x[:, :L].contiguous()
+    res = {}
+    for name, win in (("partial_swa", W), ("all_global", 0)):
+        st = HymbaStack(dims, n_layers, lambda l, ld: device_weights(torch, ld, 1000 + l, dev),
+                        win, device=dev)
+        st.alloc(B, L, L + dsteps)
+        st.prefill(meta, xp)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.prefill(meta, xp)
+        torch.cuda.synchronize()
+        tp = (time.perf_counter() - t0) / steps
+        t0 = time.perf_counter()
+        for s in range(dsteps):
+            st.decode(x[:, L + s].contiguous())
+        torch.cuda.synchronize()
+        td = (time.perf_counter() - t0) / dsteps
+        res[name] = {"prefill_ms": round(tp * 1e3, 3), "prefill_tokens_per_s": round(B * L / tp, 1),
+                     "decode_us_per_step": round(td * 1e6, 1),
+                     "decode_tokens_per_s": round(B / td, 1),
+                     "decode_cache_bytes": st.decode_cache_bytes(B, L + dsteps),
+                     "global_layers": [l for l, sc in enumerate(st.sched) if sc[0] == 0],
+                     "consumers": [l for l, sc in enumerate(st.sched) if sc[1] == 1]}
+        log(f"[bench] stack {name}: prefill {tp * 1e3:.2f} ms ({B * L / tp / 1e6:.3f} M tok/s), "
+            f"decode {td * 1e6:.1f} us/step, cache {res[name]['decode_cache_bytes'] / 1e6:.1f} MB")
+        del st
+        torch.cuda.empty_cache()
+    a, g = res["partial_swa"], res["all_global"]
+    res["ratios"] = {"prefill_speedup": round(g["prefill_ms"] / a["prefill_ms"], 3),
+                     "decode_speedup": round(g["decode_us_per_step"] / a["decode_us_per_step"], 3),
+                     "cache_reduction": round(g["decode_cache_bytes"] / a["decode_cache_bytes"], 3)}
+    res["workload"] = (f"{n_layers} layers of the prefill layer shape, B={B}, L={L}, window {W}, "
+                       f"then {dsteps} decode steps; layer l+1 takes layer l's y and y_meta")
+    return res
 
 
 def bench_decode(hy, torch, dev, args):

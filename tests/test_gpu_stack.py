@@ -1,0 +1,98 @@
+"""GPU checks of the layer stack with the partial sliding-window schedule and KV-sharing
+pairs (hybrid_attention_ssm_proj_amd.stack), through the C ABI.
+
+Prefill: every layer's output against the oracle run on that layer's own inputs (the
+GPU's outputs of the layer below, bf16) and, for a consumer, on the K/V the oracle's
+producer computes from its own inputs; bf16 gate 2e-2.  Decode: causality fixes the
+next token's output, so decode after a prefill of L tokens must give the last row of a
+prefill of L + 1 tokens, through every layer (global caches, sliding-window rings,
+shared K/V).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from hybrid_attention_ssm_proj_amd.stack import HymbaStack, schedule
+from synth import gen_activations, gen_layer_weights
+from tests.gpu_util import DEV, rel_err, to_np
+from tests.test_gpu_parity import TOL_BF16, small_dims
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack(dims, n_layers, window, case):
+    ws = {}
+
+    def weights(l, ld):
+        ws[l] = gen_layer_weights(ld, case, layer=l)
+        return {k: v for k, v in ws[l].torch.items()}
+    return HymbaStack(dims, n_layers, weights, window, device=DEV), ws
+
+
+def test_schedule_roles():
+    assert schedule(6, 40) == [(0, 0, 0), (40, 0, 1), (40, 1, 1), (0, 0, 3), (40, 0, 4), (0, 0, 5)]
+    assert schedule(8, 16) == [(0, 0, 0), (16, 0, 1), (16, 1, 1), (16, 0, 3), (0, 0, 4),
+                               (16, 0, 5), (16, 1, 5), (0, 0, 7)]
+    assert all(s[0] == 0 and s[1] == 0 for s in schedule(5, 0))
+
+
+def test_stack_prefill_each_layer_matches_oracle():
+    dims = small_dims()
+    B, L, W = 2, 96, 40
+    st, ws = _stack(dims, 6, W, 97)
+    st.alloc(B, L, L + 4)
+    meta_t, _, x_t, _ = gen_activations(dims, 97, B, L)
+    keep = []
+    st.prefill(meta_t.to(DEV), x_t.to(DEV), keep=keep)
+    torch.cuda.synchronize()
+    K = {}
+    for l, (m_in, x_in, y, ym) in enumerate(keep):
+        win, share, prod = st.sched[l]
+        ld = st.layers[l].dims
+        m_np, x_np = to_np(m_in), to_np(x_in)
+        src = None
+        if share:
+            src = [{"K": K[prod]["K"][b], "V": K[prod]["V"][b]} for b in range(B)]
+        ref = orc.prefill(ld, ws[l], m_np, x_np, kv_src=src, contract=True)
+        K[l] = ref
+        e_y, e_m = rel_err(to_np(y), ref["y"]), rel_err(to_np(ym), ref["y_meta"][0])
+        e_h = rel_err(to_np(st.states[l]["h"]), ref["h"])
+        print(l, (win, share, prod), f"y {e_y:.2e} y_meta {e_m:.2e} h {e_h:.2e}")
+        assert e_y < TOL_BF16 and e_m < TOL_BF16 and e_h < 1e-3, l
+
+
+def test_stack_decode_continues_the_prefill():
+    """decode(prefill(x[:L]), x[L + s]) == prefill(x[:L + s + 1])[L + s] for every layer
+    stack role, across a sliding-window ring that wraps."""
+    dims = small_dims()
+    B, L, W, steps = 2, 60, 24, 3
+    meta_t, _, x_t, _ = gen_activations(dims, 98, B, L + steps)
+    meta, x = meta_t.to(DEV), x_t.to(DEV)
+    a, _ = _stack(dims, 6, W, 98)
+    a.alloc(B, L, L + steps)
+    a.prefill(meta, x[:, :L].contiguous())
+    outs = []
+    for s in range(steps):
+        outs.append(a.decode(x[:, L + s].contiguous()))
+    torch.cuda.synchronize()
+    b, _ = _stack(dims, 6, W, 98)
+    b.alloc(B, L + steps, L + steps)
+    yb, _ = b.prefill(meta, x)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        e = rel_err(to_np(outs[s]), to_np(yb[:, L + s]))
+        print(f"step {s}: {e:.2e}")
+        assert e < TOL_BF16, (s, e)
+
+
+def test_cache_bytes_partial_swa_vs_all_global():
+    dims = small_dims()
+    st, _ = _stack(dims, 6, 40, 99)
+    g, _ = _stack(dims, 6, 0, 99)
+    B, ctx = 4, 1000
+    per = 2 * dims.n_kv_heads * dims.head_dim * 2
+    # producers: globals 0, 3, 5 keep ctx positions, sliding-window producers 1 and 4 keep 40
+    assert st.decode_cache_bytes(B, ctx) == per * (3 * (B * ctx + dims.n_meta) +
+                                                   2 * (B * 40 + dims.n_meta))
+    assert g.decode_cache_bytes(B, ctx) == per * 6 * (B * ctx + dims.n_meta)
