@@ -522,16 +522,19 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
 }
 
 // ------------------------------------------------------------ bf16 few-row GEMM (decode)
-// Few rows (the decode batch): a workgroup owns a 128 x 64 output tile (all rows of its
-// m-block) and one K slice (blockIdx.y, a multiple of 256).  Four LDS stages of 64-k
-// tiles, three in flight ahead of the one being multiplied, keep the weight stream
-// busy.  The MFMA runs un-swapped, so per accumulator element the 64 lanes cover two
-// rows x 32 consecutive columns.  Epilogues: fp32 atomics into an accumulator (when K
-// is split), or the decode in_proj store: Z in bf16 plus the producer's new K/V row
-// at ring slot pos[b] % slots.
+// Few rows (the decode batch): a workgroup owns a BM x 64 output tile and one K slice
+// (blockIdx.y, a multiple of 256).  NS LDS stages of 64-k tiles, NS - 1 in flight ahead
+// of the one being multiplied, keep the weight stream busy.  The MFMA runs un-swapped,
+// so per accumulator element the 64 lanes cover two rows x 32 consecutive columns.
+// Epilogues (FewRowMode): fp32 atomics into one accumulator; fp32 partials, slice p of
+// the K split at acc + p * slice_stride, plain stores (a later pass sums the slices:
+// atomics from every slice onto the same addresses serialise in L2); or the decode
+// in_proj store: Z in bf16 plus the producer's new K/V row at ring slot pos[b] % slots.
+enum FewRowMode { kFewAtomic = 0, kFewPartial = 1, kFewStore = 2 };
 struct FewRowOut {
-  float* acc;        // atomic mode: [M, ldacc] fp32
+  float* acc;        // atomic / partial mode: [M, ldacc] fp32 (per slice in partial mode)
   int64_t ldacc;
+  int64_t slice_stride;
   bf16* z;           // store mode: [M, ldz]
   int64_t ldz;
   int k_col, v_col;  // store mode: K / V column ranges (k_col < 0: no ring write)
@@ -543,30 +546,31 @@ struct FewRowOut {
   int64_t zero_n4;
 };
 
-template <bool ATOMIC, int BM>
+template <int MODE, int BM, int NS>
 __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, FewRowOut out,
                                                                int kslice) {
   constexpr int BN = 64, NW = 4, WN = 2;
   constexpr int TM = BM / 2, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int A_INS = BM / 8 / NW, B_INS = BN / 8 / NW, INS = A_INS + B_INS;
-  __shared__ __attribute__((aligned(1024))) bf16 sA0[BM * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sA1[BM * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sA2[BM * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sA3[BM * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sB0[BN * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sB1[BN * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sB2[BN * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 sB3[BN * 64];
-  bf16* const sa[4] = {sA0, sA1, sA2, sA3};
-  bf16* const sb[4] = {sB0, sB1, sB2, sB3};
+  // NS stages of one 64-k tile each: NS - 1 tiles stay in flight ahead of the one being
+  // multiplied (the memory latency is covered by the bytes in flight per CU).
+  static_assert(NS >= 2 && NS <= 8, "stages");
+  constexpr int SA = BM * 64, SB = BN * 64;  // elements per stage
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * (SA + SB)];
+  auto sa = [&](int st) { return smem + st * (SA + SB); };
+  auto sb = [&](int st) { return smem + st * (SA + SB) + SA; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.z * BM;
   const int kb = blockIdx.y * kslice;
-  if constexpr (!ATOMIC) {
+  // ring slot of row m0 + tid, loaded now and used after the K loop (one round trip per
+  // workgroup instead of one per stored element)
+  int my_slot = 0;
+  if constexpr (MODE == kFewStore) {
+    if (out.k_col >= 0 && tid < BM && m0 + tid < g.M) my_slot = max(out.pos[m0 + tid], 0) % out.slots;
     const int64_t nblk = (int64_t)gridDim.x * gridDim.z;
     for (int64_t i = (blockIdx.z * (int64_t)gridDim.x + blockIdx.x) * 256 + tid; i < out.zero_n4;
          i += nblk * 256)
@@ -589,18 +593,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
   auto issue = [&](int st, int k0) {
 #pragma unroll
     for (int j = 0; j < A_INS; ++j)
-      dma16(A + k0 + a_off[j], (lds_void_t*)(sa[st] + (j * NW + wave) * 512));
+      dma16(A + k0 + a_off[j], (lds_void_t*)(sa(st) + (j * NW + wave) * 512));
 #pragma unroll
     for (int j = 0; j < B_INS; ++j)
-      dma16(Bm + k0 + b_off[j], (lds_void_t*)(sb[st] + (j * NW + wave) * 512));
+      dma16(Bm + k0 + b_off[j], (lds_void_t*)(sb(st) + (j * NW + wave) * 512));
   };
-  floatx16 acc[FM][FN];
+  // Two accumulator sets (even / odd k-steps) so consecutive MFMAs do not wait on each
+  // other: with one 32 x 32 block per wave the tile's four k-steps would otherwise form
+  // one dependent chain.
+  floatx16 acc[FM][FN], acc2[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = acc2[i][j][e] = 0.f;
   const int rl = lane & 31;
   int koff[4];
 #pragma unroll
@@ -608,50 +615,64 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
     koff[ks] = rl * 64 + (((ks * 2 + (lane >> 5)) ^ swz(lane & 15)) * 8);
   const int a_row0 = wm * TM * 64, b_row0 = wn * TN * 64;
   auto compute = [&](int st) {
-    const bf16* a = sa[st];
-    const bf16* b = sb[st];
-    bf16x8 af[2][FM], bfr[2][FN];
-    auto frag = [&](int buf, int ks) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[buf][i] = *(const bf16x8*)(a + a_row0 + i * 2048 + koff[ks]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[buf][j] = *(const bf16x8*)(b + b_row0 + j * 2048 + koff[ks]);
-    };
-    frag(0, 0);
+    const bf16* a = sa(st);
+    const bf16* b = sb(st);
+    bf16x8 af[4][FM], bfr[4][FN];  // the whole tile's fragments, read before any MFMA
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) frag((ks + 1) & 1, ks + 1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[ks][i] = *(const bf16x8*)(a + a_row0 + i * 2048 + koff[ks]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[ks][j] = *(const bf16x8*)(b + b_row0 + j * 2048 + koff[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ks += 2)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = mfma32x32x16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j]);
-    }
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = mfma32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+          acc2[i][j] = mfma32x32x16(af[ks + 1][i], bfr[ks + 1][j], acc2[i][j]);
+        }
   };
 
-  // Step t waits for tile t (up to two later tiles may still be in flight), syncs, refills
-  // the stage tile t-1 used with tile t+3, then multiplies tile t.
-  const int KT = kslice / 64;  // multiple of 4
-  issue(0, kb);
-  issue(1, kb + 64);
-  issue(2, kb + 128);
-  auto step = [&](int t, int st) {
-    const int ahead = min(2, KT - 1 - t);
-    if (ahead == 2)
-      wait_vmcnt<2 * INS>();
-    else if (ahead == 1)
-      wait_vmcnt<INS>();
-    else
-      wait_vmcnt<0>();
+  // Step t waits for tile t (the younger tiles, up to NS - 2 of them, stay in flight),
+  // syncs, refills the stage tile t-1 used with tile t + NS - 1, then multiplies tile t.
+  const int KT = min(kslice, g.K - kb) / 64;  // the last slice may be shorter
+  for (int t = 0; t < NS - 1 && t < KT; ++t) issue(t, kb + t * 64);
+  int st = 0;
+  for (int t = 0; t < KT; ++t) {
+    const int ahead = min(NS - 2, KT - 1 - t);  // tiles issued after tile t
+    switch (ahead) {  // vmcnt counts this wave's INS transfers per tile, oldest first
+      case 6: wait_vmcnt<6 * INS>(); break;
+      case 5: wait_vmcnt<5 * INS>(); break;
+      case 4: wait_vmcnt<4 * INS>(); break;
+      case 3: wait_vmcnt<3 * INS>(); break;
+      case 2: wait_vmcnt<2 * INS>(); break;
+      case 1: wait_vmcnt<INS>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
     lds_barrier();  // keeps the younger tiles in flight
-    if (t + 3 < KT) issue((st + 3) & 3, kb + (t + 3) * 64);
+    if (t + NS - 1 < KT) {
+      const int sn = st == 0 ? NS - 1 : st - 1;  // the stage tile t - 1 used
+      issue(sn, kb + (t + NS - 1) * 64);
+    }
     compute(st);
-  };
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(kt, 0);
-    step(kt + 1, 1);
-    step(kt + 2, 2);
-    step(kt + 3, 3);
+    st = st + 1 == NS ? 0 : st + 1;
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] += acc2[i][j][e];
+
+  int* s_slot = (int*)smem;  // the stages are free after the last multiply
+  if constexpr (MODE == kFewStore) {
+    __syncthreads();
+    if (tid < BM) s_slot[tid] = my_slot;
+    __syncthreads();
   }
 
   // acc[i][j] = D of the 32 x 32 block: element e of lane l is row (e/4)*8 + (l/32)*4 + e%4,
@@ -665,8 +686,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm * TM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         if (m >= g.M || n >= g.N) continue;
-        if constexpr (ATOMIC) {
+        if constexpr (MODE == kFewAtomic) {
           unsafeAtomicAdd(out.acc + (int64_t)m * out.ldacc + n, acc[i][j][e]);
+        } else if constexpr (MODE == kFewPartial) {
+          out.acc[blockIdx.y * out.slice_stride + (int64_t)m * out.ldacc + n] = acc[i][j][e];
         } else {
           const bf16 v = (bf16)acc[i][j][e];
           out.z[(int64_t)m * out.ldz + n] = v;
@@ -682,7 +705,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
             }
             if (ring != nullptr) {
               const int gh = rel / out.head_dim, d = rel % out.head_dim;
-              const int slot = max(out.pos[m], 0) % out.slots;
+              const int slot = s_slot[m - m0];
               ring[(((int64_t)m * out.Hkv + gh) * out.slots + slot) * out.head_dim + d] = v;
             }
           }
@@ -696,19 +719,32 @@ static bool fewrow_ok(const GemmOperands& op) {
          (int64_t)op.N * op.ldb < (1ll << 31);
 }
 
+int splitk_slices(int K, int ksplit) {
+  const int units = K / 256;
+  if (units <= 0) return 1;
+  ksplit = std::max(1, std::min(ksplit, units));
+  const int kslice = (units + ksplit - 1) / ksplit;
+  return (units + kslice - 1) / kslice;
+}
+
 hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t ldacc,
-                                   int ksplit, hipStream_t s) {
+                                   int ksplit, hipStream_t s, int64_t slice_stride) {
   if (op.M <= 0 || op.N <= 0) return hipSuccess;
   if (!fewrow_ok(op)) return hipErrorInvalidValue;
   const int units = op.K / 256;
   ksplit = std::max(1, std::min(ksplit, units));
   const int kslice = ((units + ksplit - 1) / ksplit) * 256;
   const int ns = (op.K + kslice - 1) / kslice;
+  if (slice_stride > 0 && slice_stride < (int64_t)op.M * ldacc) return hipErrorInvalidValue;
   FewRowOut out{};
   out.acc = acc;
   out.ldacc = ldacc;
+  out.slice_stride = slice_stride;
   dim3 grid((op.N + 63) / 64, ns, (op.M + 127) / 128);
-  gemm_bf16_fewrow_kernel<true, 128><<<grid, dim3(256), 0, s>>>(op, out, kslice);
+  if (slice_stride > 0)
+    gemm_bf16_fewrow_kernel<kFewPartial, 128, 4><<<grid, dim3(256), 0, s>>>(op, out, kslice);
+  else
+    gemm_bf16_fewrow_kernel<kFewAtomic, 128, 4><<<grid, dim3(256), 0, s>>>(op, out, kslice);
   return hipGetLastError();
 }
 
@@ -735,7 +771,7 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
   // 64-row blocks: twice the workgroups of one 128-row block per column tile (the
   // weight slice is then read by two workgroups, mostly from L2)
   dim3 grid((op.N + 63) / 64, 1, (op.M + 63) / 64);
-  gemm_bf16_fewrow_kernel<false, 64><<<grid, dim3(256), 0, s>>>(op, out, op.K);
+  gemm_bf16_fewrow_kernel<kFewStore, 64, 4><<<grid, dim3(256), 0, s>>>(op, out, op.K);
   return hipGetLastError();
 }
 

@@ -159,6 +159,24 @@ bool fused_dt(const Shape& s) { return s.bf16 && scan_fused_supported(s.N, s.R, 
 
 // Prefill: rows = meta rows + batch * tokens.  dt is materialised only when the scan
 // does not compute it in place.
+// K slices for a split-K projection so that the grid holds ~1 workgroup per CU.
+int splitk_factor(int M, int N, int K) {
+  const int tiles = std::max(1, ((N + 63) / 64) * ((M + 127) / 128));
+  const int want = (256 + tiles - 1) / tiles;
+  return std::max(1, std::min(want, K / 256));
+}
+
+// Decode projections split along K (bf16, every K a multiple of 256): x_proj into fp32
+// atomics, out_proj into per-slice fp32 partials summed by the row store.
+bool decode_splitk(const Shape& s) {
+  return s.bf16 && s.d % 256 == 0 && s.Di % 256 == 0 && s.fw % 256 == 0;
+}
+
+int out_proj_slices(const Shape& s, int rows) {
+  if (rows <= 0 || s.d <= 0) return 1;
+  return splitk_slices((int)s.fw, splitk_factor(rows, s.d, (int)s.fw));
+}
+
 Carve carve_prefill(const Shape& s, int64_t rows, int B, int L, bool cached = false) {
   Carve c{};
   size_t off = 0;
@@ -174,8 +192,8 @@ Carve carve_prefill(const Shape& s, int64_t rows, int B, int L, bool cached = fa
   off = align_up(off + (size_t)rows * s.fw * s.es);
   c.vt = off;  // bf16 attention: V^T staging
   if (s.bf16) off = align_up(off + attention_vt_bytes(s.M, L, B, s.Hkv, s.dh));
-  c.macc = off;  // bf16: fp32 accumulator of the split-K out_proj over the meta rows
-  if (s.bf16 && !cached) off = align_up(off + (size_t)s.M * s.d * 4);
+  c.macc = off;  // bf16: fp32 partials of the split-K out_proj over the meta rows
+  if (s.bf16 && !cached) off = align_up(off + (size_t)out_proj_slices(s, s.M) * s.M * s.d * 4);
   c.ssp = off;   // bf16 + fused scan: per-row partial sums of squares of the branches
   if (s.bf16 && fused_dt(s))
     off = align_up(off + (size_t)rows * (s.Hq + scan_channel_blocks(s.N, s.Di)) * 4);
@@ -198,17 +216,10 @@ Carve carve_decode(const Shape& s, int batch, int nsplit) {
   off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 4) * 4);
   c.xdbl = off;
   off = align_up(off + (size_t)batch * (s.R + 2 * s.N) * 4);
-  c.yacc = off;
-  off = align_up(off + (size_t)batch * s.d * 4);
+  c.yacc = off;  // out_proj partials, one [batch, d] fp32 block per K slice
+  off = align_up(off + (size_t)(decode_splitk(s) ? out_proj_slices(s, batch) : 1) * batch * s.d * 4);
   c.total = off;
   return c;
-}
-
-// K slices for a split-K projection so that the grid holds ~1 workgroup per CU.
-int splitk_factor(int M, int N, int K) {
-  const int tiles = ((N + 63) / 64) * ((M + 127) / 128);
-  const int want = (256 + tiles - 1) / tiles;
-  return std::max(1, std::min(want, K / 256));
 }
 
 bool misaligned(const void* p) { return p != nullptr && ((uintptr_t)p & 15) != 0; }
@@ -540,13 +551,14 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
   }
   if (Mr > 0 && y_meta != nullptr) {
     GemmOperands op{f, s.fw, nullptr, 0, M, w->w_out, s.fw, M, s.d, (int)s.fw};
-    if (few_meta) {  // K is long: split it into fp32 atomics, then round to bf16
+    if (few_meta) {  // K is long: split it into fp32 partials, then sum and round to bf16
       float* macc = (float*)ws_ptr(workspace, cv.macc);
-      HYMBA_LAUNCH(HYMBA_STAGE_META, launch_zero_f32(macc, (int64_t)M * s.d, stream));
+      const int64_t stride = (int64_t)M * s.d;
       HYMBA_LAUNCH(HYMBA_STAGE_META,
                    launch_gemm_bf16_splitk(op, macc, s.d, splitk_factor(M, s.d, (int)s.fw),
-                                           stream));
-      HYMBA_LAUNCH(HYMBA_STAGE_META, launch_store_rows(true, macc, y_meta, M, s.d, stream));
+                                           stream, stride));
+      HYMBA_LAUNCH(HYMBA_STAGE_META, launch_store_rows(true, macc, y_meta, M, s.d, stream,
+                                                       out_proj_slices(s, M), stride));
     } else {
       GemmOutput out{EpiKind::Store, y_meta, s.d, nullptr, 0, M, 0, nullptr};
       HYMBA_LAUNCH(HYMBA_STAGE_META, gemm(op, out, GemmShape::Large));
@@ -648,18 +660,18 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   // producer's new K/V row into its ring slot in the same pass, and x_proj / out_proj
   // run split-K into fp32 accumulators.  Otherwise the tiled GEMM writes Z directly and
   // a copy kernel fills the ring.
-  const bool splitk = b16 && s.d % 256 == 0 && s.Di % 256 == 0 && s.fw % 256 == 0;
+  const bool splitk = decode_splitk(s);
   auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
     return b16 ? launch_gemm_bf16(op, out, GemmShape::Skinny, stream)
                : launch_gemm_f32(op, out, stream);
   };
   if (splitk) {
-    // the same launch clears the x_proj / out_proj accumulators (contiguous, last)
+    // the same launch clears the x_proj accumulator
     GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
     HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ,
                  launch_gemm_bf16_decode_in(op, z, s.n_in, s.share ? -1 : (int)s.k_col,
                                             (int)s.v_col, kv->k, kv->v, kv->slots, s.Hkv, s.dh,
-                                            state->pos, xdbl, (int64_t)(cv.total - cv.xdbl) / 4,
+                                            state->pos, xdbl, (int64_t)(cv.yacc - cv.xdbl) / 4,
                                             stream));
   } else {
     GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
@@ -742,10 +754,12 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   {
     GemmOperands op{f, s.fw, nullptr, 0, B, w->w_out, s.fw, B, s.d, (int)s.fw};
     if (splitk) {
+      const int64_t stride = (int64_t)B * s.d;
       HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ,
                    launch_gemm_bf16_splitk(op, yacc, s.d, splitk_factor(B, s.d, (int)s.fw),
-                                           stream));
-      HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_store_rows(true, yacc, y, B, s.d, stream));
+                                           stream, stride));
+      HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_store_rows(true, yacc, y, B, s.d, stream,
+                                                       out_proj_slices(s, B), stride));
     } else {
       GemmOutput out{EpiKind::Store, y, s.d, nullptr, 0, B, 0, nullptr};
       HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ, gemm(op, out));

@@ -54,10 +54,13 @@ hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmS
                             hipStream_t s);
 hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStream_t s);
 // Few-row (decode) GEMMs, K % 256 == 0, single-source A.
-// acc[M, N] (fp32, row stride ldacc) += A B^T, K split into up to `ksplit` slices that
-// run as separate workgroups and meet through atomics.
+// K split into up to `ksplit` slices that run as separate workgroups (splitk_slices
+// gives the count).  slice_stride == 0: acc[M, N] (fp32, row stride ldacc) += A B^T
+// through atomics.  slice_stride > 0: slice p stores its partial product at
+// acc + p * slice_stride (stride >= M * ldacc); nothing is accumulated.
+int splitk_slices(int K, int ksplit);
 hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t ldacc, int ksplit,
-                                   hipStream_t s);
+                                   hipStream_t s, int64_t slice_stride = 0);
 // bf16 C = row-scaled A B^T (see RowScale) with the plain store epilogue; K and k_split
 // multiples of 128, 0 < k_split < K.  Returns hipErrorInvalidValue when the operands do
 // not suit the 256-wide tile kernel (check with gemm_bf16_rowscaled_ok first).
@@ -216,8 +219,10 @@ hipError_t launch_kv_write_decode(bool bf16, const void* z, int64_t z_stride, in
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int n, hipStream_t s);
 // Zero `n` floats (n % 4 == 0, 16-byte aligned).
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
-// y[B, d] (storage type, row stride y_stride) = acc[B, d] fp32.
-hipError_t launch_store_rows(bool bf16, const float* acc, void* y, int B, int d, hipStream_t s);
+// y[B, d] (storage type, contiguous) = sum over p < nslices of acc[p * slice_stride +
+// (B, d)] fp32; slice_stride % 4 == 0 when nslices > 1.
+hipError_t launch_store_rows(bool bf16, const float* acc, void* y, int B, int d, hipStream_t s,
+                             int nslices = 1, int64_t slice_stride = 0);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 }  // namespace hymba

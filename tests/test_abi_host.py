@@ -53,7 +53,9 @@ def test_workspace_sizes(lib):
     # Z, delta (bf16), B|C (fp32), F (bf16); this shape computes dt inside the scan;
     # plus V^T staging for attention: B x Hkv x head_dim x (keys rounded up to 64), bf16
     vt = 8 * 4 * 128 * ((128 + 2048 + 63) // 64 * 64) * 2
-    macc = 128 * 2048 * 4  # fp32 accumulator of the meta-row out_proj
+    # fp32 partials of the meta-row out_proj: K = 6144 in 8 slices (32 column tiles of 64
+    # want 8 workgroups each to fill 256 CUs), one [128, 2048] block per slice
+    macc = 8 * 128 * 2048 * 4
     # per-row partial sums of squares (16 heads + 64 scan channel blocks) and the two
     # row factors of the branch norms, all fp32
     ss = rows * (16 + 64) * 4 + rows * 2 * 4

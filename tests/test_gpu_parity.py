@@ -210,6 +210,34 @@ def test_small_bf16_decode_ring_wrap():
     assert np.all(st["pos"].cpu().numpy() == L + steps)
 
 
+def test_bf16_ragged_k_slices():
+    """d_model 1024 and out_proj K = 1024 + 3328 = 4352 (17 units of 256): the split-K
+    out_proj (meta rows in prefill, the batch in decode) wants 16 slices of its 16 column
+    tiles, so it runs 9 slices of 2 units with a last slice of 1 unit."""
+    dims = small_dims(d_model=1024, d_inner=3328, window=32)
+    B, L, S, steps = 2, 40, 32, 4
+    w = gen_layer_weights(dims, 85)
+    meta_t, meta, x_t, x = gen_activations(dims, 85, B, L + steps)
+    ref = orc.prefill(dims, w, meta, x[:, :L], contract=True, ring_slots=S)
+    got = gpu_prefill(dims, w, meta_t, x_t[:, :L].contiguous(), ring_slots=S)
+    check_prefill(dims, got, ref, TOL_BF16, TOL_H, ring=True)
+    layer = make_layer(dims, w)
+    to_dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(DEV)
+    kv = {k: to_dev(ref[k], torch.bfloat16) for k in ("k_meta", "v_meta", "k", "v")}
+    st = {"h": to_dev(ref["h"], torch.float32),
+          "pos": torch.full((B,), L, dtype=torch.int32, device=DEV)}
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    xb = x_t.to(DEV)
+    for s in range(steps):
+        y = layer.decode(xb[:, L + s].contiguous(), kv_struct(kv), state_struct(st))
+        o = orc.decode_step(dims, w, x[:, L + s], ref["k_meta"], ref["v_meta"], o["k"], o["v"],
+                            o["h"], o["pos"], contract=True)
+        torch.cuda.synchronize()
+        e = rel_err(to_np(y), o["y"])
+        assert e < TOL_BF16, (s, e)
+    assert rel_err(to_np(st["h"]), o["h"]) < TOL_H
+
+
 @pytest.mark.parametrize("head_dim,n_kv", [(128, 2), (64, 4)])
 def test_bf16_decode_streaming_attention(head_dim, n_kv):
     """Batches whose sequences x kv heads fill the chip (>= 256) take the decode
