@@ -524,8 +524,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16_dl_kernel(GemmOperands g, E
 // ------------------------------------------------------------ bf16 few-row GEMM (decode)
 // Few rows (the decode batch): a workgroup owns a BM x 64 output tile and one K slice
 // (blockIdx.y, a multiple of 256).  NS LDS stages of 64-k tiles, NS - 1 in flight ahead
-// of the one being multiplied, keep the weight stream busy.  The MFMA runs un-swapped,
-// so per accumulator element the 64 lanes cover two rows x 32 consecutive columns.
+// of the one being multiplied, keep the weight stream busy.  The MFMA takes the weight
+// tile as its first operand, so a lane's accumulators hold runs of 4 consecutive
+// columns of one row, which interior tiles turn into 16-byte stores.
 // Epilogues (FewRowMode): fp32 atomics into one accumulator; fp32 partials, slice p of
 // the K split at acc + p * slice_stride, plain stores (a later pass sums the slices:
 // atomics from every slice onto the same addresses serialise in L2); or the decode
@@ -544,6 +545,7 @@ struct FewRowOut {
   const int32_t* pos;
   floatx4* zero;     // store mode: accumulators cleared by the grid (zero_n4 vectors)
   int64_t zero_n4;
+  int vec;           // 16-byte stores allowed (aligned bases and strides)
 };
 
 template <int MODE, int BM, int NS>
@@ -631,8 +633,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          acc[i][j] = mfma32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
-          acc2[i][j] = mfma32x32x16(af[ks + 1][i], bfr[ks + 1][j], acc2[i][j]);
+          if constexpr (MODE == kFewAtomic) {  // D = C: lanes along columns
+            acc[i][j] = mfma32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+            acc2[i][j] = mfma32x32x16(af[ks + 1][i], bfr[ks + 1][j], acc2[i][j]);
+          } else {  // D = C^T: lanes along rows
+            acc[i][j] = mfma32x32x16(bfr[ks][j], af[ks][i], acc[i][j]);
+            acc2[i][j] = mfma32x32x16(bfr[ks + 1][j], af[ks + 1][i], acc2[i][j]);
+          }
         }
   };
 
@@ -675,16 +682,77 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
     __syncthreads();
   }
 
-  // acc[i][j] = D of the 32 x 32 block: element e of lane l is row (e/4)*8 + (l/32)*4 + e%4,
-  // column l % 32.
+  // Store / partial modes: the MFMA runs with B as its first operand, so acc[i][j] holds
+  // C^T of the 32 x 32 block: lane l has row l % 32, columns (e/4)*8 + (l/32)*4 + e%4.
+  // Atomic mode keeps C (lane l has column l % 32, rows (e/4)*8 + (l/32)*4 + e%4): one
+  // atomic instruction then covers two rows x 32 consecutive columns, two cache lines.
+  auto ring_of = [&](int n, int& rel) -> bf16* {  // K / V ring holding column n, if any
+    if (out.k_col < 0) return nullptr;
+    if (n >= out.k_col && n < out.k_col + out.kvw) {
+      rel = n - out.k_col;
+      return out.ring_k;
+    }
+    if (n >= out.v_col && n < out.v_col + out.kvw) {
+      rel = n - out.v_col;
+      return out.ring_v;
+    }
+    return nullptr;
+  };
+  if (MODE != kFewAtomic && out.vec && m0 + BM <= g.M && n0 + BN <= g.N) {
+    // Interior tile: v_permlane32_swap of the column groups 2p and 2p + 1 leaves lane
+    // l < 32 with columns 16p + 0..7 of row l and lane l + 32 with columns 16p + 8..15,
+    // so every lane stores 8 consecutive columns (16 bytes of bf16, two float4 partials).
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          float lo[4], hi[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // (vector elements are copied to scalars first: a bit cast applied to the
+            // subscript itself reads element 0)
+            const float x0 = acc[i][j][8 * pp + r], x1 = acc[i][j][8 * pp + 4 + r];
+            const auto sw = __builtin_amdgcn_permlane32_swap(
+                __builtin_bit_cast(unsigned, x0), __builtin_bit_cast(unsigned, x1), false, false);
+            lo[r] = __builtin_bit_cast(float, (unsigned)sw[0]);
+            hi[r] = __builtin_bit_cast(float, (unsigned)sw[1]);
+          }
+          const int m = m0 + wm * TM + i * 32 + rl;
+          const int n = n0 + wn * TN + j * 32 + pp * 16 + (lane >> 5) * 8;
+          if constexpr (MODE == kFewPartial) {
+            float* dst = out.acc + blockIdx.y * out.slice_stride + (int64_t)m * out.ldacc + n;
+            *(floatx4*)dst = floatx4{lo[0], lo[1], lo[2], lo[3]};
+            *(floatx4*)(dst + 4) = floatx4{hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            bf16x8 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = (bf16)lo[r];
+              v[4 + r] = (bf16)hi[r];
+            }
+            *(bf16x8*)(out.z + (int64_t)m * out.ldz + n) = v;
+            int rel = 0;
+            bf16* ring = ring_of(n, rel);  // the 8 columns share one head (head_dim % 8 == 0)
+            if (ring != nullptr) {
+              const int gh = rel / out.head_dim, d = rel % out.head_dim;
+              *(bf16x8*)(ring + (((int64_t)m * out.Hkv + gh) * out.slots + s_slot[m - m0]) *
+                                    out.head_dim + d) = v;
+            }
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * TN + j * 32 + rl;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * TM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int ec = (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int m = m0 + wm * TM + i * 32 + (MODE == kFewAtomic ? ec : rl);
+        const int n = n0 + wn * TN + j * 32 + (MODE == kFewAtomic ? rl : ec);
         if (m >= g.M || n >= g.N) continue;
         if constexpr (MODE == kFewAtomic) {
           unsafeAtomicAdd(out.acc + (int64_t)m * out.ldacc + n, acc[i][j][e]);
@@ -693,21 +761,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
         } else {
           const bf16 v = (bf16)acc[i][j][e];
           out.z[(int64_t)m * out.ldz + n] = v;
-          if (out.k_col >= 0) {
-            bf16* ring = nullptr;
-            int rel = 0;
-            if (n >= out.k_col && n < out.k_col + out.kvw) {
-              ring = out.ring_k;
-              rel = n - out.k_col;
-            } else if (n >= out.v_col && n < out.v_col + out.kvw) {
-              ring = out.ring_v;
-              rel = n - out.v_col;
-            }
-            if (ring != nullptr) {
-              const int gh = rel / out.head_dim, d = rel % out.head_dim;
-              const int slot = s_slot[m - m0];
-              ring[(((int64_t)m * out.Hkv + gh) * out.slots + slot) * out.head_dim + d] = v;
-            }
+          int rel = 0;
+          bf16* ring = ring_of(n, rel);
+          if (ring != nullptr) {
+            const int gh = rel / out.head_dim, d = rel % out.head_dim;
+            ring[(((int64_t)m * out.Hkv + gh) * out.slots + s_slot[m - m0]) * out.head_dim + d] = v;
           }
         }
       }
@@ -740,6 +798,7 @@ hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t l
   out.acc = acc;
   out.ldacc = ldacc;
   out.slice_stride = slice_stride;
+  out.vec = ((uintptr_t)acc & 15) == 0 && ldacc % 4 == 0 && slice_stride % 4 == 0;
   dim3 grid((op.N + 63) / 64, ns, (op.M + 127) / 128);
   if (slice_stride > 0)
     gemm_bf16_fewrow_kernel<kFewPartial, 128, 4><<<grid, dim3(256), 0, s>>>(op, out, kslice);
@@ -768,6 +827,9 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
   out.head_dim = head_dim;
   out.Hkv = Hkv;
   out.pos = pos;
+  out.vec = ((uintptr_t)z & 15) == 0 && ldz % 8 == 0 &&
+            (k_col < 0 || (((uintptr_t)ring_k & 15) == 0 && ((uintptr_t)ring_v & 15) == 0 &&
+                           head_dim % 8 == 0 && k_col % 8 == 0 && v_col % 8 == 0));
   // 64-row blocks: twice the workgroups of one 128-row block per column tile (the
   // weight slice is then read by two workgroups, mostly from L2)
   dim3 grid((op.N + 63) / 64, 1, (op.M + 63) / 64);
