@@ -32,6 +32,17 @@ first; [HYMBA-SUM] Design formulation):
   F = 0.5 [ beta1 * rms(O) ; beta2 * rms(Y_ssm) ],  rms(v) = v / sqrt(mean(v^2) + eps)
   Y = F W_out^T ;  y = Y[M:], y_meta = Y[:M]
 
+SSM head variant (dims.ssm_heads = H > 0; [HYMBA-ZH] 实现细节, where the layer's SSM head is
+a Mamba-2 head built with a number of heads; its internals are not printed).  Reading:
+the standard Mamba-2 head with one group: the Di channels form H heads of P = Di / H
+channels; x_proj gives [u | B | C] with one u per head, dt = softplus(u + b_dt[h]) is
+shared by the head's channels, A is one negative scalar per head, B and C are shared by
+all heads; D per channel; no convolution or internal norm (the branch norm follows):
+      h_t[c,n] = exp(dt_t[h] A[h]) h_{t-1}[c,n] + dt_t[h] x_t[c] B_t[n],  c in head h
+      y_t[c]   = sum_n C_t[n] h_t[c,n] + D[c] x_t[c]
+It is the selective scan above with dt and A constant across a head's channels and
+states.
+
 Readings where the pages are silent or disagree (each one also listed in the design
 notes): softmax scale 1/sqrt(dh); no positional encoding; causal mask; a window of W
 keys counts the query itself; contiguous GQA groups; no short convolution before the
@@ -61,7 +72,7 @@ __all__ = [
     "bf16_round", "softplus", "silu", "rms_normalize", "in_proj", "split_z",
     "attention", "ssm_params", "selective_scan", "ssm_alpha", "ssm_mixing_form",
     "gate", "fuse", "out_proj", "prefill_sequence", "prefill", "decode_step",
-    "visible",
+    "visible", "ssm2_params", "ssm2_scan", "ssd_matrix_form",
 ]
 
 
@@ -223,6 +234,69 @@ def selective_scan(x, dt, A, B, C, D, h0=None):
     return y, h
 
 
+def ssm2_params(xs, w_x, dt_bias, n_heads: int, d_state: int):
+    """Mamba-2 head: [u | B | C] = Xs W_x^T and dt = softplus(u + b_dt), one dt per
+    head (reading of [HYMBA-ZH] 实现细节, see the module docstring).  Returns dt [T, H],
+    B, C [T, N]."""
+    xbc = np.asarray(xs, np.float64) @ np.asarray(w_x, np.float64).T
+    u = xbc[:, :n_heads]
+    B = xbc[:, n_heads:n_heads + d_state]
+    C = xbc[:, n_heads + d_state:n_heads + 2 * d_state]
+    dt = softplus(u + np.asarray(dt_bias, np.float64)[None, :])
+    return dt, B, C
+
+
+def ssm2_scan(x, dt, A, B, C, D, h0=None):
+    """Mamba-2 head recurrence, one step per token: head h owns channels
+    [h*P, (h+1)*P), P = Di / H, and a P x N state matrix S_h:
+        S_h <- exp(dt_t[h] A[h]) S_h + dt_t[h] x_t[head h] B_t^T
+        y_t[head h] = S_h C_t + D[head h] * x_t[head h]
+    x [T, Di]; dt [T, H]; A [H]; B, C [T, N]; D [Di]; h0 [Di, N] or None (zero).
+    Returns (y [T, Di], h_T [Di, N])."""
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    D = np.asarray(D, np.float64)
+    T, Di = x.shape
+    H = A.shape[0]
+    P = Di // H
+    N = B.shape[1]
+    S = np.zeros((H, P, N)) if h0 is None else np.array(h0, np.float64).reshape(H, P, N)
+    y = np.empty((T, Di))
+    for t in range(T):
+        xt = x[t].reshape(H, P)
+        for h in range(H):
+            S[h] = np.exp(dt[t, h] * A[h]) * S[h] + dt[t, h] * np.outer(xt[h], B[t])
+            y[t, h * P:(h + 1) * P] = S[h] @ C[t]
+        y[t] += D * x[t]
+    return y, S.reshape(Di, N)
+
+
+def ssd_matrix_form(x, dt, A, B, C, D):
+    """The same head as one lower-triangular matrix per head (its "dual" form):
+        y_i[head h] = sum_{j <= i} exp(A[h] sum_{k=j+1..i} dt_k[h]) (C_i . B_j) dt_j[h] x_j
+                      + D x_i.
+    Written from the recurrence unrolled from a zero state; O(T^2) per head."""
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    T, Di = x.shape
+    H = A.shape[0]
+    P = Di // H
+    y = np.asarray(D, np.float64)[None, :] * x
+    for h in range(H):
+        cols = slice(h * P, (h + 1) * P)
+        for i in range(T):
+            for j in range(i + 1):
+                decay = np.exp(A[h] * dt[j + 1:i + 1, h].sum())
+                y[i, cols] += decay * (C[i] @ B[j]) * dt[j, h] * x[j, cols]
+    return y
+
+
 def ssm_alpha(dt, A, B, C):
     """The SSM head's mixing coefficients, straight from [HYMBA-SUM] Design
     formulation: alpha_{i,j}[c] = sum_n C_i[n] (prod_{k=j+1..i} exp(A[c,n] dt_k[c]))
@@ -286,6 +360,19 @@ def _rnd(a, contract):
     return bf16_round(a) if contract else a
 
 
+def _ssm_branch(dims, w, xs, h0, contract):
+    """dt, B, C and the scan for the layer's SSM head type (ssm_heads = 0: Mamba,
+    > 0: Mamba-2 head)."""
+    if getattr(dims, "ssm_heads", 0):
+        dt, B, C = ssm2_params(xs, w.w_x, w.dt_bias, dims.ssm_heads, dims.d_state)
+        y, h = ssm2_scan(xs, dt, w.A, B, C, w.D, h0=h0)
+    else:
+        dt, B, C = ssm_params(xs, w.w_x, w.w_dt, w.dt_bias, dims.dt_rank, dims.d_state,
+                              contract)
+        y, h = selective_scan(xs, dt, w.A, B, C, w.D, h0=h0)
+    return dt, B, C, y, h
+
+
 def prefill_sequence(dims, w, meta, x, kv_src: Optional[Dict[str, np.ndarray]] = None,
                      contract: bool = False, keep: bool = False):
     """One sequence through the layer.  meta [M, d], x [L, d].
@@ -308,9 +395,7 @@ def prefill_sequence(dims, w, meta, x, kv_src: Optional[Dict[str, np.ndarray]] =
     pos = np.arange(T)
     O = attention(parts["Q"], K, V, pos, pos, M, dims.window, dims.scale)
     O = _rnd(O.reshape(T, -1), contract)
-    dt, B, C = ssm_params(parts["Xs"], w.w_x, w.w_dt, w.dt_bias, dims.dt_rank,
-                          dims.d_state, contract)
-    y, h = selective_scan(parts["Xs"], dt, w.A, B, C, w.D)
+    dt, B, C, y, h = _ssm_branch(dims, w, parts["Xs"], None, contract)
     Yssm = _rnd(gate(y, parts["G"]), contract)
     F = _rnd(fuse(O, Yssm, w.beta_attn, w.beta_ssm, dims.rms_eps), contract)
     Y = out_proj(F, w.w_out)
@@ -393,9 +478,7 @@ def decode_step(dims, w, x_new, k_meta, v_meta, k_ring, v_ring, h, pos,
         kpos = np.concatenate([np.arange(M), M + ring_pos])
         O = attention(parts["Q"], K, V, np.array([M + p]), kpos, M, dims.window, dims.scale)
         O = _rnd(O.reshape(1, -1), contract)
-        dt, Bm, Cm = ssm_params(parts["Xs"], w.w_x, w.w_dt, w.dt_bias, dims.dt_rank,
-                                dims.d_state, contract)
-        ys, h[b] = selective_scan(parts["Xs"], dt, w.A, Bm, Cm, w.D, h0=h[b])
+        _, _, _, ys, h[b] = _ssm_branch(dims, w, parts["Xs"], h[b], contract)
         Yssm = _rnd(gate(ys, parts["G"]), contract)
         F = _rnd(fuse(O, Yssm, w.beta_attn, w.beta_ssm, dims.rms_eps), contract)
         y[b] = out_proj(F, w.w_out)[0]

@@ -40,6 +40,8 @@ class LayerDims:
     dtype: str = BF16
     rms_eps: float = 1e-6
     softmax_scale: float = 0.0  # 0 => 1/sqrt(head_dim)
+    ssm_heads: int = 0          # 0 = Mamba head (per-channel A, dt of rank dt_rank);
+                                # H > 0 = Mamba-2 head: H heads, scalar A and dt per head
 
     @property
     def q_width(self) -> int:
@@ -56,7 +58,7 @@ class LayerDims:
 
     @property
     def n_xproj(self) -> int:
-        return self.dt_rank + 2 * self.d_state
+        return (self.ssm_heads or self.dt_rank) + 2 * self.d_state
 
     @property
     def f_width(self) -> int:
@@ -129,10 +131,10 @@ class LayerWeights:
     """Weights of one layer.  `np_*` are float32 arrays holding exactly the values
     the device sees; `t_*` are the torch CPU tensors in storage dtype (or fp32)."""
     w_in: np.ndarray      # [n_in, d]
-    w_x: np.ndarray       # [R + 2N, Di]
-    w_dt: np.ndarray      # [Di, R]
-    dt_bias: np.ndarray   # [Di] fp32
-    A: np.ndarray         # [Di, N] fp32
+    w_x: np.ndarray       # [R + 2N, Di]  (Mamba-2 head: [H + 2N, Di])
+    w_dt: np.ndarray      # [Di, R]       (Mamba-2 head: empty, [Di, 0])
+    dt_bias: np.ndarray   # [Di] fp32     (Mamba-2 head: [H])
+    A: np.ndarray         # [Di, N] fp32  (Mamba-2 head: [H])
     D: np.ndarray         # [Di] fp32
     w_out: np.ndarray     # [d, Hq*dh + Di]
     beta_attn: np.ndarray  # [Hq*dh] fp32
@@ -145,10 +147,17 @@ def gen_layer_weights(dims: LayerDims, case_id: int, layer: int = 0,
     g = rng(case_id, 10 + layer)
     d, Di, N, R = dims.d_model, dims.d_inner, dims.d_state, dims.dt_rank
     w_in = _normal(g, (dims.n_in, d), std)
-    w_x = _normal(g, (R + 2 * N, Di), std)
-    w_dt = _normal(g, (Di, R), std)
-    dt_bias = g.uniform(-4.0, -2.0, size=(Di,)).astype(np.float32)
-    A = (-np.exp(g.uniform(0.0, 2.0, size=(Di, N)))).astype(np.float32)
+    if dims.ssm_heads:  # Mamba-2 head: one dt and one A per head, no dt projection
+        H = dims.ssm_heads
+        w_x = _normal(g, (H + 2 * N, Di), std)
+        w_dt = np.zeros((Di, 0), np.float32)
+        dt_bias = g.uniform(-4.0, -2.0, size=(H,)).astype(np.float32)
+        A = (-np.exp(g.uniform(0.0, 2.0, size=(H,)))).astype(np.float32)
+    else:
+        w_x = _normal(g, (R + 2 * N, Di), std)
+        w_dt = _normal(g, (Di, R), std)
+        dt_bias = g.uniform(-4.0, -2.0, size=(Di,)).astype(np.float32)
+        A = (-np.exp(g.uniform(0.0, 2.0, size=(Di, N)))).astype(np.float32)
     D = g.standard_normal(size=(Di,)).astype(np.float32)
     w_out = _normal(g, (d, dims.f_width), std)
     beta_attn = np.ones(dims.q_width, np.float32)
