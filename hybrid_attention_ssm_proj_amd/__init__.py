@@ -44,14 +44,15 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_q_heads", "n_kv_heads", "head_dim", "d_inner", "d_state", "dt_rank",
         "n_meta", "window", "kv_share", "dtype")] + [
-        ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+        ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("ssm_heads", ctypes.c_int32)]
 
     @classmethod
     def from_dims(cls, dims) -> "LayerDesc":
         return cls(dims.d_model, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.d_inner,
                    dims.d_state, dims.dt_rank, dims.n_meta, dims.window, dims.kv_share,
                    DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, dims.rms_eps,
-                   dims.softmax_scale)
+                   dims.softmax_scale, getattr(dims, "ssm_heads", 0))
 
 
 class LayerWeights(ctypes.Structure):
@@ -283,7 +284,9 @@ class HymbaLayer:
         self.dims = dims
         self.desc = LayerDesc.from_dims(dims)
         self.w = {k: v.to(device).contiguous() for k, v in w.items()}
-        self.weights = LayerWeights(*[self.w[n].data_ptr() for n, _ in LayerWeights._fields_])
+        # an empty tensor (w_dt of a Mamba-2 head layer) is passed as NULL
+        self.weights = LayerWeights(*[self.w[n].data_ptr() if self.w[n].numel() else None
+                                      for n, _ in LayerWeights._fields_])
         self.device = device
         self.store = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
         self._ws = None

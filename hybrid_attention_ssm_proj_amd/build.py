@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhymba.so")
-SOURCES = ["gemm.hip", "attention.hip", "scan.hip", "scan_fused.hip", "misc.hip", "hymba.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "scan.hip", "scan_fused.hip", "scan_ssd.hip", "misc.hip", "hymba.cpp"]
 ARCH = "gfx950"
 
 

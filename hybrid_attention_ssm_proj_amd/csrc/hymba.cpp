@@ -78,6 +78,8 @@ struct TimerScope {
 // ----------------------------------------------------------------- shapes
 struct Shape {
   int d, Hq, Hkv, dh, Di, N, R, M, W, share, es;
+  int H2;  // Mamba-2 heads (0: Mamba head with per-channel A and a rank-R dt projection)
+  int nx;  // x_proj output width: (H2 ? H2 : R) + 2N
   bool bf16;
   int64_t qw, kvw, n_in, fw, xs_col, g_col, k_col, v_col;
   float scale;
@@ -92,8 +94,10 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
   if (desc == nullptr) return HYMBA_ERR_INVALID_ARG;
   const hymba_layer_desc& d = *desc;
   if (d.d_model <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 ||
-      d.d_inner <= 0 || d.d_state <= 0 || d.dt_rank <= 0 || d.n_meta < 0 || d.window < 0)
+      d.d_inner <= 0 || d.d_state <= 0 || d.n_meta < 0 || d.window < 0 || d.ssm_heads < 0)
     return HYMBA_ERR_INVALID_ARG;
+  const bool head_ssm = d.ssm_heads > 0;
+  if (!head_ssm && d.dt_rank <= 0) return HYMBA_ERR_INVALID_ARG;
   if (d.kv_share != 0 && d.kv_share != 1) return HYMBA_ERR_INVALID_ARG;
   if (d.dtype != HYMBA_DTYPE_F32 && d.dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
   if (!(d.rms_eps >= 0.f) || !std::isfinite(d.rms_eps)) return HYMBA_ERR_INVALID_ARG;
@@ -101,21 +105,26 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
   if (d.n_q_heads % d.n_kv_heads != 0) return HYMBA_ERR_INVALID_ARG;
   const bool bf16 = d.dtype == HYMBA_DTYPE_BF16;
   // kernels: 16-byte row chunks, 4-column epilogue groups, <= 16 q heads per kv head
-  if (d.d_model % 8 || d.d_inner % 8 || d.dt_rank % 8 || d.head_dim % 8)
+  if (d.d_model % 8 || d.d_inner % 8 || d.head_dim % 8 || (!head_ssm && d.dt_rank % 8))
+    return HYMBA_ERR_UNSUPPORTED;
+  // Mamba-2 heads: bf16, heads of 64 channels, a multiple of 4 heads, N in {16..128}
+  if (head_ssm && (!bf16 || !scan_ssd_supported(d.d_state, d.d_inner, d.ssm_heads)))
     return HYMBA_ERR_UNSUPPORTED;
   const int grp = d.n_q_heads / d.n_kv_heads;
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return HYMBA_ERR_UNSUPPORTED;
   if (bf16 ? (d.head_dim != 64 && d.head_dim != 128) : (d.head_dim != 32 && d.head_dim != 64))
     return HYMBA_ERR_UNSUPPORTED;
   if (!is_pow2_in(d.d_state, 4, 128)) return HYMBA_ERR_UNSUPPORTED;
-  if (d.dt_rank > 512) return HYMBA_ERR_UNSUPPORTED;
+  if (!head_ssm && d.dt_rank > 512) return HYMBA_ERR_UNSUPPORTED;
   s.d = d.d_model;
   s.Hq = d.n_q_heads;
   s.Hkv = d.n_kv_heads;
   s.dh = d.head_dim;
   s.Di = d.d_inner;
   s.N = d.d_state;
-  s.R = d.dt_rank;
+  s.R = head_ssm ? 0 : d.dt_rank;
+  s.H2 = head_ssm ? d.ssm_heads : 0;
+  s.nx = (head_ssm ? d.ssm_heads : d.dt_rank) + 2 * d.d_state;
   s.M = d.n_meta;
   s.W = d.window;
   s.share = d.kv_share;
@@ -155,7 +164,9 @@ int decode_nsplit(const Shape& s, int span_max) {
   return (s.M + span_max + k - 1) / k;
 }
 
-bool fused_dt(const Shape& s) { return s.bf16 && scan_fused_supported(s.N, s.R, s.Di); }
+bool fused_dt(const Shape& s) {
+  return s.H2 == 0 && s.bf16 && scan_fused_supported(s.N, s.R, s.Di);
+}
 
 // Prefill: rows = meta rows + batch * tokens.  dt is materialised only when the scan
 // does not compute it in place.
@@ -182,12 +193,12 @@ Carve carve_prefill(const Shape& s, int64_t rows, int B, int L, bool cached = fa
   size_t off = 0;
   c.z = off;
   off = align_up(off + (size_t)rows * s.n_in * s.es);
-  c.delta = off;
+  c.delta = off;  // Mamba head: delta [rows, R]; Mamba-2 heads: none
   off = align_up(off + (size_t)rows * s.R * s.es);
-  c.bc = off;
-  off = align_up(off + (size_t)rows * 2 * s.N * 4);
+  c.bc = off;     // [rows, 2N] fp32 (B | C); Mamba-2 heads: [rows, H2 + 2N] (u | B | C)
+  off = align_up(off + (size_t)rows * (s.H2 + 2 * s.N) * 4);
   c.dt = off;
-  if (!fused_dt(s)) off = align_up(off + (size_t)rows * s.Di * 4);
+  if (s.H2 == 0 && !fused_dt(s)) off = align_up(off + (size_t)rows * s.Di * 4);
   c.f = off;
   off = align_up(off + (size_t)rows * s.fw * s.es);
   c.vt = off;  // bf16 attention: V^T staging
@@ -215,7 +226,7 @@ Carve carve_decode(const Shape& s, int batch, int nsplit) {
   c.part = off;
   off = align_up(off + (size_t)batch * s.Hq * nsplit * (s.dh + 4) * 4);
   c.xdbl = off;
-  off = align_up(off + (size_t)batch * (s.R + 2 * s.N) * 4);
+  off = align_up(off + (size_t)batch * s.nx * 4);
   c.yacc = off;  // out_proj partials, one [batch, d] fp32 block per K slice
   off = align_up(off + (size_t)(decode_splitk(s) ? out_proj_slices(s, batch) : 1) * batch * s.d * 4);
   c.total = off;
@@ -229,9 +240,9 @@ bool any_misaligned(P... ptrs) {
   return (misaligned((const void*)ptrs) || ...);
 }
 
-hymba_status check_weights(const hymba_layer_weights* w) {
-  if (w == nullptr || !w->w_in || !w->w_x || !w->w_dt || !w->w_out || !w->dt_bias || !w->A ||
-      !w->D || !w->beta_attn || !w->beta_ssm)
+hymba_status check_weights(const hymba_layer_weights* w, const Shape& s) {
+  if (w == nullptr || !w->w_in || !w->w_x || (s.H2 == 0 && !w->w_dt) || !w->w_out ||
+      !w->dt_bias || !w->A || !w->D || !w->beta_attn || !w->beta_ssm)
     return HYMBA_ERR_INVALID_ARG;
   if (any_misaligned(w->w_in, w->w_x, w->w_dt, w->w_out, w->dt_bias, w->A, w->D, w->beta_attn,
                      w->beta_ssm))
@@ -323,7 +334,7 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
   Shape s;
   hymba_status st = make_shape(desc, s);
   if (st != HYMBA_OK) return st;
-  if ((st = check_weights(w)) != HYMBA_OK) return st;
+  if ((st = check_weights(w, s)) != HYMBA_OK) return st;
   if (batch < 0 || seq_len < 0) return HYMBA_ERR_INVALID_ARG;
   const bool cached = cache != nullptr;
   const int B = batch, L = seq_len, M = s.M, Mr = cached ? 0 : s.M;
@@ -476,16 +487,18 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
                  b16 ? launch_attention_prefill_bf16_dl(ap, ws_ptr(workspace, cv.vt), stream)
                      : launch_attention_prefill_f32(ap, stream));
   }
-  // 4. x_proj: [delta | B | C] = Xs W_x^T.
+  // 4. x_proj: [delta | B | C] = Xs W_x^T (Mamba-2 heads: [u | B | C], all fp32).
   {
     GemmOperands op{z + s.xs_col * s.es, s.n_in, nullptr, 0, (int)rows, w->w_x, s.Di, (int)rows,
-                    s.R + 2 * s.N, s.Di};
-    GemmOutput out{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
+                    s.nx, s.Di};
+    GemmOutput out = s.H2 ? GemmOutput{EpiKind::StoreF32, bc, s.nx, nullptr, 0, 0, 0, nullptr}
+                          : GemmOutput{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
     HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out, GemmShape::Narrow));
   }
-  // 5. dt_proj + softplus (unless the scan computes it in place).
+  // 5. dt_proj + softplus (unless the scan computes it in place, or the heads take dt
+  // straight from x_proj).
   const bool fuse = fused_dt(s);
-  if (!fuse) {
+  if (!fuse && s.H2 == 0) {
     GemmOperands op{delta, s.R, nullptr, 0, (int)rows, w->w_dt, s.R, (int)rows, s.Di, s.R};
     GemmOutput out{EpiKind::Softplus, dt, s.Di, nullptr, 0, 0, 0, w->dt_bias};
     HYMBA_LAUNCH(HYMBA_STAGE_DTPROJ, gemm(op, out, GemmShape::Narrow));
@@ -518,7 +531,28 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
       sp.B = 1;
       sp.h_out = h_meta_out;
     }
-    if (fuse) {
+    if (s.H2) {
+      SsdParams qp{};
+      qp.z = z;
+      qp.z_stride = s.n_in;
+      qp.xs_col = (int)s.xs_col;
+      qp.g_col = (int)s.g_col;
+      qp.xbc = bc;
+      qp.xbc_ld = s.nx;
+      qp.dt_bias = w->dt_bias;
+      qp.A = w->A;
+      qp.D = w->D;
+      qp.h0 = sp.h0;
+      qp.y = sp.y;
+      qp.y_stride = sp.y_stride;
+      qp.h_out = sp.h_out;
+      qp.n_meta = Mr;
+      qp.L = L;
+      qp.B = sp.B;
+      qp.H = s.H2;
+      qp.N = s.N;
+      HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_ssd(qp, stream));
+    } else if (fuse) {
       HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill_fused(sp, delta, w->w_dt, w->dt_bias,
                                                                s.R, stream));
     } else {
@@ -627,7 +661,7 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   Shape s;
   hymba_status st = make_shape(desc, s);
   if (st != HYMBA_OK) return st;
-  if ((st = check_weights(w)) != HYMBA_OK) return st;
+  if ((st = check_weights(w, s)) != HYMBA_OK) return st;
   if (batch < 0) return HYMBA_ERR_INVALID_ARG;
   const int B = batch, M = s.M;
   if (kv == nullptr || state == nullptr) return HYMBA_ERR_INVALID_ARG;
@@ -651,7 +685,7 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   float* xdbl = (float*)ws_ptr(workspace, cv.xdbl);
   float* yacc = (float*)ws_ptr(workspace, cv.yacc);
   const bool b16 = s.bf16;
-  const int nx = s.R + 2 * s.N;
+  const int nx = s.nx;
   // Attention (bf16): one workgroup per (sequence, kv head) streaming all keys once the
   // pairs fill the chip (256 CUs), else key splits merged by the combine kernel.
   const bool stream_attn = b16 && (int64_t)B * s.Hkv >= 256 && kv->slots >= 64;
@@ -740,7 +774,9 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     sp.Di = s.Di;
     sp.N = s.N;
     sp.R = s.R;
-    HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_ssm_step(b16, sp, stream));
+    sp.heads = s.H2;
+    HYMBA_LAUNCH(HYMBA_STAGE_SCAN,
+                 s.H2 ? launch_ssm2_step(sp, stream) : launch_ssm_step(b16, sp, stream));
   }
   if (stream_attn) {
     HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, B, (int)s.qw, s.Di,

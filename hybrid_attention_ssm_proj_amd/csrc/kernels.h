@@ -163,6 +163,28 @@ int scan_channel_blocks(int N, int Di);
 hipError_t launch_scan_prefill_fused(const ScanParams& p, const void* delta, const void* w_dt,
                                      const float* dt_bias, int R, hipStream_t s);
 
+// Mamba-2 SSM head (heads of 64 channels, one dt and one A per head, B and C shared),
+// bf16 prefill in the chunked matrix form.  xbc [rows, H + 2N] fp32 holds u | B | C per
+// row (dt = softplus(u + dt_bias[h])); rows as for ScanParams (the meta prefix then the
+// sequence's own rows); y is the gated output; h0 / h_out as for ScanParams.
+struct SsdParams {
+  const void* z;
+  int64_t z_stride;
+  int xs_col, g_col;
+  const float* xbc;
+  int64_t xbc_ld;
+  const float* dt_bias;  // [H]
+  const float* A;        // [H]
+  const float* D;        // [Di]
+  const float* h0;       // [Di, N] or nullptr
+  void* y;
+  int64_t y_stride;
+  float* h_out;          // [B, Di, N] or nullptr
+  int n_meta, L, B, H, N;
+};
+bool scan_ssd_supported(int N, int Di, int H);
+hipError_t launch_scan_ssd(const SsdParams& p, hipStream_t s);
+
 // Decode: one step per sequence, h updated in place, pos[b] += 1 when pos != nullptr.
 // dt is computed in place from the x_proj output: dt = softplus(delta W_dt^T + b) with
 // delta = xdbl[b, :R] (rounded to bf16 first when round_delta), B = xdbl[b, R:R+N],
@@ -181,8 +203,10 @@ struct SsmStepParams {
   int64_t y_stride;
   int32_t* pos;
   int B, Di, N, R;
+  int heads;            // > 0: Mamba-2 head; xdbl rows are [u (heads) | B | C], no w_dt
 };
 hipError_t launch_ssm_step(bool bf16, const SsmStepParams& p, hipStream_t s);
+hipError_t launch_ssm2_step(const SsmStepParams& p, hipStream_t s);  // bf16, heads > 0
 
 // ----------------------------------------------------------------- fusion
 // F[r, :] = 0.5 * [beta_a * rms(F[r, :wa]) ; beta_s * rms(F[r, wa:wa+ws])], in place.

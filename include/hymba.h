@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HYMBA_ABI_VERSION 1
+#define HYMBA_ABI_VERSION 2
 
 typedef enum {
   HYMBA_DTYPE_F32 = 0,
@@ -69,7 +69,15 @@ typedef enum {
 
 /* Layer shape.  Supported: head_dim 64 or 128 (bf16) / 32 or 64 (fp32); d_state a power
  * of two from 4 to 128; n_q_heads / n_kv_heads in {1, 2, 4, 8}; d_model, d_inner,
- * dt_rank and head_dim multiples of 8; dt_rank <= 512. */
+ * dt_rank and head_dim multiples of 8; dt_rank <= 512.
+ *
+ * SSM head type.  ssm_heads = 0: the Mamba head of the Hymba summary's design
+ * formulation (per-channel A [Di, N], dt = softplus(delta W_dt^T + b) with delta of rank
+ * dt_rank).  ssm_heads = H > 0: the Mamba-2 head of the Chinese summary's implementation
+ * pseudocode ("实现细节"), read as one group: H heads of P = Di / H channels, one
+ * dt = softplus(u + b[h]) and one A[h] per head, B and C shared, D per channel; x_proj
+ * gives [u | B | C] (H + 2N rows of w_x), there is no w_dt and dt_rank is ignored.
+ * Supported for bf16 with P = 64, H a multiple of 4 and d_state in {16, 32, 64, 128}. */
 typedef struct {
   int32_t d_model;      /* d                                                      */
   int32_t n_q_heads;    /* Hq                                                     */
@@ -86,17 +94,19 @@ typedef struct {
   int32_t dtype;        /* hymba_dtype                                            */
   float rms_eps;        /* RMSNorm epsilon, e.g. 1e-6                             */
   float softmax_scale;  /* 0 => 1/sqrt(head_dim)                                  */
+  int32_t ssm_heads;    /* 0 = Mamba head; H > 0 = Mamba-2 head with H heads      */
 } hymba_layer_desc;
 
 /* Weights (device).  n_in = Hq*dh + (kv_share ? 0 : 2*Hkv*dh) + 2*Di; column
  * blocks of w_in's output in that order: Q, K, V, Xs, G. */
 typedef struct {
   const void *w_in;       /* [n_in, d]            dtype                          */
-  const void *w_x;        /* [R + 2N, Di]         dtype  (rows: delta, B, C)     */
-  const void *w_dt;       /* [Di, R]              dtype                          */
+  const void *w_x;        /* [R + 2N, Di]         dtype  (rows: delta, B, C)
+                             Mamba-2 heads: [H + 2N, Di] (rows: u, B, C)        */
+  const void *w_dt;       /* [Di, R]              dtype  (Mamba-2 heads: NULL)   */
   const void *w_out;      /* [d, Hq*dh + Di]      dtype                          */
-  const float *dt_bias;   /* [Di]                                                */
-  const float *A;         /* [Di, N]                                             */
+  const float *dt_bias;   /* [Di]                        (Mamba-2 heads: [H])    */
+  const float *A;         /* [Di, N]                     (Mamba-2 heads: [H])    */
   const float *D;         /* [Di]                                                */
   const float *beta_attn; /* [Hq*dh]                                             */
   const float *beta_ssm;  /* [Di]                                                */

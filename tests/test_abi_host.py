@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert hy.hymba_abi_version() == 1
+    assert hy.hymba_abi_version() == 2
     assert hy.hymba_status_str(0) == "ok"
     assert hy.hymba_status_str(3).startswith("workspace")
 
@@ -87,12 +87,38 @@ def _weights_struct(addr=4096):
     (dict(window=-1), 1),
     (dict(kv_share=2), 1),
     (dict(rms_eps=float("nan")), 1),
+    (dict(ssm_heads=-1), 1),
+    (dict(ssm_heads=32), 2),          # Mamba-2 heads of 128 channels: no kernel
+    (dict(ssm_heads=62), 2),          # 4096 / 62 is not a whole head
+    (dict(ssm_heads=64, d_state=8), 2),
+    (dict(ssm_heads=64, dtype="f32"), 2),
+    (dict(dt_rank=0), 1),             # the Mamba head needs a dt rank
 ])
 def test_prefill_rejects_bad_descriptors(lib, change, status):
     d = desc_of(1, **change)
     st = hy.hymba_layer_prefill(d, _weights_struct(), 4096, 8192, 1, 4, None, None, None, 12288,
                                 None, 1 << 20, 1 << 40, stream=0, check=False)
     assert st == status
+
+
+def test_head_ssm_layer_shapes(lib):
+    """Mamba-2 heads: dt_rank is ignored, x_proj writes [u | B | C] in fp32 (no delta, no
+    dt buffer), w_dt may be NULL, and there is no deferred norm."""
+    d = desc_of(1, ssm_heads=64, dt_rank=0)
+    rows = 128 + 8 * 2048
+    n_in = 16 * 128 + 2 * 4 * 128 + 2 * 4096
+    vt = 8 * 4 * 128 * ((128 + 2048 + 63) // 64 * 64) * 2
+    macc = 8 * 128 * 2048 * 4
+    floor = rows * (n_in * 2 + (64 + 32) * 4 + 6144 * 2) + vt + macc
+    got = hy.hymba_layer_workspace_bytes(d, 8, 2048, 0)
+    assert floor <= got <= floor + 8 * 256
+    # a NULL w_dt passes the weight checks (the too-small workspace then stops the call
+    # before any launch); the Mamba head rejects it
+    w = hy.LayerWeights(4096, 4096, None, *([4096] * 6))
+    assert hy.hymba_layer_prefill(d, w, 4096, 8192, 1, 4, None, None, None, 12288, None,
+                                  1 << 20, 1000, stream=0, check=False) == 3
+    assert hy.hymba_layer_prefill(desc_of(1), w, 4096, 8192, 1, 4, None, None, None, 12288,
+                                  None, 1 << 20, 1000, stream=0, check=False) == 1
 
 
 def test_prefill_argument_errors(lib):
