@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 16-layer partial-SWA vs all-global stack comparison")
+    ap.add_argument("--no-head-ssm", action="store_true",
+                    help="skip the Mamba-2 head variant of the layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the prefill workload the CPU oracle runs (8 = all)")
@@ -300,6 +302,10 @@ def main():
     if not args.no_stack:
         stack = bench_stack(hy, torch, dev)
 
+    head_ssm = None
+    if not args.no_head_ssm:
+        head_ssm = bench_head_ssm(hy, torch, dev, args, stages)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
@@ -318,9 +324,73 @@ def main():
         "decode": decode,
         "prefill_meta_cached": cached,
         "stack": stack,
+        "head_ssm": head_ssm,
         "stages": stage_report,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_head_ssm(hy, torch, dev, args, mamba_stages):
+    """The same prefill and decode workloads with the Mamba-2 SSM head (64 heads of 64
+    channels, scalar A and dt per head): the scan runs in the chunked matrix form on MFMA.
+    Reports step times, the scan's time against the Mamba head's, and the scan's HBM
+    roofline (it reads x, G and [u | B | C] per token of every sequence, the meta prefix
+    included, and writes y once per row and the final state)."""
+    from synth import CASES, gen_layer_weights
+    case = CASES[1]
+    dims = case.dims.replace(ssm_heads=64, dt_rank=0)
+    B, L, M = case.batch, case.seq_len, dims.n_meta
+    log(f"[bench] head-SSM variant: ssm_heads={dims.ssm_heads}, prefill B={B} L={L}")
+    w = gen_layer_weights(dims, case.case_id)
+    layer = hy.HymbaLayer(dims, w.torch, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1005)
+    meta = torch.randn(M, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    x = torch.randn(B, L, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    y = torch.empty(B, L, dims.d_model, dtype=torch.bfloat16, device=dev)
+    y_meta = torch.empty(M, dims.d_model, dtype=torch.bfloat16, device=dev)
+    h = torch.empty(B, dims.d_inner, dims.d_state, dtype=torch.float32, device=dev)
+    pos = torch.empty(B, dtype=torch.int32, device=dev)
+    state = hy.make_state(h, pos)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.prefill(meta, x, state_out=state, y=y, y_meta=y_meta, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    stages = stage_pass(hy, torch, step, max(3, args.steps // 2), -1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    T, Di, N, H = M + L, dims.d_inner, dims.d_state, dims.ssm_heads
+    scan_bytes = B * T * (2 * Di * 2 + (H + 2 * N) * 4) + (M + B * L) * Di * 2 + B * Di * N * 4
+    scan_ms = stages["scan"]["avg_ms"]
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    del layer
+    torch.cuda.empty_cache()
+    dec = None if args.no_decode else bench_decode(hy, torch, dev, args, dims=CASES[4].dims.replace(
+        ssm_heads=64, dt_rank=0))
+    out = {"workload": f"the prefill workload with the Mamba-2 SSM head: {H} heads of "
+                       f"{Di // H} channels, one dt and A per head, N={N}",
+           "prefill_ms": round(ms, 4), "prefill_tokens_per_s": round(B * L / ms * 1e3, 1),
+           "scan_ms": round(scan_ms, 4),
+           "mamba_head_scan_ms": round(mamba_stages["scan"]["avg_ms"], 4),
+           "scan_roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(achieved / PEAK_HBM_GBS, 4),
+                             "bytes_per_launch": scan_bytes},
+           "stages_ms": {k: round(v["avg_ms"], 4) for k, v in stages.items()}}
+    if dec is not None:
+        out["decode_us_per_step"] = dec["us_per_step"]
+        out["decode_tokens_per_s"] = dec["value"]
+    log(f"[bench] head-SSM variant: prefill {ms:.3f} ms ({B * L / ms / 1e3:.3f} M tok/s), "
+        f"scan {scan_ms:.3f} ms (Mamba head {mamba_stages['scan']['avg_ms']:.3f} ms), "
+        f"{achieved:.0f} GB/s" + (f"; decode {dec['us_per_step']} us/step" if dec else ""))
+    return out
 
 
 def device_weights(torch, dims, seed, dev):
@@ -388,12 +458,13 @@ def bench_stack(hy, torch, dev, n_layers=16, B=1, L=8192, W=1024, dsteps=16, ste
     return res
 
 
-def bench_decode(hy, torch, dev, args):
+def bench_decode(hy, torch, dev, args, dims=None):
     from synth import CASES, gen_layer_weights
     case = CASES[4]
-    dims = case.dims
+    dims = dims or case.dims
     B, S, prior = case.batch, case.ring_slots, case.prior_tokens
-    log(f"[bench] decode workload {case.name}: B={B} ring={S} prior={prior}")
+    log(f"[bench] decode workload {case.name}: B={B} ring={S} prior={prior}"
+        f"{' ssm_heads=%d' % dims.ssm_heads if dims.ssm_heads else ''}")
     w = gen_layer_weights(dims, case.case_id)
     layer = hy.HymbaLayer(dims, w.torch, device=dev)
     gen = torch.Generator(device=dev)

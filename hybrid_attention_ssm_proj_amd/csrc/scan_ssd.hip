@@ -16,8 +16,8 @@
 //         into a bf16 high part and a bf16 low part so the carried state keeps about
 //         16 significant bits;
 // and the state stays in fp32 accumulators from chunk to chunk.  A workgroup owns one
-// (sequence, head) and walks its chunks in order; the next chunk's operands are
-// loaded into registers while the current one is multiplied.  Every sequence replays
+// (sequence, head) and walks its chunks in order; the operands of the next one or two
+// chunks are in flight to registers while the current one is multiplied.  Every sequence replays
 // the batch-shared meta prefix; only sequence 0 stores the meta rows.
 #include "common.h"
 #include "kernels.h"
@@ -43,27 +43,27 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
 
 template <int N>
 struct SsdCfg {
-  static constexpr int CP = N + 8;                       // row pitch (bf16) of C, B, S
-  static constexpr int NB = N / 16;                      // 16-column state blocks
-  static constexpr int BC_PER_T = N / 4;                 // float4 per token for B (or C)
-  static constexpr int BC_LOADS = kQ * BC_PER_T / 256;   // per thread
-  static_assert(BC_LOADS >= 1 && (kQ * BC_PER_T) % 256 == 0, "B/C staging");
+  static constexpr int CP = N + 8;         // row pitch (bf16) of C, B, S
+  static constexpr int NB = N / 16;        // 16-column state blocks
+  static constexpr int BC_LOADS = N / 16;  // float4 groups of B (and of C) per thread
 };
 
 }  // namespace
 
-template <int N>
+template <int N, int PD>
 __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
   using Cfg = SsdCfg<N>;
-  constexpr int CP = Cfg::CP, NB = Cfg::NB, BCL = Cfg::BC_LOADS, BPT = Cfg::BC_PER_T;
+  constexpr int CP = Cfg::CP, NB = Cfg::NB, BCL = Cfg::BC_LOADS;
   __shared__ __attribute__((aligned(16))) bf16 c_s[kQ * CP];    // C [i][n]
   __shared__ __attribute__((aligned(16))) bf16 b_s[kQ * CP];    // B [j][n]
   __shared__ __attribute__((aligned(16))) bf16 xt_s[kP * kXP];  // X^T [p][j]
+  __shared__ __attribute__((aligned(16))) bf16 gt_s[kP * kXP];  // G^T [p][i]
   __shared__ __attribute__((aligned(16))) bf16 m_s[kQ * kXP];   // M [i][j]
+  __shared__ __attribute__((aligned(16))) bf16 y_s[kQ * kXP];   // gated output [i][p]
   __shared__ __attribute__((aligned(16))) bf16 wh_s[N * kXP];   // (w B)^T [n][j], high
   __shared__ __attribute__((aligned(16))) bf16 wl_s[N * kXP];   // low part
   __shared__ __attribute__((aligned(16))) bf16 s_s[kP * CP];    // S_prev [p][n]
-  __shared__ float cs_s[kQ], dt_s[kQ], ecs_s[kQ];
+  __shared__ __attribute__((aligned(16))) float cs_s[kQ], dt_s[kQ], ecs_s[kQ];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -72,53 +72,33 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
   const int c0 = hd * kP;
   const float A = p.A[hd], bias = p.dt_bias[hd];
   const bf16* z = (const bf16*)p.z;
+  const int64_t seq_off = (int64_t)b * p.L;  // row(t) = t, or t + b L past the meta prefix
 
-  // ---- operand registers of one chunk (filled one chunk ahead)
-  float u_r = 0.f;
-  floatx4 b_r[BCL], c_r[BCL];
-  bf16x8 x_r[2];
-  auto fetch = [&](int t0) {
-    if (tid < kQ) {
-      const int t = t0 + tid;
-      u_r = t < T ? p.xbc[ssd_row(t, b, p.n_meta, p.L) * p.xbc_ld + hd] : 0.f;
-    }
+  // Every global access of a chunk is made by the thread whose lane is the token: lane j
+  // moves token t0 + j's u (wave 0), B and C (4-float groups wave + 4r), x and G (8-channel
+  // groups wave + 4r), and its y row.  Tokens past the end read the last token's row
+  // (no load waits at its issue) and are zeroed where the values are used.
+  auto row_of = [&](int t) { return (int64_t)t + (t >= p.n_meta ? seq_off : 0); };
+  struct Ops {
+    float u;
+    floatx4 b[BCL], c[BCL];
+    bf16x8 x[2], g[2];
+  };
+  auto fetch = [&](Ops& o, int t0) {
+    const int64_t row = row_of(min(t0 + lane, T - 1));
+    const float* xr = p.xbc + row * p.xbc_ld;
+    if (wave == 0) o.u = xr[hd];
 #pragma unroll
     for (int r = 0; r < BCL; ++r) {
-      const int idx = tid + 256 * r, j = idx / BPT, n4 = (idx % BPT) * 4, t = t0 + j;
-      if (t < T) {
-        const float* base = p.xbc + ssd_row(t, b, p.n_meta, p.L) * p.xbc_ld + p.H + n4;
-        b_r[r] = *(const floatx4*)base;
-        c_r[r] = *(const floatx4*)(base + N);
-      } else {
-        b_r[r] = floatx4{0.f, 0.f, 0.f, 0.f};
-        c_r[r] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
+      const float* base = xr + p.H + (wave + 4 * r) * 4;
+      o.b[r] = *(const floatx4*)base;
+      o.c[r] = *(const floatx4*)(base + N);
     }
+    const bf16* zr = z + row * p.z_stride + c0;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int idx = tid + 256 * r, j = idx >> 3, p8 = (idx & 7) * 8, t = t0 + j;
-      if (t < T) {
-        x_r[r] = *(const bf16x8*)(z + ssd_row(t, b, p.n_meta, p.L) * p.z_stride + p.xs_col +
-                                  c0 + p8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x_r[r][e] = (bf16)0.f;
-      }
-    }
-  };
-
-  // ---- Y block of this wave: rows i in [yi*32, +32), channels p in [yp*32, +32); the
-  // gate values of the lane's 16 outputs are loaded one chunk ahead as well
-  const int yi = wave >> 1, yp = wave & 1;
-  const int pl = yp * 32 + (lane & 31);
-  const int c = c0 + pl;
-  const float Dc = p.D[c];
-  float g_r[16];
-  auto fetch_g = [&](int t0) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = t0 + yi * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-      g_r[e] = t < T ? (float)z[ssd_row(t, b, p.n_meta, p.L) * p.z_stride + p.g_col + c] : 0.f;
+      o.x[r] = *(const bf16x8*)(zr + p.xs_col + (wave + 4 * r) * 8);
+      o.g[r] = *(const bf16x8*)(zr + p.g_col + (wave + 4 * r) * 8);
     }
   };
 
@@ -138,20 +118,24 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
       for (int r = 0; r < 4; ++r) s_s[(sp0 + r) * CP + nb * 16 + (lane & 15)] = (bf16)st[nb][r];
   };
 
+  // Y block of this wave: rows i in [yi*32, +32), channels p in [yp*32, +32)
+  const int yi = wave >> 1, yp = wave & 1;
+  const int pl = yp * 32 + (lane & 31);
+  const float Dc = p.D[c0 + pl];
+
   const int nchunks = (T + kQ - 1) / kQ;
-  fetch(0);
-  fetch_g(0);
-  write_s();
-  for (int k = 0; k < nchunks; ++k) {
+  // One chunk from the operand set o, which is then refilled with chunk k + PD.
+  auto chunk = [&](int k, Ops& o) {
     const int t0 = k * kQ;
+    const bool ok = t0 + lane < T;
     // ---- A: dt, the decay prefix, and the operands into LDS
     if (wave == 0) {
-      const float dt = t0 + lane < T ? softplus_f(u_r + bias) : 0.f;
+      const float dt = ok ? softplus_f(o.u + bias) : 0.f;
       float cs = dt * A;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(cs, off, 64);
-        if (lane >= off) cs += o;
+        const float v = __shfl_up(cs, off, 64);
+        if (lane >= off) cs += v;
       }
       cs_s[lane] = cs;
       dt_s[lane] = dt;
@@ -159,37 +143,40 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
     }
 #pragma unroll
     for (int r = 0; r < BCL; ++r) {
-      const int idx = tid + 256 * r, j = idx / BPT, n4 = (idx % BPT) * 4;
+      const int n4 = (wave + 4 * r) * 4;
       bf16x4 cb, bb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        cb[e] = (bf16)c_r[r][e];
-        bb[e] = (bf16)b_r[r][e];
+        if (!ok) o.b[r][e] = 0.f;  // also zeroes this token's w B below
+        cb[e] = (bf16)(ok ? o.c[r][e] : 0.f);
+        bb[e] = (bf16)o.b[r][e];
       }
-      *(bf16x4*)(c_s + j * CP + n4) = cb;
-      *(bf16x4*)(b_s + j * CP + n4) = bb;
+      *(bf16x4*)(c_s + lane * CP + n4) = cb;
+      *(bf16x4*)(b_s + lane * CP + n4) = bb;
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int idx = tid + 256 * r, j = idx >> 3, p8 = (idx & 7) * 8;
+      const int p8 = (wave + 4 * r) * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xt_s[(p8 + e) * kXP + j] = x_r[r][e];
+      for (int e = 0; e < 8; ++e) {
+        xt_s[(p8 + e) * kXP + lane] = ok ? o.x[r][e] : (bf16)0.f;
+        gt_s[(p8 + e) * kXP + lane] = o.g[r][e];
+      }
     }
     lds_barrier();
 
     // ---- B: (w B)^T in two bf16 parts, and M from G^T = B C^T
     {
-      const float cl = cs_s[kQ - 1];
+      const float w = __expf(cs_s[kQ - 1] - cs_s[lane]) * dt_s[lane];
 #pragma unroll
       for (int r = 0; r < BCL; ++r) {
-        const int idx = tid + 256 * r, j = idx / BPT, n4 = (idx % BPT) * 4;
-        const float w = __expf(cl - cs_s[j]) * dt_s[j];
+        const int n4 = (wave + 4 * r) * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = w * b_r[r][e];
+          const float v = w * o.b[r][e];
           const bf16 hi = (bf16)v;
-          wh_s[(n4 + e) * kXP + j] = hi;
-          wl_s[(n4 + e) * kXP + j] = (bf16)(v - (float)hi);
+          wh_s[(n4 + e) * kXP + lane] = hi;
+          wl_s[(n4 + e) * kXP + lane] = (bf16)(v - (float)hi);
         }
       }
     }
@@ -210,20 +197,18 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int j0 = bj * 32 + q * 8 + (lane >> 5) * 4;
-        bf16x4 o;
+        const floatx4 csj = *(const floatx4*)(cs_s + j0), dtj = *(const floatx4*)(dt_s + j0);
+        bf16x4 m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + r;
-          o[r] = (bf16)(j <= i ? g[4 * q + r] * __expf(csi - cs_s[j]) * dt_s[j] : 0.f);
-        }
-        *(bf16x4*)(m_s + i * kXP + j0) = o;
+        for (int r = 0; r < 4; ++r)
+          m[r] = (bf16)(j0 + r <= i ? g[4 * q + r] * __expf(csi - csj[r]) * dtj[r] : 0.f);
+        *(bf16x4*)(m_s + i * kXP + j0) = m;
       }
     }
-    // the next chunk's operands (the current ones are all in LDS now)
-    if (k + 1 < nchunks) fetch(t0 + kQ);
+    if (k + PD < nchunks) fetch(o, t0 + PD * kQ);  // o is all in LDS now
     lds_barrier();
 
-    // ---- C: Y = exp(cs) (C S_prev^T) + M X, gated and stored; then the state
+    // ---- C: Y = exp(cs) (C S_prev^T) + M X, gated into y_s; then the state
     {
       floatx16 y;
 #pragma unroll
@@ -236,7 +221,11 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
         y = mfma32(fc, fs, y);  // D[i][p]
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) y[e] *= ecs_s[yi * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)];
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 e4 = *(const floatx4*)(ecs_s + yi * 32 + q * 8 + (lane >> 5) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[4 * q + r] *= e4[r];
+      }
       const int kend = yi == 0 ? 2 : 4;  // rows i < 32 see keys j < 32 only
       for (int ks = 0; ks < kend; ++ks) {
         const int ko = ks * 16 + (lane >> 5) * 8;
@@ -245,15 +234,15 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
         y = mfma32(fm, fx, y);
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = yi * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3), t = t0 + i;
-        if (t < T && (t >= p.n_meta || b == 0)) {
-          const float xv = (float)xt_s[pl * kXP + i];
-          const float out = (y[e] + Dc * xv) * silu_f(g_r[e]);
-          ((bf16*)p.y)[ssd_row(t, b, p.n_meta, p.L) * p.y_stride + c] = (bf16)out;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int i4 = yi * 32 + q * 8 + (lane >> 5) * 4;
+        const bf16x4 xv = *(const bf16x4*)(xt_s + pl * kXP + i4);
+        const bf16x4 gv = *(const bf16x4*)(gt_s + pl * kXP + i4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          y_s[(i4 + r) * kXP + pl] =
+              (bf16)((y[4 * q + r] + Dc * (float)xv[r]) * silu_f((float)gv[r]));
       }
-      if (k + 1 < nchunks) fetch_g(t0 + kQ);
     }
     {
       const float el = ecs_s[kQ - 1];
@@ -275,6 +264,33 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
     }
     lds_barrier();
     write_s();  // S_prev of the next chunk (read only after the next barrier)
+    // token t0 + lane's output row: 16-byte stores of 8 channels each; the meta rows
+    // are stored by sequence 0 only
+    const int t = t0 + lane;
+    if (ok && (t >= p.n_meta || b == 0)) {
+      bf16* yr = (bf16*)p.y + row_of(t) * p.y_stride + c0;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int p8 = (wave + 4 * r) * 8;
+        *(bf16x8*)(yr + p8) = *(const bf16x8*)(y_s + lane * kXP + p8);
+      }
+    }
+  };
+
+  write_s();
+  if constexpr (PD == 1) {
+    Ops o0;
+    fetch(o0, 0);
+    for (int k = 0; k < nchunks; ++k) chunk(k, o0);
+  } else {
+    static_assert(PD == 2, "prefetch depth");
+    Ops o0, o1;
+    fetch(o0, 0);
+    if (nchunks > 1) fetch(o1, kQ);
+    for (int k = 0; k < nchunks; k += 2) {
+      chunk(k, o0);
+      if (k + 1 < nchunks) chunk(k + 1, o1);
+    }
   }
 
   if (p.h_out != nullptr) {
@@ -292,14 +308,16 @@ bool scan_ssd_supported(int N, int Di, int H) {
 
 hipError_t launch_scan_ssd(const SsdParams& p, hipStream_t s) {
   if (p.B == 0 || p.n_meta + p.L == 0) return hipSuccess;
-  if (!scan_ssd_supported(p.N, p.H * kP, p.H) || p.xbc_ld % 4 || p.z_stride % 8 || p.xs_col % 8)
+  if (!scan_ssd_supported(p.N, p.H * kP, p.H) || p.xbc_ld % 4 || p.z_stride % 8 ||
+      p.xs_col % 8 || p.g_col % 8 || p.y_stride % 8)
     return hipErrorInvalidValue;
   const dim3 grid(p.H, p.B);
   switch (p.N) {
-    case 16: scan_ssd_kernel<16><<<grid, dim3(256), 0, s>>>(p); break;
-    case 32: scan_ssd_kernel<32><<<grid, dim3(256), 0, s>>>(p); break;
-    case 64: scan_ssd_kernel<64><<<grid, dim3(256), 0, s>>>(p); break;
-    case 128: scan_ssd_kernel<128><<<grid, dim3(256), 0, s>>>(p); break;
+    // two chunks of operands in flight where the registers allow it
+    case 16: scan_ssd_kernel<16, 2><<<grid, dim3(256), 0, s>>>(p); break;
+    case 32: scan_ssd_kernel<32, 1><<<grid, dim3(256), 0, s>>>(p); break;
+    case 64: scan_ssd_kernel<64, 1><<<grid, dim3(256), 0, s>>>(p); break;
+    case 128: scan_ssd_kernel<128, 1><<<grid, dim3(256), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

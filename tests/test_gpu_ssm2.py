@@ -116,3 +116,26 @@ def test_head_ssm_cached_prefill_matches_plain_and_oracle():
     print({k: f"{v:.1e}" for k, v in errs.items()})
     assert errs["h"] <= 1e-4 and errs["y_meta"] <= 1e-6 and errs["y"] < TOL_BF16
     assert errs["y vs oracle"] < TOL_BF16 and errs["h vs oracle"] < TOL_H
+
+
+def test_head_ssm_full_size_sampled_sequence():
+    """The prefill workload's layer shape with the Mamba-2 head (d 2048, Di 4096 in 64
+    heads of 64 channels, N 16), B=8, L=2048, 128 meta tokens, run on the whole batch;
+    sequence 5 is recomputed by the oracle (y, y_meta and the final state)."""
+    from synth import CASES
+    case = CASES[1]
+    dims = case.dims.replace(ssm_heads=64, dt_rank=0)
+    B, L = case.batch, case.seq_len
+    w = gen_layer_weights(dims, case.case_id)
+    meta_t, meta, x_t, x = gen_activations(dims, case.case_id, B, L)
+    layer = make_layer(dims, w)
+    st = alloc_state(dims, B)
+    y, ym = layer.prefill(meta_t.to(DEV), x_t.to(DEV), state_out=state_struct(st))
+    torch.cuda.synchronize()
+    b = 5
+    ref = orc.prefill(dims, w, meta, x[b:b + 1], contract=True)
+    errs = {"y": rel_err(to_np(y[b]), ref["y"][0]), "y_meta": rel_err(to_np(ym), ref["y_meta"][0]),
+            "h": rel_err(to_np(st["h"][b]), ref["h"][0])}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] < TOL_BF16 and errs["y_meta"] < TOL_BF16 and errs["h"] < TOL_H
+    assert np.all(st["pos"].cpu().numpy() == L)
