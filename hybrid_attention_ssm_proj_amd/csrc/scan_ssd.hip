@@ -74,9 +74,9 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
   const bf16* z = (const bf16*)p.z;
   const int64_t seq_off = (int64_t)b * p.L;  // row(t) = t, or t + b L past the meta prefix
 
-  // Every global access of a chunk is made by the thread whose lane is the token: lane j
-  // moves token t0 + j's u (wave 0), B and C (4-float groups wave + 4r), x and G (8-channel
-  // groups wave + 4r), and its y row.  Tokens past the end read the last token's row
+  // Every load of a chunk is made by the thread whose lane is the token: lane j moves
+  // token t0 + j's u (wave 0), B and C (4-float groups wave + 4r), x and G (8-channel
+  // groups wave + 4r), so the transposes into LDS are conflict-free.  Tokens past the end read the last token's row
   // (no load waits at its issue) and are zeroed where the values are used.
   auto row_of = [&](int t) { return (int64_t)t + (t >= p.n_meta ? seq_off : 0); };
   struct Ops {
@@ -264,16 +264,14 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
     }
     lds_barrier();
     write_s();  // S_prev of the next chunk (read only after the next barrier)
-    // token t0 + lane's output row: 16-byte stores of 8 channels each; the meta rows
-    // are stored by sequence 0 only
-    const int t = t0 + lane;
-    if (ok && (t >= p.n_meta || b == 0)) {
-      bf16* yr = (bf16*)p.y + row_of(t) * p.y_stride + c0;
+    // the chunk's output rows: 8 lanes store one row's 64 channels (one 128-byte line),
+    // so a wave instruction writes 8 whole lines; the meta rows are stored by sequence 0
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int p8 = (wave + 4 * r) * 8;
-        *(bf16x8*)(yr + p8) = *(const bf16x8*)(y_s + lane * kXP + p8);
-      }
+    for (int r = 0; r < 2; ++r) {
+      const int idx = tid + 256 * r, j = idx >> 3, p8 = (idx & 7) * 8, t = t0 + j;
+      if (t < T && (t >= p.n_meta || b == 0))
+        *(bf16x8*)((bf16*)p.y + row_of(t) * p.y_stride + c0 + p8) =
+            *(const bf16x8*)(y_s + j * kXP + p8);
     }
   };
 
