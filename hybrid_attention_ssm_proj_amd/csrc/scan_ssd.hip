@@ -28,7 +28,15 @@ namespace {
 
 constexpr int kP = 64;       // channels per head
 constexpr int kQ = 64;       // tokens per chunk
-constexpr int kXP = kQ + 8;  // row pitch (bf16) of X^T, M and (w B)^T
+constexpr int kXP = kQ + 8;  // row pitch (bf16) of M, (w B)^T and the output tile
+
+// X^T and G^T rows (channel p, 64 tokens) keep their eight 16-byte token chunks
+// XOR-permuted by f(p) = (p ^ (p >> 3)) & 7: the transposing writes (8 lanes, channels
+// 8 apart, same token) and the operand reads (8 lanes, 8 consecutive channels, same
+// chunk) then each touch 8 distinct chunks, i.e. all 32 banks once.
+__device__ __forceinline__ int xt_at(int p, int j) {
+  return p * kQ + ((((j >> 3) ^ p ^ (p >> 3)) & 7) << 3) + (j & 7);
+}
 
 __device__ __forceinline__ int64_t ssd_row(int t, int b, int n_meta, int L) {
   return t < n_meta ? (int64_t)t : (int64_t)n_meta + (int64_t)b * L + (t - n_meta);
@@ -43,9 +51,11 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
 
 template <int N>
 struct SsdCfg {
-  static constexpr int CP = N + 8;         // row pitch (bf16) of C, B, S
-  static constexpr int NB = N / 16;        // 16-column state blocks
-  static constexpr int BC_LOADS = N / 16;  // float4 groups of B (and of C) per thread
+  static constexpr int CP = N + 8;        // row pitch (bf16) of C, B, S
+  static constexpr int NB = N / 16;       // 16-column state blocks
+  static constexpr int LPR = N / 2;       // lanes per token row of [B | C] (16 bytes each)
+  static constexpr int RPP = 256 / LPR;   // token rows per pass of the workgroup
+  static constexpr int PASSES = kQ / RPP; // float4 loads of [B | C] per thread
 };
 
 }  // namespace
@@ -53,11 +63,11 @@ struct SsdCfg {
 template <int N, int PD>
 __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
   using Cfg = SsdCfg<N>;
-  constexpr int CP = Cfg::CP, NB = Cfg::NB, BCL = Cfg::BC_LOADS;
+  constexpr int CP = Cfg::CP, NB = Cfg::NB, LPR = Cfg::LPR, RPP = Cfg::RPP, PASSES = Cfg::PASSES;
   __shared__ __attribute__((aligned(16))) bf16 c_s[kQ * CP];    // C [i][n]
   __shared__ __attribute__((aligned(16))) bf16 b_s[kQ * CP];    // B [j][n]
-  __shared__ __attribute__((aligned(16))) bf16 xt_s[kP * kXP];  // X^T [p][j]
-  __shared__ __attribute__((aligned(16))) bf16 gt_s[kP * kXP];  // G^T [p][i]
+  __shared__ __attribute__((aligned(16))) bf16 xt_s[kP * kQ];   // X^T [p][j] (xt_at)
+  __shared__ __attribute__((aligned(16))) bf16 gt_s[kP * kQ];   // G^T [p][i] (xt_at)
   __shared__ __attribute__((aligned(16))) bf16 m_s[kQ * kXP];   // M [i][j]
   __shared__ __attribute__((aligned(16))) bf16 y_s[kQ * kXP];   // gated output [i][p]
   __shared__ __attribute__((aligned(16))) bf16 wh_s[N * kXP];   // (w B)^T [n][j], high
@@ -74,31 +84,28 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
   const bf16* z = (const bf16*)p.z;
   const int64_t seq_off = (int64_t)b * p.L;  // row(t) = t, or t + b L past the meta prefix
 
-  // Every load of a chunk is made by the thread whose lane is the token: lane j moves
-  // token t0 + j's u (wave 0), B and C (4-float groups wave + 4r), x and G (8-channel
-  // groups wave + 4r), so the transposes into LDS are conflict-free.  Tokens past the end read the last token's row
-  // (no load waits at its issue) and are zeroed where the values are used.
+  // Loads are coalesced: 8 lanes take one token's 64 channels of x (and of G), LPR lanes
+  // one token's [B | C] row; wave 0's lane j takes token t0 + j's u.  Tokens past the end
+  // read the last token's row (no load waits at its issue) and are zeroed where used.
   auto row_of = [&](int t) { return (int64_t)t + (t >= p.n_meta ? seq_off : 0); };
+  const int xq = tid & 7, xj = tid >> 3;           // x / G: channel group, token (+32 r)
+  const int bq = tid % LPR, bj = tid / LPR;        // [B | C]: float4 index, token (+RPP r)
   struct Ops {
     float u;
-    floatx4 b[BCL], c[BCL];
+    floatx4 bc[PASSES];
     bf16x8 x[2], g[2];
   };
   auto fetch = [&](Ops& o, int t0) {
-    const int64_t row = row_of(min(t0 + lane, T - 1));
-    const float* xr = p.xbc + row * p.xbc_ld;
-    if (wave == 0) o.u = xr[hd];
+    if (wave == 0) o.u = p.xbc[row_of(min(t0 + lane, T - 1)) * p.xbc_ld + hd];
 #pragma unroll
-    for (int r = 0; r < BCL; ++r) {
-      const float* base = xr + p.H + (wave + 4 * r) * 4;
-      o.b[r] = *(const floatx4*)base;
-      o.c[r] = *(const floatx4*)(base + N);
-    }
-    const bf16* zr = z + row * p.z_stride + c0;
+    for (int r = 0; r < PASSES; ++r)
+      o.bc[r] = *(const floatx4*)(p.xbc + row_of(min(t0 + bj + r * RPP, T - 1)) * p.xbc_ld +
+                                  p.H + bq * 4);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      o.x[r] = *(const bf16x8*)(zr + p.xs_col + (wave + 4 * r) * 8);
-      o.g[r] = *(const bf16x8*)(zr + p.g_col + (wave + 4 * r) * 8);
+      const bf16* zr = z + row_of(min(t0 + xj + 32 * r, T - 1)) * p.z_stride + c0 + xq * 8;
+      o.x[r] = *(const bf16x8*)(zr + p.xs_col);
+      o.g[r] = *(const bf16x8*)(zr + p.g_col);
     }
   };
 
@@ -142,41 +149,41 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
       ecs_s[lane] = __expf(cs);
     }
 #pragma unroll
-    for (int r = 0; r < BCL; ++r) {
-      const int n4 = (wave + 4 * r) * 4;
-      bf16x4 cb, bb;
+    for (int r = 0; r < PASSES; ++r) {  // B (first N/4 lanes of a row) or C
+      const int j = bj + r * RPP;
+      const bool okj = t0 + j < T;
+      bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (!ok) o.b[r][e] = 0.f;  // also zeroes this token's w B below
-        cb[e] = (bf16)(ok ? o.c[r][e] : 0.f);
-        bb[e] = (bf16)o.b[r][e];
-      }
-      *(bf16x4*)(c_s + lane * CP + n4) = cb;
-      *(bf16x4*)(b_s + lane * CP + n4) = bb;
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(okj ? o.bc[r][e] : 0.f);
+      if (bq < LPR / 2)
+        *(bf16x4*)(b_s + j * CP + bq * 4) = v;
+      else
+        *(bf16x4*)(c_s + j * CP + (bq - LPR / 2) * 4) = v;
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int p8 = (wave + 4 * r) * 8;
+      const int j = xj + 32 * r;
+      const bool okj = t0 + j < T;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xt_s[(p8 + e) * kXP + lane] = ok ? o.x[r][e] : (bf16)0.f;
-        gt_s[(p8 + e) * kXP + lane] = o.g[r][e];
+        xt_s[xt_at(xq * 8 + e, j)] = okj ? o.x[r][e] : (bf16)0.f;
+        gt_s[xt_at(xq * 8 + e, j)] = o.g[r][e];
       }
     }
     lds_barrier();
 
     // ---- B: (w B)^T in two bf16 parts, and M from G^T = B C^T
-    {
-      const float w = __expf(cs_s[kQ - 1] - cs_s[lane]) * dt_s[lane];
+    if (bq < LPR / 2) {  // threads holding B: w_j = 0 for tokens past the end (dt = 0)
 #pragma unroll
-      for (int r = 0; r < BCL; ++r) {
-        const int n4 = (wave + 4 * r) * 4;
+      for (int r = 0; r < PASSES; ++r) {
+        const int j = bj + r * RPP;
+        const float w = __expf(cs_s[kQ - 1] - cs_s[j]) * dt_s[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = w * o.b[r][e];
+          const float v = w * o.bc[r][e];
           const bf16 hi = (bf16)v;
-          wh_s[(n4 + e) * kXP + lane] = hi;
-          wl_s[(n4 + e) * kXP + lane] = (bf16)(v - (float)hi);
+          wh_s[(bq * 4 + e) * kXP + j] = hi;
+          wl_s[(bq * 4 + e) * kXP + j] = (bf16)(v - (float)hi);
         }
       }
     }
@@ -230,14 +237,14 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
       for (int ks = 0; ks < kend; ++ks) {
         const int ko = ks * 16 + (lane >> 5) * 8;
         const bf16x8 fm = *(const bf16x8*)(m_s + (yi * 32 + (lane & 31)) * kXP + ko);
-        const bf16x8 fx = *(const bf16x8*)(xt_s + (yp * 32 + (lane & 31)) * kXP + ko);
+        const bf16x8 fx = *(const bf16x8*)(xt_s + xt_at(yp * 32 + (lane & 31), ko));
         y = mfma32(fm, fx, y);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i4 = yi * 32 + q * 8 + (lane >> 5) * 4;
-        const bf16x4 xv = *(const bf16x4*)(xt_s + pl * kXP + i4);
-        const bf16x4 gv = *(const bf16x4*)(gt_s + pl * kXP + i4);
+        const bf16x4 xv = *(const bf16x4*)(xt_s + xt_at(pl, i4));
+        const bf16x4 gv = *(const bf16x4*)(gt_s + xt_at(pl, i4));
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           y_s[(i4 + r) * kXP + pl] =
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(256) void scan_ssd_kernel(SsdParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int ko = ks * 32 + (lane >> 4) * 8;
-        const bf16x8 fx = *(const bf16x8*)(xt_s + (wave * 16 + (lane & 15)) * kXP + ko);
+        const bf16x8 fx = *(const bf16x8*)(xt_s + xt_at(wave * 16 + (lane & 15), ko));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int row = (nb * 16 + (lane & 15)) * kXP + ko;
