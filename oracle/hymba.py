@@ -13,6 +13,9 @@ Sources (web pages on Hymba; cited by title and section):
                attention" and "Cross-layer KV sharing" for the mask and the cache.
   [HYMBA-ABS]  the same title, paper abstract (chatpaper.ai): meta tokens prepended
                to the prompt, cross-layer KV sharing, partial sliding-window attention.
+  [HYB]        Korean summary of a study of hybrid Transformer-Mamba architectures
+               (inter- and intra-layer), section "설계 통찰 / 아키텍처 변형": group
+               normalisation and difference / concatenation fusion for intra-layer hybrids.
   [HYMBA-ZH]   Chinese summary "Hymba ... hybrid attention-SSM heads"
                (metaphor-xennon.pages.dev), sections "核心架构" (normalise then average
                the two branches) and "实现细节" (RMSNorm per branch, 0.5 average,
@@ -43,6 +46,13 @@ all heads; D per channel; no convolution or internal norm (the branch norm follo
 It is the selective scan above with dt and A constant across a head's channels and
 states.
 
+Fusion variant (dims.norm_group = g > 0; [HYB] "Hybrid architectures ... design
+insights": group normalisation in the intra-layer hybrid, with difference or
+concatenation fusion): each branch is normalised in groups of g consecutive channels,
+(v - mean) / sqrt(var + eps) per group, then scaled by its beta and averaged as above.
+Concatenation is the default fusion; a difference fusion through the concatenated W_out
+is the same map with the SSM half of W_out negated, so it needs no code of its own.
+
 Readings where the pages are silent or disagree (each one also listed in the design
 notes): softmax scale 1/sqrt(dh); no positional encoding; causal mask; a window of W
 keys counts the query itself; contiguous GQA groups; no short convolution before the
@@ -72,7 +82,7 @@ __all__ = [
     "bf16_round", "softplus", "silu", "rms_normalize", "in_proj", "split_z",
     "attention", "ssm_params", "selective_scan", "ssm_alpha", "ssm_mixing_form",
     "gate", "fuse", "out_proj", "prefill_sequence", "prefill", "decode_step",
-    "visible", "ssm2_params", "ssm2_scan", "ssd_matrix_form",
+    "visible", "ssm2_params", "ssm2_scan", "ssd_matrix_form", "group_normalize",
 ]
 
 
@@ -106,6 +116,19 @@ def rms_normalize(v, eps: float):
     """Per row (last axis): v / sqrt(mean(v^2) + eps).  [HYMBA-ZH] 实现细节: RMSNorm per branch."""
     v = np.asarray(v, dtype=np.float64)
     return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+
+
+def group_normalize(v, group: int, eps: float):
+    """Group normalisation of each row (last axis) in consecutive groups of `group`
+    channels: (v - mean_g) / sqrt(var_g + eps), the variance taken about the group mean
+    ([HYB] design insights: group normalisation in the intra-layer hybrid; reading: no
+    affine term of its own, the branch's beta scales afterwards)."""
+    v = np.asarray(v, dtype=np.float64)
+    shp = v.shape
+    g = v.reshape(shp[:-1] + (shp[-1] // group, group))
+    mu = g.mean(axis=-1, keepdims=True)
+    var = ((g - mu) ** 2).mean(axis=-1, keepdims=True)
+    return ((g - mu) / np.sqrt(var + eps)).reshape(shp)
 
 
 # ---------------------------------------------------------------------------
@@ -335,15 +358,19 @@ def gate(y, g):
     return np.asarray(y, np.float64) * silu(g)
 
 
-def fuse(O, Yssm, beta_attn, beta_ssm, eps: float):
+def fuse(O, Yssm, beta_attn, beta_ssm, eps: float, norm_group: int = 0):
     """F = 0.5 [beta1 * rms(O) ; beta2 * rms(Y_ssm)].
 
     [HYMBA-SUM] Design formulation, total fusion equation: each branch normalised
     and rescaled by a learnable vector; [HYMBA-ZH] 核心架构/实现细节: the two are
     averaged.  The branches differ in width, so they are concatenated; projecting
     F with W_out = [W_a | W_s] equals averaging W_a(beta1 rms(O)) and W_s(beta2 rms(Y))."""
-    a = np.asarray(beta_attn, np.float64) * rms_normalize(O, eps)
-    s = np.asarray(beta_ssm, np.float64) * rms_normalize(Yssm, eps)
+    if norm_group:  # the group-normalisation variant of the fusion
+        a = np.asarray(beta_attn, np.float64) * group_normalize(O, norm_group, eps)
+        s = np.asarray(beta_ssm, np.float64) * group_normalize(Yssm, norm_group, eps)
+    else:
+        a = np.asarray(beta_attn, np.float64) * rms_normalize(O, eps)
+        s = np.asarray(beta_ssm, np.float64) * rms_normalize(Yssm, eps)
     return 0.5 * np.concatenate([a, s], axis=-1)
 
 
@@ -397,7 +424,8 @@ def prefill_sequence(dims, w, meta, x, kv_src: Optional[Dict[str, np.ndarray]] =
     O = _rnd(O.reshape(T, -1), contract)
     dt, B, C, y, h = _ssm_branch(dims, w, parts["Xs"], None, contract)
     Yssm = _rnd(gate(y, parts["G"]), contract)
-    F = _rnd(fuse(O, Yssm, w.beta_attn, w.beta_ssm, dims.rms_eps), contract)
+    F = _rnd(fuse(O, Yssm, w.beta_attn, w.beta_ssm, dims.rms_eps,
+                         getattr(dims, "norm_group", 0)), contract)
     Y = out_proj(F, w.w_out)
     out = {"y": Y[M:], "y_meta": Y[:M], "K": K, "V": V, "h": h}
     if keep:
@@ -480,7 +508,8 @@ def decode_step(dims, w, x_new, k_meta, v_meta, k_ring, v_ring, h, pos,
         O = _rnd(O.reshape(1, -1), contract)
         _, _, _, ys, h[b] = _ssm_branch(dims, w, parts["Xs"], h[b], contract)
         Yssm = _rnd(gate(ys, parts["G"]), contract)
-        F = _rnd(fuse(O, Yssm, w.beta_attn, w.beta_ssm, dims.rms_eps), contract)
+        F = _rnd(fuse(O, Yssm, w.beta_attn, w.beta_ssm, dims.rms_eps,
+                         getattr(dims, "norm_group", 0)), contract)
         y[b] = out_proj(F, w.w_out)[0]
         pos[b] = p + 1
     return {"y": y, "k": k_ring, "v": v_ring, "h": h, "pos": pos}

@@ -42,6 +42,7 @@ class LayerDims:
     softmax_scale: float = 0.0  # 0 => 1/sqrt(head_dim)
     ssm_heads: int = 0          # 0 = Mamba head (per-channel A, dt of rank dt_rank);
                                 # H > 0 = Mamba-2 head: H heads, scalar A and dt per head
+    norm_group: int = 0         # 0 = RMSNorm per branch; g > 0 = group norm, g channels
 
     @property
     def q_width(self) -> int:

@@ -139,3 +139,48 @@ def test_head_ssm_decode_continues_prefill(window, slots, L, k):
         np.testing.assert_allclose(out["y"], long["y"][:, L + s], rtol=1e-11, atol=1e-12)
         st = out
     np.testing.assert_allclose(st["h"], long["h"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- group-norm fusion
+
+def test_group_normalize_matches_torch_group_norm():
+    """The oracle's group normalisation is torch's group_norm (no affine) on rows of
+    [batch, channels], and closed forms on tiny groups."""
+    g = rs(21)
+    x = g.standard_normal((5, 48)) * 3 + 1
+    for group in (8, 16, 48):
+        ref = TF.group_norm(torch.from_numpy(x), 48 // group, eps=1e-5).numpy()
+        np.testing.assert_allclose(orc.group_normalize(x, group, 1e-5), ref, rtol=1e-12, atol=1e-12)
+    # a constant group maps to 0; a two-value group (a, b) to (-1, +1) sqrt(v / (v + eps))
+    np.testing.assert_allclose(orc.group_normalize(np.full((1, 4), 7.0), 4, 1e-6), 0.0, atol=0)
+    v = ((3.0 - 1.0) / 2) ** 2
+    np.testing.assert_allclose(orc.group_normalize(np.array([[1.0, 3.0]]), 2, 1e-6),
+                               [[-np.sqrt(v / (v + 1e-6)), np.sqrt(v / (v + 1e-6))]], rtol=1e-14)
+
+
+def test_group_norm_layer_matches_torch_composition():
+    """The layer with norm_group = 4: the branch norms by torch's group_norm, the rest as
+    in the default layer (SDPA attention, the SSM through the alpha mixing matrix)."""
+    dims = LayerDims(d_model=16, n_q_heads=4, n_kv_heads=2, head_dim=8, d_inner=12, d_state=3,
+                     dt_rank=2, n_meta=2, window=0, kv_share=0, dtype=F32, norm_group=4)
+    w, meta, X = _layer(dims, B=1, L=6, case=97)
+    out = orc.prefill(dims, w, meta, X)
+    f64 = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    z = f64(np.concatenate([meta, X[0]])) @ f64(w.w_in).T
+    qw, kw, Di, N, R = 32, 16, 12, 3, 2
+    T = z.shape[0]
+    q = z[:, :qw].reshape(T, 4, 8).permute(1, 0, 2)
+    k = z[:, qw:qw + kw].reshape(T, 2, 8).permute(1, 0, 2).repeat_interleave(2, 0)
+    v = z[:, qw + kw:qw + 2 * kw].reshape(T, 2, 8).permute(1, 0, 2).repeat_interleave(2, 0)
+    o = TF.scaled_dot_product_attention(q, k, v, is_causal=True).permute(1, 0, 2).reshape(T, qw)
+    xs, gg = z[:, qw + 2 * kw:qw + 2 * kw + Di], z[:, qw + 2 * kw + Di:]
+    xdbl = xs @ f64(w.w_x).T
+    dt = TF.softplus(xdbl[:, :R] @ f64(w.w_dt).T + f64(w.dt_bias), threshold=1e9)
+    ymix = orc.ssm_mixing_form(xs.numpy(), dt.numpy(), w.A, xdbl[:, R:R + N].numpy(),
+                               xdbl[:, R + N:].numpy(), w.D)
+    yssm = torch.from_numpy(ymix) * TF.silu(gg)
+    fa = TF.group_norm(o, qw // 4, eps=1e-6) * f64(w.beta_attn)
+    fs = TF.group_norm(yssm, Di // 4, eps=1e-6) * f64(w.beta_ssm)
+    Y = 0.5 * torch.cat([fa, fs], 1) @ f64(w.w_out).T
+    np.testing.assert_allclose(out["y"][0], Y[2:].numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(out["y_meta"][0], Y[:2].numpy(), rtol=1e-10, atol=1e-12)
