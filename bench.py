@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 16-layer partial-SWA vs all-global stack comparison")
     ap.add_argument("--no-head-ssm", action="store_true",
-                    help="skip the Mamba-2 head variant of the layer")
+                    help="skip the layer variants (Mamba-2 head, group-norm fusion)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the prefill workload the CPU oracle runs (8 = all)")
@@ -302,9 +302,10 @@ def main():
     if not args.no_stack:
         stack = bench_stack(hy, torch, dev)
 
-    head_ssm = None
+    head_ssm = group_norm = None
     if not args.no_head_ssm:
         head_ssm = bench_head_ssm(hy, torch, dev, args, stages)
+        group_norm = bench_group_norm(hy, torch, dev, args, stages)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -325,9 +326,73 @@ def main():
         "prefill_meta_cached": cached,
         "stack": stack,
         "head_ssm": head_ssm,
+        "group_norm": group_norm,
         "stages": stage_report,
     }
     print(json.dumps(out), flush=True)
+
+
+def prefill_variant(hy, torch, dev, args, dims, seed):
+    """Prefill of the prefill workload with layer `dims`: (ms per step, stage times)."""
+    from synth import CASES, gen_layer_weights
+    case = CASES[1]
+    B, L, M = case.batch, case.seq_len, dims.n_meta
+    w = gen_layer_weights(dims, case.case_id)
+    layer = hy.HymbaLayer(dims, w.torch, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    meta = torch.randn(M, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    x = torch.randn(B, L, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    y = torch.empty(B, L, dims.d_model, dtype=torch.bfloat16, device=dev)
+    y_meta = torch.empty(M, dims.d_model, dtype=torch.bfloat16, device=dev)
+    h = torch.empty(B, dims.d_inner, dims.d_state, dtype=torch.float32, device=dev)
+    pos = torch.empty(B, dtype=torch.int32, device=dev)
+    state = hy.make_state(h, pos)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.prefill(meta, x, state_out=state, y=y, y_meta=y_meta, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    stages = stage_pass(hy, torch, step, max(3, args.steps // 2), -1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    del layer
+    torch.cuda.empty_cache()
+    return ms, stages
+
+
+def bench_group_norm(hy, torch, dev, args, default_stages):
+    """The prefill workload with the group-normalisation fusion (groups of 128 channels):
+    the branch norms can no longer be folded into out_proj as per-row factors, so F is
+    normalised in place by one pass (reads and writes F once)."""
+    from synth import CASES
+    case = CASES[1]
+    dims = case.dims.replace(norm_group=128)
+    B, L = case.batch, case.seq_len
+    log(f"[bench] group-norm variant: norm_group={dims.norm_group}")
+    ms, stages = prefill_variant(hy, torch, dev, args, dims, 1006)
+    rows = dims.n_meta + B * L
+    f_bytes = 2 * rows * dims.f_width * 2
+    norm_ms = stages["norm"]["avg_ms"]
+    achieved = f_bytes / (norm_ms * 1e-3) / 1e9
+    log(f"[bench] group-norm variant: prefill {ms:.3f} ms ({B * L / ms / 1e3:.3f} M tok/s), "
+        f"norm pass {norm_ms:.3f} ms ({achieved:.0f} GB/s)")
+    return {"workload": "the prefill workload with group normalisation of each branch in "
+                        "groups of 128 channels",
+            "prefill_ms": round(ms, 4), "prefill_tokens_per_s": round(B * L / ms * 1e3, 1),
+            "norm_ms": round(norm_ms, 4),
+            "default_norm_ms": round(default_stages["norm"]["avg_ms"], 4),
+            "norm_roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(achieved / PEAK_HBM_GBS, 4),
+                              "bytes_per_launch": f_bytes},
+            "stages_ms": {k: round(v["avg_ms"], 4) for k, v in stages.items()}}
 
 
 def bench_head_ssm(hy, torch, dev, args, mamba_stages):

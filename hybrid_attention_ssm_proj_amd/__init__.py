@@ -45,14 +45,15 @@ class LayerDesc(ctypes.Structure):
         "d_model", "n_q_heads", "n_kv_heads", "head_dim", "d_inner", "d_state", "dt_rank",
         "n_meta", "window", "kv_share", "dtype")] + [
         ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-        ("ssm_heads", ctypes.c_int32)]
+        ("ssm_heads", ctypes.c_int32), ("norm_group", ctypes.c_int32)]
 
     @classmethod
     def from_dims(cls, dims) -> "LayerDesc":
         return cls(dims.d_model, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.d_inner,
                    dims.d_state, dims.dt_rank, dims.n_meta, dims.window, dims.kv_share,
                    DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, dims.rms_eps,
-                   dims.softmax_scale, getattr(dims, "ssm_heads", 0))
+                   dims.softmax_scale, getattr(dims, "ssm_heads", 0),
+                   getattr(dims, "norm_group", 0))
 
 
 class LayerWeights(ctypes.Structure):

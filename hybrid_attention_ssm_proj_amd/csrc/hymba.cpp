@@ -79,6 +79,7 @@ struct TimerScope {
 struct Shape {
   int d, Hq, Hkv, dh, Di, N, R, M, W, share, es;
   int H2;  // Mamba-2 heads (0: Mamba head with per-channel A and a rank-R dt projection)
+  int G;   // branch-norm groups of G channels (0: RMSNorm over each branch)
   int nx;  // x_proj output width: (H2 ? H2 : R) + 2N
   bool bf16;
   int64_t qw, kvw, n_in, fw, xs_col, g_col, k_col, v_col;
@@ -116,6 +117,11 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
     return HYMBA_ERR_UNSUPPORTED;
   if (!is_pow2_in(d.d_state, 4, 128)) return HYMBA_ERR_UNSUPPORTED;
   if (!head_ssm && d.dt_rank > 512) return HYMBA_ERR_UNSUPPORTED;
+  if (d.norm_group < 0) return HYMBA_ERR_INVALID_ARG;
+  if (d.norm_group > 0 &&
+      (!is_pow2_in(d.norm_group, 8, 512) || (d.n_q_heads * d.head_dim) % d.norm_group ||
+       d.d_inner % d.norm_group))
+    return HYMBA_ERR_UNSUPPORTED;
   s.d = d.d_model;
   s.Hq = d.n_q_heads;
   s.Hkv = d.n_kv_heads;
@@ -124,6 +130,7 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
   s.N = d.d_state;
   s.R = head_ssm ? 0 : d.dt_rank;
   s.H2 = head_ssm ? d.ssm_heads : 0;
+  s.G = d.norm_group;
   s.nx = (head_ssm ? d.ssm_heads : d.dt_rank) + 2 * d.d_state;
   s.M = d.n_meta;
   s.W = d.window;
@@ -399,7 +406,7 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
   const bool few_meta = b16 && s.d % 256 == 0 && s.fw % 256 == 0;
   const GemmOperands op_out{f + (size_t)Mr * s.fw * s.es, s.fw, nullptr, 0, (int)BL, w->w_out,
                             s.fw, (int)BL, s.d, (int)s.fw};
-  const bool defer_norm = b16 && fused_dt(s) && s.qw % 128 == 0 &&
+  const bool defer_norm = b16 && fused_dt(s) && s.G == 0 && s.qw % 128 == 0 &&
                           (BL == 0 || gemm_bf16_rowscaled_ok(op_out, (int)s.qw)) &&
                           !any_misaligned(w->beta_attn, w->beta_ssm);
   const int n_sblk = defer_norm ? scan_channel_blocks(s.N, s.Di) : 0;
@@ -566,6 +573,10 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
                  launch_row_factors(ssp, ssp_ld, s.Hq, n_sblk, (int)rows, (int)s.qw, s.Di,
                                     desc->rms_eps, fac, f, s.fw,
                                     y_meta != nullptr ? Mr : 0, stream));
+  } else if (s.G) {
+    HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_group_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
+                                                     w->beta_attn, w->beta_ssm, desc->rms_eps,
+                                                     s.G, stream));
   } else {
     HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, (int)rows, (int)s.qw, s.Di,
                                                     w->beta_attn, w->beta_ssm, desc->rms_eps,
@@ -778,7 +789,15 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     HYMBA_LAUNCH(HYMBA_STAGE_SCAN,
                  s.H2 ? launch_ssm2_step(sp, stream) : launch_ssm_step(b16, sp, stream));
   }
-  if (stream_attn) {
+  if (s.G) {  // group norm: merge the key splits first (if any), then normalise F
+    if (!stream_attn) {
+      HYMBA_LAUNCH(HYMBA_STAGE_NORM,
+                   launch_decode_combine(b16, part, nsplit, f, s.fw, B, s.Hq, s.dh, stream));
+    }
+    HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_group_norm(b16, f, s.fw, B, (int)s.qw, s.Di,
+                                                     w->beta_attn, w->beta_ssm, desc->rms_eps,
+                                                     s.G, stream));
+  } else if (stream_attn) {
     HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, B, (int)s.qw, s.Di,
                                                     w->beta_attn, w->beta_ssm, desc->rms_eps,
                                                     stream));

@@ -210,6 +210,15 @@ hipError_t launch_ssm2_step(const SsmStepParams& p, hipStream_t s);  // bf16, he
 
 // ----------------------------------------------------------------- fusion
 // F[r, :] = 0.5 * [beta_a * rms(F[r, :wa]) ; beta_s * rms(F[r, wa:wa+ws])], in place.
+// Group-normalisation variant of launch_fuse_norm: each branch in groups of g channels
+// (power of two, 8..512, dividing wa and ws), (v - mean) / sqrt(var + eps) per group,
+// then 0.5 * beta.
+hipError_t launch_group_norm(bool bf16, void* f, int64_t f_stride, int rows, int wa, int ws,
+                             const float* beta_a, const float* beta_s, float eps, int g,
+                             hipStream_t s);
+// Decode: merge the split-key attention partials into F's attention columns (no norm).
+hipError_t launch_decode_combine(bool bf16, const float* part, int nsplit, void* f,
+                                 int64_t f_stride, int B, int Hq, int head_dim, hipStream_t s);
 hipError_t launch_fuse_norm(bool bf16, void* f, int64_t f_stride, int rows, int wa, int ws,
                             const float* beta_a, const float* beta_s, float eps,
                             hipStream_t s);

@@ -120,6 +120,55 @@ hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int
   return hipGetLastError();
 }
 
+// Group normalisation of one row of F per workgroup.  A thread holds 8 channels; the
+// g / 8 threads of a group are adjacent lanes of one wave (g <= 512), so the group's
+// mean and then its variance about the mean are xor-shuffle sums over them.  The groups
+// never straddle the branch boundary (g divides wa).
+template <typename T>
+__global__ __launch_bounds__(256) void group_norm_kernel(T* f, int64_t stride, int wa, int ws,
+                                                         const float* ba, const float* bs,
+                                                         float eps, int g) {
+  T* row = f + (int64_t)blockIdx.x * stride;
+  const int tpg = g / 8;  // threads per group
+  const float inv_g = 1.f / (float)g;
+  for (int i = threadIdx.x * 8; i < wa + ws; i += 256 * 8) {
+    float v[8];
+    Vec8<T>::load(row + i, v);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += v[e];
+    for (int off = 1; off < tpg; off <<= 1) sum += __shfl_xor(sum, off, 64);
+    const float mean = sum * inv_g;
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] -= mean;
+      sq = fmaf(v[e], v[e], sq);
+    }
+    for (int off = 1; off < tpg; off <<= 1) sq += __shfl_xor(sq, off, 64);
+    const float sc = 0.5f * rsqrtf(sq * inv_g + eps);
+    const bool att = i < wa;
+    const float* beta = att ? ba + i : bs + (i - wa);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * sc * beta[e];
+    Vec8<T>::store(row + i, v);
+  }
+}
+
+hipError_t launch_group_norm(bool bf16_, void* f, int64_t f_stride, int rows, int wa, int ws,
+                             const float* beta_a, const float* beta_s, float eps, int g,
+                             hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (g < 8 || g > 512 || (g & (g - 1)) || wa % g || ws % g) return hipErrorInvalidValue;
+  if (bf16_)
+    group_norm_kernel<bf16><<<dim3(rows), dim3(256), 0, s>>>((bf16*)f, f_stride, wa, ws, beta_a,
+                                                             beta_s, eps, g);
+  else
+    group_norm_kernel<float><<<dim3(rows), dim3(256), 0, s>>>((float*)f, f_stride, wa, ws,
+                                                              beta_a, beta_s, eps, g);
+  return hipGetLastError();
+}
+
 // Row factors of the deferred branch norms.  Blocks [0, nfac) take 256 rows each, one
 // row per thread (consecutive threads read consecutive rows of each partial column);
 // blocks from nfac on scale one of the first scale_rows rows of F in place, recomputing
@@ -328,6 +377,32 @@ __global__ __launch_bounds__(256) void decode_combine_wide_kernel(const float* p
   }
   __syncthreads();
   norm_row<T>(row, wa, ws, ba, bs, eps);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* part, int nsplit, T* f,
+                                                            int64_t stride, int Hq, int dh) {
+  const int b = blockIdx.x;
+  T* row = f + (int64_t)b * stride;
+  const int wa = Hq * dh, rec = dh + 4;
+  for (int i = threadIdx.x * 8; i < wa; i += 256 * 8) {
+    const int h = i / dh;
+    float v[8];
+    combine_chunk<T>(part + ((int64_t)b * Hq + h) * nsplit * rec, nsplit, rec, i - h * dh, v);
+    Vec8<T>::store(row + i, v);
+  }
+}
+
+hipError_t launch_decode_combine(bool bf16_, const float* part, int nsplit, void* f,
+                                 int64_t f_stride, int B, int Hq, int head_dim, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (bf16_)
+    decode_combine_kernel<bf16><<<dim3(B), dim3(256), 0, s>>>(part, nsplit, (bf16*)f, f_stride,
+                                                              Hq, head_dim);
+  else
+    decode_combine_kernel<float><<<dim3(B), dim3(256), 0, s>>>(part, nsplit, (float*)f, f_stride,
+                                                               Hq, head_dim);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_combine_norm(bool bf16_, const float* part, int nsplit, void* f,

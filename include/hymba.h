@@ -77,7 +77,13 @@ typedef enum {
  * pseudocode ("实现细节"), read as one group: H heads of P = Di / H channels, one
  * dt = softplus(u + b[h]) and one A[h] per head, B and C shared, D per channel; x_proj
  * gives [u | B | C] (H + 2N rows of w_x), there is no w_dt and dt_rank is ignored.
- * Supported for bf16 with P = 64, H a multiple of 4 and d_state in {16, 32, 64, 128}. */
+ * Supported for bf16 with P = 64, H a multiple of 4 and d_state in {16, 32, 64, 128}.
+ *
+ * Branch normalisation.  norm_group = 0: each branch is RMS-normalised over its full
+ * width (the Chinese summary's RMSNorm per branch).  norm_group = g > 0: group
+ * normalisation, the variant the hybrid-architecture summary ("설계 통찰 / 아키텍처 변형")
+ * recommends for intra-layer hybrids, in groups of g channels; beta and the 0.5
+ * average apply as before. */
 typedef struct {
   int32_t d_model;      /* d                                                      */
   int32_t n_q_heads;    /* Hq                                                     */
@@ -95,6 +101,9 @@ typedef struct {
   float rms_eps;        /* RMSNorm epsilon, e.g. 1e-6                             */
   float softmax_scale;  /* 0 => 1/sqrt(head_dim)                                  */
   int32_t ssm_heads;    /* 0 = Mamba head; H > 0 = Mamba-2 head with H heads      */
+  int32_t norm_group;   /* 0 = RMSNorm over each branch; g > 0 = group norm in
+                           groups of g channels (a power of two, 8..512, dividing
+                           Hq*dh and Di): (v - mean) / sqrt(var + eps) per group   */
 } hymba_layer_desc;
 
 /* Weights (device).  n_in = Hq*dh + (kv_share ? 0 : 2*Hkv*dh) + 2*Di; column

@@ -93,6 +93,10 @@ def _weights_struct(addr=4096):
     (dict(ssm_heads=64, d_state=8), 2),
     (dict(ssm_heads=64, dtype="f32"), 2),
     (dict(dt_rank=0), 1),             # the Mamba head needs a dt rank
+    (dict(norm_group=-1), 1),
+    (dict(norm_group=24), 2),         # group size not a power of two
+    (dict(norm_group=1024), 2),       # wider than one wave's 512 channels
+    (dict(norm_group=4), 2),
 ])
 def test_prefill_rejects_bad_descriptors(lib, change, status):
     d = desc_of(1, **change)
