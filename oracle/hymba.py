@@ -83,6 +83,7 @@ __all__ = [
     "attention", "ssm_params", "selective_scan", "ssm_alpha", "ssm_mixing_form",
     "gate", "fuse", "out_proj", "prefill_sequence", "prefill", "decode_step",
     "visible", "ssm2_params", "ssm2_scan", "ssd_matrix_form", "group_normalize",
+    "rms_norm_weighted", "ffn", "block_prefill", "block_decode_step",
 ]
 
 
@@ -513,3 +514,62 @@ def decode_step(dims, w, x_new, k_meta, v_meta, k_ring, v_ring, h, pos,
         y[b] = out_proj(F, w.w_out)[0]
         pos[b] = p + 1
     return {"y": y, "k": k_ring, "v": v_ring, "h": h, "pos": pos}
+
+
+# ---------------------------------------------------------------------------
+# block wrapper (pre-norm, residual, FFN)
+# ---------------------------------------------------------------------------
+# [HYMBA-ZH] 实现细节 prints the layer's configuration with an FFN intermediate size; the
+# block around the layer is otherwise not printed.  Reading: a pre-norm residual block,
+#     u   = x + Layer(rms(x) * g1)                 (over every row, meta rows included)
+#     out = u + FFN(rms(u) * g2),   FFN(v) = W_down SiLU(W_up v)
+# with W_up [I, d], W_down [d, I], I the intermediate size, learnable RMSNorm weights
+# g1, g2 [d], and SiLU, the one activation the pages use.
+
+def rms_norm_weighted(v, g, eps: float):
+    """RMSNorm of each row with a learnable weight: rms(v) * g."""
+    return rms_normalize(v, eps) * np.asarray(g, np.float64)
+
+
+def ffn(v, w_up, w_down):
+    """FFN(v) = W_down SiLU(W_up v) per row (the block reading above)."""
+    h = silu(np.asarray(v, np.float64) @ np.asarray(w_up, np.float64).T)
+    return h @ np.asarray(w_down, np.float64).T
+
+
+def _ffn_rows(u, bw, eps, contract):
+    vn = _rnd(rms_norm_weighted(u, bw.norm2, eps), contract)
+    h = _rnd(silu(vn @ np.asarray(bw.w_up, np.float64).T), contract)
+    return u + h @ np.asarray(bw.w_down, np.float64).T
+
+
+def block_prefill(dims, w, bw, meta, X, contract: bool = False,
+                  ring_slots: Optional[int] = None):
+    """The block over [meta; X_b] for every sequence b.  bw: norm1, norm2 [d], w_up
+    [I, d], w_down [d, I].  Returns y [B, L, d], y_meta [B, M, d], and the layer's cache
+    and state outputs (as prefill)."""
+    eps = dims.rms_eps
+    meta = np.asarray(meta, np.float64)
+    X = np.asarray(X, np.float64)
+    mn = _rnd(rms_norm_weighted(meta, bw.norm1, eps), contract)
+    xn = _rnd(rms_norm_weighted(X, bw.norm1, eps), contract)
+    out = prefill(dims, w, mn, xn, contract=contract, ring_slots=ring_slots)
+    u = _rnd(X + _rnd(out["y"], contract), contract)
+    um = _rnd(meta[None] + _rnd(out["y_meta"], contract), contract)
+    out["y"] = _ffn_rows(u, bw, eps, contract)
+    out["y_meta"] = _ffn_rows(um, bw, eps, contract)
+    return out
+
+
+def block_decode_step(dims, w, bw, x_new, k_meta, v_meta, k_ring, v_ring, h, pos,
+                      contract: bool = False):
+    """One block step per sequence: the layer's decode step on rms(x_new) * g1, then the
+    residual, the FFN and its residual (as block_prefill)."""
+    eps = dims.rms_eps
+    x_new = np.asarray(x_new, np.float64)
+    xn = _rnd(rms_norm_weighted(x_new, bw.norm1, eps), contract)
+    out = decode_step(dims, w, xn, k_meta, v_meta, k_ring, v_ring, h, pos, contract=contract)
+    u = _rnd(x_new + _rnd(out["y"], contract), contract)
+    out["y"] = _ffn_rows(u, bw, eps, contract)
+    return out
+

@@ -205,3 +205,32 @@ def gen_decode_state(dims: LayerDims, case_id: int, batch: int, ring_slots: int,
         pos = np.full((batch,), prior_tokens, np.int32)
     out["pos"] = np.asarray(pos, np.int32)
     return out
+
+
+@dataclasses.dataclass
+class BlockWeights:
+    """The block wrapper around a layer: RMSNorm weights before the layer and before the
+    FFN, and the FFN's two projections (float32 values the device sees, plus torch)."""
+    norm1: np.ndarray   # [d] fp32
+    norm2: np.ndarray   # [d] fp32
+    w_up: np.ndarray    # [I, d]
+    w_down: np.ndarray  # [d, I]
+    torch: Dict[str, object]
+
+
+def gen_block_weights(dims: LayerDims, case_id: int, intermediate: int, layer: int = 0,
+                      std: float = 0.02) -> BlockWeights:
+    """Norm weights ~ 1 + N(0, 0.1); W_up, W_down ~ N(0, std).  Stream role 300 + layer."""
+    g = rng(case_id, 300 + layer)
+    d = dims.d_model
+    n1 = (1.0 + 0.1 * g.standard_normal(size=(d,))).astype(np.float32)
+    n2 = (1.0 + 0.1 * g.standard_normal(size=(d,))).astype(np.float32)
+    up = _normal(g, (intermediate, d), std)
+    down = _normal(g, (d, intermediate), std)
+    tt, vals = {}, {}
+    for name, arr in (("w_up", up), ("w_down", down)):
+        tt[name], vals[name] = to_storage(arr, dims.dtype)
+    for name, arr in (("norm1", n1), ("norm2", n2)):
+        tt[name], vals[name] = to_storage(arr, F32)
+    return BlockWeights(torch=tt, **vals)
+
