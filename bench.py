@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 16-layer partial-SWA vs all-global stack comparison")
     ap.add_argument("--no-head-ssm", action="store_true",
-                    help="skip the layer variants (Mamba-2 head, group-norm fusion)")
+                    help="skip the layer variants (Mamba-2 head, group-norm fusion, block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the prefill workload the CPU oracle runs (8 = all)")
@@ -302,10 +302,11 @@ def main():
     if not args.no_stack:
         stack = bench_stack(hy, torch, dev)
 
-    head_ssm = group_norm = None
+    head_ssm = group_norm = block = None
     if not args.no_head_ssm:
         head_ssm = bench_head_ssm(hy, torch, dev, args, stages)
         group_norm = bench_group_norm(hy, torch, dev, args, stages)
+        block = bench_block(hy, torch, dev, args, ms_per_step)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -327,6 +328,7 @@ def main():
         "stack": stack,
         "head_ssm": head_ssm,
         "group_norm": group_norm,
+        "block": block,
         "stages": stage_report,
     }
     print(json.dumps(out), flush=True)
@@ -365,6 +367,54 @@ def prefill_variant(hy, torch, dev, args, dims, seed):
     del layer
     torch.cuda.empty_cache()
     return ms, stages
+
+
+def bench_block(hy, torch, dev, args, layer_ms):
+    """The prefill workload through the block wrapper: pre-norm, the layer, residual, FFN
+    (intermediate 5632, SiLU), residual.  Reports the step, the FFN's two GEMMs against
+    the bf16 MFMA peak, and the block's cost over the bare layer."""
+    from synth import CASES, gen_block_weights, gen_layer_weights
+    case = CASES[1]
+    dims, inter = case.dims, 5632
+    B, L, M = case.batch, case.seq_len, dims.n_meta
+    log(f"[bench] block wrapper: intermediate={inter}")
+    w = gen_layer_weights(dims, case.case_id)
+    bw = gen_block_weights(dims, case.case_id, inter)
+    blk = hy.HymbaBlock(dims, w.torch, bw.torch, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1007)
+    meta = torch.randn(M, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    x = torch.randn(B, L, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    y = torch.empty(B, L, dims.d_model, dtype=torch.bfloat16, device=dev)
+    y_meta = torch.empty(M, dims.d_model, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        blk.prefill(meta, x, y=y, y_meta=y_meta, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    stages = stage_pass(hy, torch, step, max(3, args.steps // 2), 1 << hy.STAGES.index("block"))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    rows = M + B * L
+    ffn_flop = 2 * 2 * rows * dims.d_model * inter
+    blk_ms = stages["block"]["avg_ms"] * stages["block"]["per_step"]
+    del blk
+    torch.cuda.empty_cache()
+    log(f"[bench] block wrapper: prefill {ms:.3f} ms ({B * L / ms / 1e3:.3f} M tok/s), "
+        f"wrapper kernels {blk_ms:.3f} ms per step")
+    return {"workload": "the prefill workload through the block wrapper (pre-norm, residual, "
+                        "FFN with intermediate 5632 and SiLU)",
+            "prefill_ms": round(ms, 4), "prefill_tokens_per_s": round(B * L / ms * 1e3, 1),
+            "layer_prefill_ms": round(layer_ms, 4),
+            "wrapper_ms_per_step": round(blk_ms, 4),
+            "ffn_flop_per_step": ffn_flop,
+            "ffn_and_norms_tflops": round(ffn_flop / (blk_ms * 1e-3) / 1e12, 1)}
 
 
 def bench_group_norm(hy, torch, dev, args, default_stages):

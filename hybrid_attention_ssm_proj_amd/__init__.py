@@ -13,6 +13,8 @@ from typing import Optional
 
 __all__ = [
     "MetaCache", "hymba_layer_meta_cache_build", "hymba_layer_prefill_cached",
+    "BlockWeights", "HymbaBlock", "hymba_block_workspace_bytes", "hymba_block_prefill",
+    "hymba_block_decode",
     "hymba_op_attn", "hymba_op_attn_workspace_bytes", "hymba_op_scan",
     "hymba_op_scan_workspace_bytes",
     "HymbaError", "LayerDesc", "LayerWeights", "KV", "SSMState", "load_library",
@@ -27,7 +29,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE",
           4: "ERR_ALIGNMENT", 5: "ERR_HIP"}
 STAGES = ["in_proj", "attn", "x_proj", "dt_proj", "scan", "norm", "out_proj", "kv_write",
-          "meta", "misc"]
+          "meta", "misc", "block"]
 
 
 class HymbaError(RuntimeError):
@@ -54,6 +56,11 @@ class LayerDesc(ctypes.Structure):
                    DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, dims.rms_eps,
                    dims.softmax_scale, getattr(dims, "ssm_heads", 0),
                    getattr(dims, "norm_group", 0))
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [("norm1", ctypes.c_void_p), ("norm2", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("intermediate", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -102,6 +109,14 @@ def load_library() -> ctypes.CDLL:
                                              ctypes.POINTER(MetaCache), P, I32, I32,
                                              ctypes.POINTER(KV), ctypes.POINTER(KV),
                                              ctypes.POINTER(SSMState), P, P, SZ, P]),
+        "hymba_block_workspace_bytes": (SZ, [ctypes.POINTER(LayerDesc), I32, I32, I32, I32]),
+        "hymba_block_prefill": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                      ctypes.POINTER(BlockWeights), P, P, I32, I32,
+                                      ctypes.POINTER(KV), ctypes.POINTER(KV),
+                                      ctypes.POINTER(SSMState), P, P, P, SZ, P]),
+        "hymba_block_decode": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                     ctypes.POINTER(BlockWeights), P, I32, ctypes.POINTER(KV),
+                                     ctypes.POINTER(SSMState), P, P, SZ, P]),
         "hymba_status_str": (ctypes.c_char_p, [I32]),
         "hymba_abi_version": (I32, []),
         "hymba_last_hip_error": (I32, []),
@@ -208,6 +223,33 @@ def hymba_layer_prefill_cached(desc, weights, cache, x, batch, seq_len, kv_in, k
         _stream(stream))
     if check:
         _check(st, "hymba_layer_prefill_cached")
+    return st
+
+
+def hymba_block_workspace_bytes(desc: LayerDesc, intermediate: int, batch: int, seq_len: int,
+                                mode: int) -> int:
+    return load_library().hymba_block_workspace_bytes(ctypes.byref(desc), intermediate, batch,
+                                                      seq_len, mode)
+
+
+def hymba_block_prefill(desc, weights, block, meta, x, batch, seq_len, kv_in, kv_out, state_out,
+                        y, y_meta, workspace, workspace_bytes, stream=None, check=True) -> int:
+    st = load_library().hymba_block_prefill(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(block), _ptr(meta), _ptr(x),
+        batch, seq_len, _ref(kv_in), _ref(kv_out), _ref(state_out), _ptr(y), _ptr(y_meta),
+        _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "hymba_block_prefill")
+    return st
+
+
+def hymba_block_decode(desc, weights, block, x, batch, kv, state, y, workspace, workspace_bytes,
+                       stream=None, check=True) -> int:
+    st = load_library().hymba_block_decode(
+        ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(block), _ptr(x), batch, _ref(kv),
+        _ref(state), _ptr(y), _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "hymba_block_decode")
     return st
 
 
@@ -354,6 +396,45 @@ class HymbaLayer:
         nb = hymba_layer_workspace_bytes(self.desc, B, kv.slots, 1)
         ws = self.workspace(nb)
         hymba_layer_decode(self.desc, self.weights, x, B, kv, state, y, ws, ws.numel(), stream)
+        return y
+
+
+class HymbaBlock(HymbaLayer):
+    """The layer inside its block wrapper (pre-norm, residual, FFN).  `bw` maps norm1,
+    norm2, w_up, w_down to device tensors."""
+
+    def __init__(self, dims, w: dict, bw: dict, device="cuda"):
+        super().__init__(dims, w, device=device)
+        self.bw = {k: v.to(device).contiguous() for k, v in bw.items()}
+        self.inter = int(self.bw["w_up"].shape[0])
+        self.block = BlockWeights(self.bw["norm1"].data_ptr(), self.bw["norm2"].data_ptr(),
+                                  self.bw["w_up"].data_ptr(), self.bw["w_down"].data_ptr(),
+                                  self.inter)
+
+    def prefill(self, meta, x, kv_in: Optional[KV] = None, kv_out: Optional[KV] = None,
+                state_out: Optional[SSMState] = None, y=None, y_meta=None, stream=None):
+        import torch
+        B, L = x.shape[0], x.shape[1]
+        d = self.dims.d_model
+        if y is None:
+            y = torch.empty(B, L, d, dtype=self.store, device=self.device)
+        if y_meta is None:
+            y_meta = torch.empty(self.dims.n_meta, d, dtype=self.store, device=self.device)
+        nb = hymba_block_workspace_bytes(self.desc, self.inter, B, L, 0)
+        ws = self.workspace(nb)
+        hymba_block_prefill(self.desc, self.weights, self.block, meta, x, B, L, kv_in, kv_out,
+                            state_out, y, y_meta, ws, ws.numel(), stream)
+        return y, y_meta
+
+    def decode(self, x, kv: KV, state: SSMState, y=None, stream=None):
+        import torch
+        B = x.shape[0]
+        if y is None:
+            y = torch.empty(B, self.dims.d_model, dtype=self.store, device=self.device)
+        nb = hymba_block_workspace_bytes(self.desc, self.inter, B, kv.slots, 1)
+        ws = self.workspace(nb)
+        hymba_block_decode(self.desc, self.weights, self.block, x, B, kv, state, y, ws,
+                           ws.numel(), stream)
         return y
 
 

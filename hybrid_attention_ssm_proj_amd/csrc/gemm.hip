@@ -51,7 +51,7 @@ struct Epilogue {
   __device__ __forceinline__ void operator()(int m, int n, const float v[4], int M, int N) const {
     if (m >= M || n >= N) return;
     const int valid = N - n;
-    if constexpr (K == EpiKind::Store) {
+    if constexpr (K == EpiKind::Store || K == EpiKind::Silu || K == EpiKind::AddStore) {
       T* base;
       int64_t ld;
       int mm;
@@ -66,7 +66,14 @@ struct Epilogue {
       }
       if (base == nullptr) return;
       T* p = base + mm * ld + n;
-      store4<T>(p, v, valid, ((uintptr_t)p & (4 * sizeof(T) - 1)) == 0);
+      float w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w[r] = v[r];
+        if constexpr (K == EpiKind::Silu) w[r] = silu_f(v[r]);
+        if constexpr (K == EpiKind::AddStore) w[r] = r < valid ? to_f32(p[r]) + v[r] : 0.f;
+      }
+      store4<T>(p, w, valid, ((uintptr_t)p & (4 * sizeof(T) - 1)) == 0);
     } else if constexpr (K == EpiKind::StoreF32) {
       float* p = (float*)o.c0 + m * o.ldc0 + n;
       store4<float>(p, v, valid, ((uintptr_t)p & 15) == 0);
@@ -90,7 +97,7 @@ struct Epilogue {
   // destination of the storage type, written with 16-byte stores (Store; XProj when the
   // tile lies in the delta columns).  The caller checks the bounds.
   __device__ __forceinline__ bool tile_fast(int m0, int m1, int n0, int n1) const {
-    if constexpr (K == EpiKind::Store) {
+    if constexpr (K == EpiKind::Store || K == EpiKind::Silu || K == EpiKind::AddStore) {
       const bool first = m1 <= o.c_split;
       if (!first && m0 < o.c_split) return false;
       const T* base = (const T*)(first ? o.c0 : o.c1);
@@ -104,16 +111,29 @@ struct Epilogue {
   }
   // Output (m, n..n+7) = lo[0..3], hi[0..3]; valid after tile_fast() returned true.
   __device__ __forceinline__ void store8(int m, int n, const float lo[4], const float hi[4]) const {
-    if constexpr (K == EpiKind::Store || K == EpiKind::XProj) {
+    if constexpr (K == EpiKind::Store || K == EpiKind::XProj || K == EpiKind::Silu ||
+                  K == EpiKind::AddStore) {
       const bool first = K == EpiKind::XProj || m < o.c_split;
       T* p = (T*)(first ? o.c0 : o.c1) + (int64_t)(first ? m : m - o.c_split) *
                                              (first ? o.ldc0 : o.ldc1) + n;
-      bf16x8 w;
+      float v[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        w[r] = (bf16)lo[r];
-        w[4 + r] = (bf16)hi[r];
+        v[r] = lo[r];
+        v[4 + r] = hi[r];
       }
+      if constexpr (K == EpiKind::Silu) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = silu_f(v[e]);
+      }
+      if constexpr (K == EpiKind::AddStore) {
+        const bf16x8 old = *(const bf16x8*)p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += (float)old[e];
+      }
+      bf16x8 w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = (bf16)v[e];
       *(bf16x8*)p = w;
     }
   }
@@ -871,7 +891,9 @@ static hipError_t dispatch_bf16(const GemmOperands& op, const Epi& epi, GemmShap
                                 hipStream_t s) {
   switch (shape) {
     case GemmShape::Large:
-      if constexpr (std::is_same_v<Epi, Epilogue<bf16, EpiKind::Store>>) {
+      if constexpr (std::is_same_v<Epi, Epilogue<bf16, EpiKind::Store>> ||
+                    std::is_same_v<Epi, Epilogue<bf16, EpiKind::Silu>> ||
+                    std::is_same_v<Epi, Epilogue<bf16, EpiKind::AddStore>>) {
         const bool one_src = op.a_split >= op.M;
         const bool fits32 = (int64_t)op.M * op.lda0 < (1ll << 31) && (int64_t)op.N * op.ldb < (1ll << 31);
         if (op.K % 64 == 0 && one_src && fits32) {
@@ -917,12 +939,18 @@ hipError_t launch_gemm_bf16_rowscaled(const GemmOperands& op, const GemmOutput& 
 hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmShape shape,
                             hipStream_t s) {
   if (op.M <= 0 || op.N <= 0) return hipSuccess;
-  // The wide tile is kept for plain stores; epilogues with per-element math use the
+  // The wide tile is kept for stores (plain, SiLU, add); the fp32 epilogues use the
   // narrower tiles (fewer live accumulators, no spills).
-  if (shape == GemmShape::Large && out.kind != EpiKind::Store) shape = GemmShape::Narrow;
+  if (shape == GemmShape::Large && out.kind != EpiKind::Store && out.kind != EpiKind::Silu &&
+      out.kind != EpiKind::AddStore)
+    shape = GemmShape::Narrow;
   switch (out.kind) {
     case EpiKind::Store:
       return dispatch_bf16(op, Epilogue<bf16, EpiKind::Store>{out}, shape, s);
+    case EpiKind::Silu:
+      return dispatch_bf16(op, Epilogue<bf16, EpiKind::Silu>{out}, shape, s);
+    case EpiKind::AddStore:
+      return dispatch_bf16(op, Epilogue<bf16, EpiKind::AddStore>{out}, shape, s);
     case EpiKind::StoreF32:
       return dispatch_bf16(op, Epilogue<bf16, EpiKind::StoreF32>{out}, shape, s);
     case EpiKind::XProj:
@@ -998,6 +1026,12 @@ hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStr
       break;
     case EpiKind::XProj:
       run_f32(op, Epilogue<float, EpiKind::XProj>{out}, nblk, s);
+      break;
+    case EpiKind::Silu:
+      run_f32(op, Epilogue<float, EpiKind::Silu>{out}, nblk, s);
+      break;
+    case EpiKind::AddStore:
+      run_f32(op, Epilogue<float, EpiKind::AddStore>{out}, nblk, s);
       break;
     default:
       run_f32(op, Epilogue<float, EpiKind::Softplus>{out}, nblk, s);

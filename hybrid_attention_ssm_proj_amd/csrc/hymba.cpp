@@ -977,4 +977,158 @@ hymba_status hymba_op_copy(const void* src, void* dst, size_t bytes, void* strea
   return e == hipSuccess ? HYMBA_OK : fail_hip(e);
 }
 
+
 }  // extern "C"
+
+// ----------------------------------------------------------------- block wrapper
+
+namespace {
+
+// Workspace of a block call: the layer's, then xn (the pre-normed rows), v (the
+// pre-normed residual rows) and h (the FFN's hidden rows), all in the storage type.
+struct BlockCarve {
+  size_t layer, xn, v, h, total;
+};
+
+BlockCarve carve_block(const Shape& s, size_t layer_bytes, int64_t rows, int inter) {
+  BlockCarve c{};
+  c.layer = 0;
+  size_t off = align_up(layer_bytes);
+  c.xn = off;
+  off = align_up(off + (size_t)rows * s.d * s.es);
+  c.v = off;
+  off = align_up(off + (size_t)rows * s.d * s.es);
+  c.h = off;
+  off = align_up(off + (size_t)rows * inter * s.es);
+  c.total = off;
+  return c;
+}
+
+hymba_status check_block(const Shape& s, const hymba_block_weights* bw) {
+  if (bw == nullptr || !bw->norm1 || !bw->norm2 || !bw->w_up || !bw->w_down ||
+      bw->intermediate <= 0)
+    return HYMBA_ERR_INVALID_ARG;
+  if (bw->intermediate % 8) return HYMBA_ERR_UNSUPPORTED;
+  if (any_misaligned(bw->norm1, bw->norm2, bw->w_up, bw->w_down)) return HYMBA_ERR_ALIGNMENT;
+  (void)s;
+  return HYMBA_OK;
+}
+
+// The FFN half of the block over `rows` rows of v (contiguous): h = SiLU(v W_up^T), then
+// out += h W_down^T into c0 (rows < split) / c1 (the rest).
+hymba_status block_ffn(const Shape& s, const hymba_block_weights* bw, const void* v, void* h,
+                       int rows, void* c0, int64_t ldc0, void* c1, int64_t ldc1, int split,
+                       bool skinny, hipStream_t stream) {
+  const int I = bw->intermediate;
+  auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
+    return s.bf16 ? launch_gemm_bf16(op, out, skinny ? GemmShape::Skinny : GemmShape::Large,
+                                     stream)
+                  : launch_gemm_f32(op, out, stream);
+  };
+  {
+    GemmOperands op{v, s.d, nullptr, 0, rows, bw->w_up, s.d, rows, I, s.d};
+    GemmOutput out{EpiKind::Silu, h, I, nullptr, 0, rows, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, gemm(op, out));
+  }
+  {
+    GemmOperands op{h, I, nullptr, 0, rows, bw->w_down, I, rows, s.d, I};
+    GemmOutput out{EpiKind::AddStore, c0, ldc0, c1, ldc1, split, 0, nullptr};
+    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, gemm(op, out));
+  }
+  return HYMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hymba_block_workspace_bytes(const hymba_layer_desc* desc, int32_t intermediate,
+                                   int32_t batch, int32_t seq_len, int32_t mode) {
+  Shape s;
+  if (make_shape(desc, s) != HYMBA_OK || intermediate <= 0 || intermediate % 8) return 0;
+  if (mode != 0 && mode != 1) return 0;
+  const size_t lb = hymba_layer_workspace_bytes(desc, batch, seq_len, mode);
+  if (lb == 0) return 0;
+  const int64_t rows = mode == 0 ? (int64_t)s.M + (int64_t)batch * seq_len : batch;
+  return carve_block(s, lb, rows, intermediate).total;
+}
+
+hymba_status hymba_block_prefill(const hymba_layer_desc* desc, const hymba_layer_weights* w,
+                                 const hymba_block_weights* bw, const void* meta,
+                                 const void* x, int32_t batch, int32_t seq_len,
+                                 const hymba_kv* kv_in, hymba_kv* kv_out,
+                                 hymba_ssm_state* state_out, void* y, void* y_meta,
+                                 void* workspace, size_t workspace_bytes, void* stream_) {
+  Shape s;
+  hymba_status st = make_shape(desc, s);
+  if (st != HYMBA_OK) return st;
+  if ((st = check_block(s, bw)) != HYMBA_OK) return st;
+  if (batch < 0 || seq_len < 0) return HYMBA_ERR_INVALID_ARG;
+  const int B = batch, L = seq_len, M = s.M;
+  const int64_t BL = (int64_t)B * L, rows = M + BL;
+  if ((BL > 0 && (x == nullptr || y == nullptr)) || (M > 0 && meta == nullptr))
+    return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
+  const size_t lb = hymba_layer_workspace_bytes(desc, B, L, 0);
+  const BlockCarve cv = carve_block(s, lb, rows, bw->intermediate);
+  if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
+  if (rows == 0) return HYMBA_OK;
+  hipStream_t stream = (hipStream_t)stream_;
+  const bool b16 = s.bf16;
+  char* xn = ws_ptr(workspace, cv.xn);
+  char* v = ws_ptr(workspace, cv.v);
+  char* hbuf = ws_ptr(workspace, cv.h);
+  const size_t rb = (size_t)s.d * s.es;  // bytes per row
+  const float eps = desc->rms_eps;
+  // pre-norm of [meta; X] into xn (meta rows first)
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_rms_norm_rows(b16, meta, s.d, xn, s.d, M, s.d,
+                                                      bw->norm1, eps, stream));
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_rms_norm_rows(b16, x, s.d, xn + M * rb, s.d, (int)BL,
+                                                      s.d, bw->norm1, eps, stream));
+  // the layer on the normed rows: its outputs land in y / y_meta
+  st = hymba_layer_prefill(desc, w, xn, xn + M * rb, batch, seq_len, kv_in, kv_out, state_out,
+                           y, y_meta, workspace, lb, stream_);
+  if (st != HYMBA_OK) return st;
+  // residuals (u over y / y_meta) and the FFN's pre-norm into v (meta rows first)
+  const int Mf = y_meta != nullptr ? M : 0;  // meta rows carried through the block
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_residual_norm(b16, meta, s.d, y_meta, s.d, v, s.d, Mf,
+                                                      s.d, bw->norm2, eps, stream));
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK,
+               launch_residual_norm(b16, x, s.d, y, s.d, v + Mf * rb, s.d, (int)BL, s.d,
+                                    bw->norm2, eps, stream));
+  return block_ffn(s, bw, v, hbuf, (int)(Mf + BL), y_meta, s.d, y, s.d, Mf, false, stream);
+}
+
+hymba_status hymba_block_decode(const hymba_layer_desc* desc, const hymba_layer_weights* w,
+                                const hymba_block_weights* bw, const void* x, int32_t batch,
+                                hymba_kv* kv, hymba_ssm_state* state, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream_) {
+  Shape s;
+  hymba_status st = make_shape(desc, s);
+  if (st != HYMBA_OK) return st;
+  if ((st = check_block(s, bw)) != HYMBA_OK) return st;
+  if (batch < 0 || kv == nullptr) return HYMBA_ERR_INVALID_ARG;
+  const int B = batch;
+  if (B > 0 && (x == nullptr || y == nullptr)) return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(x, y, workspace)) return HYMBA_ERR_ALIGNMENT;
+  const size_t lb = hymba_layer_workspace_bytes(desc, B, kv->slots, 1);
+  const BlockCarve cv = carve_block(s, lb, B, bw->intermediate);
+  if (B > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
+  if (B == 0) return HYMBA_OK;
+  hipStream_t stream = (hipStream_t)stream_;
+  const bool b16 = s.bf16;
+  char* xn = ws_ptr(workspace, cv.xn);
+  char* v = ws_ptr(workspace, cv.v);
+  char* hbuf = ws_ptr(workspace, cv.h);
+  const float eps = desc->rms_eps;
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_rms_norm_rows(b16, x, s.d, xn, s.d, B, s.d, bw->norm1,
+                                                      eps, stream));
+  st = hymba_layer_decode(desc, w, xn, batch, kv, state, y, workspace, lb, stream_);
+  if (st != HYMBA_OK) return st;
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_residual_norm(b16, x, s.d, y, s.d, v, s.d, B, s.d,
+                                                      bw->norm2, eps, stream));
+  return block_ffn(s, bw, v, hbuf, B, nullptr, s.d, y, s.d, 0, true, stream);
+}
+
+}  // extern "C"
+

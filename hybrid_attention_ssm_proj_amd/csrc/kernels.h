@@ -21,7 +21,7 @@ struct GemmOperands {
   int M, N, K;
 };
 
-enum class EpiKind { Store, StoreF32, XProj, Softplus };
+enum class EpiKind { Store, StoreF32, XProj, Softplus, Silu, AddStore };
 
 // Output description for the epilogues.
 //  Store:    rows < c_split -> c0 (stride ldc0, skipped if c0 == nullptr), others ->
@@ -30,6 +30,8 @@ enum class EpiKind { Store, StoreF32, XProj, Softplus };
 //  XProj:    columns < split_col -> c0 (storage type, stride ldc0), columns >= split_col
 //            -> c1 fp32 (stride ldc1, column - split_col).
 //  Softplus: fp32 c0[m, n] = softplus(acc + bias[n]).
+//  Silu:     as Store, of SiLU(acc).
+//  AddStore: as Store, of the destination's value plus acc (c += A B^T, in place).
 struct GemmOutput {
   EpiKind kind;
   void* c0;
@@ -216,6 +218,14 @@ hipError_t launch_ssm2_step(const SsmStepParams& p, hipStream_t s);  // bf16, he
 hipError_t launch_group_norm(bool bf16, void* f, int64_t f_stride, int rows, int wa, int ws,
                              const float* beta_a, const float* beta_s, float eps, int g,
                              hipStream_t s);
+// Block wrapper.  out[r, :] = rms(in[r, :]) * g (storage type, d % 8 == 0).
+hipError_t launch_rms_norm_rows(bool bf16, const void* in, int64_t in_ld, void* out,
+                                int64_t out_ld, int rows, int d, const float* g, float eps,
+                                hipStream_t s);
+// u = x + y written over y (rounded to the storage type), then v = rms(u) * g.
+hipError_t launch_residual_norm(bool bf16, const void* x, int64_t x_ld, void* y, int64_t y_ld,
+                                void* v, int64_t v_ld, int rows, int d, const float* g,
+                                float eps, hipStream_t s);
 // Decode: merge the split-key attention partials into F's attention columns (no norm).
 hipError_t launch_decode_combine(bool bf16, const float* part, int nsplit, void* f,
                                  int64_t f_stride, int B, int Hq, int head_dim, hipStream_t s);

@@ -120,6 +120,89 @@ hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int
   return hipGetLastError();
 }
 
+// Block wrapper norms: one workgroup per row, 8 elements per thread per pass.
+template <typename T>
+__global__ __launch_bounds__(256) void rms_norm_rows_kernel(const T* in, int64_t in_ld, T* out,
+                                                            int64_t out_ld, int d, const float* g,
+                                                            float eps) {
+  const T* r = in + (int64_t)blockIdx.x * in_ld;
+  T* o = out + (int64_t)blockIdx.x * out_ld;
+  float sq = 0.f, dummy = 0.f;
+  for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
+    float v[8];
+    Vec8<T>::load(r + i, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq = fmaf(v[e], v[e], sq);
+  }
+  block_sum2(sq, dummy);
+  const float sc = rsqrtf(sq / (float)d + eps);
+  for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
+    float v[8];
+    Vec8<T>::load(r + i, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * sc * g[i + e];
+    Vec8<T>::store(o + i, v);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void residual_norm_kernel(const T* x, int64_t x_ld, T* y,
+                                                            int64_t y_ld, T* v, int64_t v_ld,
+                                                            int d, const float* g, float eps) {
+  const T* xr = x + (int64_t)blockIdx.x * x_ld;
+  T* yr = y + (int64_t)blockIdx.x * y_ld;
+  T* vr = v + (int64_t)blockIdx.x * v_ld;
+  float sq = 0.f, dummy = 0.f;
+  for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
+    float a[8], b[8];
+    Vec8<T>::load(xr + i, a);
+    Vec8<T>::load(yr + i, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = to_f32(from_f32<T>(a[e] + b[e]));  // u as stored
+      sq = fmaf(b[e], b[e], sq);
+    }
+    Vec8<T>::store(yr + i, b);
+  }
+  block_sum2(sq, dummy);  // (its barrier also orders the u stores before the reads below)
+  const float sc = rsqrtf(sq / (float)d + eps);
+  for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
+    float u[8];
+    Vec8<T>::load(yr + i, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = u[e] * sc * g[i + e];
+    Vec8<T>::store(vr + i, u);
+  }
+}
+
+hipError_t launch_rms_norm_rows(bool bf16_, const void* in, int64_t in_ld, void* out,
+                                int64_t out_ld, int rows, int d, const float* g, float eps,
+                                hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 8) return hipErrorInvalidValue;
+  if (bf16_)
+    rms_norm_rows_kernel<bf16><<<dim3(rows), dim3(256), 0, s>>>((const bf16*)in, in_ld,
+                                                                (bf16*)out, out_ld, d, g, eps);
+  else
+    rms_norm_rows_kernel<float><<<dim3(rows), dim3(256), 0, s>>>((const float*)in, in_ld,
+                                                                 (float*)out, out_ld, d, g, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_norm(bool bf16_, const void* x, int64_t x_ld, void* y, int64_t y_ld,
+                                void* v, int64_t v_ld, int rows, int d, const float* g,
+                                float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 8) return hipErrorInvalidValue;
+  if (bf16_)
+    residual_norm_kernel<bf16><<<dim3(rows), dim3(256), 0, s>>>(
+        (const bf16*)x, x_ld, (bf16*)y, y_ld, (bf16*)v, v_ld, d, g, eps);
+  else
+    residual_norm_kernel<float><<<dim3(rows), dim3(256), 0, s>>>(
+        (const float*)x, x_ld, (float*)y, y_ld, (float*)v, v_ld, d, g, eps);
+  return hipGetLastError();
+}
+
 // Group normalisation of one row of F per workgroup.  A thread holds 8 channels; the
 // g / 8 threads of a group are adjacent lanes of one wave (g <= 512), so the group's
 // mean and then its variance about the mean are xor-shuffle sums over them.  The groups

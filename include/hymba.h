@@ -224,6 +224,48 @@ hymba_status hymba_layer_prefill_cached(const hymba_layer_desc *desc,
 size_t hymba_layer_workspace_bytes(const hymba_layer_desc *desc, int32_t batch,
                                    int32_t seq_len, int32_t mode);
 
+/* ---------------------------------------------------------------------------
+ * Block wrapper: the layer inside a pre-norm residual block with an FFN.  The Chinese
+ * summary's implementation details ("实现细节") print the layer's configuration with an
+ * FFN intermediate size and nothing else of the block; reading, over every row of
+ * [meta; X]:
+ *     u   = x + Layer(rms(x) * norm1)
+ *     out = u + W_down SiLU(W_up (rms(u) * norm2))
+ * with rms the RMSNorm of the descriptor's rms_eps, W_up [I, d], W_down [d, I] in the
+ * layer's dtype (I = intermediate, a multiple of 8) and norm1, norm2 [d] fp32.  The
+ * layer's meta input is rms(meta) * norm1; its y_meta feeds the meta rows' residual.
+ * Host structs, device pointers, 16-byte aligned. */
+typedef struct {
+  const float *norm1;   /* [d]    */
+  const float *norm2;   /* [d]    */
+  const void *w_up;     /* [I, d] */
+  const void *w_down;   /* [d, I] */
+  int32_t intermediate; /* I      */
+} hymba_block_weights;
+
+/* Workspace of the block calls: mode 0 = hymba_block_prefill for (batch, seq_len),
+ * mode 1 = hymba_block_decode for batch sequences with a ring of seq_len slots.  0 on
+ * an invalid descriptor or intermediate size. */
+size_t hymba_block_workspace_bytes(const hymba_layer_desc *desc, int32_t intermediate,
+                                   int32_t batch, int32_t seq_len, int32_t mode);
+
+/* The block over [meta; X_b] for every sequence b: arguments as hymba_layer_prefill
+ * (kv_in, kv_out, state_out are the layer's), plus bw.  y [B, L, d] receives the block
+ * output; y_meta [M, d] (may be NULL: the meta rows' block outputs are then skipped)
+ * the meta rows'. */
+hymba_status hymba_block_prefill(const hymba_layer_desc *desc, const hymba_layer_weights *w,
+                                 const hymba_block_weights *bw, const void *meta,
+                                 const void *x, int32_t batch, int32_t seq_len,
+                                 const hymba_kv *kv_in, hymba_kv *kv_out,
+                                 hymba_ssm_state *state_out, void *y, void *y_meta,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* One block step per sequence: arguments as hymba_layer_decode, plus bw. */
+hymba_status hymba_block_decode(const hymba_layer_desc *desc, const hymba_layer_weights *w,
+                                const hymba_block_weights *bw, const void *x, int32_t batch,
+                                hymba_kv *kv, hymba_ssm_state *state, void *y,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 const char *hymba_status_str(hymba_status s);
 int32_t hymba_abi_version(void);
 /* Last hipError_t seen by a failing call on this thread (0 if none). */
@@ -248,7 +290,8 @@ typedef enum {
   HYMBA_STAGE_KV_WRITE = 7,  /* cache writes                                     */
   HYMBA_STAGE_META = 8,      /* in_proj and out_proj GEMMs over the meta rows   */
   HYMBA_STAGE_MISC = 9,      /* accumulator clears, format conversions, pos fill */
-  HYMBA_NUM_STAGES = 10
+  HYMBA_STAGE_BLOCK = 10,    /* block wrapper: pre-norms, residuals, FFN GEMMs    */
+  HYMBA_NUM_STAGES = 11
 } hymba_stage;
 
 hymba_status hymba_timer_enable(int32_t stage_mask);
