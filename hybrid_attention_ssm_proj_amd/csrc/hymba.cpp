@@ -987,10 +987,23 @@ namespace {
 // Workspace of a block call: the layer's, then xn (the pre-normed rows), v (the
 // pre-normed residual rows) and h (the FFN's hidden rows), all in the storage type.
 struct BlockCarve {
-  size_t layer, xn, v, h, total;
+  size_t layer, xn, v, h, acc, total;
 };
 
-BlockCarve carve_block(const Shape& s, size_t layer_bytes, int64_t rows, int inter) {
+// FFN down-projections over few rows (the meta rows of a prefill, a decode batch) split
+// K = intermediate into fp32 partial slices, summed onto the residual by the row store.
+bool ffn_down_splitk(const Shape& s, int inter) {
+  return s.bf16 && inter % 256 == 0 && s.d % 64 == 0;
+}
+
+int ffn_down_slices(const Shape& s, int rows, int inter) {
+  if (rows <= 0 || !ffn_down_splitk(s, inter)) return 0;
+  return splitk_slices(inter, splitk_factor(rows, s.d, inter));
+}
+
+// few_rows: the rows that take the few-row down-projection (meta rows / the batch).
+BlockCarve carve_block(const Shape& s, size_t layer_bytes, int64_t rows, int inter,
+                       int few_rows) {
   BlockCarve c{};
   c.layer = 0;
   size_t off = align_up(layer_bytes);
@@ -1000,6 +1013,8 @@ BlockCarve carve_block(const Shape& s, size_t layer_bytes, int64_t rows, int int
   off = align_up(off + (size_t)rows * s.d * s.es);
   c.h = off;
   off = align_up(off + (size_t)rows * inter * s.es);
+  c.acc = off;
+  off = align_up(off + (size_t)ffn_down_slices(s, few_rows, inter) * few_rows * s.d * 4);
   c.total = off;
   return c;
 }
@@ -1014,27 +1029,41 @@ hymba_status check_block(const Shape& s, const hymba_block_weights* bw) {
   return HYMBA_OK;
 }
 
-// The FFN half of the block over `rows` rows of v (contiguous): h = SiLU(v W_up^T), then
-// out += h W_down^T into c0 (rows < split) / c1 (the rest).
-hymba_status block_ffn(const Shape& s, const hymba_block_weights* bw, const void* v, void* h,
-                       int rows, void* c0, int64_t ldc0, void* c1, int64_t ldc1, int split,
-                       bool skinny, hipStream_t stream) {
+// The FFN's two GEMMs.  ffn_up: h = SiLU(v W_up^T) over `rows` rows of v (contiguous).
+// ffn_down: out += h W_down^T over `rows` rows of h, written to c (leading dimension ldc).
+hipError_t ffn_gemm(const Shape& s, const GemmOperands& op, const GemmOutput& out, bool skinny,
+                    hipStream_t stream) {
+  return s.bf16 ? launch_gemm_bf16(op, out, skinny ? GemmShape::Skinny : GemmShape::Large, stream)
+                : launch_gemm_f32(op, out, stream);
+}
+
+hymba_status ffn_up(const Shape& s, const hymba_block_weights* bw, const void* v, void* h,
+                    int rows, bool skinny, hipStream_t stream) {
   const int I = bw->intermediate;
-  auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
-    return s.bf16 ? launch_gemm_bf16(op, out, skinny ? GemmShape::Skinny : GemmShape::Large,
-                                     stream)
-                  : launch_gemm_f32(op, out, stream);
-  };
-  {
-    GemmOperands op{v, s.d, nullptr, 0, rows, bw->w_up, s.d, rows, I, s.d};
-    GemmOutput out{EpiKind::Silu, h, I, nullptr, 0, rows, 0, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, gemm(op, out));
+  GemmOperands op{v, s.d, nullptr, 0, rows, bw->w_up, s.d, rows, I, s.d};
+  GemmOutput out{EpiKind::Silu, h, I, nullptr, 0, rows, 0, nullptr};
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, ffn_gemm(s, op, out, skinny, stream));
+  return HYMBA_OK;
+}
+
+// few: the rows are few (the meta rows, a decode batch); c is then contiguous (ldc = d)
+// and, where ffn_down_splitk holds, K is split into fp32 partials at acc.
+hymba_status ffn_down(const Shape& s, const hymba_block_weights* bw, const void* h, int rows,
+                      void* c, int64_t ldc, bool few, float* acc, hipStream_t stream) {
+  const int I = bw->intermediate;
+  GemmOperands op{h, I, nullptr, 0, rows, bw->w_down, I, rows, s.d, I};
+  const int slices = few ? ffn_down_slices(s, rows, I) : 0;
+  if (slices > 0) {
+    const int64_t stride = (int64_t)rows * s.d;
+    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_gemm_bf16_splitk(op, acc, s.d,
+                                                           splitk_factor(rows, s.d, I), stream,
+                                                           stride));
+    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK,
+                 launch_store_rows(true, acc, c, rows, s.d, stream, slices, stride, true));
+    return HYMBA_OK;
   }
-  {
-    GemmOperands op{h, I, nullptr, 0, rows, bw->w_down, I, rows, s.d, I};
-    GemmOutput out{EpiKind::AddStore, c0, ldc0, c1, ldc1, split, 0, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, gemm(op, out));
-  }
+  GemmOutput out{EpiKind::AddStore, c, ldc, nullptr, 0, rows, 0, nullptr};
+  HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, ffn_gemm(s, op, out, few, stream));
   return HYMBA_OK;
 }
 
@@ -1050,7 +1079,7 @@ size_t hymba_block_workspace_bytes(const hymba_layer_desc* desc, int32_t interme
   const size_t lb = hymba_layer_workspace_bytes(desc, batch, seq_len, mode);
   if (lb == 0) return 0;
   const int64_t rows = mode == 0 ? (int64_t)s.M + (int64_t)batch * seq_len : batch;
-  return carve_block(s, lb, rows, intermediate).total;
+  return carve_block(s, lb, rows, intermediate, mode == 0 ? s.M : batch).total;
 }
 
 hymba_status hymba_block_prefill(const hymba_layer_desc* desc, const hymba_layer_weights* w,
@@ -1070,7 +1099,7 @@ hymba_status hymba_block_prefill(const hymba_layer_desc* desc, const hymba_layer
     return HYMBA_ERR_INVALID_ARG;
   if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
   const size_t lb = hymba_layer_workspace_bytes(desc, B, L, 0);
-  const BlockCarve cv = carve_block(s, lb, rows, bw->intermediate);
+  const BlockCarve cv = carve_block(s, lb, rows, bw->intermediate, M);
   if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   if (rows == 0) return HYMBA_OK;
   hipStream_t stream = (hipStream_t)stream_;
@@ -1096,7 +1125,16 @@ hymba_status hymba_block_prefill(const hymba_layer_desc* desc, const hymba_layer
   HYMBA_LAUNCH(HYMBA_STAGE_BLOCK,
                launch_residual_norm(b16, x, s.d, y, s.d, v + Mf * rb, s.d, (int)BL, s.d,
                                     bw->norm2, eps, stream));
-  return block_ffn(s, bw, v, hbuf, (int)(Mf + BL), y_meta, s.d, y, s.d, Mf, false, stream);
+  // The up-projection takes the meta and X rows in one launch.  The down-projection's
+  // output has d columns only, so its tiles over the X rows fill whole waves when B*L is a
+  // multiple of the tile height; the meta rows take the few-row tiles in a launch of their
+  // own instead of adding a nearly empty wave.
+  if ((st = ffn_up(s, bw, v, hbuf, (int)(Mf + BL), false, stream)) != HYMBA_OK) return st;
+  const size_t hb = (size_t)bw->intermediate * s.es;  // bytes per row of h
+  if ((st = ffn_down(s, bw, hbuf + Mf * hb, (int)BL, y, s.d, false, nullptr, stream)) !=
+      HYMBA_OK)
+    return st;
+  return ffn_down(s, bw, hbuf, Mf, y_meta, s.d, true, (float*)ws_ptr(workspace, cv.acc), stream);
 }
 
 hymba_status hymba_block_decode(const hymba_layer_desc* desc, const hymba_layer_weights* w,
@@ -1112,7 +1150,7 @@ hymba_status hymba_block_decode(const hymba_layer_desc* desc, const hymba_layer_
   if (B > 0 && (x == nullptr || y == nullptr)) return HYMBA_ERR_INVALID_ARG;
   if (any_misaligned(x, y, workspace)) return HYMBA_ERR_ALIGNMENT;
   const size_t lb = hymba_layer_workspace_bytes(desc, B, kv->slots, 1);
-  const BlockCarve cv = carve_block(s, lb, B, bw->intermediate);
+  const BlockCarve cv = carve_block(s, lb, B, bw->intermediate, B);
   if (B > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   if (B == 0) return HYMBA_OK;
   hipStream_t stream = (hipStream_t)stream_;
@@ -1127,7 +1165,8 @@ hymba_status hymba_block_decode(const hymba_layer_desc* desc, const hymba_layer_
   if (st != HYMBA_OK) return st;
   HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_residual_norm(b16, x, s.d, y, s.d, v, s.d, B, s.d,
                                                       bw->norm2, eps, stream));
-  return block_ffn(s, bw, v, hbuf, B, nullptr, s.d, y, s.d, 0, true, stream);
+  if ((st = ffn_up(s, bw, v, hbuf, B, true, stream)) != HYMBA_OK) return st;
+  return ffn_down(s, bw, hbuf, B, y, s.d, true, (float*)ws_ptr(workspace, cv.acc), stream);
 }
 
 }  // extern "C"

@@ -21,7 +21,11 @@ def _block(dims, w, bw):
     return hy.HymbaBlock(dims, dict(w.torch), dict(bw.torch), device=DEV)
 
 
-@pytest.mark.parametrize("inter,window,L,B", [(512, 0, 100, 2), (768, 40, 70, 3)])
+@pytest.mark.parametrize("inter,window,L,B", [
+    (512, 0, 100, 2),   # intermediate a multiple of 256: few-row down-projections split K
+    (768, 40, 70, 3),
+    (520, 0, 33, 2),    # not a multiple of 64: generic-K tiles, few rows without split-K
+])
 def test_block_prefill_and_decode_match_oracle(inter, window, L, B):
     dims = small_dims(window=window)
     S, steps = max(L, 1), 3
