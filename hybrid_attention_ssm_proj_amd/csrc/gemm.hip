@@ -850,10 +850,10 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
   out.vec = ((uintptr_t)z & 15) == 0 && ldz % 8 == 0 &&
             (k_col < 0 || (((uintptr_t)ring_k & 15) == 0 && ((uintptr_t)ring_v & 15) == 0 &&
                            head_dim % 8 == 0 && k_col % 8 == 0 && v_col % 8 == 0));
-  // 64-row blocks: twice the workgroups of one 128-row block per column tile (the
-  // weight slice is then read by two workgroups, mostly from L2)
-  dim3 grid((op.N + 63) / 64, 1, (op.M + 63) / 64);
-  gemm_bf16_fewrow_kernel<kFewStore, 64, 4><<<grid, dim3(256), 0, s>>>(op, out, op.K);
+  // 128-row blocks: each weight slice is streamed by one workgroup (64-row blocks, twice
+  // the workgroups, measured about 10% slower at 128 rows)
+  dim3 grid((op.N + 63) / 64, 1, (op.M + 127) / 128);
+  gemm_bf16_fewrow_kernel<kFewStore, 128, 4><<<grid, dim3(256), 0, s>>>(op, out, op.K);
   return hipGetLastError();
 }
 
