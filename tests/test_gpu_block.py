@@ -66,3 +66,25 @@ def test_block_fp32_prefill_matches_oracle():
     torch.cuda.synchronize()
     assert rel_err(to_np(y), ref["y"]) < TOL_F32
     assert rel_err(to_np(ym), ref["y_meta"][0]) < TOL_F32
+
+
+def test_block_full_size_sampled_sequence():
+    """The block around the prefill workload's layer with intermediate 5632 (the shape
+    the benchmark times), B=8, L=2048, 128 meta tokens, run on the whole batch; sequence 6
+    is recomputed by the oracle's block (y, y_meta and the final state)."""
+    case = CASES[1]
+    dims, inter = case.dims, 5632
+    B, L = case.batch, case.seq_len
+    w = gen_layer_weights(dims, case.case_id)
+    bw = gen_block_weights(dims, case.case_id, inter)
+    meta_t, meta, x_t, x = gen_activations(dims, case.case_id, B, L)
+    blk = _block(dims, w, bw)
+    st = alloc_state(dims, B)
+    y, ym = blk.prefill(meta_t.to(DEV), x_t.to(DEV), state_out=state_struct(st))
+    torch.cuda.synchronize()
+    b = 6
+    ref = orc.block_prefill(dims, w, bw, meta, x[b:b + 1], contract=True)
+    errs = {"y": rel_err(to_np(y[b]), ref["y"][0]), "y_meta": rel_err(to_np(ym), ref["y_meta"][0]),
+            "h": rel_err(to_np(st["h"][b]), ref["h"][0])}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] < TOL_BF16 and errs["y_meta"] < TOL_BF16 and errs["h"] < TOL_H

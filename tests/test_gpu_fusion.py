@@ -60,3 +60,25 @@ def test_group_norm_decode_continues_prefill(B, n_kv):
         e = rel_err(to_np(y), o["y"])
         assert e < TOL_BF16, (s, e)
     assert rel_err(to_np(st["h"]), o["h"]) < TOL_H
+
+
+def test_group_norm_full_size_sampled_sequence():
+    """The prefill workload's layer (d 2048, 16 x 128 q / 4 kv heads, Di 4096, N 16, 128
+    meta tokens) with g = 128, B=8, L=2048, run on the whole batch; sequence 3 is
+    recomputed by the oracle (y, y_meta and the final state)."""
+    from tests.gpu_util import alloc_state, make_layer
+    case = CASES[1]
+    dims = case.dims.replace(norm_group=128)
+    B, L = case.batch, case.seq_len
+    w = gen_layer_weights(dims, case.case_id)
+    meta_t, meta, x_t, x = gen_activations(dims, case.case_id, B, L)
+    layer = make_layer(dims, w)
+    st = alloc_state(dims, B)
+    y, ym = layer.prefill(meta_t.to(DEV), x_t.to(DEV), state_out=state_struct(st))
+    torch.cuda.synchronize()
+    b = 3
+    ref = orc.prefill(dims, w, meta, x[b:b + 1], contract=True)
+    errs = {"y": rel_err(to_np(y[b]), ref["y"][0]), "y_meta": rel_err(to_np(ym), ref["y_meta"][0]),
+            "h": rel_err(to_np(st["h"][b]), ref["h"][0])}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] < TOL_BF16 and errs["y_meta"] < TOL_BF16 and errs["h"] < TOL_H
