@@ -218,3 +218,58 @@ def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
     assert scan(batch=0, n_meta=0) == 0
     assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64) == 0
     assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 16) == (8 + 128) * 512 * 4
+
+
+def test_block_workspace_sizes(lib):
+    """Block workspace: the layer's, then xn and v ([rows, d] each), h ([rows, I]) and the
+    fp32 partial slices of the few-row down-projection (8 slices of [few rows, d] for
+    K = 5632 split into 256-wide units, 3 units a slice)."""
+    d = desc_of(1)
+    rows, inter = 128 + 8 * 2048, 5632
+    floor = (hy.hymba_layer_workspace_bytes(d, 8, 2048, 0) + rows * (2048 * 2 * 2 + inter * 2)
+             + 8 * 128 * 2048 * 4)
+    got = hy.hymba_block_workspace_bytes(d, inter, 8, 2048, 0)
+    assert floor <= got <= floor + 4 * 256
+    d4 = desc_of(4)
+    floor = (hy.hymba_layer_workspace_bytes(d4, 128, 1024, 1) + 128 * (2048 * 2 * 2 + inter * 2)
+             + 8 * 128 * 2048 * 4)
+    got = hy.hymba_block_workspace_bytes(d4, inter, 128, 1024, 1)
+    assert floor <= got <= floor + 4 * 256
+    assert hy.hymba_block_workspace_bytes(d, 5630, 8, 2048, 0) == 0   # not a multiple of 8
+    assert hy.hymba_block_workspace_bytes(d, 0, 8, 2048, 0) == 0
+    assert hy.hymba_block_workspace_bytes(d, inter, 8, 2048, 2) == 0  # no such mode
+
+
+def test_block_argument_errors(lib):
+    """Every rejection happens before a launch; valid arguments with a workspace that is
+    too small stop at the workspace check."""
+    d = desc_of(1)
+    w = _weights_struct()
+    bw = hy.BlockWeights(4096, 4352, 4608, 4864, 5632)
+    call = lambda **kw: hy.hymba_block_prefill(**{**dict(
+        desc=d, weights=w, block=bw, meta=4096, x=8192, batch=1, seq_len=4, kv_in=None,
+        kv_out=None, state_out=None, y=12288, y_meta=None, workspace=1 << 20,
+        workspace_bytes=1000, stream=0, check=False), **kw})
+    assert call() == 3
+    assert call(block=hy.BlockWeights(4096, None, 4608, 4864, 5632)) == 1
+    assert call(block=hy.BlockWeights(4096, 4352, 4608, 4864, 0)) == 1
+    assert call(block=hy.BlockWeights(4096, 4352, 4608, 4864, 5630)) == 2
+    assert call(block=hy.BlockWeights(4104, 4352, 4608, 4864, 5632)) == 4
+    assert call(batch=-1) == 1
+    assert call(x=None) == 1
+    assert call(meta=None) == 1
+    assert call(y=12290) == 4
+    assert call(desc=desc_of(1, head_dim=96)) == 2
+    assert hy.hymba_block_prefill(desc_of(1, n_meta=0), w, bw, None, None, 0, 0, None, None,
+                                  None, None, None, None, 0, stream=0, check=False) == 0
+    kv = hy.KV(4096, 4096, 4096, 4096, 1024)
+    state = hy.SSMState(4096, 4096)
+    dcall = lambda **kw: hy.hymba_block_decode(**{**dict(
+        desc=desc_of(4), weights=w, block=bw, x=4096, batch=2, kv=kv, state=state, y=4096,
+        workspace=4096, workspace_bytes=16, stream=0, check=False), **kw})
+    assert dcall() == 3
+    assert dcall(block=hy.BlockWeights(None, 4352, 4608, 4864, 5632)) == 1
+    assert dcall(kv=None) == 1
+    assert dcall(batch=-1) == 1
+    assert dcall(x=4100) == 4
+    assert dcall(batch=0) == 0

@@ -88,3 +88,30 @@ def test_block_full_size_sampled_sequence():
             "h": rel_err(to_np(st["h"][b]), ref["h"][0])}
     print({k: f"{v:.2e}" for k, v in errs.items()})
     assert errs["y"] < TOL_BF16 and errs["y_meta"] < TOL_BF16 and errs["h"] < TOL_H
+
+
+def test_block_without_meta_tokens():
+    """No meta tokens (M = 0: no meta rows, no few-row down-projection), one sequence of
+    a ragged length, then two decode steps."""
+    dims = small_dims(n_meta=0, window=0)
+    B, L, steps = 1, 45, 2
+    w = gen_layer_weights(dims, 620)
+    bw = gen_block_weights(dims, 620, 512)
+    meta_t, meta, x_t, x = gen_activations(dims, 620, B, L + steps)
+    ref = orc.block_prefill(dims, w, bw, meta, x[:, :L], contract=True, ring_slots=L + steps)
+    blk = _block(dims, w, bw)
+    kv = alloc_kv(dims, B, L + steps)
+    st = alloc_state(dims, B)
+    y, _ = blk.prefill(meta_t.to(DEV), x_t[:, :L].contiguous().to(DEV), kv_out=kv_struct(kv),
+                       state_out=state_struct(st))
+    torch.cuda.synchronize()
+    assert rel_err(to_np(y), ref["y"]) < TOL_BF16
+    assert rel_err(to_np(st["h"]), ref["h"]) < TOL_H
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    xb = x_t.to(DEV)
+    for s in range(steps):
+        yd = blk.decode(xb[:, L + s].contiguous(), kv_struct(kv), state_struct(st))
+        o = orc.block_decode_step(dims, w, bw, x[:, L + s], ref["k_meta"], ref["v_meta"], o["k"],
+                                  o["v"], o["h"], o["pos"], contract=True)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(yd), o["y"]) < TOL_BF16, s
