@@ -408,13 +408,20 @@ def bench_block(hy, torch, dev, args, layer_ms):
     torch.cuda.empty_cache()
     log(f"[bench] block wrapper: prefill {ms:.3f} ms ({B * L / ms / 1e3:.3f} M tok/s), "
         f"wrapper kernels {blk_ms:.3f} ms per step")
-    return {"workload": "the prefill workload through the block wrapper (pre-norm, residual, "
-                        "FFN with intermediate 5632 and SiLU)",
-            "prefill_ms": round(ms, 4), "prefill_tokens_per_s": round(B * L / ms * 1e3, 1),
-            "layer_prefill_ms": round(layer_ms, 4),
-            "wrapper_ms_per_step": round(blk_ms, 4),
-            "ffn_flop_per_step": ffn_flop,
-            "ffn_and_norms_tflops": round(ffn_flop / (blk_ms * 1e-3) / 1e12, 1)}
+    out = {"workload": "the prefill workload through the block wrapper (pre-norm, residual, "
+                       "FFN with intermediate 5632 and SiLU)",
+           "prefill_ms": round(ms, 4), "prefill_tokens_per_s": round(B * L / ms * 1e3, 1),
+           "layer_prefill_ms": round(layer_ms, 4),
+           "wrapper_ms_per_step": round(blk_ms, 4),
+           "ffn_flop_per_step": ffn_flop,
+           "ffn_and_norms_tflops": round(ffn_flop / (blk_ms * 1e-3) / 1e12, 1)}
+    if not args.no_decode:
+        dec = bench_decode(hy, torch, dev, args, block_inter=inter)
+        out["decode_us_per_step"] = dec["us_per_step"]
+        out["decode_tokens_per_s"] = dec["value"]
+        out["decode_hbm_frac_of_peak"] = dec["hbm_frac_of_peak"]
+        out["decode_block_us"] = dec["stage_us"].get("block", {}).get("us")
+    return out
 
 
 def bench_group_norm(hy, torch, dev, args, default_stages):
@@ -573,15 +580,22 @@ def bench_stack(hy, torch, dev, n_layers=16, B=1, L=8192, W=1024, dsteps=16, ste
     return res
 
 
-def bench_decode(hy, torch, dev, args, dims=None):
-    from synth import CASES, gen_layer_weights
+def bench_decode(hy, torch, dev, args, dims=None, block_inter=0):
+    """The decode workload (config 4) on the layer, or (block_inter > 0) on the layer
+    inside its block wrapper with that FFN intermediate size."""
+    from synth import CASES, gen_block_weights, gen_layer_weights
     case = CASES[4]
     dims = dims or case.dims
     B, S, prior = case.batch, case.ring_slots, case.prior_tokens
     log(f"[bench] decode workload {case.name}: B={B} ring={S} prior={prior}"
-        f"{' ssm_heads=%d' % dims.ssm_heads if dims.ssm_heads else ''}")
+        f"{' ssm_heads=%d' % dims.ssm_heads if dims.ssm_heads else ''}"
+        f"{' block intermediate=%d' % block_inter if block_inter else ''}")
     w = gen_layer_weights(dims, case.case_id)
-    layer = hy.HymbaLayer(dims, w.torch, device=dev)
+    if block_inter:
+        bw = gen_block_weights(dims, case.case_id, block_inter)
+        layer = hy.HymbaBlock(dims, w.torch, bw.torch, device=dev)
+    else:
+        layer = hy.HymbaLayer(dims, w.torch, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(1004)
     Hkv, M, dh = dims.n_kv_heads, dims.n_meta, dims.head_dim
@@ -634,7 +648,8 @@ def bench_decode(hy, torch, dev, args, dims=None):
           for name, r in st_rec.items()}
     # algorithmic bytes per step: weights, ring K/V read, meta K/V, state read + write
     wbytes = 2 * (dims.n_in * dims.d_model + dims.n_xproj * dims.d_inner +
-                  dims.d_inner * dims.dt_rank + dims.d_model * dims.f_width)
+                  dims.d_inner * dims.dt_rank + dims.d_model * dims.f_width +
+                  2 * dims.d_model * block_inter)
     ring_bytes = B * dims.n_kv_heads * min(S, dims.window) * dims.head_dim * 2 * 2
     meta_bytes = dims.n_kv_heads * M * dh * 2 * 2
     h_bytes = B * dims.d_inner * dims.d_state * 4 * 2
@@ -645,7 +660,8 @@ def bench_decode(hy, torch, dev, args, dims=None):
     return {"value": round(tps, 1), "unit": "tokens/s", "us_per_step": round(us, 2),
             "steps": steps, "batch": B,
             "workload": "decode, bf16, B=128, 1 token per sequence after 4096 prior tokens, "
-                        "window 1024 ring + 128 meta entries, same layer shape",
+                        "window 1024 ring + 128 meta entries, same layer shape" +
+                        (f", inside the block wrapper (FFN {block_inter})" if block_inter else ""),
             "hbm_bytes_per_step": step_bytes,
             "hbm_frac_of_peak": round(step_bytes / (span / steps) / 1e9 / PEAK_HBM_GBS, 4),
             "stage_us": st}

@@ -1001,6 +1001,13 @@ int ffn_down_slices(const Shape& s, int rows, int inter) {
   return splitk_slices(inter, splitk_factor(rows, s.d, inter));
 }
 
+// The up-projection over few rows (a decode batch) likewise: K = d split into fp32
+// partials, summed, passed through SiLU and rounded by the row store.
+int ffn_up_slices(const Shape& s, int rows, int inter) {
+  if (rows <= 0 || !s.bf16 || s.d % 256 != 0 || inter % 64 != 0) return 0;
+  return splitk_slices(s.d, splitk_factor(rows, inter, s.d));
+}
+
 // few_rows: the rows that take the few-row down-projection (meta rows / the batch).
 BlockCarve carve_block(const Shape& s, size_t layer_bytes, int64_t rows, int inter,
                        int few_rows) {
@@ -1014,7 +1021,9 @@ BlockCarve carve_block(const Shape& s, size_t layer_bytes, int64_t rows, int int
   c.h = off;
   off = align_up(off + (size_t)rows * inter * s.es);
   c.acc = off;
-  off = align_up(off + (size_t)ffn_down_slices(s, few_rows, inter) * few_rows * s.d * 4);
+  off = align_up(off + std::max((size_t)ffn_down_slices(s, few_rows, inter) * s.d,
+                                (size_t)ffn_up_slices(s, few_rows, inter) * inter) *
+                           few_rows * 4);
   c.total = off;
   return c;
 }
@@ -1038,9 +1047,19 @@ hipError_t ffn_gemm(const Shape& s, const GemmOperands& op, const GemmOutput& ou
 }
 
 hymba_status ffn_up(const Shape& s, const hymba_block_weights* bw, const void* v, void* h,
-                    int rows, bool skinny, hipStream_t stream) {
+                    int rows, bool skinny, float* acc, hipStream_t stream) {
   const int I = bw->intermediate;
   GemmOperands op{v, s.d, nullptr, 0, rows, bw->w_up, s.d, rows, I, s.d};
+  const int slices = skinny && acc != nullptr ? ffn_up_slices(s, rows, I) : 0;
+  if (slices > 0) {
+    const int64_t stride = (int64_t)rows * I;
+    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_gemm_bf16_splitk(op, acc, I,
+                                                           splitk_factor(rows, I, s.d), stream,
+                                                           stride));
+    HYMBA_LAUNCH(HYMBA_STAGE_BLOCK,
+                 launch_store_rows(true, acc, h, rows, I, stream, slices, stride, false, true));
+    return HYMBA_OK;
+  }
   GemmOutput out{EpiKind::Silu, h, I, nullptr, 0, rows, 0, nullptr};
   HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, ffn_gemm(s, op, out, skinny, stream));
   return HYMBA_OK;
@@ -1129,7 +1148,8 @@ hymba_status hymba_block_prefill(const hymba_layer_desc* desc, const hymba_layer
   // output has d columns only, so its tiles over the X rows fill whole waves when B*L is a
   // multiple of the tile height; the meta rows take the few-row tiles in a launch of their
   // own instead of adding a nearly empty wave.
-  if ((st = ffn_up(s, bw, v, hbuf, (int)(Mf + BL), false, stream)) != HYMBA_OK) return st;
+  if ((st = ffn_up(s, bw, v, hbuf, (int)(Mf + BL), false, nullptr, stream)) != HYMBA_OK)
+    return st;
   const size_t hb = (size_t)bw->intermediate * s.es;  // bytes per row of h
   if ((st = ffn_down(s, bw, hbuf + Mf * hb, (int)BL, y, s.d, false, nullptr, stream)) !=
       HYMBA_OK)
@@ -1165,7 +1185,9 @@ hymba_status hymba_block_decode(const hymba_layer_desc* desc, const hymba_layer_
   if (st != HYMBA_OK) return st;
   HYMBA_LAUNCH(HYMBA_STAGE_BLOCK, launch_residual_norm(b16, x, s.d, y, s.d, v, s.d, B, s.d,
                                                       bw->norm2, eps, stream));
-  if ((st = ffn_up(s, bw, v, hbuf, B, true, stream)) != HYMBA_OK) return st;
+  if ((st = ffn_up(s, bw, v, hbuf, B, true, (float*)ws_ptr(workspace, cv.acc), stream)) !=
+      HYMBA_OK)
+    return st;
   return ffn_down(s, bw, hbuf, B, y, s.d, true, (float*)ws_ptr(workspace, cv.acc), stream);
 }
 

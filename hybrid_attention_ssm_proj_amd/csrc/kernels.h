@@ -263,10 +263,11 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, int n, hipStream_t s);
 // Zero `n` floats (n % 4 == 0, 16-byte aligned).
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // y[B, d] (storage type, contiguous) = sum over p < nslices of acc[p * slice_stride +
-// (B, d)] fp32, plus y's old value when `accumulate` (one rounding of the fp32 sum);
-// slice_stride % 4 == 0 when nslices > 1.
+// (B, d)] fp32, plus y's old value when `accumulate`, then SiLU when `silu` (one rounding
+// of the fp32 result); slice_stride % 4 == 0 when nslices > 1.
 hipError_t launch_store_rows(bool bf16, const float* acc, void* y, int B, int d, hipStream_t s,
-                             int nslices = 1, int64_t slice_stride = 0, bool accumulate = false);
+                             int nslices = 1, int64_t slice_stride = 0, bool accumulate = false,
+                             bool silu = false);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 }  // namespace hymba

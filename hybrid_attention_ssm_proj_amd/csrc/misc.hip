@@ -638,7 +638,7 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 template <typename T>
 __global__ __launch_bounds__(256) void store_rows_kernel(const float* acc, T* y, int64_t n,
                                                          int nslices, int64_t slice_stride,
-                                                         bool accumulate) {
+                                                         bool accumulate, bool silu) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
   floatx4 a = *(const floatx4*)(acc + i);
@@ -651,12 +651,16 @@ __global__ __launch_bounds__(256) void store_rows_kernel(const float* acc, T* y,
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] += to_f32(y[i + e]);
   }
+  if (silu) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = silu_f(a[e]);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) y[i + e] = from_f32<T>(a[e]);
 }
 
 hipError_t launch_store_rows(bool bf16_, const float* acc, void* y, int B, int d, hipStream_t s,
-                             int nslices, int64_t slice_stride, bool accumulate) {
+                             int nslices, int64_t slice_stride, bool accumulate, bool silu) {
   const int64_t n = (int64_t)B * d;
   if (n == 0) return hipSuccess;
   if (nslices < 1 || (nslices > 1 && (slice_stride < n || slice_stride % 4 != 0)))
@@ -664,10 +668,10 @@ hipError_t launch_store_rows(bool bf16_, const float* acc, void* y, int B, int d
   const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
   if (bf16_)
     store_rows_kernel<bf16><<<dim3(blocks), dim3(256), 0, s>>>(acc, (bf16*)y, n, nslices,
-                                                               slice_stride, accumulate);
+                                                               slice_stride, accumulate, silu);
   else
     store_rows_kernel<float><<<dim3(blocks), dim3(256), 0, s>>>(acc, (float*)y, n, nslices,
-                                                                slice_stride, accumulate);
+                                                                slice_stride, accumulate, silu);
   return hipGetLastError();
 }
 

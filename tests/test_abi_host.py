@@ -222,17 +222,19 @@ def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
 
 def test_block_workspace_sizes(lib):
     """Block workspace: the layer's, then xn and v ([rows, d] each), h ([rows, I]) and the
-    fp32 partial slices of the few-row down-projection (8 slices of [few rows, d] for
-    K = 5632 split into 256-wide units, 3 units a slice)."""
+    fp32 partial slices of the few-row FFN projections, the larger of: the down-projection's
+    8 slices of [few rows, d] (K = 5632 in 22 units of 256, 3 units a slice) and the
+    up-projection's 3 slices of [few rows, I] (K = 2048 in 8 units, 3 units a slice)."""
     d = desc_of(1)
     rows, inter = 128 + 8 * 2048, 5632
+    acc = max(8 * 2048, 3 * inter) * 128 * 4
     floor = (hy.hymba_layer_workspace_bytes(d, 8, 2048, 0) + rows * (2048 * 2 * 2 + inter * 2)
-             + 8 * 128 * 2048 * 4)
+             + acc)
     got = hy.hymba_block_workspace_bytes(d, inter, 8, 2048, 0)
     assert floor <= got <= floor + 4 * 256
     d4 = desc_of(4)
     floor = (hy.hymba_layer_workspace_bytes(d4, 128, 1024, 1) + 128 * (2048 * 2 * 2 + inter * 2)
-             + 8 * 128 * 2048 * 4)
+             + acc)
     got = hy.hymba_block_workspace_bytes(d4, inter, 128, 1024, 1)
     assert floor <= got <= floor + 4 * 256
     assert hy.hymba_block_workspace_bytes(d, 5630, 8, 2048, 0) == 0   # not a multiple of 8
