@@ -60,16 +60,16 @@ def parse():
 
 
 def scan_channels(N):
-    """Channels per workgroup of the fused bf16 scan (4, 8, 8, 16 lanes per channel)."""
-    return 64 if N == 16 else (16 if N == 128 else 32)
+    """Channels per workgroup of the bf16 scan (one per lane of a wave, for every N)."""
+    return 64
 
 
 def deferred_norm(dims):
     """The library applies the branch norms inside out_proj for bf16 layers whose scan
     has the fused dt projection (dt_rank 64 or 128, d_state 16..128)."""
     return (dims.dtype == "bf16" and dims.dt_rank in (64, 128) and
-            dims.d_state in (16, 32, 64, 128) and dims.d_inner % scan_channels(dims.d_state) == 0
-            and dims.q_width % 128 == 0)
+            dims.d_state in (4, 8, 16, 32, 64, 128) and
+            dims.d_inner % scan_channels(dims.d_state) == 0 and dims.q_width % 128 == 0)
 
 
 def stage_work(dims, B, L):

@@ -47,7 +47,8 @@ class LayerDesc(ctypes.Structure):
         "d_model", "n_q_heads", "n_kv_heads", "head_dim", "d_inner", "d_state", "dt_rank",
         "n_meta", "window", "kv_share", "dtype")] + [
         ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-        ("ssm_heads", ctypes.c_int32), ("norm_group", ctypes.c_int32)]
+        ("ssm_heads", ctypes.c_int32), ("norm_group", ctypes.c_int32),
+        ("scan_chunk", ctypes.c_int32)]
 
     @classmethod
     def from_dims(cls, dims) -> "LayerDesc":
@@ -55,7 +56,7 @@ class LayerDesc(ctypes.Structure):
                    dims.d_state, dims.dt_rank, dims.n_meta, dims.window, dims.kv_share,
                    DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, dims.rms_eps,
                    dims.softmax_scale, getattr(dims, "ssm_heads", 0),
-                   getattr(dims, "norm_group", 0))
+                   getattr(dims, "norm_group", 0), getattr(dims, "scan_chunk", 0))
 
 
 class BlockWeights(ctypes.Structure):
@@ -127,9 +128,9 @@ def load_library() -> ctypes.CDLL:
         "hymba_op_attn_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "hymba_op_attn": (I32, [I32, P, I64, P, P, I64, P, I64, I32, I32, I32, I32, I32, I32,
                                 I32, ctypes.c_float, P, SZ, P]),
-        "hymba_op_scan_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32, I32]),
+        "hymba_op_scan_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32, I32, I32]),
         "hymba_op_scan": (I32, [I32, P, I64, I32, I32, P, P, P, P, P, P, P, I64, P, I32, I32, I32,
-                                I32, I32, I32, P, SZ, P]),
+                                I32, I32, I32, I32, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -298,18 +299,19 @@ def hymba_op_attn(dtype, q, q_ld, k, v, kv_ld, o, o_ld, n_meta, seq_len, batch, 
 
 
 def hymba_op_scan_workspace_bytes(dtype, n_meta, seq_len, batch, d_inner, d_state,
-                                  dt_rank) -> int:
+                                  dt_rank, chunk_tokens=0) -> int:
     return load_library().hymba_op_scan_workspace_bytes(dtype, n_meta, seq_len, batch, d_inner,
-                                                        d_state, dt_rank)
+                                                        d_state, dt_rank, chunk_tokens)
 
 
 def hymba_op_scan(dtype, z, z_ld, xs_col, g_col, delta, bc, w_dt, dt_bias, A, D, y, y_ld, h_out,
-                  n_meta, seq_len, batch, d_inner, d_state, dt_rank, workspace, workspace_bytes,
-                  stream=None, check=True) -> int:
+                  n_meta, seq_len, batch, d_inner, d_state, dt_rank, chunk_tokens, workspace,
+                  workspace_bytes, stream=None, check=True) -> int:
     st = load_library().hymba_op_scan(dtype, _ptr(z), z_ld, xs_col, g_col, _ptr(delta), _ptr(bc),
                                       _ptr(w_dt), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(y), y_ld,
                                       _ptr(h_out), n_meta, seq_len, batch, d_inner, d_state,
-                                      dt_rank, _ptr(workspace), workspace_bytes, _stream(stream))
+                                      dt_rank, chunk_tokens, _ptr(workspace), workspace_bytes,
+                                      _stream(stream))
     if check:
         _check(st, "hymba_op_scan")
     return st

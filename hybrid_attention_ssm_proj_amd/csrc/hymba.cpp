@@ -81,6 +81,7 @@ struct Shape {
   int H2;  // Mamba-2 heads (0: Mamba head with per-channel A and a rank-R dt projection)
   int G;   // branch-norm groups of G channels (0: RMSNorm over each branch)
   int nx;  // x_proj output width: (H2 ? H2 : R) + 2N
+  int chunk;  // time chunk of the Mamba-head scan in tokens (0: chosen per call)
   bool bf16;
   int64_t qw, kvw, n_in, fw, xs_col, g_col, k_col, v_col;
   float scale;
@@ -117,7 +118,8 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
     return HYMBA_ERR_UNSUPPORTED;
   if (!is_pow2_in(d.d_state, 4, 128)) return HYMBA_ERR_UNSUPPORTED;
   if (!head_ssm && d.dt_rank > 512) return HYMBA_ERR_UNSUPPORTED;
-  if (d.norm_group < 0) return HYMBA_ERR_INVALID_ARG;
+  if (d.norm_group < 0 || d.scan_chunk < 0) return HYMBA_ERR_INVALID_ARG;
+  if (d.scan_chunk % 16) return HYMBA_ERR_UNSUPPORTED;
   if (d.norm_group > 0 &&
       (!is_pow2_in(d.norm_group, 8, 512) || (d.n_q_heads * d.head_dim) % d.norm_group ||
        d.d_inner % d.norm_group))
@@ -131,6 +133,7 @@ hymba_status make_shape(const hymba_layer_desc* desc, Shape& s) {
   s.R = head_ssm ? 0 : d.dt_rank;
   s.H2 = head_ssm ? d.ssm_heads : 0;
   s.G = d.norm_group;
+  s.chunk = d.scan_chunk;
   s.nx = (head_ssm ? d.ssm_heads : d.dt_rank) + 2 * d.d_state;
   s.M = d.n_meta;
   s.W = d.window;
@@ -154,7 +157,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Carve {
-  size_t z, delta, bc, dt, f, vt, macc, ssp, fac, part, xdbl, yacc, total;
+  size_t z, delta, bc, dt, f, vt, macc, ssp, fac, hmeta, hsum, ssum, part, xdbl, yacc, total;
 };
 
 
@@ -172,7 +175,28 @@ int decode_nsplit(const Shape& s, int span_max) {
 }
 
 bool fused_dt(const Shape& s) {
-  return s.H2 == 0 && s.bf16 && scan_fused_supported(s.N, s.R, s.Di);
+  return s.H2 == 0 && s.bf16 && scan_chunk_supported(s.N, s.R, s.Di);
+}
+
+// Time chunk of the chunk-carried scan over B sequences of T tokens (chunk_override > 0:
+// the caller's), the number of chunks, and the chunk summaries one launch needs (in
+// units of a [Di, N] state plus a [Di] sum of dt).
+int scan_chunk_for(int chunk_override, int B, int Di, int T) {
+  return chunk_override > 0 ? chunk_override : scan_default_chunk(B, Di, T);
+}
+int scan_chunks(int chunk_override, int B, int Di, int T) {
+  return scan_chunk_count(T, scan_chunk_for(chunk_override, B, Di, T));
+}
+int64_t scan_summaries(int chunk_override, int B, int Di, int T) {
+  if (B <= 0 || T <= 0) return 0;
+  return (int64_t)B * (scan_chunks(chunk_override, B, Di, T) - 1);
+}
+// At most 65 chunks (the carry scan runs over one wavefront) and a grid of at most 65535
+// (sequence, chunk) rows.
+bool scan_chunks_ok(int chunk_override, int B, int Di, int T) {
+  if (B <= 0 || T <= 0) return true;
+  const int k = scan_chunks(chunk_override, B, Di, T);
+  return k <= 65 && (int64_t)B * k <= 65535;
 }
 
 // Prefill: rows = meta rows + batch * tokens.  dt is materialised only when the scan
@@ -217,6 +241,18 @@ Carve carve_prefill(const Shape& s, int64_t rows, int B, int L, bool cached = fa
     off = align_up(off + (size_t)rows * (s.Hq + scan_channel_blocks(s.N, s.Di)) * 4);
   c.fac = off;   // and the two row factors derived from them
   if (s.bf16 && fused_dt(s)) off = align_up(off + (size_t)rows * 2 * 4);
+  // fused scan: the state after the meta rows (scanned once, then every sequence starts
+  // from it) and the chunk summaries of the larger of its two launches
+  c.hmeta = off;
+  const int Mr = cached ? 0 : s.M;
+  if (fused_dt(s) && Mr > 0 && B > 0) off = align_up(off + (size_t)s.Di * s.N * 4);
+  const int64_t nsum = fused_dt(s) ? std::max(scan_summaries(s.chunk, 1, s.Di, Mr),
+                                              scan_summaries(s.chunk, B, s.Di, L))
+                                   : 0;
+  c.hsum = off;
+  off = align_up(off + (size_t)nsum * s.Di * s.N * 4);
+  c.ssum = off;
+  off = align_up(off + (size_t)nsum * s.Di * 4);
   c.total = off;
   return c;
 }
@@ -347,7 +383,7 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
   const int B = batch, L = seq_len, M = s.M, Mr = cached ? 0 : s.M;
   const int64_t BL = (int64_t)B * L;
   const int64_t rows = Mr + BL;
-  if (rows > (int64_t)1 << 31 || BL > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  if (rows >= (int64_t)1 << 31 || BL >= (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
   if (Mr > 0 && meta == nullptr) return HYMBA_ERR_INVALID_ARG;
   if (h_meta_out != nullptr && BL != 0) return HYMBA_ERR_INVALID_ARG;
   if (cached) {
@@ -381,6 +417,8 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
     if (any_misaligned(state_out->h, state_out->pos)) return HYMBA_ERR_ALIGNMENT;
   }
   if (any_misaligned(meta, x, y, y_meta, workspace)) return HYMBA_ERR_ALIGNMENT;
+  if (fused_dt(s) && (!scan_chunks_ok(s.chunk, 1, s.Di, Mr) || !scan_chunks_ok(s.chunk, B, s.Di, L)))
+    return HYMBA_ERR_UNSUPPORTED;
   const Carve cv = carve_prefill(s, rows, B, L, cached);
   if (rows > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_;
@@ -530,10 +568,6 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
     sp.B = B;
     sp.Di = s.Di;
     sp.N = s.N;
-    sp.ssp = ssp;
-    sp.ssp_ld = ssp_ld;
-    sp.ssp_col0 = s.Hq;
-    sp.beta = w->beta_ssm;
     if (B == 0) {  // meta rows only: run them as one sequence of length 0
       sp.B = 1;
       sp.h_out = h_meta_out;
@@ -560,8 +594,52 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
       qp.N = s.N;
       HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_ssd(qp, stream));
     } else if (fuse) {
-      HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill_fused(sp, delta, w->w_dt, w->dt_bias,
-                                                               s.R, stream));
+      // The meta rows once from h = 0 (their state is batch-shared), then every sequence
+      // from that state (or from the cache's), each launch chunk-carried over time.
+      ScanChunkParams cp{};
+      cp.z = z;
+      cp.z_stride = s.n_in;
+      cp.xs_col = (int)s.xs_col;
+      cp.g_col = (int)s.g_col;
+      cp.delta = delta;
+      cp.bc = bc;
+      cp.w_dt = w->w_dt;
+      cp.dt_bias = w->dt_bias;
+      cp.A = w->A;
+      cp.D = w->D;
+      cp.y = sp.y;
+      cp.y_stride = s.fw;
+      cp.Di = s.Di;
+      cp.N = s.N;
+      cp.R = s.R;
+      cp.hsum = (float*)ws_ptr(workspace, cv.hsum);
+      cp.ssum = (float*)ws_ptr(workspace, cv.ssum);
+      cp.ssp = ssp;
+      cp.ssp_ld = ssp_ld;
+      cp.ssp_col0 = s.Hq;
+      cp.beta = defer_norm ? w->beta_ssm : nullptr;
+      float* hmeta = (float*)ws_ptr(workspace, cv.hmeta);
+      if (Mr > 0) {
+        ScanChunkParams mp = cp;
+        mp.row0 = 0;
+        mp.T = Mr;
+        mp.B = 1;
+        mp.h0 = nullptr;
+        mp.h_out = B > 0 ? hmeta : h_meta_out;
+        mp.chunk = scan_chunk_for(s.chunk, 1, s.Di, Mr);
+        mp.nchunks = scan_chunk_count(Mr, mp.chunk);
+        HYMBA_LAUNCH(HYMBA_STAGE_META, launch_scan_chunk(mp, stream));
+      }
+      if (B > 0) {
+        cp.row0 = Mr;
+        cp.T = L;
+        cp.B = B;
+        cp.h0 = cached ? cache->h : (M > 0 ? hmeta : nullptr);
+        cp.h_out = state_out ? state_out->h : nullptr;
+        cp.chunk = scan_chunk_for(s.chunk, B, s.Di, L);
+        cp.nchunks = scan_chunk_count(L, cp.chunk);
+        HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_chunk(cp, stream));
+      }
     } else {
       HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_prefill(b16, sp, stream));
     }
@@ -863,7 +941,7 @@ hymba_status hymba_op_attn(int32_t dtype, const void* q, int64_t q_ld, const voi
   if (b16 ? (head_dim != 64 && head_dim != 128) : (head_dim != 32 && head_dim != 64))
     return HYMBA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)n_meta + (int64_t)batch * seq_len;
-  if (rows > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  if (rows >= (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
   if (q_ld < (int64_t)n_q_heads * head_dim || kv_ld < (int64_t)n_kv_heads * head_dim ||
       o_ld < (int64_t)n_q_heads * head_dim)
     return HYMBA_ERR_INVALID_ARG;
@@ -907,10 +985,17 @@ hymba_status hymba_op_attn(int32_t dtype, const void* q, int64_t q_ld, const voi
 
 size_t hymba_op_scan_workspace_bytes(int32_t dtype, int32_t n_meta, int32_t seq_len,
                                      int32_t batch, int32_t d_inner, int32_t d_state,
-                                     int32_t dt_rank) {
-  if (n_meta < 0 || seq_len < 0 || batch < 0 || d_inner <= 0) return 0;
+                                     int32_t dt_rank, int32_t chunk_tokens) {
+  if (n_meta < 0 || seq_len < 0 || batch < 0 || d_inner <= 0 || chunk_tokens < 0) return 0;
   const int64_t rows = (int64_t)n_meta + (int64_t)batch * seq_len;
-  if (dtype == HYMBA_DTYPE_BF16 && scan_fused_supported(d_state, dt_rank, d_inner)) return 0;
+  if (dtype == HYMBA_DTYPE_BF16 && scan_chunk_supported(d_state, dt_rank, d_inner)) {
+    // the post-meta state, then the chunk summaries of the larger launch
+    const int64_t nsum = std::max(scan_summaries(chunk_tokens, 1, d_inner, n_meta),
+                                  scan_summaries(chunk_tokens, batch, d_inner, seq_len));
+    size_t need = (n_meta > 0 && batch > 0) ? align_up((size_t)d_inner * d_state * 4) : 0;
+    need += align_up((size_t)nsum * d_inner * d_state * 4) + align_up((size_t)nsum * d_inner * 4);
+    return need;
+  }
   return (size_t)rows * d_inner * 4;
 }
 
@@ -919,47 +1004,95 @@ hymba_status hymba_op_scan(int32_t dtype, const void* z, int64_t z_ld, int32_t x
                            const float* dt_bias, const float* A, const float* D, void* y,
                            int64_t y_ld, float* h_out, int32_t n_meta, int32_t seq_len,
                            int32_t batch, int32_t d_inner, int32_t d_state, int32_t dt_rank,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   if (dtype != HYMBA_DTYPE_F32 && dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
   if (n_meta < 0 || seq_len < 0 || batch < 0 || d_inner <= 0 || dt_rank <= 0 || xs_col < 0 ||
-      g_col < 0 || xs_col + d_inner > z_ld || g_col + d_inner > z_ld || y_ld < d_inner)
+      g_col < 0 || xs_col + d_inner > z_ld || g_col + d_inner > z_ld || y_ld < d_inner ||
+      chunk_tokens < 0)
     return HYMBA_ERR_INVALID_ARG;
   if (d_state < 4 || d_state > 128 || (d_state & (d_state - 1)) || d_inner % 8 || dt_rank % 8 ||
-      dt_rank > 512 || z_ld % 8 || xs_col % 8 || g_col % 8 || y_ld % 8)
+      dt_rank > 512 || z_ld % 8 || xs_col % 8 || g_col % 8 || y_ld % 8 || chunk_tokens % 16)
     return HYMBA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)n_meta + (int64_t)batch * seq_len;
-  if (rows > (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  if (rows >= (int64_t)1 << 31) return HYMBA_ERR_UNSUPPORTED;
+  const bool chunked = dtype == HYMBA_DTYPE_BF16 && scan_chunk_supported(d_state, dt_rank, d_inner);
+  if (chunked && (!scan_chunks_ok(chunk_tokens, 1, d_inner, n_meta) ||
+                  !scan_chunks_ok(chunk_tokens, batch, d_inner, seq_len)))
+    return HYMBA_ERR_UNSUPPORTED;
   if (rows == 0 || batch == 0) return HYMBA_OK;
   if (z == nullptr || delta == nullptr || bc == nullptr || w_dt == nullptr || dt_bias == nullptr ||
       A == nullptr || D == nullptr || y == nullptr)
     return HYMBA_ERR_INVALID_ARG;
   if (any_misaligned(z, delta, bc, w_dt, y, h_out, workspace)) return HYMBA_ERR_ALIGNMENT;
   const size_t need = hymba_op_scan_workspace_bytes(dtype, n_meta, seq_len, batch, d_inner,
-                                                    d_state, dt_rank);
+                                                    d_state, dt_rank, chunk_tokens);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HYMBA_ERR_WORKSPACE;
   const bool b16 = dtype == HYMBA_DTYPE_BF16;
   hipStream_t st = (hipStream_t)stream;
-  ScanParams sp{};
-  sp.z = z;
-  sp.z_stride = z_ld;
-  sp.xs_col = xs_col;
-  sp.g_col = g_col;
-  sp.dt = (const float*)workspace;
-  sp.bc = bc;
-  sp.A = A;
-  sp.D = D;
-  sp.y = y;
-  sp.y_stride = y_ld;
-  sp.h_out = h_out;
-  sp.n_meta = n_meta;
-  sp.L = seq_len;
-  sp.B = batch;
-  sp.Di = d_inner;
-  sp.N = d_state;
-  hipError_t e;
-  if (need == 0) {
-    e = launch_scan_prefill_fused(sp, delta, w_dt, dt_bias, dt_rank, st);
+  hipError_t e = hipSuccess;
+  if (chunked) {
+    // the meta rows once, then every sequence from the state after them
+    const size_t hm = (n_meta > 0) ? align_up((size_t)d_inner * d_state * 4) : 0;
+    const int64_t nsum = std::max(scan_summaries(chunk_tokens, 1, d_inner, n_meta),
+                                  scan_summaries(chunk_tokens, batch, d_inner, seq_len));
+    ScanChunkParams cp{};
+    cp.z = z;
+    cp.z_stride = z_ld;
+    cp.xs_col = xs_col;
+    cp.g_col = g_col;
+    cp.delta = delta;
+    cp.bc = bc;
+    cp.w_dt = w_dt;
+    cp.dt_bias = dt_bias;
+    cp.A = A;
+    cp.D = D;
+    cp.y = y;
+    cp.y_stride = y_ld;
+    cp.Di = d_inner;
+    cp.N = d_state;
+    cp.R = dt_rank;
+    cp.hsum = (float*)ws_ptr(workspace, hm);
+    cp.ssum = (float*)ws_ptr(workspace, hm + align_up((size_t)nsum * d_inner * d_state * 4));
+    float* hmeta = (float*)workspace;
+    if (n_meta > 0) {
+      ScanChunkParams mp = cp;
+      mp.row0 = 0;
+      mp.T = n_meta;
+      mp.B = 1;
+      mp.h_out = hmeta;
+      mp.chunk = scan_chunk_for(chunk_tokens, 1, d_inner, n_meta);
+      mp.nchunks = scan_chunk_count(n_meta, mp.chunk);
+      e = launch_scan_chunk(mp, st);
+    }
+    if (e == hipSuccess) {
+      cp.row0 = n_meta;
+      cp.T = seq_len;
+      cp.B = batch;
+      cp.h0 = n_meta > 0 ? hmeta : nullptr;
+      cp.h_out = h_out;
+      cp.chunk = scan_chunk_for(chunk_tokens, batch, d_inner, seq_len);
+      cp.nchunks = scan_chunk_count(seq_len, cp.chunk);
+      e = launch_scan_chunk(cp, st);
+    }
   } else {
+    ScanParams sp{};
+    sp.z = z;
+    sp.z_stride = z_ld;
+    sp.xs_col = xs_col;
+    sp.g_col = g_col;
+    sp.dt = (const float*)workspace;
+    sp.bc = bc;
+    sp.A = A;
+    sp.D = D;
+    sp.y = y;
+    sp.y_stride = y_ld;
+    sp.h_out = h_out;
+    sp.n_meta = n_meta;
+    sp.L = seq_len;
+    sp.B = batch;
+    sp.Di = d_inner;
+    sp.N = d_state;
     GemmOperands op{delta, dt_rank, nullptr, 0, (int)rows, w_dt, dt_rank, (int)rows, d_inner,
                     dt_rank};
     GemmOutput out{EpiKind::Softplus, workspace, d_inner, nullptr, 0, 0, 0, dt_bias};

@@ -149,21 +149,47 @@ struct ScanParams {
   float* h_out;        // [B, Di, N] or nullptr
   const float* h0;     // [Di, N] initial state of every sequence, or nullptr (zero)
   int n_meta, L, B, Di, N;
-  // fused bf16 scan only: with ssp != nullptr the kernel writes beta[c] * y and the
-  // row's sum of y^2 over the workgroup's channel block j to ssp[(ssp_col0 + j) * ssp_ld
-  // + row] (scan_channel_blocks() blocks)
+};
+hipError_t launch_scan_prefill(bool bf16, const ScanParams& p, hipStream_t s);
+
+// bf16 prefill SSM heads with the dt projection inside (dt = softplus(delta W_dt^T + b),
+// delta [rows, R] bf16, W_dt [Di, R] bf16), chunk-carried over time.  Sequence b's token
+// t is row row0 + b * T + t of z, delta, bc, y (and ssp).  The T tokens are cut into
+// nchunks = scan_chunk_count(T, chunk) chunks of `chunk` tokens (a multiple of 16, at most
+// 65 chunks); with more than one, hsum [B, nchunks - 1, Di, N] and ssum [B, nchunks - 1,
+// Di] (fp32) receive the chunk summaries and carries.  h0 [Di, N] is every sequence's
+// state before token 0 (zero when null); h_out [B, Di, N] the state after token T - 1.
+// ssp / ssp_col0 / beta as for ScanParams (scan_channel_blocks() blocks of 64 channels).
+struct ScanChunkParams {
+  const void* z;
+  int64_t z_stride;
+  int xs_col, g_col;
+  const void* delta;
+  const float* bc;       // [rows, 2N] (B then C)
+  const void* w_dt;
+  const float* dt_bias;  // [Di]
+  const float* A;        // [Di, N]
+  const float* D;        // [Di]
+  void* y;
+  int64_t y_stride;
+  const float* h0;
+  float* h_out;
+  int row0, T, B, Di, N, R;
+  int chunk, nchunks;
+  float* hsum;
+  float* ssum;
   float* ssp;
   int64_t ssp_ld;
   int ssp_col0;
   const float* beta;
 };
-hipError_t launch_scan_prefill(bool bf16, const ScanParams& p, hipStream_t s);
-// bf16 prefill scan with the dt projection fused in (ScanParams::dt unused): dt =
-// softplus(delta W_dt^T + dt_bias) with delta [rows, R] bf16, W_dt [Di, R] bf16.
-bool scan_fused_supported(int N, int R, int Di);
+bool scan_chunk_supported(int N, int R, int Di);
 int scan_channel_blocks(int N, int Di);
-hipError_t launch_scan_prefill_fused(const ScanParams& p, const void* delta, const void* w_dt,
-                                     const float* dt_bias, int R, hipStream_t s);
+int scan_chunk_count(int T, int chunk);
+// Chunk length for B sequences of T tokens: enough (sequence, chunk) workgroups to give
+// every CU two, with chunks of at least 256 tokens.
+int scan_default_chunk(int B, int Di, int T);
+hipError_t launch_scan_chunk(const ScanChunkParams& p, hipStream_t s);
 
 // Mamba-2 SSM head (heads of 64 channels, one dt and one A per head, B and C shared),
 // bf16 prefill in the chunked matrix form.  xbc [rows, H + 2N] fp32 holds u | B | C per

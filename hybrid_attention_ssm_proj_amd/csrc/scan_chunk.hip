@@ -1,0 +1,497 @@
+// Prefill SSM heads (bf16 path): dt projection, selective scan and gate, chunk-carried
+// over time.
+//
+// Source: "Hymba: A Hybrid-head Architecture for Small Language Models" (outta.ai
+// summary), Design formulation: the SSM head's mixing coefficient
+// alpha_{i,j} = C_i (prod_{k=j+1..i} exp(A dt_k)) B_j dt_j and the gated output
+// Y_ssm = G * (SSM output); dt = softplus(delta W_dt^T + b) with delta a low-rank linear
+// map of the SSM input (Mamba).  Recurrent form per channel c and state n:
+//   h_t[c,n] = exp(dt_t[c] A[c,n]) h_{t-1}[c,n] + dt_t[c] x_t[c] B_t[n]
+//   y_t[c]   = sum_n C_t[n] h_t[c,n] + D[c] x_t[c];      out = y * SiLU(G)
+//
+// Time chunks.  Because the recurrence is linear in h, the state after a span of tokens
+// is P * h_in + h_loc, where P[c,n] = prod exp(A dt_k) = exp(A[c,n] * sum_k dt_k[c]) and
+// h_loc is the span's end state when it starts from zero.  A sequence of T tokens is cut
+// into chunks of `chunk` tokens and scanned in three launches:
+//   1. summary: every chunk but the last, from zero -> h_loc and sum(dt) per channel;
+//   2. carry: per (sequence, channel, state), an inclusive scan over the chunks inside a
+//      wavefront (lanes = chunks, shuffles in log2 steps) with the composition
+//      (P1, h1) then (P2, h2) = (P1 P2, P2 h1 + h2), seeded with the initial state;
+//   3. main: every chunk from its carried state, producing outputs and the final h.
+// With one chunk only launch 3 runs.  Chunks multiply the workgroups available to a
+// short batch (B * Di / 64 without them) at the price of a second pass over all but the
+// last chunk (about 3/4 of the main pass's instructions: no C, no outputs).
+//
+// Workgroup layout.  A workgroup owns 64 channels (one per lane) of one (sequence,
+// chunk); wave w owns states [w*NS, (w+1)*NS) of those channels.  B_t and C_t are then
+// the same for every lane of a wave and are read through the scalar data cache into
+// scalar registers: no vector memory or LDS bandwidth is spent broadcasting them.  Per
+// step of 16 tokens:
+//  * x, G and the delta rows move global -> LDS by DMA (double-buffered);
+//  * dt for 16 tokens x 64 channels is one 16x16x32 MFMA tile per 16 channels over the
+//    rank (the W_dt rows stay in registers), then bias + softplus; (dt, dt x) go to LDS;
+//  * each wave runs its NS states over the 16 tokens in registers (4 VALU + 1 exp per
+//    state and token) and writes its part of sum_n C h to LDS;
+//  * the parts of the W waves are added, D x and the gate applied, and the row stored.
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace hymba {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((ext_vector_type(2))) float floatx2;
+typedef __attribute__((address_space(4))) const floatx4 const_floatx4;
+typedef __attribute__((address_space(4))) const floatx2 const_floatx2;
+
+// NS floats at a wave-uniform address, loaded through the scalar data cache.  The buffer
+// is written by an earlier launch and only read here.
+template <int NS>
+__device__ __forceinline__ void uniform_load(float (&d)[NS], const float* p) {
+  if constexpr (NS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < NS; j += 4) {
+      const floatx4 v = *(const const_floatx4*)(p + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[j + e] = v[e];
+    }
+  } else {
+    static_assert(NS == 2, "2 or a multiple of 4 states");
+    const floatx2 v = *(const const_floatx2*)p;
+    d[0] = v[0];
+    d[1] = v[1];
+  }
+}
+// NS consecutive floats per lane (16- or 8-byte accesses).
+template <int NS>
+__device__ __forceinline__ void lane_load(float (&d)[NS], const float* p) {
+  if constexpr (NS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < NS; j += 4) {
+      const floatx4 v = *(const floatx4*)(p + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[j + e] = v[e];
+    }
+  } else {
+    const floatx2 v = *(const floatx2*)p;
+    d[0] = v[0];
+    d[1] = v[1];
+  }
+}
+template <int NS>
+__device__ __forceinline__ void lane_store(float* p, const float (&d)[NS]) {
+  if constexpr (NS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < NS; j += 4) {
+      const floatx4 v = {d[j], d[j + 1], d[j + 2], d[j + 3]};
+      *(floatx4*)(p + j) = v;
+    }
+  } else {
+    const floatx2 v = {d[0], d[1]};
+    *(floatx2*)p = v;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// Sum over each row of 16 lanes.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
+template <int NS, int W, int R>
+struct ChunkCfg {
+  static constexpr int N = NS * W;
+  static constexpr int CB = 64;              // channels per workgroup, one per lane
+  static constexpr int TC = 16;              // tokens per step
+  static constexpr int NT = 64 * W;          // threads
+  static constexpr int NC = R / 8;           // 16-byte pieces per delta row
+  static constexpr int SWM = (NC < 16 ? NC : 16) - 1;  // delta piece swizzle mask
+  static constexpr int X_SLOTS = TC * CB / 8;          // 16-byte pieces of x (or G) per step
+  static constexpr int D_SLOTS = TC * NC;              // ... of delta per step
+  static constexpr int TPW = (4 + W - 1) / W;  // dt tiles (16 channels each) per wave
+  static_assert((NS == 2 || NS % 4 == 0) && NS <= 16, "state group");
+  static_assert(TC == 16, "one 16-token MFMA tile row per step");
+  static_assert(R % 32 == 0, "MFMA k-steps");
+};
+
+}  // namespace
+
+// kSum: summary pass (chunks 0 .. nchunks-2 from zero: end state and sum of dt).
+template <int NS, int W, int R, bool kSum>
+__global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
+  using C = ChunkCfg<NS, W, R>;
+  constexpr int N = C::N, CB = C::CB, TC = C::TC, NC = C::NC, NT = C::NT;
+  // Tokens per group of scalar loads.  With up to 8 states per wave two groups' B and C
+  // rows are in flight at once (32 scalar registers; the summary pass reads B only);
+  // with 16 the scalar registers hold one group, loaded just before it runs.
+  constexpr bool kDB = NS <= 8;
+  constexpr int GT = (kSum ? 16 : 8) / NS > 0 ? (kSum ? 16 : 8) / NS : 1;
+  __shared__ __attribute__((aligned(1024))) bf16 x_s[2][TC * CB];
+  __shared__ __attribute__((aligned(1024))) bf16 g_s[2][kSum ? 8 : TC * CB];
+  __shared__ __attribute__((aligned(1024))) bf16 d_s[2][TC * R];
+  __shared__ __attribute__((aligned(16))) float2 dd_s[TC * CB];
+  __shared__ __attribute__((aligned(16))) float part_s[kSum ? 4 : W * TC * CB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = blockIdx.x * CB;
+  const int c = c0 + lane;
+  const int nck = kSum ? p.nchunks - 1 : p.nchunks;
+  const int b = blockIdx.y / nck, k = blockIdx.y % nck;
+  const int tb = k * p.chunk, te = min(tb + p.chunk, p.T);
+  const int n0 = wave * NS;
+  // Everything the step loop addresses, from the sequence's token 0 (rows are consecutive).
+  const int64_t rbase = (int64_t)p.row0 + (int64_t)b * p.T;
+  const int64_t zst = p.z_stride;
+  const bf16* zx = (const bf16*)p.z + rbase * zst + c0 + p.xs_col;
+  const int64_t gofs = (int64_t)p.g_col - p.xs_col;
+  const bf16* dl = (const bf16*)p.delta + rbase * R;
+  const float* bcs = p.bc + rbase * (2 * N) + n0;
+  bf16* ys = (bf16*)p.y + rbase * p.y_stride + c0;
+  const int64_t yst = p.y_stride;
+  float* ssps = p.ssp != nullptr ? p.ssp + (p.ssp_col0 + blockIdx.x) * p.ssp_ld + rbase : nullptr;
+  const int64_t DN = (int64_t)p.Di * N;
+  float* hdst = kSum ? p.hsum + ((int64_t)b * (p.nchunks - 1) + k) * DN
+                     : (k == p.nchunks - 1 && p.h_out != nullptr ? p.h_out + (int64_t)b * DN
+                                                                 : nullptr);
+  float* sdst = kSum ? p.ssum + ((int64_t)b * (p.nchunks - 1) + k) * p.Di : nullptr;
+
+  // The W_dt rows of this wave's dt tiles (the MFMA's B operand: lane l holds channel
+  // rbk * 16 + l % 16, pieces ks * 4 + l / 16 of the rank) and their biases stay in
+  // registers for the whole chunk.
+  bf16x8 wfrag[C::TPW][R / 32];
+  float bias[C::TPW];
+#pragma unroll
+  for (int t = 0; t < C::TPW; ++t) {
+    const int rbk = wave + t * W;
+    const int ch = c0 + (rbk < CB / 16 ? rbk : 0) * 16 + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < R / 32; ++ks)
+      wfrag[t][ks] = *(const bf16x8*)((const bf16*)p.w_dt + (int64_t)ch * R +
+                                      (ks * 4 + (lane >> 4)) * 8);
+    bias[t] = p.dt_bias[ch];
+  }
+
+  float A2[NS], h[NS];
+  {
+    const float* src = nullptr;
+    if (!kSum) src = k == 0 ? p.h0 : p.hsum + ((int64_t)b * (p.nchunks - 1) + (k - 1)) * DN;
+    lane_load<NS>(A2, p.A + (int64_t)c * N + n0);
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+      A2[e] *= kLog2eF;
+      h[e] = 0.f;
+    }
+    if (src != nullptr) lane_load<NS>(h, src + (int64_t)c * N + n0);
+  }
+  float D4[4] = {0.f, 0.f, 0.f, 0.f}, beta4[4] = {1.f, 1.f, 1.f, 1.f};
+  if (!kSum) {
+    const int cj = c0 + (tid & 15) * 4;  // the epilogue's 4 channels (fixed per thread)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      D4[e] = p.D[cj + e];
+      if (p.beta != nullptr) beta4[e] = p.beta[cj + e];
+    }
+  }
+  float dtsum = 0.f;
+
+  // Stage the step starting at sequence token s0 into buffer `buf`.  Piece q of an array
+  // is written by lane q % 64 of the wave instruction covering pieces [64*(q/64), +64), at
+  // LDS address base + 16*q.  Tokens past the chunk load its last row (never used).
+  auto stage = [&](int buf, int s0) {
+#pragma unroll
+    for (int i = 0; i * NT < C::X_SLOTS; ++i) {
+      const int q0 = i * NT + wave * 64;
+      if (q0 < C::X_SLOTS) {
+        const int q = q0 + lane, tt = q >> 3, j16 = q & 7;
+        const bf16* src = zx + min(s0 + tt, te - 1) * zst + j16 * 8;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(x_s[buf] + q0 * 8), 16,
+                                         0, 0);
+        if (!kSum)
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(src + gofs),
+                                           (lds_void_t*)(g_s[buf] + q0 * 8), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i * NT < C::D_SLOTS; ++i) {
+      const int q0 = i * NT + wave * 64;
+      if (q0 < C::D_SLOTS) {
+        const int q = q0 + lane, tt = q / NC, s = q % NC;
+        const int cidx = s ^ (tt & C::SWM);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dl + min(s0 + tt, te - 1) * R + cidx * 8),
+                                         (lds_void_t*)(d_s[buf] + q0 * 8), 16, 0, 0);
+      }
+    }
+  };
+
+  const int nst = (te - tb + TC - 1) / TC;  // 0 for an empty sequence: h passes through
+  if (nst > 0) stage(0, tb);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const int s0 = tb + st * TC;
+    const int tn = min(TC, te - s0);
+    if (st + 1 < nst) stage(cur ^ 1, s0 + TC);
+
+    // dt [16 tokens x 16 channels] per tile: delta rows (A operand) times W_dt rows
+    // (B operand) over the rank; lane l ends with tokens 4*(l/16) + i of channel l % 16.
+#pragma unroll
+    for (int tw = 0; tw < C::TPW; ++tw) {
+      const int rbk = wave + tw * W;
+      if (rbk >= CB / 16) break;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int tt = lane & 15;
+      const int chl = rbk * 16 + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < R / 32; ++ks) {
+        const int cidx = ks * 4 + (lane >> 4);
+        const bf16x8 a = *(const bf16x8*)(d_s[cur] + (tt * NC + (cidx ^ (tt & C::SWM))) * 8);
+        acc = mfma16x16x32(a, wfrag[tw][ks], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * (lane >> 4) + i;
+        const float dt = t < tn ? softplus_f(acc[i] + bias[tw]) : 0.f;
+        const float xv = (float)x_s[cur][t * CB + chl];
+        dd_s[t * CB + chl] = make_float2(dt, dt * xv);
+      }
+    }
+    lds_barrier();
+
+    // The recurrence over the step's tokens, GT at a time; the B (and C) rows of a group
+    // arrive in scalar registers through the scalar cache.  Tokens past the chunk have
+    // dt = 0, which leaves h unchanged (exp(0) = 1, zero input term).
+    // kFull: a whole step, whose rows are consecutive from the step's first, so every
+    // scalar load is the step's base address plus a constant; the last step of a chunk
+    // may be partial and clamps its rows to the chunk's last.
+    auto recurrence = [&](auto full) {
+      constexpr bool kFull = decltype(full)::value;
+      const float* bstep = bcs + (int64_t)s0 * (2 * N);
+      const int tlast = te - 1 - s0;
+      constexpr int NCQ = kSum ? 1 : NS;  // the summary pass reads no C
+      float bq0[GT][NS], cq0[GT][NCQ], bq1[GT][NS], cq1[GT][NCQ];
+      float2 dd0[GT], dd1[GT];
+      // a group's operands: (dt, dt x) from LDS, the B (and C) rows from the scalar cache
+      auto load = [&](float2 (&dd)[GT], float (&bq)[GT][NS], float (&cq)[GT][NCQ], int g0) {
+#pragma unroll
+        for (int u = 0; u < GT; ++u) {
+          dd[u] = dd_s[(g0 + u) * CB + lane];
+          const float* brow = bstep + (kFull ? g0 + u : min(g0 + u, tlast)) * (2 * N);
+          uniform_load<NS>(bq[u], brow);
+          if constexpr (!kSum) uniform_load<NS>(cq[u], brow + N);
+        }
+      };
+      auto run = [&](const float2 (&dd)[GT], const float (&bq)[GT][NS],
+                     const float (&cq)[GT][NCQ], int g0) {
+#pragma unroll
+        for (int u = 0; u < GT; ++u) {
+          const float2 d = dd[u];
+          float acc = 0.f;
+#pragma unroll
+          for (int kk = 0; kk < NS; ++kk) {
+            const float a = __builtin_amdgcn_exp2f(d.x * A2[kk]);
+            h[kk] = fmaf(a, h[kk], d.y * bq[u][kk]);
+            if constexpr (!kSum) acc = fmaf(h[kk], cq[u][kk], acc);
+          }
+          if (kSum) dtsum += d.x;
+          else part_s[(wave * TC + g0 + u) * CB + lane] = acc;
+        }
+      };
+      if constexpr (!kDB) {
+#pragma unroll
+        for (int g0 = 0; g0 < TC; g0 += GT) {
+          load(dd0, bq0, cq0, g0);
+          run(dd0, bq0, cq0, g0);
+        }
+        return;
+      }
+      // Two operand sets: the next group's loads are issued before the current group
+      // runs, behind an explicit wait for everything requested so far (scalar loads
+      // complete out of order, so only a full wait is exact).
+      load(dd0, bq0, cq0, 0);
+#pragma unroll
+      for (int g0 = 0; g0 < TC; g0 += 2 * GT) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        if (g0 + GT < TC) load(dd1, bq1, cq1, g0 + GT);
+        __builtin_amdgcn_sched_barrier(0);
+        run(dd0, bq0, cq0, g0);
+        if (g0 + GT < TC) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __builtin_amdgcn_sched_barrier(0);
+          if (g0 + 2 * GT < TC) load(dd0, bq0, cq0, g0 + 2 * GT);
+          __builtin_amdgcn_sched_barrier(0);
+          run(dd1, bq1, cq1, g0 + GT);
+        }
+      }
+    };
+    if (tn == TC) recurrence(std::true_type());
+    else recurrence(std::false_type());
+
+    if (!kSum) {
+      lds_barrier();
+      // Output: thread q takes 4 channels of one token (16 threads per token row): the
+      // waves' parts of sum_n C h, plus D x, times SiLU(G).  With p.ssp the row's sum of
+      // y^2 over the 64 channels (of the rounded y, as a norm reading the stored Y_ssm
+      // sees it) goes to ssp[ssp_col0 + blockIdx.x, row] and beta * y is stored.
+      for (int q = tid; q < TC * 16; q += NT) {
+        const int tt = q >> 4, j4 = q & 15;
+        floatx4 sum = *(const floatx4*)(part_s + tt * CB + j4 * 4);
+#pragma unroll
+        for (int w = 1; w < W; ++w) sum += *(const floatx4*)(part_s + (w * TC + tt) * CB + j4 * 4);
+        const bf16x4 xv = *(const bf16x4*)(x_s[cur] + tt * CB + j4 * 4);
+        const bf16x4 gv = *(const bf16x4*)(g_s[cur] + tt * CB + j4 * 4);
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (bf16)(fmaf(D4[e], (float)xv[e], sum[e]) * silu_f((float)gv[e]));
+        const bool keep = tt < tn;
+        const int t = s0 + min(tt, tn - 1);
+        if (ssps != nullptr) {
+          float sq = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sq = fmaf((float)o[e], (float)o[e], sq);
+          sq = row16_sum(sq);
+          if (keep && j4 == 0) ssps[t] = sq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)((float)o[e] * beta4[e]);
+        }
+        if (keep) *(bf16x4*)(ys + t * yst + j4 * 4) = o;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA for the next step has landed
+    lds_barrier();
+  }
+
+  if (hdst != nullptr) lane_store<NS>(hdst + (int64_t)c * N + n0, h);
+  if (kSum && wave == 0) sdst[c] = dtsum;
+}
+
+// Carries of the chunk summaries, in place: on entry hsum[b][k] is chunk k's end state
+// from zero and ssum[b][k] its sum of dt; on exit hsum[b][k] is the state after chunks
+// 0..k of sequence b started from h0 (zero when h0 is null), the initial state of chunk
+// k + 1.  Lane (kc, j) of a wave holds chunk kc of state element e = base + j (J = 64 / KP
+// elements per wave); the inclusive scan over kc runs with shuffles by J, 2J, 4J, ...
+template <int KP>
+__global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ hsum,
+                                                         const float* __restrict__ ssum,
+                                                         const float* __restrict__ A,
+                                                         const float* __restrict__ h0, int B,
+                                                         int Di, int N, int Kc) {
+  constexpr int J = 64 / KP;
+  const int lane = threadIdx.x & 63;
+  const int kc = lane / J, j = lane % J;
+  const int64_t DN = (int64_t)Di * N;
+  const int64_t e_all = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * J + j;
+  const bool valid = e_all < (int64_t)B * DN && kc < Kc;
+  const int64_t bb = valid ? e_all / DN : 0, e = valid ? e_all % DN : 0;
+  const int64_t idx = (bb * Kc + kc) * DN + e;
+  float P = 1.f, hh = 0.f;
+  if (valid) {
+    hh = hsum[idx];
+    P = __builtin_amdgcn_exp2f(A[e] * kLog2eF * ssum[(bb * Kc + kc) * Di + e / N]);
+  }
+#pragma unroll
+  for (int d = 1; d < KP; d <<= 1) {
+    const float Pp = __shfl_up(P, d * J, 64);
+    const float hp = __shfl_up(hh, d * J, 64);
+    if (kc >= d) {
+      hh = fmaf(P, hp, hh);
+      P *= Pp;
+    }
+  }
+  if (valid) {
+    if (h0 != nullptr) hh = fmaf(P, h0[e], hh);
+    hsum[idx] = hh;
+  }
+}
+
+namespace {
+
+template <int NS, int W, int R>
+hipError_t run_chunk(const ScanChunkParams& p, hipStream_t s) {
+  const dim3 blk(64 * W);
+  const int cbk = p.Di / 64;
+  if (p.nchunks > 1) {
+    scan_chunk_kernel<NS, W, R, true><<<dim3(cbk, p.B * (p.nchunks - 1)), blk, 0, s>>>(p);
+    const int Kc = p.nchunks - 1;
+    const int64_t elems = (int64_t)p.B * p.Di * p.N;
+    auto carry = [&](auto kp) {
+      constexpr int KP = decltype(kp)::value;
+      const int64_t waves = (elems + 64 / KP - 1) / (64 / KP);
+      scan_carry_kernel<KP><<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(
+          p.hsum, p.ssum, p.A, p.h0, p.B, p.Di, p.N, Kc);
+    };
+    if (Kc <= 1) carry(std::integral_constant<int, 1>());
+    else if (Kc <= 2) carry(std::integral_constant<int, 2>());
+    else if (Kc <= 4) carry(std::integral_constant<int, 4>());
+    else if (Kc <= 8) carry(std::integral_constant<int, 8>());
+    else if (Kc <= 16) carry(std::integral_constant<int, 16>());
+    else if (Kc <= 32) carry(std::integral_constant<int, 32>());
+    else carry(std::integral_constant<int, 64>());
+  }
+  scan_chunk_kernel<NS, W, R, false><<<dim3(cbk, p.B * p.nchunks), blk, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t chunk_by_state(const ScanChunkParams& p, hipStream_t s) {
+  switch (p.N) {
+    case 4: return run_chunk<4, 1, R>(p, s);
+    case 8: return run_chunk<4, 2, R>(p, s);
+    case 16: return run_chunk<4, 4, R>(p, s);
+    case 32: return run_chunk<8, 4, R>(p, s);
+    case 64: return run_chunk<8, 8, R>(p, s);
+    case 128: return run_chunk<16, 8, R>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool scan_chunk_supported(int N, int R, int Di) {
+  return (R == 64 || R == 128) && Di % 64 == 0 && N >= 4 && N <= 128 && (N & (N - 1)) == 0;
+}
+
+int scan_channel_blocks(int /*N*/, int Di) { return Di / 64; }
+
+int scan_chunk_count(int T, int chunk) { return T <= 0 ? 1 : (T + chunk - 1) / chunk; }
+
+int scan_default_chunk(int B, int Di, int T) {
+  // About 1024 (sequence, chunk) workgroups: measured on MI355X, more chunks pay for their
+  // summary pass up to about four resident workgroups per CU.  Chunks of at least 256
+  // tokens.
+  const int wgs = std::max(1, B * (Di / 64));
+  int k = (1024 + wgs - 1) / wgs;
+  k = std::min(k, std::max(1, T / 256));
+  k = std::max(1, std::min(k, 64));
+  const int per = (T + k - 1) / k;
+  return std::max(16, (per + 15) / 16 * 16);
+}
+
+hipError_t launch_scan_chunk(const ScanChunkParams& p, hipStream_t s) {
+  if (p.B == 0 || p.Di == 0 || (p.T == 0 && p.h_out == nullptr)) return hipSuccess;
+  if (p.chunk <= 0 || p.chunk % 16 || p.nchunks != scan_chunk_count(p.T, p.chunk) ||
+      p.nchunks > 65 || !scan_chunk_supported(p.N, p.R, p.Di))
+    return hipErrorInvalidValue;
+  if (p.nchunks > 1 && (p.hsum == nullptr || p.ssum == nullptr)) return hipErrorInvalidValue;
+  if (p.R == 128) return chunk_by_state<128>(p, s);
+  return chunk_by_state<64>(p, s);
+}
+
+}  // namespace hymba

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HYMBA_ABI_VERSION 2
+#define HYMBA_ABI_VERSION 3
 
 typedef enum {
   HYMBA_DTYPE_F32 = 0,
@@ -83,7 +83,15 @@ typedef enum {
  * width (the Chinese summary's RMSNorm per branch).  norm_group = g > 0: group
  * normalisation, the variant the hybrid-architecture summary ("설계 통찰 / 아키텍처 변형")
  * recommends for intra-layer hybrids, in groups of g channels; beta and the 0.5
- * average apply as before. */
+ * average apply as before.
+ *
+ * Time chunks of the Mamba-head scan (bf16, dt_rank 64 or 128, d_inner a multiple of
+ * 64).  The recurrence is linear in h, so a span of tokens maps h_in to P * h_in + h_loc
+ * with P = exp(A * sum dt); the prefill cuts each sequence into chunks of scan_chunk
+ * tokens, summarises every chunk but the last from h = 0, carries the summaries across
+ * chunks and rescans each chunk from its carried state (the same result up to rounding
+ * order).  scan_chunk = 0 lets the library choose (one chunk when the batch fills the
+ * GPU); otherwise a multiple of 16 giving at most 65 chunks per sequence. */
 typedef struct {
   int32_t d_model;      /* d                                                      */
   int32_t n_q_heads;    /* Hq                                                     */
@@ -104,6 +112,7 @@ typedef struct {
   int32_t norm_group;   /* 0 = RMSNorm over each branch; g > 0 = group norm in
                            groups of g channels (a power of two, 8..512, dividing
                            Hq*dh and Di): (v - mean) / sqrt(var + eps) per group   */
+  int32_t scan_chunk;   /* tokens per time chunk of the scan (0 = chosen per call)  */
 } hymba_layer_desc;
 
 /* Weights (device).  n_in = Hq*dh + (kv_share ? 0 : 2*Hkv*dh) + 2*Di; column
@@ -343,21 +352,23 @@ hymba_status hymba_op_attn(int32_t dtype, const void *q, int64_t q_ld, const voi
  *   dt_bias [d_inner], A [d_inner, d_state], D [d_inner] fp32.
  *   Every sequence starts from h = 0 and runs over the meta rows, then its own rows:
  *     dt = softplus(delta W_dt^T + dt_bias); h = exp(dt A) h + dt x B; y = C.h + D x;
- *   y [rows, y_ld] (dtype) receives y * SiLU(G) (meta rows from sequence 0);
+ *   y [rows, y_ld] (dtype) receives y * SiLU(G) (the meta rows once);
  *   h_out [batch, d_inner, d_state] fp32 (may be NULL) the final states.
- *   workspace: hymba_op_scan_workspace_bytes(...) bytes (fp32 dt when the shape has no
- *   fused kernel; may be NULL when that is 0).  Errors as for the layer calls.
+ *   chunk_tokens: time chunk of the bf16 scan, as hymba_layer_desc.scan_chunk.
+ *   workspace: hymba_op_scan_workspace_bytes(...) bytes (the post-meta state and chunk
+ *   summaries of the bf16 scan, or fp32 dt for the other shapes; may be NULL when that
+ *   is 0).  Errors as for the layer calls.
  * ------------------------------------------------------------------------- */
 size_t hymba_op_scan_workspace_bytes(int32_t dtype, int32_t n_meta, int32_t seq_len,
                                      int32_t batch, int32_t d_inner, int32_t d_state,
-                                     int32_t dt_rank);
+                                     int32_t dt_rank, int32_t chunk_tokens);
 hymba_status hymba_op_scan(int32_t dtype, const void *z, int64_t z_ld, int32_t xs_col,
                            int32_t g_col, const void *delta, const float *bc,
                            const void *w_dt, const float *dt_bias, const float *A,
                            const float *D, void *y, int64_t y_ld, float *h_out,
                            int32_t n_meta, int32_t seq_len, int32_t batch, int32_t d_inner,
-                           int32_t d_state, int32_t dt_rank, void *workspace,
-                           size_t workspace_bytes, void *stream);
+                           int32_t d_state, int32_t dt_rank, int32_t chunk_tokens,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

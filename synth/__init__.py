@@ -43,6 +43,7 @@ class LayerDims:
     ssm_heads: int = 0          # 0 = Mamba head (per-channel A, dt of rank dt_rank);
                                 # H > 0 = Mamba-2 head: H heads, scalar A and dt per head
     norm_group: int = 0         # 0 = RMSNorm per branch; g > 0 = group norm, g channels
+    scan_chunk: int = 0         # tokens per time chunk of the scan (0 = chosen per call)
 
     @property
     def q_width(self) -> int:

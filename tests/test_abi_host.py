@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert hy.hymba_abi_version() == 2
+    assert hy.hymba_abi_version() == 3
     assert hy.hymba_status_str(0) == "ok"
     assert hy.hymba_status_str(3).startswith("workspace")
 
@@ -59,8 +59,13 @@ def test_workspace_sizes(lib):
     # per-row partial sums of squares (16 heads + 64 scan channel blocks) and the two
     # row factors of the branch norms, all fp32
     ss = rows * (16 + 64) * 4 + rows * 2 * 4
-    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss
-    assert floor <= got <= floor + 8 * 256
+    # the SSM state after the meta rows ([Di, N] fp32), scanned once per call; 8 sequences
+    # of 64 channel blocks are 512 workgroups, so the scan takes two time chunks of 1024
+    # tokens: one chunk summary per sequence ([Di, N] state and [Di] sum of dt, fp32)
+    hmeta = 4096 * 16 * 4
+    summ = 8 * (4096 * 16 * 4 + 4096 * 4)
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss + hmeta + summ
+    assert floor <= got <= floor + 10 * 256
     # fp32 layers keep a separate fp32 dt buffer
     d0 = desc_of(0)
     rows0 = 8 + 64
@@ -72,6 +77,22 @@ def test_workspace_sizes(lib):
     assert hy.hymba_layer_workspace_bytes(d, 1, 10, 7) == 0
     bad = desc_of(1, d_state=24)
     assert hy.hymba_layer_workspace_bytes(bad, 1, 10, 0) == 0
+
+
+def test_scan_chunk_workspace(lib):
+    """The chunk-carried scan's summaries: (chunks - 1) x [Di, N] states and [Di] sums of
+    dt per sequence, sized for the larger of the meta launch and the sequence launch."""
+    # B = 1, L = 32768, N = 128: 64 channel blocks -> 16 chunks of 2048 (1024 workgroups)
+    base = hy.hymba_layer_workspace_bytes(desc_of(3), 1, 32768, 0)
+    assert base > 0
+    one = hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=32768), 1, 32768, 0)
+    assert base - one == 15 * 4096 * 128 * 4 + 15 * 4096 * 4
+    # a caller's chunk: 1024 tokens -> 32 chunks, 31 summaries
+    c32 = hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=1024), 1, 32768, 0)
+    assert c32 - one == 31 * 4096 * 128 * 4 + 31 * 4096 * 4
+    # not a multiple of 16; negative
+    assert hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=24), 1, 32768, 0) == 0
+    assert hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=-16), 1, 32768, 0) == 0
 
 
 def _weights_struct(addr=4096):
@@ -97,6 +118,8 @@ def _weights_struct(addr=4096):
     (dict(norm_group=24), 2),         # group size not a power of two
     (dict(norm_group=1024), 2),       # wider than one wave's 512 channels
     (dict(norm_group=4), 2),
+    (dict(scan_chunk=-16), 1),
+    (dict(scan_chunk=40), 2),         # time chunks are whole steps of 16 tokens
 ])
 def test_prefill_rejects_bad_descriptors(lib, change, status):
     d = desc_of(1, **change)
@@ -149,6 +172,14 @@ def test_prefill_argument_errors(lib):
                 kv_out=hy.KV(4096, 4096, 4096, 4096, 4)) == 1
     assert call(kv_out=hy.KV(4096, 4096, 4096, None, 4)) == 1
     assert call(state_out=hy.SSMState(None, None)) == 1
+    # more than 65 time chunks per sequence: the carry scan spans one wavefront
+    assert call(desc=desc_of(1, scan_chunk=16), seq_len=2048) == 2
+    assert call(desc=desc_of(1, scan_chunk=32), seq_len=2048,
+                workspace_bytes=1000) == 3                            # 64 chunks: valid
+    # row counts must stay below 2^31 (int32 shapes inside)
+    assert call(desc=desc_of(1, n_meta=0), batch=2, seq_len=1 << 30) == 2
+    assert call(desc=desc_of(1, n_meta=0), batch=1, seq_len=(1 << 31) - 1,
+                workspace_bytes=1000) == 3
     # nothing to do: zero rows is a successful no-op that launches nothing
     assert hy.hymba_layer_prefill(desc_of(1, n_meta=0), w, None, None, 0, 0, None, None, None,
                                   None, None, None, 0, stream=0, check=False) == 0
@@ -208,7 +239,8 @@ def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
     scan = lambda **kw: hy.hymba_op_scan(**{**dict(
         dtype=bf, z=p, z_ld=1024, xs_col=0, g_col=512, delta=p, bc=p, w_dt=p, dt_bias=p, A=p,
         D=p, y=p, y_ld=512, h_out=None, n_meta=8, seq_len=64, batch=2, d_inner=512, d_state=16,
-        dt_rank=64, workspace=None, workspace_bytes=0), **kw}, stream=0, check=False)
+        dt_rank=64, chunk_tokens=0, workspace=None, workspace_bytes=0), **kw}, stream=0,
+        check=False)
     assert scan(dtype=3) == 1
     assert scan(d_state=24) == 2
     assert scan(g_col=600) == 1                           # G columns past the row
@@ -216,7 +248,17 @@ def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
     assert scan(y=p + 4) == 4
     assert scan(dt_rank=16) == 3                          # unfused: needs the fp32 dt buffer
     assert scan(batch=0, n_meta=0) == 0
-    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64) == 0
+    assert scan() == 3                                    # the post-meta state needs room
+    assert scan(chunk_tokens=24) == 2
+    assert scan(chunk_tokens=-16) == 1
+    assert scan(n_meta=(1 << 31) - 128, seq_len=64) == 2  # rows reach 2^31
+    assert attn(n_meta=(1 << 31) - 128, seq_len=64) == 2
+    # bf16 chunked scan: the post-meta state [Di, N] fp32; one chunk here
+    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64) == 512 * 16 * 4
+    assert hy.hymba_op_scan_workspace_bytes(bf, 0, 64, 2, 512, 16, 64) == 0
+    # chunks of 16 tokens: 4 per sequence, 3 summaries each ([Di, N] states + [Di] sums)
+    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64, 16) == (
+        512 * 16 * 4 + 6 * 512 * 16 * 4 + 6 * 512 * 4)
     assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 16) == (8 + 128) * 512 * 4
 
 

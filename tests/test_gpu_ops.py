@@ -12,7 +12,7 @@ import torch
 import hybrid_attention_ssm_proj_amd as hy
 import oracle as orc
 from synth import BF16, F32, rng, to_storage
-from tests.gpu_util import DEV, rel_err, to_np
+from tests.gpu_util import DEV, h_err, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -58,13 +58,21 @@ def test_op_attn_matches_oracle(dtype, Hq, Hkv, dh, M, L, B, window):
     assert err < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,Di,N,R,M,L,B", [
-    (BF16, 256, 16, 64, 16, 100, 2),   # fused dt projection + scan
-    (BF16, 128, 32, 128, 8, 70, 1),    # fused, 8 lanes per channel
-    (BF16, 128, 16, 16, 8, 64, 2),     # dt_rank outside the fused set: dt GEMM, then scan
-    (F32, 64, 16, 16, 4, 48, 2),
+@pytest.mark.parametrize("dtype,Di,N,R,M,L,B,chunk", [
+    (BF16, 256, 16, 64, 16, 100, 2, 0),    # fused dt projection + scan, one time chunk
+    (BF16, 256, 16, 64, 16, 100, 2, 16),   # 7 chunks per sequence, the last of 4 tokens
+    (BF16, 256, 16, 64, 16, 100, 2, 48),   # 3 chunks: 48, 48, 4
+    (BF16, 256, 16, 64, 0, 100, 2, 32),    # no meta rows: chunk 0 starts from zero
+    (BF16, 128, 32, 128, 8, 70, 1, 0),
+    (BF16, 128, 32, 128, 8, 70, 1, 16),
+    (BF16, 64, 4, 64, 8, 70, 3, 32),       # one wave per workgroup
+    (BF16, 64, 8, 128, 8, 70, 1, 64),
+    (BF16, 128, 64, 128, 8, 70, 1, 16),
+    (BF16, 128, 128, 128, 8, 133, 1, 32),  # 5 chunks, ragged last step
+    (BF16, 128, 16, 16, 8, 64, 2, 0),      # dt_rank outside the fused set: dt GEMM, then scan
+    (F32, 64, 16, 16, 4, 48, 2, 0),
 ])
-def test_op_scan_matches_oracle(dtype, Di, N, R, M, L, B):
+def test_op_scan_matches_oracle(dtype, Di, N, R, M, L, B, chunk):
     g = rng(60 + Di + N + R, 2)
     rows = M + B * L
     zld = 2 * Di + 16
@@ -79,11 +87,12 @@ def test_op_scan_matches_oracle(dtype, Di, N, R, M, L, B):
     code = DT[dtype]
     y = torch.zeros(rows, Di, dtype=zt.dtype, device=DEV)
     h = torch.zeros(B, Di, N, dtype=torch.float32, device=DEV)
-    ws_n = hy.hymba_op_scan_workspace_bytes(code, M, L, B, Di, N, R)
+    ws_n = hy.hymba_op_scan_workspace_bytes(code, M, L, B, Di, N, R, chunk)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=DEV)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     hy.hymba_op_scan(code, zt.to(DEV), zld, xs_col, g_col, dlt_t.to(DEV), dev(bc), wdt_t.to(DEV),
-                     dev(bias), dev(A), dev(D), y, Di, h, M, L, B, Di, N, R, ws, ws.numel())
+                     dev(bias), dev(A), dev(D), y, Di, h, M, L, B, Di, N, R, chunk, ws,
+                     ws.numel())
     torch.cuda.synchronize()
     dt = orc.softplus(dlt.astype(np.float64) @ wdt.astype(np.float64).T + bias)
     ref_y = np.zeros((rows, Di))
@@ -98,7 +107,8 @@ def test_op_scan_matches_oracle(dtype, Di, N, R, M, L, B):
         else:
             ref_y[idx[M:]] = out[M:]
         ref_h[b] = hT
-    ey, eh = rel_err(to_np(y), ref_y), rel_err(to_np(h), ref_h)
+    ey = rel_err(to_np(y), ref_y)
+    eh = (h_err if dtype == BF16 else rel_err)(to_np(h), ref_h)
     print(f"op_scan y err {ey:.2e} h err {eh:.2e}")
     assert ey < TOL[dtype]
     assert eh < (1e-3 if dtype == BF16 else 1e-4)

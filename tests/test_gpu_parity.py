@@ -12,7 +12,7 @@ import torch
 
 import oracle as orc
 from synth import BF16, F32, CASES, LayerDims, gen_activations, gen_layer_weights
-from tests.gpu_util import (DEV, alloc_kv, alloc_state, kv_struct, make_layer, rel_err,
+from tests.gpu_util import (DEV, alloc_kv, alloc_state, h_err, kv_struct, make_layer, rel_err,
                             state_struct, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -48,7 +48,7 @@ def gpu_prefill(dims, wts, meta_t, x_t, ring_slots=None, kv_in=None):
 
 def check_prefill(dims, g, ref, tol_y, tol_h, pure=None, ring=False):
     M = dims.n_meta
-    errs = {"y": rel_err(g["y"], ref["y"]), "h": rel_err(g["h"], ref["h"])}
+    errs = {"y": rel_err(g["y"], ref["y"]), "h": h_err(g["h"], ref["h"])}
     if M:
         errs["y_meta"] = rel_err(g["y_meta"], ref["y_meta"][0])
     if ring:
@@ -204,7 +204,7 @@ def test_small_bf16_decode_ring_wrap():
         torch.cuda.synchronize()
         e = rel_err(to_np(y), o["y"])
         assert e < TOL_BF16, (s, e)
-    assert rel_err(to_np(st["h"]), o["h"]) < TOL_H
+    assert h_err(to_np(st["h"]), o["h"]) < TOL_H
     assert rel_err(to_np(kv["k"]), o["k"]) < TOL_BF16
     assert rel_err(to_np(kv["v"]), o["v"]) < TOL_BF16
     assert np.all(st["pos"].cpu().numpy() == L + steps)
@@ -235,7 +235,7 @@ def test_bf16_ragged_k_slices():
         torch.cuda.synchronize()
         e = rel_err(to_np(y), o["y"])
         assert e < TOL_BF16, (s, e)
-    assert rel_err(to_np(st["h"]), o["h"]) < TOL_H
+    assert h_err(to_np(st["h"]), o["h"]) < TOL_H
 
 
 @pytest.mark.parametrize("head_dim,n_kv", [(128, 2), (64, 4)])
@@ -263,7 +263,7 @@ def test_bf16_decode_streaming_attention(head_dim, n_kv):
         e = rel_err(to_np(y), o["y"])
         assert e < TOL_BF16, (s, e)
     print("last step y err", f"{e:.2e}")
-    assert rel_err(to_np(st["h"]), o["h"]) < TOL_H
+    assert h_err(to_np(st["h"]), o["h"]) < TOL_H
     assert rel_err(to_np(kv["k"]), o["k"]) < TOL_BF16
     assert np.all(st["pos"].cpu().numpy() == L + steps)
 
@@ -313,7 +313,7 @@ def test_config1_full_size_sampled_sequences():
     for b in (0, case.batch - 1):
         ref = orc.prefill(dims, w, meta, x[b:b + 1], contract=True, ring_slots=1024)
         errs = {"y": rel_err(g["y"][b], ref["y"][0]), "y_meta": rel_err(g["y_meta"], ref["y_meta"][0]),
-                "h": rel_err(g["h"][b], ref["h"][0]), "k": rel_err(g["k"][b], ref["k"][0]),
+                "h": h_err(g["h"][b], ref["h"][0]), "k": rel_err(g["k"][b], ref["k"][0]),
                 "v": rel_err(g["v"][b], ref["v"][0])}
         print(b, {k: f"{v:.2e}" for k, v in errs.items()})
         for k, v in errs.items():
