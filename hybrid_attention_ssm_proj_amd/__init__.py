@@ -18,7 +18,8 @@ __all__ = [
     "hymba_op_attn", "hymba_op_attn_workspace_bytes", "hymba_op_scan",
     "hymba_op_scan_workspace_bytes",
     "HymbaError", "LayerDesc", "LayerWeights", "KV", "SSMState", "load_library",
-    "hymba_layer_prefill", "hymba_layer_decode", "hymba_layer_workspace_bytes",
+    "hymba_layer_prefill", "hymba_layer_decode", "hymba_layer_decode_static",
+    "hymba_layer_workspace_bytes",
     "hymba_status_str", "hymba_abi_version", "hymba_last_hip_error", "hymba_timer_enable",
     "hymba_timer_read", "hymba_op_gemm", "hymba_op_copy", "HymbaLayer", "STAGES",
     "DTYPE_F32", "DTYPE_BF16", "LIB_PATH",
@@ -102,6 +103,10 @@ def load_library() -> ctypes.CDLL:
         "hymba_layer_decode": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P,
                                      I32, ctypes.POINTER(KV), ctypes.POINTER(SSMState), P, P, SZ,
                                      P]),
+        "hymba_layer_decode_static": (I32, [ctypes.POINTER(LayerDesc),
+                                            ctypes.POINTER(LayerWeights), P, I32,
+                                            ctypes.POINTER(KV), ctypes.POINTER(SSMState), P,
+                                            P]),
         "hymba_layer_workspace_bytes": (SZ, [ctypes.POINTER(LayerDesc), I32, I32, I32]),
         "hymba_layer_meta_cache_build": (I32, [ctypes.POINTER(LayerDesc),
                                                ctypes.POINTER(LayerWeights), P, ctypes.POINTER(KV),
@@ -203,6 +208,16 @@ def hymba_layer_decode(desc, weights, x, batch, kv, state, y, workspace, workspa
         _ptr(workspace), workspace_bytes, _stream(stream))
     if check:
         _check(st, "hymba_layer_decode")
+    return st
+
+
+def hymba_layer_decode_static(desc, weights, x, batch, kv, state, y, stream=None,
+                              check=True) -> int:
+    st = load_library().hymba_layer_decode_static(
+        ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, _ref(kv), _ref(state), _ptr(y),
+        _stream(stream))
+    if check:
+        _check(st, "hymba_layer_decode_static")
     return st
 
 

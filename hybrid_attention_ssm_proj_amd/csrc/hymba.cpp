@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -294,6 +295,34 @@ hymba_status check_weights(const hymba_layer_weights* w, const Shape& s) {
 }
 
 char* ws_ptr(void* ws, size_t off) { return (char*)ws + off; }
+
+// ----------------------------------------------------------------- static scratch
+// The workspace of hymba_layer_decode_static: a fixed array in device memory, one copy per
+// device the library runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in; its device address on the current device comes from
+// hipGetSymbolAddress, once per device, and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = HYMBA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hymba_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return HYMBA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e);
+    if (p == nullptr) return fail_hip(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HYMBA_OK;
+}
 
 }  // namespace
 
@@ -741,6 +770,24 @@ hymba_status hymba_layer_prefill_cached(const hymba_layer_desc* desc,
   if (cache == nullptr) return HYMBA_ERR_INVALID_ARG;
   return prefill_impl(desc, w, nullptr, x, batch, seq_len, kv_in, kv_out, state_out, y, nullptr,
                       cache, nullptr, workspace, workspace_bytes, stream);
+}
+
+hymba_status hymba_layer_decode_static(const hymba_layer_desc* desc,
+                                       const hymba_layer_weights* w, const void* x,
+                                       int32_t batch, hymba_kv* kv, hymba_ssm_state* state,
+                                       void* y, void* stream) {
+  if (batch < 0 || kv == nullptr || kv->slots <= 0) return HYMBA_ERR_INVALID_ARG;
+  const size_t need = hymba_layer_workspace_bytes(desc, batch, kv->slots, 1);
+  if (need == 0 && batch > 0) {  // the descriptor itself is rejected: let the call say why
+    return hymba_layer_decode(desc, w, x, batch, kv, state, y, nullptr, 0, stream);
+  }
+  if (need > kStaticScratchBytes) return HYMBA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (batch > 0) {
+    hymba_status st = static_scratch(&ws);
+    if (st != HYMBA_OK) return st;
+  }
+  return hymba_layer_decode(desc, w, x, batch, kv, state, y, ws, kStaticScratchBytes, stream);
 }
 
 hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_weights* w,

@@ -185,6 +185,27 @@ hymba_status hymba_layer_decode(const hymba_layer_desc *desc, const hymba_layer_
                                 size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * hymba_layer_decode_static: hymba_layer_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as hymba_layer_decode, without the workspace:
+ * the library uses a fixed scratch array of HYMBA_STATIC_SCRATCH_BYTES in device memory
+ * instead (one per device, resident from the library's first use on that device until
+ * the process ends; its address is looked up once per device, with that device current).
+ * The call allocates nothing and frees nothing.
+ *   Returns HYMBA_ERR_WORKSPACE when the decode workspace for this batch and ring
+ *   (hymba_layer_workspace_bytes(desc, batch, kv->slots, 1)) exceeds the array.
+ *   Every call on a device shares that device's array and leaves its contents behind;
+ *   nothing is assumed about them on entry (the split-K accumulators are cleared by the
+ *   call's own first kernel).  Calls that overlap on one device (other streams, other host
+ *   threads) race on the array: order them on one stream.
+ * ------------------------------------------------------------------------- */
+#define HYMBA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+hymba_status hymba_layer_decode_static(const hymba_layer_desc *desc,
+                                       const hymba_layer_weights *w, const void *x,
+                                       int32_t batch, hymba_kv *kv, hymba_ssm_state *state,
+                                       void *y, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Meta-prefix cache: what a layer computes over its M meta tokens alone.  The meta
  * tokens are fixed at inference and act as a learned initialisation of the KV cache and
  * of the SSM state ("Meta Tokens"), so these values do not depend on X and can be built

@@ -202,6 +202,27 @@ def test_decode_argument_errors(lib):
     assert call(batch=0) == 0
 
 
+def test_decode_static_rejects_before_any_launch(lib):
+    """The static-scratch decode: a batch whose workspace exceeds the fixed array is
+    refused with HYMBA_ERR_WORKSPACE, bad arguments with HYMBA_ERR_INVALID_ARG, before
+    the device is touched."""
+    d = desc_of(4)
+    w = _weights_struct()
+    kv = hy.KV(4096, 4096, 4096, 4096, 1024)
+    state = hy.SSMState(4096, 4096)
+    call = lambda **kw: hy.hymba_layer_decode_static(**{**dict(
+        desc=d, weights=w, x=4096, batch=2, kv=kv, state=state, y=4096), **kw}, stream=0,
+        check=False)
+    big = 4096  # 4096 sequences: about 0.6 GB of decode workspace
+    assert hy.hymba_layer_workspace_bytes(d, big, 1024, 1) > (64 << 20)
+    assert call(batch=big) == 3
+    assert 0 < hy.hymba_layer_workspace_bytes(d, 128, 1024, 1) <= (64 << 20)
+    assert call(kv=None) == 1
+    assert call(batch=-1) == 1
+    assert call(kv=hy.KV(4096, 4096, 4096, 4096, 0)) == 1
+    assert call(desc=desc_of(4, d_state=24)) == 2       # the descriptor's own error
+
+
 def test_op_gemm_argument_errors(lib):
     call = lambda **kw: lib.hymba_op_gemm(*[{**dict(
         dtype=1, a=4096, lda=64, b=4096, ldb=64, c=4096, ldc=64, c_dtype=1, m=4, n=4, k=64,
