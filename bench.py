@@ -50,6 +50,9 @@ def parse():
                     help="skip the 16-layer partial-SWA vs all-global stack comparison")
     ap.add_argument("--no-head-ssm", action="store_true",
                     help="skip the layer variants (Mamba-2 head, group-norm fusion, block)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the layer-pair (B=4, L=8192) and long-context (L=32768) "
+                         "prefill workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the prefill workload the CPU oracle runs (8 = all)")
@@ -82,16 +85,17 @@ def stage_work(dims, B, L):
     pairs_meta = M * (M + 1) // 2
     attn_flops = 4 * dims.head_dim * dims.n_q_heads * (B * pairs_seq + pairs_meta)
     return {
-        # the batch-shared meta rows go through in_proj and out_proj in launches of
-        # their own (two per step)
+        # the batch-shared meta rows go through in_proj, the scan and out_proj in
+        # launches of their own
         "meta": ("mfma", 2.0 * M * (dims.n_in + dims.f_width) * d),
         "in_proj": ("mfma", 2.0 * B * L * dims.n_in * d),
         "attn": ("mfma", float(attn_flops)),
         "x_proj": ("mfma", 2.0 * rows * dims.n_xproj * Di),
         "dt_proj": ("mfma", 2.0 * rows * Di * R),
         # bytes: x, G, y (bf16) per (row, channel), delta (bf16) and B, C (fp32) per row,
-        # h once; dt is computed in the scan and never stored
-        "scan": ("hbm", float(rows * (Di * 6 + 2 * R + 8 * N) + B * Di * N * 4)),
+        # h once; dt is computed in the scan and never stored.  The scan stage is the
+        # launch over the B*L sequence rows (the meta rows are scanned once, in "meta")
+        "scan": ("hbm", float(B * L * (Di * 6 + 2 * R + 8 * N) + B * Di * N * 4)),
         # bytes: bf16 prefill with the fused scan derives two factors per row from the
         # partial sums of squares (read), writes them, and rescales the meta rows of F in
         # place (out_proj applies the factors); otherwise the pass reads O and Y_ssm and
@@ -245,7 +249,7 @@ def main():
             entry.update(roofline_entry(bound, wk / rec["per_step"], rec["avg_ms"]))
         if name == "scan":
             # exponentials rows * Di * N against the v_exp_f32 rate measured on this chip
-            exps = (dims.n_meta + B * L) * dims.d_inner * dims.d_state
+            exps = B * L * dims.d_inner * dims.d_state
             rate = exps / (rec["avg_ms"] * 1e-3)
             entry["exp"] = {"achieved": round(rate / 1e12, 3), "peak": PEAK_EXP_TPS,
                             "unit": "Texp/s", "frac": round(rate / 1e12 / PEAK_EXP_TPS, 4)}
@@ -302,6 +306,11 @@ def main():
     if not args.no_stack:
         stack = bench_stack(hy, torch, dev)
 
+    pair = long_ctx = None
+    if not args.no_long:
+        pair = bench_pair(hy, torch, dev, args)
+        long_ctx = bench_long(hy, torch, dev, args)
+
     head_ssm = group_norm = block = None
     if not args.no_head_ssm:
         head_ssm = bench_head_ssm(hy, torch, dev, args, stages)
@@ -326,6 +335,8 @@ def main():
         "decode": decode,
         "prefill_meta_cached": cached,
         "stack": stack,
+        "layer_pair": pair,
+        "long_context": long_ctx,
         "head_ssm": head_ssm,
         "group_norm": group_norm,
         "block": block,
@@ -367,6 +378,132 @@ def prefill_variant(hy, torch, dev, args, dims, seed):
     del layer
     torch.cuda.empty_cache()
     return ms, stages
+
+
+def _scan_entry(dims, B, L, rec):
+    """The sequence launch of the scan: its time, its algorithmic HBM bytes (x, G, y bf16
+    per (row, channel); delta bf16, B and C fp32 per row; h once) and exponentials
+    (rows x Di x N) against the v_exp_f32 rate of this chip."""
+    Di, N, R = dims.d_inner, dims.d_state, dims.dt_rank
+    rows = B * L
+    nbytes = rows * (Di * 6 + 2 * R + 8 * N) + B * Di * N * 4
+    exps = rows * Di * N
+    ms = rec["avg_ms"]
+    out = roofline_entry("hbm", nbytes, ms)
+    out["avg_ms"] = round(ms, 4)
+    out["exp"] = {"achieved": round(exps / (ms * 1e-3) / 1e12, 3), "peak": PEAK_EXP_TPS,
+                  "unit": "Texp/s", "frac": round(exps / (ms * 1e-3) / 1e12 / PEAK_EXP_TPS, 4)}
+    return out
+
+
+def _layer_io(torch, dims, B, L, seed, dev):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    meta = torch.randn(dims.n_meta, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    x = torch.randn(B, L, dims.d_model, generator=gen, device=dev).to(torch.bfloat16)
+    return meta, x
+
+
+def bench_pair(hy, torch, dev, args):
+    """The layer-pair workload: two sliding-window layers (window 1024) over B=4, L=8192
+    with 128 meta tokens; the first is a producer keeping every position of its K/V, the
+    second a consumer reading them (cross-layer KV sharing).  Layer 2 takes layer 1's y
+    and y_meta.  tokens/s counts B*L per pair; stage times are per layer."""
+    from synth import CASES
+    case = CASES[2]
+    p_dims = case.dims
+    c_dims = p_dims.replace(kv_share=1)
+    B, L, M = case.batch, case.seq_len, p_dims.n_meta
+    log(f"[bench] layer pair {case.name}: B={B} L={L} W={p_dims.window}")
+    l1 = hy.HymbaLayer(p_dims, device_weights(torch, p_dims, 2001, dev), device=dev)
+    l2 = hy.HymbaLayer(c_dims, device_weights(torch, c_dims, 2002, dev), device=dev)
+    meta, x = _layer_io(torch, p_dims, B, L, 2003, dev)
+    Hkv, dh = p_dims.n_kv_heads, p_dims.head_dim
+    kv = {n: torch.empty(shape, dtype=torch.bfloat16, device=dev) for n, shape in (
+        ("k_meta", (Hkv, M, dh)), ("v_meta", (Hkv, M, dh)), ("k", (B, Hkv, L, dh)),
+        ("v", (B, Hkv, L, dh)))}
+    kvs = hy.make_kv(kv["k_meta"], kv["v_meta"], kv["k"], kv["v"])
+    y1 = torch.empty(B, L, p_dims.d_model, dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty_like(y1)
+    ym1 = torch.empty(M, p_dims.d_model, dtype=torch.bfloat16, device=dev)
+    ym2 = torch.empty_like(ym1)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        l1.prefill(meta, x, kv_out=kvs, y=y1, y_meta=ym1, stream=stream)
+        l2.prefill(ym1, y1, kv_in=kvs, y=y2, y_meta=ym2, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    stages = stage_pass(hy, torch, step, 3, -1)
+    steps = max(3, args.steps // 4)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    scan = _scan_entry(p_dims, B, L, {"avg_ms": stages["scan"]["avg_ms"]})
+    del l1, l2, kv, y1, y2
+    torch.cuda.empty_cache()
+    log(f"[bench] layer pair: {ms:.3f} ms per pair, {B * L / ms / 1e3:.3f} M tokens/s; "
+        f"scan {scan['avg_ms']:.3f} ms per layer")
+    return {"workload": "two layers, bf16, B=4, L=8192, 128 meta tokens, window 1024; the "
+                        "second reuses the first's K/V; d=2048, 16x128 q / 4 kv heads, "
+                        "Di=4096, N=16",
+            "value": round(B * L / ms * 1e3, 1), "unit": "tokens/s", "ms_per_pair": round(ms, 4),
+            "scan_per_layer": scan,
+            "stages_ms_per_layer": {k: round(v["avg_ms"] * v["per_step"] / 2, 4)
+                                    for k, v in stages.items()}}
+
+
+def bench_long(hy, torch, dev, args):
+    """The long-context workload: one layer, B=1, L=32768 after 128 meta tokens, window
+    1024, state 128.  The scan runs in time chunks chosen by the library; the same
+    layer with one chunk (the plain serial scan) is timed beside it."""
+    from synth import CASES
+    case = CASES[3]
+    dims = case.dims
+    B, L, M = case.batch, case.seq_len, dims.n_meta
+    log(f"[bench] long context {case.name}: B={B} L={L} N={dims.d_state}")
+    w = device_weights(torch, dims, 3001, dev)
+    meta, x = _layer_io(torch, dims, B, L, 3002, dev)
+    y = torch.empty(B, L, dims.d_model, dtype=torch.bfloat16, device=dev)
+    ym = torch.empty(M, dims.d_model, dtype=torch.bfloat16, device=dev)
+    h = torch.empty(B, dims.d_inner, dims.d_state, device=dev)
+    pos = torch.empty(B, dtype=torch.int32, device=dev)
+    state = hy.make_state(h, pos)
+    stream = torch.cuda.current_stream()
+    out = {"workload": "one layer, bf16, B=1, L=32768, 128 meta tokens, window 1024, d=2048, "
+                       "16x128 q / 4 kv heads, Di=4096, N=128"}
+    for name, chunk in (("chunked", 0), ("one_chunk", L)):
+        layer = hy.HymbaLayer(dims.replace(scan_chunk=chunk), w, device=dev)
+
+        def step():
+            layer.prefill(meta, x, state_out=state, y=y, y_meta=ym, stream=stream)
+
+        step()
+        stages = stage_pass(hy, torch, step, 2, -1)
+        if name == "chunked":
+            steps = max(3, args.steps // 4)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) / steps * 1e3
+            out.update(value=round(B * L / ms * 1e3, 1), unit="tokens/s", ms_per_step=round(ms, 4),
+                       scan=_scan_entry(dims, B, L, stages["scan"]),
+                       stages_ms={k: round(v["avg_ms"] * v["per_step"], 4)
+                                  for k, v in stages.items()})
+        else:
+            out["one_chunk_scan_ms"] = round(stages["scan"]["avg_ms"], 4)
+        del layer
+        torch.cuda.empty_cache()
+    log(f"[bench] long context: {out['ms_per_step']:.3f} ms/step, "
+        f"{out['value'] / 1e6:.3f} M tokens/s; scan {out['scan']['avg_ms']:.3f} ms "
+        f"(one chunk: {out['one_chunk_scan_ms']:.3f} ms)")
+    return out
 
 
 def bench_block(hy, torch, dev, args, layer_ms):

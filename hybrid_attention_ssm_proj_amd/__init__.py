@@ -19,6 +19,7 @@ __all__ = [
     "hymba_op_scan_workspace_bytes",
     "HymbaError", "LayerDesc", "LayerWeights", "KV", "SSMState", "load_library",
     "hymba_layer_prefill", "hymba_layer_decode", "hymba_layer_decode_static",
+    "hymba_kv_ring_fill",
     "hymba_layer_workspace_bytes",
     "hymba_status_str", "hymba_abi_version", "hymba_last_hip_error", "hymba_timer_enable",
     "hymba_timer_read", "hymba_op_gemm", "hymba_op_copy", "HymbaLayer", "STAGES",
@@ -72,7 +73,8 @@ class LayerWeights(ctypes.Structure):
 
 class KV(ctypes.Structure):
     _fields_ = [("k_meta", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
-                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slots", ctypes.c_int32)]
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slots", ctypes.c_int32),
+                ("is_ring", ctypes.c_int32)]
 
 
 class SSMState(ctypes.Structure):
@@ -108,6 +110,8 @@ def load_library() -> ctypes.CDLL:
                                             ctypes.POINTER(KV), ctypes.POINTER(SSMState), P,
                                             P]),
         "hymba_layer_workspace_bytes": (SZ, [ctypes.POINTER(LayerDesc), I32, I32, I32]),
+        "hymba_kv_ring_fill": (I32, [ctypes.POINTER(KV), ctypes.POINTER(KV), I32, I32, I32, I32,
+                                     I32, I32, P]),
         "hymba_layer_meta_cache_build": (I32, [ctypes.POINTER(LayerDesc),
                                                ctypes.POINTER(LayerWeights), P, ctypes.POINTER(KV),
                                                ctypes.POINTER(MetaCache), P, SZ, P]),
@@ -218,6 +222,15 @@ def hymba_layer_decode_static(desc, weights, x, batch, kv, state, y, stream=None
         _stream(stream))
     if check:
         _check(st, "hymba_layer_decode_static")
+    return st
+
+
+def hymba_kv_ring_fill(src, dst, batch, seq_len, n_meta, n_kv_heads, head_dim, dtype,
+                       stream=None, check=True) -> int:
+    st = load_library().hymba_kv_ring_fill(ctypes.byref(src), ctypes.byref(dst), batch, seq_len,
+                                           n_meta, n_kv_heads, head_dim, dtype, _stream(stream))
+    if check:
+        _check(st, "hymba_kv_ring_fill")
     return st
 
 
@@ -455,8 +468,10 @@ class HymbaBlock(HymbaLayer):
         return y
 
 
-def make_kv(k_meta, v_meta, k, v) -> KV:
-    return KV(_ptr(k_meta), _ptr(v_meta), _ptr(k), _ptr(v), int(k.shape[2]))
+def make_kv(k_meta, v_meta, k, v, is_ring: bool = True) -> KV:
+    """A cache over tensors k/v [B, Hkv, slots, dh]: a ring of the last `slots` positions
+    (is_ring) or one slot per position."""
+    return KV(_ptr(k_meta), _ptr(v_meta), _ptr(k), _ptr(v), int(k.shape[2]), int(bool(is_ring)))
 
 
 def make_state(h, pos) -> SSMState:

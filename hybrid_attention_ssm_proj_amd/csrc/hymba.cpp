@@ -435,6 +435,8 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
     if (kv_out != nullptr) {
       if (kv_out->slots <= 0 || kv_out->k == nullptr || kv_out->v == nullptr)
         return HYMBA_ERR_INVALID_ARG;
+      if (kv_out->is_ring != 0 && kv_out->is_ring != 1) return HYMBA_ERR_INVALID_ARG;
+      if (!kv_out->is_ring && kv_out->slots < L) return HYMBA_ERR_INVALID_ARG;
       if (Mr > 0 && (kv_out->k_meta == nullptr || kv_out->v_meta == nullptr))
         return HYMBA_ERR_INVALID_ARG;
       if (any_misaligned(kv_out->k, kv_out->v, kv_out->k_meta, kv_out->v_meta))
@@ -770,6 +772,45 @@ hymba_status hymba_layer_prefill_cached(const hymba_layer_desc* desc,
   if (cache == nullptr) return HYMBA_ERR_INVALID_ARG;
   return prefill_impl(desc, w, nullptr, x, batch, seq_len, kv_in, kv_out, state_out, y, nullptr,
                       cache, nullptr, workspace, workspace_bytes, stream);
+}
+
+hymba_status hymba_kv_ring_fill(const hymba_kv* src, hymba_kv* dst, int32_t batch,
+                                int32_t seq_len, int32_t n_meta, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t dtype, void* stream) {
+  if (src == nullptr || dst == nullptr || batch < 0 || seq_len < 0 || n_meta < 0 ||
+      n_kv_heads <= 0 || head_dim <= 0)
+    return HYMBA_ERR_INVALID_ARG;
+  if (dtype != HYMBA_DTYPE_F32 && dtype != HYMBA_DTYPE_BF16) return HYMBA_ERR_INVALID_ARG;
+  if ((src->is_ring != 0 && src->is_ring != 1) || (dst->is_ring != 0 && dst->is_ring != 1))
+    return HYMBA_ERR_INVALID_ARG;
+  const bool b16 = dtype == HYMBA_DTYPE_BF16;
+  if (head_dim % (b16 ? 8 : 4)) return HYMBA_ERR_UNSUPPORTED;
+  if (src->slots <= 0 || dst->slots <= 0) return HYMBA_ERR_INVALID_ARG;
+  const int n_last = std::min(seq_len, dst->slots);
+  // src must hold positions [L - n_last, L); a non-ring dst must hold every position
+  if (src->is_ring ? src->slots < n_last : src->slots < seq_len) return HYMBA_ERR_INVALID_ARG;
+  if (!dst->is_ring && dst->slots < seq_len) return HYMBA_ERR_INVALID_ARG;
+  const bool copy_meta = n_meta > 0 && (src->k_meta != dst->k_meta || src->v_meta != dst->v_meta);
+  if (batch > 0 && n_last > 0 &&
+      (src->k == nullptr || src->v == nullptr || dst->k == nullptr || dst->v == nullptr))
+    return HYMBA_ERR_INVALID_ARG;
+  if (copy_meta && (src->k_meta == nullptr || src->v_meta == nullptr || dst->k_meta == nullptr ||
+                    dst->v_meta == nullptr))
+    return HYMBA_ERR_INVALID_ARG;
+  if (any_misaligned(src->k, src->v, src->k_meta, src->v_meta, dst->k, dst->v, dst->k_meta,
+                     dst->v_meta))
+    return HYMBA_ERR_ALIGNMENT;
+  if ((int64_t)batch * n_last + n_meta >= ((int64_t)1 << 31)) return HYMBA_ERR_UNSUPPORTED;
+  hipStream_t stream_ = (hipStream_t)stream;
+  {
+    hipStream_t stream = stream_;  // for the stage timer
+    HYMBA_LAUNCH(HYMBA_STAGE_KV_WRITE,
+                 launch_kv_ring_fill(b16, src->k, src->v, src->slots, src->k_meta, src->v_meta,
+                                     dst->k, dst->v, dst->slots, dst->k_meta, dst->v_meta,
+                                     copy_meta, n_meta, seq_len, n_last, batch, n_kv_heads,
+                                     head_dim, stream));
+  }
+  return HYMBA_OK;
 }
 
 hymba_status hymba_layer_decode_static(const hymba_layer_desc* desc,

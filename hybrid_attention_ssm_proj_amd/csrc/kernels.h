@@ -280,6 +280,13 @@ hipError_t launch_kv_write_prefill(bool bf16, const void* z, int64_t z_stride, i
                                    int v_col, void* k_meta, void* v_meta, void* k, void* v,
                                    int slots, int n_meta, int L, int B, int Hkv,
                                    int head_dim, hipStream_t s);
+// Copy the last n_last positions p of every sequence from src (slot p % src_slots) to
+// dst (slot p % dst_slots), and the n_meta meta entries when copy_meta.
+hipError_t launch_kv_ring_fill(bool bf16, const void* src_k, const void* src_v, int src_slots,
+                               const void* src_k_meta, const void* src_v_meta, void* dst_k,
+                               void* dst_v, int dst_slots, void* dst_k_meta, void* dst_v_meta,
+                               bool copy_meta, int n_meta, int L, int n_last, int B, int Hkv,
+                               int head_dim, hipStream_t s);
 // Decode: write row b's K/V at slot pos[b] % slots.
 hipError_t launch_kv_write_decode(bool bf16, const void* z, int64_t z_stride, int k_col,
                                   int v_col, void* k, void* v, int slots,

@@ -570,6 +570,65 @@ hipError_t launch_kv_write_prefill(bool bf16_, const void* z, int64_t z_stride, 
   return hipGetLastError();
 }
 
+// One 16-byte piece per thread: rows [meta entries (when copying them) | B * n_last
+// positions] x Hkv heads x head_dim pieces x {K, V}.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_ring_fill_kernel(const T* sk, const T* sv, int sslots,
+                                                           const T* skm, const T* svm, T* dk,
+                                                           T* dv, int dslots, T* dkm, T* dvm,
+                                                           int n_meta_copy, int n_meta, int L,
+                                                           int n_last, int B, int Hkv, int dh) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int cpr = dh / EPC;
+  const int64_t total = (int64_t)(n_meta_copy + (int64_t)B * n_last) * Hkv * cpr * 2;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  int64_t r = gid;
+  const int which = (int)(r % 2);
+  r /= 2;
+  const int dc = (int)(r % cpr);
+  r /= cpr;
+  const int g = (int)(r % Hkv);
+  r /= Hkv;
+  const T* src;
+  T* dst;
+  if (r < n_meta_copy) {
+    const int64_t o = ((int64_t)g * n_meta + r) * dh;
+    src = (which ? svm : skm) + o;
+    dst = (which ? dvm : dkm) + o;
+  } else {
+    const int64_t q = r - n_meta_copy;
+    const int b = (int)(q / n_last);
+    const int p = L - n_last + (int)(q % n_last);
+    src = (which ? sv : sk) + (((int64_t)b * Hkv + g) * sslots + (p % sslots)) * dh;
+    dst = (which ? dv : dk) + (((int64_t)b * Hkv + g) * dslots + (p % dslots)) * dh;
+  }
+  *(u32x4*)(dst + dc * EPC) = *(const u32x4*)(src + dc * EPC);
+}
+
+hipError_t launch_kv_ring_fill(bool bf16_, const void* src_k, const void* src_v, int src_slots,
+                               const void* src_k_meta, const void* src_v_meta, void* dst_k,
+                               void* dst_v, int dst_slots, void* dst_k_meta, void* dst_v_meta,
+                               bool copy_meta, int n_meta, int L, int n_last, int B, int Hkv,
+                               int head_dim, hipStream_t s) {
+  const int esz = bf16_ ? 2 : 4;
+  const int nm = copy_meta ? n_meta : 0;
+  const int64_t total = (int64_t)(nm + (int64_t)B * n_last) * Hkv * (head_dim * esz / 16) * 2;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (bf16_)
+    kv_ring_fill_kernel<bf16><<<dim3(blocks), dim3(256), 0, s>>>(
+        (const bf16*)src_k, (const bf16*)src_v, src_slots, (const bf16*)src_k_meta,
+        (const bf16*)src_v_meta, (bf16*)dst_k, (bf16*)dst_v, dst_slots, (bf16*)dst_k_meta,
+        (bf16*)dst_v_meta, nm, n_meta, L, n_last, B, Hkv, head_dim);
+  else
+    kv_ring_fill_kernel<float><<<dim3(blocks), dim3(256), 0, s>>>(
+        (const float*)src_k, (const float*)src_v, src_slots, (const float*)src_k_meta,
+        (const float*)src_v_meta, (float*)dst_k, (float*)dst_v, dst_slots, (float*)dst_k_meta,
+        (float*)dst_v_meta, nm, n_meta, L, n_last, B, Hkv, head_dim);
+  return hipGetLastError();
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void kv_write_decode_kernel(const T* z, int64_t zs, int k_col,
                                                               int v_col, T* k, T* v, int slots,

@@ -24,7 +24,8 @@ from __future__ import annotations
 
 from typing import List, Optional
 
-from . import (HymbaLayer, KV, SSMState, make_kv, make_state)
+from . import (DTYPE_BF16, DTYPE_F32, HymbaLayer, KV, SSMState, hymba_kv_ring_fill, make_kv,
+               make_state)
 
 
 def schedule(n_layers: int, window: int, global_layers: Optional[List[int]] = None):
@@ -123,13 +124,15 @@ class HymbaStack:
                       and self.sched[l + 1][1] == 1)
             if share:
                 c = self.caches[prod]
-                kv_in = make_kv(c["k_meta"], c["v_meta"], self.scratch["k"], self.scratch["v"])
+                kv_in = make_kv(c["k_meta"], c["v_meta"], self.scratch["k"], self.scratch["v"],
+                                is_ring=False)
                 y, ym = layer.prefill(meta, x, kv_in=kv_in, state_out=self._state(l),
                                       stream=stream)
-                self._fill_ring(prod, L)
+                self._fill_ring(prod, B, L, stream)
             elif paired:
                 c = self.caches[l]
-                kv_out = make_kv(c["k_meta"], c["v_meta"], self.scratch["k"], self.scratch["v"])
+                kv_out = make_kv(c["k_meta"], c["v_meta"], self.scratch["k"], self.scratch["v"],
+                                 is_ring=False)
                 y, ym = layer.prefill(meta, x, kv_out=kv_out, state_out=self._state(l),
                                       stream=stream)
             else:
@@ -140,16 +143,17 @@ class HymbaStack:
             meta, x = ym, y
         return x, meta
 
-    def _fill_ring(self, l: int, L: int):
-        """Producer l's ring of `window` slots from the scratch cache: position p at
-        slot p mod window, for the last min(L, window) positions."""
-        import torch
+    def _fill_ring(self, l: int, B: int, L: int, stream=None):
+        """Producer l's ring of `window` slots from the scratch cache (the library's ring
+        fill, on the layers' stream): position p at slot p mod window, for the last
+        min(L, window) positions."""
         ring = self.caches[l]
-        S = ring["k"].shape[2]
-        n = min(L, S)
-        pos = torch.arange(L - n, L, device=self.device)
-        ring["k"][:, :, pos % S] = self.scratch["k"][:, :, pos]
-        ring["v"][:, :, pos % S] = self.scratch["v"][:, :, pos]
+        src = make_kv(ring["k_meta"], ring["v_meta"], self.scratch["k"], self.scratch["v"],
+                      is_ring=False)
+        dst = make_kv(ring["k_meta"], ring["v_meta"], ring["k"], ring["v"])
+        d = self.dims
+        hymba_kv_ring_fill(src, dst, B, L, d.n_meta, d.n_kv_heads, d.head_dim,
+                           DTYPE_BF16 if d.dtype == "bf16" else DTYPE_F32, stream)
 
     def decode(self, x, stream=None):
         """One token per sequence through every layer; returns the last layer's y."""

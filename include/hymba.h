@@ -131,13 +131,18 @@ typedef struct {
 } hymba_layer_weights;
 
 /* Attention cache (device, dtype).  X-position p of sequence b lives at slot
- * p % slots of k/v; the M meta entries are batch-shared. */
+ * p % slots of k/v; the M meta entries are batch-shared.  is_ring = 1: a ring holding the
+ * last `slots` positions (the sliding-window decode cache); is_ring = 0: every position
+ * has its own slot, so the cache must cover every position a call writes or reads
+ * (a prefill's kv_out needs slots >= L; a decode needs pos[b] < slots, which the caller
+ * guarantees).  A consumer's kv_in always needs every position (slots >= L). */
 typedef struct {
-  void *k_meta;   /* [Hkv, M, dh]            */
-  void *v_meta;   /* [Hkv, M, dh]            */
-  void *k;        /* [B, Hkv, slots, dh]     */
-  void *v;        /* [B, Hkv, slots, dh]     */
-  int32_t slots;  /* ring capacity S (> 0)   */
+  void *k_meta;    /* [Hkv, M, dh]            */
+  void *v_meta;    /* [Hkv, M, dh]            */
+  void *k;         /* [B, Hkv, slots, dh]     */
+  void *v;         /* [B, Hkv, slots, dh]     */
+  int32_t slots;   /* capacity S (> 0)        */
+  int32_t is_ring; /* 1: slot = p % slots     */
 } hymba_kv;
 
 /* SSM recurrent state (device). */
@@ -183,6 +188,20 @@ hymba_status hymba_layer_decode(const hymba_layer_desc *desc, const hymba_layer_
                                 const void *x, int32_t batch, hymba_kv *kv,
                                 hymba_ssm_state *state, void *y, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * hymba_kv_ring_fill: copies the last min(L, dst->slots) positions of every sequence
+ * from src (slot p % src->slots) into dst (slot p % dst->slots), and src's M meta entries
+ * into dst's when the two meta arrays differ.  For a KV-sharing pair whose prefill runs
+ * on a full-length cache (the consumer reads every position) while decode keeps a
+ * window-sized ring ("Cross-layer KV sharing"; "Combine global and local attention").
+ * src must hold those positions: src->slots >= L, or src->is_ring with src->slots >=
+ * min(L, dst->slots).  dtype, n_kv_heads, head_dim and n_meta describe both caches.
+ * Ordered on `stream` after the prefill that wrote src.
+ * ------------------------------------------------------------------------- */
+hymba_status hymba_kv_ring_fill(const hymba_kv *src, hymba_kv *dst, int32_t batch,
+                                int32_t seq_len, int32_t n_meta, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t dtype, void *stream);
 
 /* ---------------------------------------------------------------------------
  * hymba_layer_decode_static: hymba_layer_decode for callers that cannot allocate device

@@ -8,7 +8,8 @@ Distributions follow the layer workloads used throughout (weights N(0, 0.02),
 meta tokens and X N(0, 1), dt bias U[-4, -2], A = -exp(U[0, 2]), D N(0, 1),
 beta = 1).  Streams are numpy PCG64 seeded with SeedSequence([1000 + case, role]):
 role 0 = meta tokens, 1 = X, 10 + layer = that layer's weights, 100 + s = decode
-step s inputs, 200 + layer = synthetic decode state for that layer.
+step s inputs, 200 + layer = synthetic decode state for that layer, 300 + layer = block
+weights, 400 + b = the prior context of decode sequence b.
 
 bf16 cases are drawn in fp32 and converted with torch's round-to-nearest-even
 conversion; the float32 view of the bf16 values is what the oracle receives.
@@ -186,6 +187,14 @@ def gen_activations(dims: LayerDims, case_id: int, batch: int, seq_len: int):
 def gen_decode_inputs(dims: LayerDims, case_id: int, batch: int, step: int):
     """New-token activations for decode step `step`: [B, d] ~ N(0, 1)."""
     x = rng(case_id, 100 + step).standard_normal(size=(batch, dims.d_model), dtype=np.float32)
+    return to_storage(x, dims.dtype)
+
+
+def gen_prior_tokens(dims: LayerDims, case_id: int, seq: int, seq_len: int):
+    """The context sequence `seq` of a decode workload saw before decoding: [L, d] ~ N(0, 1),
+    one stream per sequence (role 400 + seq), so any subset of the batch can be drawn on
+    its own.  Returns (torch tensor in storage dtype, float32 numpy values)."""
+    x = rng(case_id, 400 + seq).standard_normal(size=(seq_len, dims.d_model), dtype=np.float32)
     return to_storage(x, dims.dtype)
 
 

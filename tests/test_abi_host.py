@@ -223,6 +223,36 @@ def test_decode_static_rejects_before_any_launch(lib):
     assert call(desc=desc_of(4, d_state=24)) == 2       # the descriptor's own error
 
 
+def test_kv_ring_fill_and_ring_flag_checks(lib):
+    """The ring fill and the is_ring contract are validated on the host: a non-ring
+    prefill cache must hold every position, a ring fill's source must hold the copied
+    positions; bad flags and sizes are refused before anything is launched."""
+    bf = hy.DTYPE_BF16
+    full = hy.KV(4096, 4096, 8192, 8192, 64, 0)
+    ring = hy.KV(4096, 4096, 16384, 16384, 16, 1)
+    fill = lambda **kw: hy.hymba_kv_ring_fill(**{**dict(
+        src=full, dst=ring, batch=2, seq_len=64, n_meta=8, n_kv_heads=2, head_dim=128,
+        dtype=bf), **kw}, stream=0, check=False)
+    assert fill(src=hy.KV(4096, 4096, 8192, 8192, 32, 0)) == 1   # source misses positions
+    assert fill(src=hy.KV(4096, 4096, 8192, 8192, 8, 1)) == 1    # a ring shorter than 16
+    assert fill(dst=hy.KV(4096, 4096, 16384, 16384, 16, 0)) == 1  # non-ring dst too short
+    assert fill(dst=hy.KV(4096, 4096, 16384, 16384, 16, 2)) == 1  # is_ring is 0 or 1
+    assert fill(dtype=5) == 1
+    assert fill(head_dim=12) == 2
+    assert fill(dst=hy.KV(4096, 4096, 16390, 16384, 16, 1)) == 4
+    assert fill(batch=-1) == 1
+    assert fill(batch=0, n_meta=0) == 0                          # nothing to copy
+    # a producer's non-ring cache must hold all L positions
+    d = desc_of(1)
+    call = lambda **kw: hy.hymba_layer_prefill(**{**dict(
+        desc=d, weights=_weights_struct(), meta=4096, x=8192, batch=1, seq_len=64, kv_in=None,
+        kv_out=None, state_out=None, y=12288, y_meta=None, workspace=1 << 20,
+        workspace_bytes=1000), **kw}, stream=0, check=False)
+    assert call(kv_out=hy.KV(4096, 4096, 4096, 4096, 32, 0)) == 1
+    assert call(kv_out=hy.KV(4096, 4096, 4096, 4096, 32, 1)) == 3  # a ring: valid
+    assert call(kv_out=hy.KV(4096, 4096, 4096, 4096, 64, 0)) == 3
+
+
 def test_op_gemm_argument_errors(lib):
     call = lambda **kw: lib.hymba_op_gemm(*[{**dict(
         dtype=1, a=4096, lda=64, b=4096, ldb=64, c=4096, ldc=64, c_dtype=1, m=4, n=4, k=64,

@@ -96,3 +96,32 @@ def test_cache_bytes_partial_swa_vs_all_global():
     assert st.decode_cache_bytes(B, ctx) == per * (3 * (B * ctx + dims.n_meta) +
                                                    2 * (B * 40 + dims.n_meta))
     assert g.decode_cache_bytes(B, ctx) == per * 6 * (B * ctx + dims.n_meta)
+
+
+@pytest.mark.parametrize("L,S,M", [(100, 32, 8), (20, 32, 8), (64, 64, 0)])
+def test_kv_ring_fill_matches_gather(L, S, M):
+    """hymba_kv_ring_fill: the last min(L, S) positions of a full cache land at slot
+    p mod S of the ring, and the meta entries are copied when the arrays differ."""
+    import hybrid_attention_ssm_proj_amd as hy
+    B, Hkv, dh = 3, 2, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(L + S)
+    src = {"k": torch.randn(B, Hkv, L, dh, generator=g, device=DEV).to(torch.bfloat16),
+           "v": torch.randn(B, Hkv, L, dh, generator=g, device=DEV).to(torch.bfloat16),
+           "k_meta": torch.randn(Hkv, max(M, 1), dh, generator=g, device=DEV).to(torch.bfloat16),
+           "v_meta": torch.randn(Hkv, max(M, 1), dh, generator=g, device=DEV).to(torch.bfloat16)}
+    dst = {k: torch.zeros(B, Hkv, S, dh, dtype=torch.bfloat16, device=DEV) for k in ("k", "v")}
+    dst.update({k: torch.zeros_like(src[k]) for k in ("k_meta", "v_meta")})
+    print(f"ring fill L={L} S={S} M={M}", flush=True)
+    hy.hymba_kv_ring_fill(hy.make_kv(src["k_meta"], src["v_meta"], src["k"], src["v"], False),
+                          hy.make_kv(dst["k_meta"], dst["v_meta"], dst["k"], dst["v"]), B, L, M,
+                          Hkv, dh, hy.DTYPE_BF16)
+    torch.cuda.synchronize()
+    ref = {k: torch.zeros_like(dst[k]) for k in ("k", "v")}
+    for p in range(max(0, L - S), L):
+        for k in ("k", "v"):
+            ref[k][:, :, p % S] = src[k][:, :, p]
+    for k in ("k", "v"):
+        assert torch.equal(dst[k], ref[k]), k
+    for k in ("k_meta", "v_meta"):
+        assert torch.equal(dst[k][:, :M], src[k][:, :M]), k
