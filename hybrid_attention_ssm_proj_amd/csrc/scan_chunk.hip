@@ -27,7 +27,8 @@
 // the same for every lane of a wave and are read through the scalar data cache into
 // scalar registers: no vector memory or LDS bandwidth is spent broadcasting them.  Per
 // step of 16 tokens:
-//  * x, G and the delta rows move global -> LDS by DMA (double-buffered);
+//  * x, G and the delta rows move global -> LDS by DMA (double-buffered, issued from
+//    inline asm so the compiler adds no waits for them);
 //  * dt for 16 tokens x 64 channels is one 16x16x32 MFMA tile per 16 channels over the
 //    rank (the W_dt rows stay in registers), then bias + softplus; (dt, dt x) go to LDS;
 //  * each wave runs its NS states over the 16 tokens in registers (4 VALU + 1 exp per
@@ -44,7 +45,11 @@ namespace hymba {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+// Output stores go through global-address-space pointers: through a generic pointer the
+// compiler cannot rule out an LDS target and waits for every store in flight (vmcnt(0))
+// before the next LDS read.
+typedef __attribute__((address_space(1))) bf16x4 glb_bf16x4;
+typedef __attribute__((address_space(1))) float glb_float;
 typedef __attribute__((ext_vector_type(2))) float floatx2;
 typedef __attribute__((address_space(4))) const floatx4 const_floatx4;
 typedef __attribute__((address_space(4))) const floatx2 const_floatx2;
@@ -109,6 +114,33 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x141>(v);  // row_half_mirror
   v += dpp<0x140>(v);  // row_mirror
   return v;
+}
+
+// global_load_lds_dwordx4 of one 16-byte piece per lane into the wave's 1 KB LDS block at
+// `lptr`, issued from inline asm.  The compiler does not see this LDS write, so it puts no
+// conservative vmcnt wait in front of LDS reads of the other buffer (with the builtin it
+// waits for every transfer in flight before any LDS read, which empties the double
+// buffer).  The kernel waits for its own transfers (vmcnt) and then passes a barrier.  The
+// instruction has no register result; its address operands are read at issue.
+__device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lptr) {
+  const uint32_t l = (uint32_t)(uintptr_t)lptr;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(gptr) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (at most 15; larger n waits for everything).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
 }
 
 template <int NS, int W, int R>
@@ -218,11 +250,8 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
       if (q0 < C::X_SLOTS) {
         const int q = q0 + lane, tt = q >> 3, j16 = q & 7;
         const bf16* src = zx + min(s0 + tt, te - 1) * zst + j16 * 8;
-        __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(x_s[buf] + q0 * 8), 16,
-                                         0, 0);
-        if (!kSum)
-          __builtin_amdgcn_global_load_lds((glb_void_t*)(src + gofs),
-                                           (lds_void_t*)(g_s[buf] + q0 * 8), 16, 0, 0);
+        dma16(src, (lds_void_t*)(x_s[buf] + q0 * 8));
+        if (!kSum) dma16(src + gofs, (lds_void_t*)(g_s[buf] + q0 * 8));
       }
     }
 #pragma unroll
@@ -231,12 +260,16 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
       if (q0 < C::D_SLOTS) {
         const int q = q0 + lane, tt = q / NC, s = q % NC;
         const int cidx = s ^ (tt & C::SWM);
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(dl + min(s0 + tt, te - 1) * R + cidx * 8),
-                                         (lds_void_t*)(d_s[buf] + q0 * 8), 16, 0, 0);
+        dma16(dl + min(s0 + tt, te - 1) * R + cidx * 8, (lds_void_t*)(d_s[buf] + q0 * 8));
       }
     }
   };
 
+  // store instructions this wave issues in a step's output phase (y, and the partial sum
+  // of squares when kept): its share of the TC * 16 output items, NT per round
+  const int epi_stores = kSum ? 0
+                              : max(0, (TC * 16 - wave * 64 + NT - 1) / NT) *
+                                    (ssps != nullptr ? 2 : 1);
   const int nst = (te - tb + TC - 1) / TC;  // 0 for an empty sequence: h passes through
   if (nst > 0) stage(0, tb);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -367,14 +400,19 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) sq = fmaf((float)o[e], (float)o[e], sq);
           sq = row16_sum(sq);
-          if (keep && j4 == 0) ssps[t] = sq;
+          if (keep && j4 == 0) *(glb_float*)(ssps + t) = sq;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = (bf16)((float)o[e] * beta4[e]);
         }
-        if (keep) *(bf16x4*)(ys + t * yst + j4 * 4) = o;
+        if (keep) *(glb_bf16x4*)(ys + t * yst + j4 * 4) = o;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA for the next step has landed
+    // This wave's DMA for the next step has landed.  Vector memory operations complete in
+    // issue order, so in a whole step (every output row kept, every store instruction
+    // issued) it is enough to leave this step's output stores in flight: epi_stores of
+    // them, issued after the DMA.
+    if (!kSum && tn == TC) wait_vmcnt_upto(epi_stores);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     lds_barrier();
   }
 
@@ -473,12 +511,14 @@ int scan_channel_blocks(int /*N*/, int Di) { return Di / 64; }
 int scan_chunk_count(int T, int chunk) { return T <= 0 ? 1 : (T + chunk - 1) / chunk; }
 
 int scan_default_chunk(int B, int Di, int T) {
-  // About 1024 (sequence, chunk) workgroups: measured on MI355X, more chunks pay for their
-  // summary pass up to about four resident workgroups per CU.  Chunks of at least 256
-  // tokens.
+  // Measured on MI355X (the prefill shapes of the layer, d_inner 4096): with at least two
+  // workgroups per CU from the batch alone, one chunk is fastest (the summary pass costs
+  // more than the extra occupancy returns); below that, about 2048 (sequence, chunk)
+  // workgroups, with chunks of at least 512 tokens.
   const int wgs = std::max(1, B * (Di / 64));
-  int k = (1024 + wgs - 1) / wgs;
-  k = std::min(k, std::max(1, T / 256));
+  if (wgs >= 512) return std::max(16, (T + 15) / 16 * 16);
+  int k = (2048 + wgs - 1) / wgs;
+  k = std::min(k, std::max(1, T / 512));
   k = std::max(1, std::min(k, 64));
   const int per = (T + k - 1) / k;
   return std::max(16, (per + 15) / 16 * 16);

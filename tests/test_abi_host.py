@@ -60,11 +60,10 @@ def test_workspace_sizes(lib):
     # row factors of the branch norms, all fp32
     ss = rows * (16 + 64) * 4 + rows * 2 * 4
     # the SSM state after the meta rows ([Di, N] fp32), scanned once per call; 8 sequences
-    # of 64 channel blocks are 512 workgroups, so the scan takes two time chunks of 1024
-    # tokens: one chunk summary per sequence ([Di, N] state and [Di] sum of dt, fp32)
+    # of 64 channel blocks are 512 workgroups, two per CU, so the scan runs in one time
+    # chunk (no chunk summaries)
     hmeta = 4096 * 16 * 4
-    summ = 8 * (4096 * 16 * 4 + 4096 * 4)
-    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss + hmeta + summ
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss + hmeta
     assert floor <= got <= floor + 10 * 256
     # fp32 layers keep a separate fp32 dt buffer
     d0 = desc_of(0)
@@ -82,14 +81,14 @@ def test_workspace_sizes(lib):
 def test_scan_chunk_workspace(lib):
     """The chunk-carried scan's summaries: (chunks - 1) x [Di, N] states and [Di] sums of
     dt per sequence, sized for the larger of the meta launch and the sequence launch."""
-    # B = 1, L = 32768, N = 128: 64 channel blocks -> 16 chunks of 2048 (1024 workgroups)
+    # B = 1, L = 32768, N = 128: 64 channel blocks -> 32 chunks of 1024 (2048 workgroups)
     base = hy.hymba_layer_workspace_bytes(desc_of(3), 1, 32768, 0)
     assert base > 0
     one = hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=32768), 1, 32768, 0)
-    assert base - one == 15 * 4096 * 128 * 4 + 15 * 4096 * 4
-    # a caller's chunk: 1024 tokens -> 32 chunks, 31 summaries
-    c32 = hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=1024), 1, 32768, 0)
-    assert c32 - one == 31 * 4096 * 128 * 4 + 31 * 4096 * 4
+    assert base - one == 31 * 4096 * 128 * 4 + 31 * 4096 * 4
+    # a caller's chunk: 2048 tokens -> 16 chunks, 15 summaries
+    c16 = hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=2048), 1, 32768, 0)
+    assert c16 - one == 15 * 4096 * 128 * 4 + 15 * 4096 * 4
     # not a multiple of 16; negative
     assert hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=24), 1, 32768, 0) == 0
     assert hy.hymba_layer_workspace_bytes(desc_of(3, scan_chunk=-16), 1, 32768, 0) == 0
