@@ -423,40 +423,55 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
 // Carries of the chunk summaries, in place: on entry hsum[b][k] is chunk k's end state
 // from zero and ssum[b][k] its sum of dt; on exit hsum[b][k] is the state after chunks
 // 0..k of sequence b started from h0 (zero when h0 is null), the initial state of chunk
-// k + 1.  Lane (kc, j) of a wave holds chunk kc of state element e = base + j (J = 64 / KP
-// elements per wave); the inclusive scan over kc runs with shuffles by J, 2J, 4J, ...
+// k + 1.  A workgroup takes 64 consecutive state elements of one sequence: it loads their
+// Kc summaries row by row (coalesced) into LDS with the chunk decays P = exp(A sum dt),
+// then each wave runs the inclusive scan over the chunks with lanes = chunks (J = 64 / KP
+// elements per pass, shuffles by 1, 2, 4, ... within each group of KP lanes), and the
+// carried states go back row by row.
 template <int KP>
 __global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ hsum,
                                                          const float* __restrict__ ssum,
                                                          const float* __restrict__ A,
-                                                         const float* __restrict__ h0, int B,
-                                                         int Di, int N, int Kc) {
-  constexpr int J = 64 / KP;
-  const int lane = threadIdx.x & 63;
-  const int kc = lane / J, j = lane % J;
-  const int64_t DN = (int64_t)Di * N;
-  const int64_t e_all = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * J + j;
-  const bool valid = e_all < (int64_t)B * DN && kc < Kc;
-  const int64_t bb = valid ? e_all / DN : 0, e = valid ? e_all % DN : 0;
-  const int64_t idx = (bb * Kc + kc) * DN + e;
-  float P = 1.f, hh = 0.f;
-  if (valid) {
-    hh = hsum[idx];
-    P = __builtin_amdgcn_exp2f(A[e] * kLog2eF * ssum[(bb * Kc + kc) * Di + e / N]);
+                                                         const float* __restrict__ h0, int Di,
+                                                         int N, int Kc) {
+  constexpr int EW = 64, TP = EW + 1;  // elements per workgroup; LDS row pitch
+  constexpr int J = 64 / KP;           // elements per wave pass
+  static_assert(KP >= 4 && KP <= 64 && (16 % J) == 0, "chunk lanes");
+  __shared__ float th[64 * TP], tp[64 * TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t DN = (int64_t)Di * N;  // a multiple of 64: the workgroup's elements share b
+  const int64_t base = (int64_t)blockIdx.x * EW;
+  const int64_t b = base / DN, e0 = base % DN;
+  for (int kc = wave; kc < Kc; kc += 4) {
+    const int64_t e = e0 + lane;
+    th[kc * TP + lane] = hsum[(b * Kc + kc) * DN + e];
+    tp[kc * TP + lane] =
+        __builtin_amdgcn_exp2f(A[e] * kLog2eF * ssum[(b * Kc + kc) * Di + e / N]);
   }
+  __syncthreads();
+  const int kc = lane % KP, j = lane / KP;
+  for (int e = wave * 16 + j; e < wave * 16 + 16; e += J) {
+    float hh = 0.f, P = 1.f;
+    if (kc < Kc) {
+      hh = th[kc * TP + e];
+      P = tp[kc * TP + e];
+    }
 #pragma unroll
-  for (int d = 1; d < KP; d <<= 1) {
-    const float Pp = __shfl_up(P, d * J, 64);
-    const float hp = __shfl_up(hh, d * J, 64);
-    if (kc >= d) {
-      hh = fmaf(P, hp, hh);
-      P *= Pp;
+    for (int d = 1; d < KP; d <<= 1) {
+      const float Pp = __shfl_up(P, d, 64);
+      const float hp = __shfl_up(hh, d, 64);
+      if (kc >= d) {
+        hh = fmaf(P, hp, hh);
+        P *= Pp;
+      }
+    }
+    if (kc < Kc) {
+      if (h0 != nullptr) hh = fmaf(P, h0[e0 + e], hh);
+      th[kc * TP + e] = hh;
     }
   }
-  if (valid) {
-    if (h0 != nullptr) hh = fmaf(P, h0[e], hh);
-    hsum[idx] = hh;
-  }
+  __syncthreads();
+  for (int kc = wave; kc < Kc; kc += 4) hsum[(b * Kc + kc) * DN + e0 + lane] = th[kc * TP + lane];
 }
 
 namespace {
@@ -471,13 +486,10 @@ hipError_t run_chunk(const ScanChunkParams& p, hipStream_t s) {
     const int64_t elems = (int64_t)p.B * p.Di * p.N;
     auto carry = [&](auto kp) {
       constexpr int KP = decltype(kp)::value;
-      const int64_t waves = (elems + 64 / KP - 1) / (64 / KP);
-      scan_carry_kernel<KP><<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(
-          p.hsum, p.ssum, p.A, p.h0, p.B, p.Di, p.N, Kc);
+      scan_carry_kernel<KP><<<dim3((unsigned)(elems / 64)), dim3(256), 0, s>>>(
+          p.hsum, p.ssum, p.A, p.h0, p.Di, p.N, Kc);
     };
-    if (Kc <= 1) carry(std::integral_constant<int, 1>());
-    else if (Kc <= 2) carry(std::integral_constant<int, 2>());
-    else if (Kc <= 4) carry(std::integral_constant<int, 4>());
+    if (Kc <= 4) carry(std::integral_constant<int, 4>());
     else if (Kc <= 8) carry(std::integral_constant<int, 8>());
     else if (Kc <= 16) carry(std::integral_constant<int, 16>());
     else if (Kc <= 32) carry(std::integral_constant<int, 32>());
