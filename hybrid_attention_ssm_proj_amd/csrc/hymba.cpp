@@ -334,7 +334,9 @@ int32_t hymba_abi_version(void) { return HYMBA_ABI_VERSION; }
 
 int32_t hymba_last_hip_error(void) { return g_last_hip_error; }
 
-const char* hymba_status_str(hymba_status s) {
+const char* hymba_status_str(int32_t s) {
+  // an int, not the enum: a C caller may pass any value, and a C++ enum without a fixed
+  // underlying type cannot hold values outside its enumerators' range
   switch (s) {
     case HYMBA_OK: return "ok";
     case HYMBA_ERR_INVALID_ARG: return "invalid argument";

@@ -315,7 +315,7 @@ hymba_status hymba_block_decode(const hymba_layer_desc *desc, const hymba_layer_
                                 hymba_kv *kv, hymba_ssm_state *state, void *y,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-const char *hymba_status_str(hymba_status s);
+const char *hymba_status_str(int32_t status);  /* any value; unknown ones say so */
 int32_t hymba_abi_version(void);
 /* Last hipError_t seen by a failing call on this thread (0 if none). */
 int32_t hymba_last_hip_error(void);
