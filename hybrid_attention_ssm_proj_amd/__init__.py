@@ -22,7 +22,8 @@ __all__ = [
     "hymba_kv_ring_fill",
     "hymba_layer_workspace_bytes",
     "hymba_status_str", "hymba_abi_version", "hymba_last_hip_error", "hymba_timer_enable",
-    "hymba_timer_read", "hymba_op_gemm", "hymba_op_copy", "HymbaLayer", "STAGES",
+    "hymba_timer_read", "hymba_op_gemm", "hymba_op_copy", "hymba_op_probe", "HymbaLayer",
+    "STAGES",
     "DTYPE_F32", "DTYPE_BF16", "LIB_PATH",
 ]
 
@@ -110,6 +111,7 @@ def load_library() -> ctypes.CDLL:
                                             ctypes.POINTER(KV), ctypes.POINTER(SSMState), P,
                                             P]),
         "hymba_layer_workspace_bytes": (SZ, [ctypes.POINTER(LayerDesc), I32, I32, I32]),
+        "hymba_op_probe": (I32, [I32, I32, I32, P, SZ, P, P]),
         "hymba_kv_ring_fill": (I32, [ctypes.POINTER(KV), ctypes.POINTER(KV), I32, I32, I32, I32,
                                      I32, I32, P]),
         "hymba_layer_meta_cache_build": (I32, [ctypes.POINTER(LayerDesc),
@@ -302,6 +304,11 @@ def hymba_timer_read(stage: int):
 def hymba_op_gemm(dtype, a, lda, b, ldb, c, ldc, c_dtype, m, n, k, stream=None) -> None:
     _check(load_library().hymba_op_gemm(dtype, _ptr(a), lda, _ptr(b), ldb, _ptr(c), ldc, c_dtype,
                                         m, n, k, _stream(stream)), "hymba_op_gemm")
+
+
+def hymba_op_probe(kind, blocks, iters, src, nbytes, out, stream=None) -> None:
+    _check(load_library().hymba_op_probe(kind, blocks, iters, _ptr(src), nbytes, _ptr(out),
+                                         _stream(stream)), "hymba_op_probe")
 
 
 def hymba_op_copy(src, dst, nbytes, stream=None) -> None:

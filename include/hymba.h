@@ -357,6 +357,14 @@ hymba_status hymba_op_gemm(int32_t dtype, const void *a, int64_t lda, const void
                            int64_t ldb, void *c, int64_t ldc, int32_t c_dtype, int32_t m,
                            int32_t n, int32_t k, void *stream);
 hymba_status hymba_op_copy(const void *src, void *dst, size_t bytes, void *stream);
+/* hymba_op_probe: one launch of a probe of the chip's practical ceilings, for the
+ *   benchmark's rooflines (the caller times it).  kind 0: `blocks` x 256 lanes each run
+ *   8 independent chains of `iters` base-2 exponentials (v_exp_f32); kind 1: `blocks` x 4
+ *   waves each run 4 independent chains of `iters` v_mfma_f32_32x32x16_bf16; kind 2: a
+ *   streaming read of `bytes` (multiple of 16) at `src`.  out: fp32, blocks x 256
+ *   (kinds 0, 1) or 8192 x 256 (kind 2) values, written so the work is kept. */
+hymba_status hymba_op_probe(int32_t kind, int32_t blocks, int32_t iters, const void *src,
+                            size_t bytes, float *out, void *stream);
 
 /* ---------------------------------------------------------------------------
  * hymba_op_attn: the attention heads alone (step a4), on the kernels the layer uses.

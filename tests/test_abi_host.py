@@ -263,6 +263,14 @@ def test_op_gemm_argument_errors(lib):
     assert call(a=4098) == 4
     assert call(m=0) == 0
     assert lib.hymba_op_copy(4096, 8192, 17, None) == 2
+    probe = lambda kind, blocks, iters, src, nbytes, out: lib.hymba_op_probe(
+        kind, blocks, iters, src, nbytes, out, None)
+    assert probe(3, 8, 8, None, 0, 4096) == 1
+    assert probe(0, 0, 8, None, 0, 4096) == 1
+    assert probe(0, 8, 8, None, 0, None) == 1
+    assert probe(2, 0, 0, 4096, 17, 4096) == 2
+    assert probe(2, 0, 0, None, 16, 4096) == 1
+    assert probe(1, 8, 8, None, 0, 4100) == 4
 
 
 def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
