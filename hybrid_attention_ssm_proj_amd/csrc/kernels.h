@@ -187,7 +187,8 @@ bool scan_chunk_supported(int N, int R, int Di);
 int scan_channel_blocks(int N, int Di);
 int scan_chunk_count(int T, int chunk);
 // Chunk length for B sequences of T tokens: one chunk when the batch gives every CU two
-// workgroups, otherwise about 2048 (sequence, chunk) workgroups of at least 512 tokens.
+// workgroups, otherwise about 2048 (sequence, chunk) workgroups of at least 512 tokens
+// (sequences shorter than 1024 tokens: up to 8 chunks of at least 16).
 int scan_default_chunk(int B, int Di, int T);
 hipError_t launch_scan_chunk(const ScanChunkParams& p, hipStream_t s);
 

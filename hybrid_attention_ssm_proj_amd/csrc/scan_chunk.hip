@@ -526,11 +526,13 @@ int scan_default_chunk(int B, int Di, int T) {
   // Measured on MI355X (the prefill shapes of the layer, d_inner 4096): with at least two
   // workgroups per CU from the batch alone, one chunk is fastest (the summary pass costs
   // more than the extra occupancy returns); below that, about 2048 (sequence, chunk)
-  // workgroups, with chunks of at least 512 tokens.
+  // workgroups, with chunks of at least 512 tokens.  A short sequence (the meta rows,
+  // scanned once per call) is latency-bound: up to 8 chunks of at least 16 tokens.
   const int wgs = std::max(1, B * (Di / 64));
   if (wgs >= 512) return std::max(16, (T + 15) / 16 * 16);
   int k = (2048 + wgs - 1) / wgs;
-  k = std::min(k, std::max(1, T / 512));
+  if (T < 1024) k = std::min(std::min(k, 8), (T + 15) / 16);
+  else k = std::min(k, T / 512);
   k = std::max(1, std::min(k, 64));
   const int per = (T + k - 1) / k;
   return std::max(16, (per + 15) / 16 * 16);

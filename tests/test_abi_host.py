@@ -60,10 +60,12 @@ def test_workspace_sizes(lib):
     # row factors of the branch norms, all fp32
     ss = rows * (16 + 64) * 4 + rows * 2 * 4
     # the SSM state after the meta rows ([Di, N] fp32), scanned once per call; 8 sequences
-    # of 64 channel blocks are 512 workgroups, two per CU, so the scan runs in one time
-    # chunk (no chunk summaries)
+    # of 64 channel blocks are 512 workgroups, two per CU, so the sequences' scan runs in
+    # one time chunk; the 128 meta rows alone run in 8 chunks of 16 tokens, whose first 7
+    # leave a state summary ([Di, N]) and a dt sum ([Di]) each
     hmeta = 4096 * 16 * 4
-    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss + hmeta
+    msum = 7 * (4096 * 16 * 4 + 4096 * 4)
+    floor = rows * (n_in * 2 + 128 * 2 + 32 * 4 + 6144 * 2) + vt + macc + ss + hmeta + msum
     assert floor <= got <= floor + 10 * 256
     # fp32 layers keep a separate fp32 dt buffer
     d0 = desc_of(0)
@@ -311,12 +313,15 @@ def test_op_attn_and_op_scan_reject_bad_arguments_before_any_launch(lib):
     assert scan(chunk_tokens=-16) == 1
     assert scan(n_meta=(1 << 31) - 128, seq_len=64) == 2  # rows reach 2^31
     assert attn(n_meta=(1 << 31) - 128, seq_len=64) == 2
-    # bf16 chunked scan: the post-meta state [Di, N] fp32; one chunk here
-    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64) == 512 * 16 * 4
-    assert hy.hymba_op_scan_workspace_bytes(bf, 0, 64, 2, 512, 16, 64) == 0
-    # chunks of 16 tokens: 4 per sequence, 3 summaries each ([Di, N] states + [Di] sums)
-    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64, 16) == (
-        512 * 16 * 4 + 6 * 512 * 16 * 4 + 6 * 512 * 4)
+    # bf16 chunked scan: the post-meta state [Di, N] fp32; with 512 workgroups (8
+    # sequences x 64 channel blocks) the sequences run in one chunk, and so do 8 meta rows
+    assert hy.hymba_op_scan_workspace_bytes(bf, 8, 2048, 8, 4096, 16, 64) == 4096 * 16 * 4
+    assert hy.hymba_op_scan_workspace_bytes(bf, 0, 64, 2, 512, 16, 64, 64) == 0
+    # chunks of 16 tokens: 4 per sequence, 3 summaries each ([Di, N] states + [Di] sums);
+    # a short sequence on few workgroups gets the same by default
+    for chunk in (16, 0):
+        assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 64, chunk) == (
+            512 * 16 * 4 + 6 * 512 * 16 * 4 + 6 * 512 * 4)
     assert hy.hymba_op_scan_workspace_bytes(bf, 8, 64, 2, 512, 16, 16) == (8 + 128) * 512 * 4
 
 
