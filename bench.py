@@ -174,7 +174,10 @@ def traffic_for(kernel_stage):
         return None
     h = hashlib.sha256()
     for name in rec["sources"]:
-        h.update(open(os.path.join(ROOT, "hybrid_attention_ssm_proj_amd", "csrc", name), "rb").read())
+        src = os.path.join(ROOT, "hybrid_attention_ssm_proj_amd", "csrc", name)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
     return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha"] else None
 
 

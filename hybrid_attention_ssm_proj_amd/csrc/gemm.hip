@@ -4,10 +4,12 @@
 // formulation in "Hymba: A Hybrid-head Architecture for Small Language Models"
 // (outta.ai summary); dt, B, C are linear maps of the SSM input (Mamba).
 //
-// bf16 path: LDS double-buffered MFMA (v_mfma_f32_16x16x32_bf16) tiles with fp32
-// accumulation.  Operands are both K-contiguous ([rows, K] and [cols, K]); the MFMA is
-// issued as (B-tile, A-tile) so each lane ends with 4 consecutive output columns of
-// one row, which the epilogue writes with a single vector store.
+// bf16 path: LDS-staged MFMA tiles with fp32 accumulation: the 256x256 / 128x64 tiles
+// (gemm_bf16_dl_kernel) and the few-row kernel issue v_mfma_f32_32x32x16_bf16, the 64x64
+// tile kernel (gemm_bf16_kernel) v_mfma_f32_16x16x32_bf16.  Operands are both
+// K-contiguous ([rows, K] and [cols, K]); the MFMA is issued as (B-tile, A-tile) so each
+// lane ends with runs of consecutive output columns of one row, which the epilogue
+// writes with vector stores.
 // fp32 path: a plain LDS-tiled VALU GEMM with the same epilogues.
 #include <algorithm>
 #include <type_traits>

@@ -8,8 +8,8 @@ Distributions follow the layer workloads used throughout (weights N(0, 0.02),
 meta tokens and X N(0, 1), dt bias U[-4, -2], A = -exp(U[0, 2]), D N(0, 1),
 beta = 1).  Streams are numpy PCG64 seeded with SeedSequence([1000 + case, role]):
 role 0 = meta tokens, 1 = X, 10 + layer = that layer's weights, 100 + s = decode
-step s inputs, 200 + layer = synthetic decode state for that layer, 300 + layer = block
-weights, 400 + b = the prior context of decode sequence b.
+step s inputs, 300 + layer = block weights, 400 + b = the prior context of decode
+sequence b.
 
 bf16 cases are drawn in fp32 and converted with torch's round-to-nearest-even
 conversion; the float32 view of the bf16 values is what the oracle receives.
@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, Optional
+from typing import Dict
 
 import numpy as np
 
@@ -196,25 +196,6 @@ def gen_prior_tokens(dims: LayerDims, case_id: int, seq: int, seq_len: int):
     its own.  Returns (torch tensor in storage dtype, float32 numpy values)."""
     x = rng(case_id, 400 + seq).standard_normal(size=(seq_len, dims.d_model), dtype=np.float32)
     return to_storage(x, dims.dtype)
-
-
-def gen_decode_state(dims: LayerDims, case_id: int, batch: int, ring_slots: int,
-                     prior_tokens: int, layer: int = 0, kv_std: float = 0.9,
-                     h_std: float = 0.3, pos: Optional[np.ndarray] = None):
-    """A synthetic decode state of realistic magnitude (K/V entries ~ N(0, kv_std),
-    which is the spread in_proj gives N(0,1) inputs under N(0, 0.02) weights at
-    d = 2048; h ~ N(0, h_std)).  Returns a dict of (torch, numpy) pairs and pos."""
-    g = rng(case_id, 200 + layer)
-    Hkv, M, dh, Di, N = dims.n_kv_heads, dims.n_meta, dims.head_dim, dims.d_inner, dims.d_state
-    out = {}
-    for name, shape in (("k_meta", (Hkv, M, dh)), ("v_meta", (Hkv, M, dh)),
-                        ("k", (batch, Hkv, ring_slots, dh)), ("v", (batch, Hkv, ring_slots, dh))):
-        out[name] = to_storage(_normal(g, shape, kv_std), dims.dtype)
-    out["h"] = to_storage(_normal(g, (batch, Di, N), h_std), F32)
-    if pos is None:
-        pos = np.full((batch,), prior_tokens, np.int32)
-    out["pos"] = np.asarray(pos, np.int32)
-    return out
 
 
 @dataclasses.dataclass
