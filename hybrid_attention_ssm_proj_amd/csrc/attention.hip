@@ -9,13 +9,17 @@
 // (j < M or window == 0 or i - j < window); scale 1/sqrt(head_dim) unless given.
 //
 // Prefill (bf16): flash-style, one workgroup per (query block, kv head, head
-// subgroup).  Its waves each own 32 query rows of one q head; all share the K/V tiles
-// of their kv head staged in LDS.  The waves compute S^T = K Q^T with
-// v_mfma_f32_16x16x32_bf16, so the softmax statistics of a query live in one lane
-// column, and O^T = V^T P^T takes P^T straight from the S^T accumulators (the 32-key
-// k-order of the second MFMA is permuted to match them; V is staged transposed and
-// permuted the same way).  Key tiles that hold no visible key for the block (outside
-// the meta prefix and the window) are skipped.
+// subgroup).  Its waves each own 16 * QT query rows of one q head (QT = 2: 32 rows,
+// 8 waves, two per SIMD); all share the K/V tiles of their kv head staged in LDS.  The
+// waves compute S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so the softmax statistics
+// of a query live in one lane column, and O^T = V^T P^T takes P^T straight from the S^T
+// accumulators (the 32-key k-order of the second MFMA is permuted to match them; V is
+// staged transposed and permuted the same way).  The key loop is software-pipelined:
+// a wave forms S^T of the next tile while it runs the softmax of the current one.  Key
+// tiles that hold no visible key for the block (outside the meta prefix and the
+// window) are skipped; which tiles those are is a closed form of the block's range.
+// Measured on MI355X: 4 waves of 48 or 64 query rows (one wave per SIMD, half the LDS
+// reads per MFMA) and 4 K/V stages instead of 3 were not faster.
 #include <float.h>
 
 #include <type_traits>
@@ -129,13 +133,13 @@ __global__ __launch_bounds__(256) void vt_build_kernel(AttnParams p, bf16* vt, i
   }
 }
 
-template <int DH, int NW, int NS>
-__global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kernel(
+template <int DH, int NW, int NS, int QT>
+__global__ __launch_bounds__(NW * 64, 1) void attn_prefill_dl_kernel(
     AttnParams p, const bf16* __restrict__ vt, int tpad, int gq, int qb, int nblk_seq) {
   constexpr int KT = 64;
   constexpr int KB = KT * DH;            // elements of a K tile and of a V^T tile
   constexpr int INS = DH / 8 / NW;       // 1 KB DMA wave instructions per wave, per matrix
-  static_assert(INS >= 1 && NS >= 2 && NS <= 3, "tile loader");
+  static_assert(INS >= 1 && NS >= 3 && NS <= 4, "tile loader");
   __shared__ __attribute__((aligned(1024))) bf16 smem[NS * 2 * KB];
   auto kst = [&](int st) { return smem + st * 2 * KB; };
   auto vst = [&](int st) { return smem + st * 2 * KB + KB; };
@@ -158,7 +162,8 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   const int h0 = blockIdx.y * gq;
   const int h = h0 + (wave % gq);
   const int g = (h0 * p.Hkv) / p.Hq;
-  const int wp0 = p0 + (wave / gq) * 32;
+  constexpr int QW = 16 * QT;  // queries per wave
+  const int wp0 = p0 + (wave / gq) * QW;
 
   const bf16* qbase = (const bf16*)p.q;
   // K rows of this (sequence, kv head): meta key j at kmeta + j*meta_row_stride, key
@@ -168,9 +173,9 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   const bf16* kseq = (const bf16*)p.k_seq + (int64_t)b * p.seq_batch_stride + g * p.seq_head_stride;
   const bf16* vtb = vt + ((int64_t)b * p.Hkv + g) * DH * tpad;
 
-  bf16x8 qf[2][DH / 32];
+  bf16x8 qf[QT][DH / 32];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int pos = wp0 + qt * 16 + (lane & 15);
     const bool ok = pos < plim;
     const bf16* src = qbase + q_row(p, ok ? pos : p0, b) * p.q_row_stride + h * DH +
@@ -181,164 +186,207 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
       qf[qt][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  floatx4 oacc[DH / 16][2];
+  floatx4 oacc[DH / 16][QT];
+  float mrow[QT];
+  floatx4 lacc[QT];
 #pragma unroll
-  for (int i = 0; i < DH / 16; ++i) oacc[i][0] = oacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY};
-  floatx4 lacc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) oacc[i][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    mrow[qt] = -INFINITY;
+    lacc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.f;
 
+  // Key tiles with a visible key for this block: the meta tiles [0, mt) and the tiles
+  // from the window's start wt on, up to ntile (all wave-uniform).
   const int meta_end = min(p.n_meta, plim);
   const int wlo = p.window > 0 ? max(p.n_meta, p0 - p.window + 1) : p.n_meta;
-  const int ntile = (plim + KT - 1) / KT;
-  auto tile_needed = [&](int t) {
-    const int a = t * KT, e = a + KT;
-    return a < meta_end || (e > wlo && a < plim);
-  };
+  const int ntile = __builtin_amdgcn_readfirstlane((plim + KT - 1) / KT);
+  const int mt = __builtin_amdgcn_readfirstlane((meta_end + KT - 1) / KT);
+  const int wt = __builtin_amdgcn_readfirstlane(wlo / KT);
   auto next_tile = [&](int t) {
-    ++t;
-    while (t < ntile && !tile_needed(t)) ++t;
-    return t;
+    const int u = t + 1 < mt ? t + 1 : max(t + 1, wt);
+    return min(u, ntile);
   };
 
   // DMA of tile t into stage st.  K: 1 KB block (j*NW + wave) of the tile holds rows
   // of 256 B (DH 128: 4 rows) or 128 B (DH 64: 8 rows), each row's 16-byte chunks
   // XOR-permuted (chunk ^ (row & 15), resp. chunk ^ swz8(row)).  V^T rows are 128 B
   // (64 slots), chunk ^ swz8(row).  Keys past the visible end read the last one (masked).
+  // A tile wholly inside the sequence's keys takes the per-lane offsets below plus one
+  // wave-uniform base per matrix.
+  int krow_of[INS], kof[INS], vof[INS];
+#pragma unroll
+  for (int j = 0; j < INS; ++j) {
+    const int blk = j * NW + wave;
+    int row, gch;
+    if constexpr (DH == 128) {
+      row = blk * 4 + (lane >> 4);
+      gch = (lane & 15) ^ (row & 15);
+    } else {
+      row = blk * 8 + (lane >> 3);
+      gch = (lane & 7) ^ swz8(row);
+    }
+    krow_of[j] = row;
+    kof[j] = row * p.seq_row_stride + gch * 8;
+    const int vr = blk * 8 + (lane >> 3);
+    vof[j] = vr * tpad + ((lane & 7) ^ swz8(vr)) * 8;
+  }
   auto issue = [&](int st, int t) {
     const int a = t * KT;
+    if (a >= p.n_meta && a + KT <= plim) {
+      const bf16* kb = kseq + (int64_t)(a - p.n_meta) * p.seq_row_stride;
+#pragma unroll
+      for (int j = 0; j < INS; ++j) {
+        const int blk = j * NW + wave;
+        dma16(kb + kof[j], (lds_void_t*)(kst(st) + blk * 512));
+        dma16(vtb + a + vof[j], (lds_void_t*)(vst(st) + blk * 512));
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < INS; ++j) {
       const int blk = j * NW + wave;
-      int row, gch;
-      if constexpr (DH == 128) {
-        row = blk * 4 + (lane >> 4);
-        gch = (lane & 15) ^ (row & 15);
-      } else {
-        row = blk * 8 + (lane >> 3);
-        gch = (lane & 7) ^ swz8(row);
-      }
+      const int row = krow_of[j];
+      const int gch = (kof[j] - row * p.seq_row_stride) / 8;
       const int key = min(a + row, plim - 1);
       const bf16* krow = key < p.n_meta ? kmeta + (int64_t)key * p.meta_row_stride
                                         : kseq + (int64_t)(key - p.n_meta) * p.seq_row_stride;
       dma16(krow + gch * 8, (lds_void_t*)(kst(st) + blk * 512));
-      const int vr = blk * 8 + (lane >> 3);
-      const int vch = (lane & 7) ^ swz8(vr);
-      dma16(vtb + (int64_t)vr * tpad + a + vch * 8, (lds_void_t*)(vst(st) + blk * 512));
+      dma16(vtb + a + vof[j], (lds_void_t*)(vst(st) + blk * 512));
     }
   };
 
   const float c2 = p.scale * kLog2e;
-  int t = tile_needed(0) ? 0 : next_tile(0);
-  int tq[NS];  // tiles issued into the stages after the current one
+  // Software pipeline over the key tiles: while a wave runs the softmax of tile t (VALU),
+  // it forms S^T of the next tile (MFMA), so the two kinds of work overlap inside the
+  // wave.  During step t the tiles t and tq[0] are resident in LDS; tq[1..] may be in
+  // flight.
+  int t = mt > 0 ? 0 : min(wt, ntile);
+  int tq[NS - 1];  // tiles issued after the current one, in order (ntile: none)
   int st = 0;
   if (t < ntile) issue(0, t);
-  tq[0] = t < ntile ? next_tile(t) : ntile;
-  if (tq[0] < ntile) issue(1, tq[0]);
-  if constexpr (NS == 3) {
-    tq[1] = tq[0] < ntile ? next_tile(tq[0]) : ntile;
-    if (tq[1] < ntile) issue(2, tq[1]);
-    if (tq[1] < ntile) wait_vm<4 * INS>();
-    else if (tq[0] < ntile) wait_vm<2 * INS>();
+  {
+    int prev = t;
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) {
+      tq[i] = prev < ntile ? next_tile(prev) : ntile;
+      if (tq[i] < ntile) issue(i + 1, tq[i]);
+      prev = tq[i];
+    }
+  }
+  // wait until at most n tiles' DMAs are still in flight (this wave's; a barrier follows)
+  auto wait_tiles = [&](int n) {
+    if (n >= 2) wait_vm<4 * INS>();
+    else if (n == 1) wait_vm<2 * INS>();
     else wait_vm<0>();
-  } else {
-    if (tq[0] < ntile) wait_vm<2 * INS>();
-    else wait_vm<0>();
+  };
+  {
+    int n = 0;
+#pragma unroll
+    for (int i = 1; i < NS - 1; ++i) n += tq[i] < ntile;
+    wait_tiles(n);
   }
   lds_barrier();
 
-  while (t < ntile) {
-    const bf16* kt_ = kst(st);
-    const bf16* vt_ = vst(st);
-    // All K fragments of the tile are read first; the V^T fragments (independent of S)
-    // are read between the S MFMAs, so their latency hides behind the MFMAs and the
-    // softmax instead of stalling the P V product.
-    bf16x8 kf[DH / 32][4], vf[DH / 16][2];
+  constexpr int KS = DH / 32;  // k-steps of S^T = K Q^T
+  auto load_k = [&](const bf16* kt_, int ks, bf16x8 (&kf)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int row = kt * 16 + (lane & 15), c = ks * 4 + (lane >> 4);
-        const int sw = DH == 128 ? (c ^ (row & 15)) : (c ^ swz8(row));
-        kf[ks][kt] = *(const bf16x8*)(kt_ + row * DH + sw * 8);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    floatx4 sacc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sacc[i][0] = sacc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sacc[kt][0] = mfma16x16x32(kf[ks][kt], qf[0][ks], sacc[kt][0]);
-        sacc[kt][1] = mfma16x16x32(kf[ks][kt], qf[1][ks], sacc[kt][1]);
-      }
-#pragma unroll
-    for (int d = 0; d < DH / 16; ++d)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int row = d * 16 + (lane & 15), c = k2 * 4 + (lane >> 4);
-        vf[d][k2] = *(const bf16x8*)(vt_ + row * 64 + ((c ^ swz8(row)) * 8));
-      }
-#pragma unroll
-    for (int q = 0; q < DH / 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    for (int kt = 0; kt < 4; ++kt) {
+      const int row = kt * 16 + (lane & 15), c = ks * 4 + (lane >> 4);
+      const int sw = DH == 128 ? (c ^ (row & 15)) : (c ^ swz8(row));
+      kf[kt] = *(const bf16x8*)(kt_ + row * DH + sw * 8);
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    const int a = t * KT;
-    const int i_lo = wp0, i_hi = min(wp0 + 31, plim - 1);
+  };
+  auto s_mfma = [&](const bf16x8 (&kf)[4], int ks, floatx4 (&s)[4][QT]) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16x16x32(kf[kt], qf[qt][ks], s[kt][qt]);
+  };
+  auto zero_s = [&](floatx4 (&s)[4][QT]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[i][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Mask S^T[key j][query i] of tile tt to -inf where j is not visible.  Lane holds keys
+  // j = a + c + 4 (lane / 16) with c = 16 kt + r, so each condition is one compare of
+  // the constant c with a per-lane threshold: j <= i <=> c <= lim; j < n_meta <=>
+  // c < mlim; i - j < window <=> c > lim - window.
+  auto mask = [&](floatx4 (&s)[4][QT], int tt) {
+    const int a = tt * KT;
+    const int i_lo = wp0, i_hi = min(wp0 + QW - 1, plim - 1);
     const bool full = a + KT - 1 <= i_lo &&
                       (p.window <= 0 || a + KT <= p.n_meta || i_hi - max(a, p.n_meta) < p.window);
-    if (!full) {
-      // Mask S^T[key j][query i] to -inf where j is not visible.  Lane holds keys
-      // j = a + c + 4 (lane / 16) with c = 16 kt + r, so each condition is one compare of
-      // the constant c with a per-lane threshold: j <= i <=> c <= lim; j < n_meta <=>
-      // c < mlim; i - j < window <=> c > lim - window.
-      const int lq = (lane >> 4) * 4;
+    if (full) return;
+    const int lq = (lane >> 4) * 4;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int lim = wp0 + qt * 16 + (lane & 15) - a - lq;
-        if (p.window <= 0) {
+    for (int qt = 0; qt < QT; ++qt) {
+      const int lim = wp0 + qt * 16 + (lane & 15) - a - lq;
+      if (p.window <= 0) {
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (kt * 16 + r > lim) sacc[kt][qt][r] = -INFINITY;
-        } else {
-          const int mlim = p.n_meta - a - lq, wlim = lim - p.window;
+          for (int r = 0; r < 4; ++r)
+            if (kt * 16 + r > lim) s[kt][qt][r] = -INFINITY;
+      } else {
+        const int mlim = p.n_meta - a - lq, wlim = lim - p.window;
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int c = kt * 16 + r;
-              if (c > lim || (c >= mlim && c <= wlim)) sacc[kt][qt][r] = -INFINITY;
-            }
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int c = kt * 16 + r;
+            if (c > lim || (c >= mlim && c <= wlim)) s[kt][qt][r] = -INFINITY;
+          }
       }
     }
+  };
+
+  // One step: softmax of tile t held in `sc` and its P V product, overlapped with S^T of
+  // the next tile into `sn` (kNext).  Returns true after the last tile.
+  auto step = [&](auto next_c, floatx4 (&sc)[4][QT], floatx4 (&sn)[4][QT])
+                  __attribute__((always_inline)) {
+    constexpr bool kNext = decltype(next_c)::value;
+    const bf16* ktn = kst(st + 1 == NS ? 0 : st + 1);
+    const bf16* vt_ = vst(st);
+    mask(sc, t);
     // Row maxima of the tile, then lazy rescaling: the running max m moves only when
     // some row's tile max exceeds it by more than kLazyLog2 in log2 units (wave-uniform
     // decision), so O and l are rescaled rarely and every exp2 argument stays <=
     // kLazyLog2 (P <= 2^kLazyLog2, exact in the fp32 sums and in bf16 for the MFMA).
-    // O / l is unchanged by the choice of m.
-    float tmax[2];
+    // O / l is unchanged by the choice of m.  The first half of the next tile's S^T
+    // MFMAs runs beside the maxima.
+    bf16x8 kf0[4], kf1[4];
+    if constexpr (kNext) {
+      zero_s(sn);
+      load_k(ktn, 0, kf0);
+      if constexpr (KS > 2) load_k(ktn, 1, kf1);
+    }
+    float tmax[QT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = sacc[0][qt][0];
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = sc[0][qt][0];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kt][qt][r]);
       tmax[qt] = max_over_key_lanes(mx);
     }
+    if constexpr (kNext) {
+      s_mfma(kf0, 0, sn);
+      if constexpr (KS > 2) s_mfma(kf1, 1, sn);
+    }
     const float thr = kLazyLog2 / c2;
-    if (__builtin_amdgcn_ballot_w64(tmax[0] > mrow[0] + thr || tmax[1] > mrow[1] + thr)) {
+    bool grow = false;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) grow = grow || tmax[qt] > mrow[qt] + thr;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
         const float mnew = fmaxf(mrow[qt], tmax[qt]);
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
         const float alpha = __builtin_amdgcn_exp2f((mrow[qt] - muse) * c2);  // 0 from -inf
@@ -350,53 +398,89 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
     }
     // P^T in bf16 (the B operand of both MFMAs below); the row sums l come from the same
     // rounded P through an MFMA with an all-ones A operand (every output row of it is
-    // the column sum, so each lane ends with the full sum of its query).
-    bf16x8 pf[2][2];
+    // the column sum, so each lane ends with the full sum of its query).  The second
+    // half of the next tile's S^T MFMAs runs beside the exponentials.
+    if constexpr (kNext) {
+      load_k(ktn, KS > 2 ? 2 : 1, kf0);
+      if constexpr (KS > 2) load_k(ktn, 3, kf1);
+    }
+    bf16x8 pf[2][QT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const float mc2 = (mrow[qt] == -INFINITY ? 0.f : mrow[qt]) * c2;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         bf16x8 f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          f[r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * k2][qt][r], c2, -mc2));
-          f[4 + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * k2 + 1][qt][r], c2, -mc2));
+          f[r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[2 * k2][qt][r], c2, -mc2));
+          f[4 + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[2 * k2 + 1][qt][r], c2, -mc2));
         }
         pf[k2][qt] = f;
         lacc[qt] = mfma16x16x32(ones, f, lacc[qt]);
       }
     }
+    if constexpr (kNext) {
+      s_mfma(kf0, KS > 2 ? 2 : 1, sn);
+      if constexpr (KS > 2) s_mfma(kf1, 3, sn);
+    }
+    // O^T += V^T P^T (the V^T fragments are read only now: earlier they would be live
+    // beside both S^T tiles)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 0; d < DH / 16; ++d)
+    for (int d = 0; d < DH / 16; ++d) {
+      bf16x8 vf[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        oacc[d][0] = mfma16x16x32(vf[d][k2], pf[k2][0], oacc[d][0]);
-        oacc[d][1] = mfma16x16x32(vf[d][k2], pf[k2][1], oacc[d][1]);
+        const int row = d * 16 + (lane & 15), c = k2 * 4 + (lane >> 4);
+        vf[k2] = *(const bf16x8*)(vt_ + row * 64 + ((c ^ swz8(row)) * 8));
       }
-
-    // hand-over: the next tile has landed (one more may stay in flight), every wave is
-    // done with this stage, which then takes the tile after the ones in flight
-    const int tn = tq[0];
-    if (tn >= ntile) break;
-    if constexpr (NS == 3) {
-      if (tq[1] < ntile) wait_vm<2 * INS>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[d][qt] = mfma16x16x32(vf[k2], pf[k2][qt], oacc[d][qt]);
+    }
+    if constexpr (!kNext) return true;
+    // hand-over: tiles tq[0] and tq[1] are resident, every wave is done with this stage,
+    // which then takes the tile after the ones issued
+    {
+      int n = 0;
+#pragma unroll
+      for (int i = 2; i < NS - 1; ++i) n += tq[i] < ntile;
+      wait_tiles(n);
     }
     lds_barrier();
-    const int tlast = NS == 3 ? tq[1] : tq[0];
-    const int tnew = tlast < ntile ? next_tile(tlast) : ntile;
+    int tlast = t;
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) tlast = tq[i] < ntile ? tq[i] : tlast;
+    const int tnew = tq[NS - 2] < ntile ? next_tile(tlast) : ntile;
     if (tnew < ntile) issue(st, tnew);
-    if constexpr (NS == 3) {
-      tq[0] = tq[1];
-      tq[1] = tnew;
-    } else {
-      tq[0] = tnew;
-    }
+    t = tq[0];
+#pragma unroll
+    for (int i = 0; i + 1 < NS - 1; ++i) tq[i] = tq[i + 1];
+    tq[NS - 2] = tnew;
     st = st + 1 == NS ? 0 : st + 1;
-    t = tn;
+    return false;
+  };
+
+  floatx4 sa[4][QT], sb[4][QT];
+  if (t < ntile) {  // S^T of the first tile
+    zero_s(sa);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kf[4];
+      load_k(kst(st), ks, kf);
+      s_mfma(kf, ks, sa);
+    }
+    while (tq[0] < ntile) {
+      step(std::true_type{}, sa, sb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sa[i][qt] = sb[i][qt];
+    }
+    step(std::false_type{}, sa, sb);
   }
 
   // O^T layout: lane holds head_dim entries d*16 + 4*(lane/16) + r of query lane % 16.
@@ -406,7 +490,7 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   bf16* obase = (bf16*)p.o;
   const float* bh = p.beta != nullptr ? p.beta + h * DH + (lane >> 4) * 4 : nullptr;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const float l = lacc[qt][0];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int pos = wp0 + qt * 16 + (lane & 15);
@@ -448,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, NS == 2 ? 2 : 1) void attn_prefill_dl_kern
   }
 }
 
-template <int DH, int NW, int NS>
+template <int DH, int NW, int NS, int QT>
 static hipError_t run_attn_dl(const AttnParams& p, void* vt, hipStream_t s) {
   const int total = p.n_meta + p.L;
   const int tpad = (total + 63) / 64 * 64;
@@ -458,12 +542,12 @@ static hipError_t run_attn_dl(const AttnParams& p, void* vt, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int grp = p.Hq / p.Hkv;
   const int gq = grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
-  const int qb = 32 * (NW / gq);
+  const int qb = 16 * QT * (NW / gq);
   const int nblk_seq = (p.L + qb - 1) / qb;
   const int nblk_meta = p.meta_rows > 0 ? (p.n_meta + qb - 1) / qb : 0;
   const int nx = p.B * nblk_seq + nblk_meta;
   if (nx == 0) return hipSuccess;
-  attn_prefill_dl_kernel<DH, NW, NS><<<dim3(nx, p.Hq / gq), dim3(NW * 64), 0, s>>>(
+  attn_prefill_dl_kernel<DH, NW, NS, QT><<<dim3(nx, p.Hq / gq), dim3(NW * 64), 0, s>>>(
       p, (const bf16*)vt, tpad, gq, qb, nblk_seq);
   return hipGetLastError();
 }
@@ -474,8 +558,8 @@ size_t attention_vt_bytes(int n_meta, int L, int B, int Hkv, int head_dim) {
 }
 
 hipError_t launch_attention_prefill_bf16_dl(const AttnParams& p, void* vt, hipStream_t s) {
-  if (p.head_dim == 128) return run_attn_dl<128, 8, 3>(p, vt, s);
-  if (p.head_dim == 64) return run_attn_dl<64, 8, 3>(p, vt, s);
+  if (p.head_dim == 128) return run_attn_dl<128, 8, 3, 2>(p, vt, s);
+  if (p.head_dim == 64) return run_attn_dl<64, 8, 3, 2>(p, vt, s);
   return hipErrorInvalidValue;
 }
 
