@@ -26,11 +26,12 @@
 // chunk); wave w owns states [w*NS, (w+1)*NS) of those channels.  B_t and C_t are then
 // the same for every lane of a wave and are read through the scalar data cache into
 // scalar registers: no vector memory or LDS bandwidth is spent broadcasting them.  Per
-// step of 16 tokens:
+// step of 16 or 32 tokens (32 when the grid is small enough for its LDS):
 //  * x, G and the delta rows move global -> LDS by DMA (double-buffered, issued from
 //    inline asm so the compiler adds no waits for them);
 //  * dt for 16 tokens x 64 channels is one 16x16x32 MFMA tile per 16 channels over the
-//    rank (the W_dt rows stay in registers), then bias + softplus; (dt, dt x) go to LDS;
+//    rank (the W_dt rows stay in registers; one tile row per 16 tokens of the step), then
+//    bias + softplus; (dt, dt x) go to LDS;
 //  * each wave runs its NS states over the 16 tokens in registers (4 VALU + 1 exp per
 //    state and token) and writes its part of sum_n C h to LDS;
 //  * the parts of the W waves are added, D x and the gate applied, and the row stored.
@@ -143,11 +144,11 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
   }
 }
 
-template <int NS, int W, int R>
+template <int NS, int W, int R, int TC_>
 struct ChunkCfg {
   static constexpr int N = NS * W;
   static constexpr int CB = 64;              // channels per workgroup, one per lane
-  static constexpr int TC = 16;              // tokens per step
+  static constexpr int TC = TC_;             // tokens per step
   static constexpr int NT = 64 * W;          // threads
   static constexpr int NC = R / 8;           // 16-byte pieces per delta row
   static constexpr int SWM = (NC < 16 ? NC : 16) - 1;  // delta piece swizzle mask
@@ -155,16 +156,18 @@ struct ChunkCfg {
   static constexpr int D_SLOTS = TC * NC;              // ... of delta per step
   static constexpr int TPW = (4 + W - 1) / W;  // dt tiles (16 channels each) per wave
   static_assert((NS == 2 || NS % 4 == 0) && NS <= 16, "state group");
-  static_assert(TC == 16, "one 16-token MFMA tile row per step");
+  static_assert(TC == 16 || TC == 32, "16-token MFMA tile rows per step");
   static_assert(R % 32 == 0, "MFMA k-steps");
 };
 
 }  // namespace
 
 // kSum: summary pass (chunks 0 .. nchunks-2 from zero: end state and sum of dt).
-template <int NS, int W, int R, bool kSum>
+// TC: tokens per step (32 halves the barriers and per-step costs per token where the LDS
+// it takes still lets two workgroups share a CU; 16 otherwise).
+template <int NS, int W, int R, bool kSum, int TC_>
 __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
-  using C = ChunkCfg<NS, W, R>;
+  using C = ChunkCfg<NS, W, R, TC_>;
   constexpr int N = C::N, CB = C::CB, TC = C::TC, NC = C::NC, NT = C::NT;
   // Tokens per group of scalar loads.  With up to 8 states per wave two groups' B and C
   // rows are in flight at once (32 scalar registers; the summary pass reads B only);
@@ -287,21 +290,24 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
     for (int tw = 0; tw < C::TPW; ++tw) {
       const int rbk = wave + tw * W;
       if (rbk >= CB / 16) break;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int tt = lane & 15;
       const int chl = rbk * 16 + (lane & 15);
 #pragma unroll
-      for (int ks = 0; ks < R / 32; ++ks) {
-        const int cidx = ks * 4 + (lane >> 4);
-        const bf16x8 a = *(const bf16x8*)(d_s[cur] + (tt * NC + (cidx ^ (tt & C::SWM))) * 8);
-        acc = mfma16x16x32(a, wfrag[tw][ks], acc);
-      }
+      for (int th = 0; th < TC / 16; ++th) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int tt = th * 16 + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * (lane >> 4) + i;
-        const float dt = t < tn ? softplus_f(acc[i] + bias[tw]) : 0.f;
-        const float xv = (float)x_s[cur][t * CB + chl];
-        dd_s[t * CB + chl] = make_float2(dt, dt * xv);
+        for (int ks = 0; ks < R / 32; ++ks) {
+          const int cidx = ks * 4 + (lane >> 4);
+          const bf16x8 a = *(const bf16x8*)(d_s[cur] + (tt * NC + (cidx ^ (tt & C::SWM))) * 8);
+          acc = mfma16x16x32(a, wfrag[tw][ks], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = th * 16 + 4 * (lane >> 4) + i;
+          const float dt = t < tn ? softplus_f(acc[i] + bias[tw]) : 0.f;
+          const float xv = (float)x_s[cur][t * CB + chl];
+          dd_s[t * CB + chl] = make_float2(dt, dt * xv);
+        }
       }
     }
     lds_barrier();
@@ -476,12 +482,29 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(float* __restrict__ hsu
 
 namespace {
 
+// Tokens per step of a launch of `wgs` workgroups: 32 at 4 waves when the grid leaves at
+// most two workgroups per CU, which is all the LDS of a 32-token step (about 80 KB) allows;
+// otherwise 16 (40 KB: up to four per CU).  8-wave shapes take 16 (LDS), 1- and 2-wave
+// shapes 16 (each wave would hold 4 or 2 dt tiles' MFMA operands).  Measured at
+// d_inner 4096, N = 16: 0.500 -> 0.479 ms for 8 sequences of 2048 tokens in one chunk
+// (512 workgroups); 1.09 -> 1.32 ms with 32-token steps at 4 x 8 chunks of 1024 (2048).
+template <int W>
+bool long_steps(int64_t wgs) { return W == 4 && wgs <= 512; }
+
+template <int NS, int W, int R, bool kSum>
+void launch_steps(const ScanChunkParams& p, dim3 grid, hipStream_t s) {
+  const dim3 blk(64 * W);
+  if (long_steps<W>((int64_t)grid.x * grid.y))
+    scan_chunk_kernel<NS, W, R, kSum, 32><<<grid, blk, 0, s>>>(p);
+  else
+    scan_chunk_kernel<NS, W, R, kSum, 16><<<grid, blk, 0, s>>>(p);
+}
+
 template <int NS, int W, int R>
 hipError_t run_chunk(const ScanChunkParams& p, hipStream_t s) {
-  const dim3 blk(64 * W);
   const int cbk = p.Di / 64;
   if (p.nchunks > 1) {
-    scan_chunk_kernel<NS, W, R, true><<<dim3(cbk, p.B * (p.nchunks - 1)), blk, 0, s>>>(p);
+    launch_steps<NS, W, R, true>(p, dim3(cbk, p.B * (p.nchunks - 1)), s);
     const int Kc = p.nchunks - 1;
     const int64_t elems = (int64_t)p.B * p.Di * p.N;
     auto carry = [&](auto kp) {
@@ -495,7 +518,7 @@ hipError_t run_chunk(const ScanChunkParams& p, hipStream_t s) {
     else if (Kc <= 32) carry(std::integral_constant<int, 32>());
     else carry(std::integral_constant<int, 64>());
   }
-  scan_chunk_kernel<NS, W, R, false><<<dim3(cbk, p.B * p.nchunks), blk, 0, s>>>(p);
+  launch_steps<NS, W, R, false>(p, dim3(cbk, p.B * p.nchunks), s);
   return hipGetLastError();
 }
 
