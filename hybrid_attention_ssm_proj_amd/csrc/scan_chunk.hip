@@ -488,13 +488,15 @@ namespace {
 // shapes 16 (each wave would hold 4 or 2 dt tiles' MFMA operands).  Measured at
 // d_inner 4096, N = 16: 0.500 -> 0.479 ms for 8 sequences of 2048 tokens in one chunk
 // (512 workgroups); 1.09 -> 1.32 ms with 32-token steps at 4 x 8 chunks of 1024 (2048).
+// Chunks that are not a multiple of 32 tokens (the meta rows' chunks of 16) keep
+// 16-token steps: a 32-token step would run half empty at every chunk's end.
 template <int W>
-bool long_steps(int64_t wgs) { return W == 4 && wgs <= 512; }
+bool long_steps(int64_t wgs, int chunk) { return W == 4 && wgs <= 512 && chunk % 32 == 0; }
 
 template <int NS, int W, int R, bool kSum>
 void launch_steps(const ScanChunkParams& p, dim3 grid, hipStream_t s) {
   const dim3 blk(64 * W);
-  if (long_steps<W>((int64_t)grid.x * grid.y))
+  if (long_steps<W>((int64_t)grid.x * grid.y, p.chunk))
     scan_chunk_kernel<NS, W, R, kSum, 32><<<grid, blk, 0, s>>>(p);
   else
     scan_chunk_kernel<NS, W, R, kSum, 16><<<grid, blk, 0, s>>>(p);
