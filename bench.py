@@ -735,7 +735,7 @@ def bench_stack(hy, torch, dev, n_layers=16, B=1, L=8192, W=1024, dsteps=16, ste
     for name, win in (("partial_swa", W), ("all_global", 0)):
         st = HymbaStack(dims, n_layers, lambda l, ld: device_weights(torch, ld, 1000 + l, dev),
                         win, device=dev)
-        st.alloc(B, L, L + dsteps)
+        st.alloc(B, L, L + 2 * dsteps)
         st.prefill(meta, xp)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -748,19 +748,34 @@ def bench_stack(hy, torch, dev, n_layers=16, B=1, L=8192, W=1024, dsteps=16, ste
             st.decode(x[:, L + s].contiguous())
         torch.cuda.synchronize()
         td = (time.perf_counter() - t0) / dsteps
+        # the same steps replayed from a HIP graph of one whole-stack decode step (the
+        # caches have room for 2 * dsteps positions past the prompt)
+        xs = torch.empty_like(x[:, L])
+        g, _ = st.capture_decode(xs)
+        t0 = time.perf_counter()
+        for s in range(dsteps):
+            xs.copy_(x[:, L + s])
+            g.replay()
+        torch.cuda.synchronize()
+        tg = (time.perf_counter() - t0) / dsteps
+        del g
         res[name] = {"prefill_ms": round(tp * 1e3, 3), "prefill_tokens_per_s": round(B * L / tp, 1),
                      "decode_us_per_step": round(td * 1e6, 1),
                      "decode_tokens_per_s": round(B / td, 1),
+                     "decode_graph_us_per_step": round(tg * 1e6, 1),
                      "decode_cache_bytes": st.decode_cache_bytes(B, L + dsteps),
                      "global_layers": [l for l, sc in enumerate(st.sched) if sc[0] == 0],
                      "consumers": [l for l, sc in enumerate(st.sched) if sc[1] == 1]}
         log(f"[bench] stack {name}: prefill {tp * 1e3:.2f} ms ({B * L / tp / 1e6:.3f} M tok/s), "
-            f"decode {td * 1e6:.1f} us/step, cache {res[name]['decode_cache_bytes'] / 1e6:.1f} MB")
+            f"decode {td * 1e6:.1f} us/step (graph {tg * 1e6:.1f}), "
+            f"cache {res[name]['decode_cache_bytes'] / 1e6:.1f} MB")
         del st
         torch.cuda.empty_cache()
     a, g = res["partial_swa"], res["all_global"]
     res["ratios"] = {"prefill_speedup": round(g["prefill_ms"] / a["prefill_ms"], 3),
                      "decode_speedup": round(g["decode_us_per_step"] / a["decode_us_per_step"], 3),
+                     "decode_graph_speedup": round(g["decode_graph_us_per_step"] /
+                                                   a["decode_graph_us_per_step"], 3),
                      "cache_reduction": round(g["decode_cache_bytes"] / a["decode_cache_bytes"], 3)}
     res["workload"] = (f"{n_layers} layers of the prefill layer shape, B={B}, L={L}, window {W}, "
                        f"then {dsteps} decode steps; layer l+1 takes layer l's y and y_meta")

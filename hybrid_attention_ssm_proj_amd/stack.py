@@ -162,3 +162,18 @@ class HymbaStack:
             kv = self._kv(prod)
             x = layer.decode(x, kv, self._state(l), stream=stream)
         return x
+
+    def capture_decode(self, x):
+        """One decode step of the whole stack captured as a HIP graph (torch's graph
+        object, a hipGraph on ROCm): every layer's kernels in order, replayed with no host
+        work between them.  `x` [B, d] is the graph's input buffer: copy the next token's
+        rows into it, then call replay(); the returned y is the graph's output buffer.
+        The kernels take positions, ring slots and the SSM state from device memory, so
+        each replay advances every layer's state as an eager decode step does.  Run one
+        eager decode at this batch first: the layers' workspaces must exist before the
+        capture (the library itself allocates nothing and issues no memset)."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            y = self.decode(x)
+        return g, y

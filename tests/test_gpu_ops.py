@@ -29,6 +29,14 @@ def _normal(g, shape, std=1.0):
     (BF16, 8, 2, 128, 16, 160, 2, 48),
     (BF16, 4, 2, 64, 8, 72, 3, 0),
     (BF16, 4, 4, 64, 0, 130, 1, 32),
+    # key-tile selection edge cases of the bf16 kernel (64-key tiles): meta prefixes that
+    # end inside a tile, windows whose first tile is inside / past the meta tiles, a
+    # sequence of one partial tile, 8 q heads per kv head
+    (BF16, 8, 2, 128, 70, 200, 2, 33),
+    (BF16, 8, 2, 128, 130, 300, 1, 64),
+    (BF16, 8, 4, 64, 0, 257, 2, 100),
+    (BF16, 8, 1, 128, 5, 40, 3, 0),
+    (BF16, 8, 1, 64, 64, 191, 1, 65),
     (F32, 4, 2, 32, 8, 64, 2, 0),
     (F32, 2, 1, 64, 4, 40, 1, 16),
 ])

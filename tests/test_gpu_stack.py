@@ -86,6 +86,60 @@ def test_stack_decode_continues_the_prefill():
         assert e < TOL_BF16, (s, e)
 
 
+def _snapshot(st):
+    caches = [None if c is None else {k: v.clone() for k, v in c.items()} for c in st.caches]
+    states = [{k: v.clone() for k, v in s_.items()} for s_ in st.states]
+    return caches, states
+
+
+def _restore(st, snap):
+    for c, sc in zip(st.caches, snap[0]):
+        if c is not None:
+            for k in c:
+                c[k].copy_(sc[k])
+    for s_, ss in zip(st.states, snap[1]):
+        for k in s_:
+            s_[k].copy_(ss[k])
+
+
+def test_stack_decode_graph_replays_match_eager():
+    """One decode step of a 6-layer stack (global, sliding-window producer, consumer
+    roles) captured as a HIP graph and replayed 4 times, with eager work and
+    synchronisations between the replays: every replay's y, and the states and caches
+    after the last, equal the eager steps from the same state (the x_proj split-K
+    accumulates with fp32 atomics, whose order may differ: the gate is one bf16 step)."""
+    dims = small_dims()
+    B, L, W, steps = 2, 60, 24, 4
+    meta_t, _, x_t, _ = gen_activations(dims, 96, B, L + steps)
+    meta, x = meta_t.to(DEV), x_t.to(DEV)
+    st, _ = _stack(dims, 6, W, 96)
+    st.alloc(B, L, L + steps)
+    st.prefill(meta, x[:, :L].contiguous())
+    torch.cuda.synchronize()
+    snap = _snapshot(st)
+    eager = [st.decode(x[:, L + s].contiguous()).clone() for s in range(steps)]
+    torch.cuda.synchronize()
+    after = _snapshot(st)
+    _restore(st, snap)
+    xs = torch.empty_like(x[:, L])
+    g, ys = st.capture_decode(xs)
+    for s in range(steps):
+        xs.copy_(x[:, L + s])
+        g.replay()
+        torch.cuda.synchronize()
+        junk = (x[:, :L].float() * 2).sum()  # eager work between replays
+        e = rel_err(to_np(ys), to_np(eager[s]))
+        print(f"replay {s}: y {e:.2e} (junk {float(junk):.1f})")
+        assert e < 2 ** -7, (s, e)
+    for l, (s_, sa) in enumerate(zip(st.states, after[1])):
+        assert torch.equal(s_["pos"], sa["pos"]), l
+        assert rel_err(to_np(s_["h"]), to_np(sa["h"])) < 1e-4, l
+    for l, (c, ca) in enumerate(zip(st.caches, after[0])):
+        if c is not None:
+            assert rel_err(to_np(c["k"]), to_np(ca["k"])) < 2 ** -7, l
+            assert rel_err(to_np(c["v"]), to_np(ca["v"])) < 2 ** -7, l
+
+
 def test_cache_bytes_partial_swa_vs_all_global():
     dims = small_dims()
     st, _ = _stack(dims, 6, 40, 99)
