@@ -829,6 +829,141 @@ hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t l
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ bf16 few-row streaming
+// y[m, n] = sum_k x[m, k] w[n, k] for a few rows (M <= 4: a small decode batch), where the
+// tiled few-row kernel would spend a 128-row MFMA tile on one row and leave the weight
+// stream at a fraction of HBM bandwidth.  A workgroup stages the M rows of x in LDS; each
+// wave streams CPW weight rows with 16-byte loads (lane l takes k = 8l + 512i), the next
+// slice's loads issued before the current slice's dot products (v_dot2_f32_bf16, fp32
+// sums), then sums each column over its 64 lanes and stores it.  Optional epilogue: the
+// producer's K / V columns also go to ring slot pos[m] % slots (decode in_proj).
+template <int M, int CPW>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(const bf16* __restrict__ x, int64_t ldx,
+                                                        const bf16* __restrict__ w, int64_t ldw,
+                                                        int N, int K, GemvOut out) {
+  extern __shared__ __attribute__((aligned(16))) bf16 xs[];  // [M][K]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid * 8; i < M * K; i += 256 * 8) {
+    const int m = i / K, k = i % K;
+    *(u32x4*)(xs + i) = *(const u32x4*)(x + (int64_t)m * ldx + k);
+  }
+  __syncthreads();
+  const int n0 = (blockIdx.x * 4 + wave) * CPW;
+  if (n0 >= N) return;
+  const bf16* wr[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) wr[c] = w + (int64_t)min(n0 + c, N - 1) * ldw;
+  float acc[CPW][M];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[c][m] = 0.f;
+  auto dot2 = [](uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  };
+  int k = lane * 8;
+  u32x4 wn[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) wn[c] = k < K ? *(const u32x4*)(wr[c] + k) : u32x4{0, 0, 0, 0};
+  for (; k < K; k += 512) {
+    u32x4 wc[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) wc[c] = wn[c];
+    if (k + 512 < K) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) wn[c] = *(const u32x4*)(wr[c] + k + 512);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4 xv = *(const u32x4*)(xs + m * K + k);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        float a = acc[c][m];
+        a = dot2(wc[c][0], xv[0], a);
+        a = dot2(wc[c][1], xv[1], a);
+        a = dot2(wc[c][2], xv[2], a);
+        a = dot2(wc[c][3], xv[3], a);
+        acc[c][m] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = acc[c][m];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+      acc[c][m] = v;
+    }
+  // lane c * M + m stores column n0 + c of row m
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int n = n0 + c;
+      if (lane != c * M + m || n >= N) continue;
+      const float v = acc[c][m];
+      if (out.f32) {
+        ((float*)out.y)[(int64_t)m * out.ldy + n] = v;
+        continue;
+      }
+      const bf16 b = (bf16)v;
+      ((bf16*)out.y)[(int64_t)m * out.ldy + n] = b;
+      if (out.k_col >= 0) {
+        bf16* ring = nullptr;
+        int rel = 0;
+        if (n >= out.k_col && n < out.k_col + out.kvw) {
+          ring = (bf16*)out.ring_k;
+          rel = n - out.k_col;
+        } else if (n >= out.v_col && n < out.v_col + out.kvw) {
+          ring = (bf16*)out.ring_v;
+          rel = n - out.v_col;
+        }
+        if (ring != nullptr) {
+          const int slot = max(out.pos[m], 0) % out.slots;
+          const int gh = rel / out.head_dim, d = rel % out.head_dim;
+          ring[(((int64_t)m * out.Hkv + gh) * out.slots + slot) * out.head_dim + d] = b;
+        }
+      }
+    }
+}
+
+bool gemv_bf16_ok(int M, int K, int64_t ldx, int64_t ldw) {
+  return M >= 1 && M <= kGemvMaxRows && K > 0 && K % 8 == 0 && ldx % 8 == 0 && ldw % 8 == 0 &&
+         (size_t)M * K * 2 <= 64 * 1024;
+}
+
+hipError_t launch_gemv_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, int M, int N,
+                            int K, const GemvOut& out, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!gemv_bf16_ok(M, K, ldx, ldw) || out.y == nullptr || ((uintptr_t)x & 15) ||
+      ((uintptr_t)w & 15))
+    return hipErrorInvalidValue;
+  const size_t lds = (size_t)M * K * 2;
+  // columns per wave: enough workgroups to cover the CUs, at most 4 weight rows in flight
+  const int cpw = N >= 4096 ? 4 : (N >= 1024 ? 2 : 1);
+  const dim3 grid((N + 4 * cpw - 1) / (4 * cpw)), blk(256);
+  auto go = [&](auto mc, auto cc) {
+    constexpr int MM = decltype(mc)::value, CC = decltype(cc)::value;
+    gemv_bf16_kernel<MM, CC><<<grid, blk, lds, s>>>((const bf16*)x, ldx, (const bf16*)w, ldw, N,
+                                                    K, out);
+  };
+  auto by_cpw = [&](auto mc) {
+    if (cpw == 4) go(mc, std::integral_constant<int, 4>());
+    else if (cpw == 2) go(mc, std::integral_constant<int, 2>());
+    else go(mc, std::integral_constant<int, 1>());
+  };
+  switch (M) {
+    case 1: by_cpw(std::integral_constant<int, 1>()); break;
+    case 2: by_cpw(std::integral_constant<int, 2>()); break;
+    case 3: by_cpw(std::integral_constant<int, 3>()); break;
+    default: by_cpw(std::integral_constant<int, 4>()); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t ldz, int k_col,
                                       int v_col, void* ring_k, void* ring_v, int slots, int Hkv,
                                       int head_dim, const int32_t* pos, float* zero,

@@ -874,11 +874,32 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   // run split-K into fp32 accumulators.  Otherwise the tiled GEMM writes Z directly and
   // a copy kernel fills the ring.
   const bool splitk = decode_splitk(s);
+  // A small batch (at most kGemvMaxRows sequences, bf16) streams the weights through the
+  // few-row kernel instead: its three projections store their results directly (no K
+  // slices, no accumulator to clear), and in_proj writes the producer's ring slot too.
+  const bool gemv = b16 && B <= kGemvMaxRows && (s.xs_col * s.es) % 16 == 0 &&
+                    gemv_bf16_ok(B, s.d, s.d, s.d) && gemv_bf16_ok(B, s.Di, s.n_in, s.Di) &&
+                    gemv_bf16_ok(B, (int)s.fw, s.fw, s.fw);
   auto gemm = [&](const GemmOperands& op, const GemmOutput& out) {
     return b16 ? launch_gemm_bf16(op, out, GemmShape::Skinny, stream)
                : launch_gemm_f32(op, out, stream);
   };
-  if (splitk) {
+  if (gemv) {
+    GemvOut out{z, s.n_in, false};
+    if (!s.share) {
+      out.k_col = (int)s.k_col;
+      out.v_col = (int)s.v_col;
+      out.kvw = s.Hkv * s.dh;
+      out.head_dim = s.dh;
+      out.Hkv = s.Hkv;
+      out.slots = kv->slots;
+      out.ring_k = kv->k;
+      out.ring_v = kv->v;
+      out.pos = state->pos;
+    }
+    HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ,
+                 launch_gemv_bf16(x, s.d, w->w_in, s.d, B, (int)s.n_in, s.d, out, stream));
+  } else if (splitk) {
     // the same launch clears the x_proj accumulator
     GemmOperands op{x, s.d, nullptr, 0, B, w->w_in, s.d, B, (int)s.n_in, s.d};
     HYMBA_LAUNCH(HYMBA_STAGE_IN_PROJ,
@@ -925,7 +946,11 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   // x_proj -> xdbl [B, R + 2N] fp32 (delta, B, C).
   {
     GemmOperands op{z + s.xs_col * s.es, s.n_in, nullptr, 0, B, w->w_x, s.Di, B, nx, s.Di};
-    if (splitk) {
+    if (gemv) {
+      HYMBA_LAUNCH(HYMBA_STAGE_XPROJ,
+                   launch_gemv_bf16(z + s.xs_col * s.es, s.n_in, w->w_x, s.Di, B, nx, s.Di,
+                                    GemvOut{xdbl, nx, true}, stream));
+    } else if (splitk) {
       HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, launch_gemm_bf16_splitk(op, xdbl, nx,
                                                               splitk_factor(B, nx, s.Di), stream));
     } else {
@@ -976,7 +1001,11 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   }
   {
     GemmOperands op{f, s.fw, nullptr, 0, B, w->w_out, s.fw, B, s.d, (int)s.fw};
-    if (splitk) {
+    if (gemv) {
+      HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ,
+                   launch_gemv_bf16(f, s.fw, w->w_out, s.fw, B, s.d, (int)s.fw,
+                                    GemvOut{y, s.d, false}, stream));
+    } else if (splitk) {
       const int64_t stride = (int64_t)B * s.d;
       HYMBA_LAUNCH(HYMBA_STAGE_OUT_PROJ,
                    launch_gemm_bf16_splitk(op, yacc, s.d, splitk_factor(B, s.d, (int)s.fw),

@@ -78,6 +78,24 @@ hipError_t launch_gemm_bf16_decode_in(const GemmOperands& op, void* z, int64_t l
                                       int head_dim, const int32_t* pos, float* zero,
                                       int64_t zero_n, hipStream_t s);
 
+// Few-row streaming products (gemv_bf16_kernel): y[m, n] = sum_k x[m, k] w[n, k] for
+// M <= kGemvMaxRows rows of x (row stride ldx) and N rows of w (row stride ldw), fp32 sums;
+// y bf16 or fp32 (row stride ldy).  With k_col >= 0 (bf16 y) the K / V columns of row m are
+// also written to ring slot pos[m] % slots of ring_k / ring_v ([M, Hkv, slots, head_dim]).
+constexpr int kGemvMaxRows = 4;
+struct GemvOut {
+  void* y;
+  int64_t ldy;
+  bool f32;
+  int k_col = -1, v_col = -1, kvw = 0, head_dim = 0, Hkv = 0, slots = 0;
+  void* ring_k = nullptr;  // bf16
+  void* ring_v = nullptr;
+  const int32_t* pos = nullptr;
+};
+bool gemv_bf16_ok(int M, int K, int64_t ldx, int64_t ldw);
+hipError_t launch_gemv_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, int M, int N,
+                            int K, const GemvOut& out, hipStream_t s);
+
 // ----------------------------------------------------------------- attention
 // Keys/values at X~ position j of sequence b: j < n_meta from the meta arrays
 // (meta + g*meta_head_stride + j*meta_row_stride), otherwise from the sequence
