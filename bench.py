@@ -846,6 +846,23 @@ def bench_decode(hy, torch, dev, args, dims=None, block_inter=0):
         layer.decode(xin[s], kvs, sts, y=yout, stream=stream)
     torch.cuda.synchronize()
     span = time.perf_counter() - t0
+    # the same steps replayed from a HIP graph of 8 consecutive decode steps (inputs
+    # xin[0..7], outputs into yout): the kernels without host launch gaps; every replay
+    # advances the ring, the positions and the SSM state like eager steps
+    g_steps = 8
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        for s in range(g_steps):
+            layer.decode(xin[s], kvs, sts, y=yout, stream=cs)
+    torch.cuda.synchronize()
+    reps = max(1, steps // g_steps)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    g_us = (time.perf_counter() - t0) / (reps * g_steps) * 1e6
+    del graph
     st = {name: {"us": round(r["avg_ms"] * 1e3, 2), "launches_per_step": r["per_step"]}
           for name, r in st_rec.items()}
     # algorithmic bytes per step: weights, ring K/V read, meta K/V, state read + write
@@ -858,9 +875,12 @@ def bench_decode(hy, torch, dev, args, dims=None, block_inter=0):
     step_bytes = wbytes + ring_bytes + meta_bytes + h_bytes
     us = span / steps * 1e6
     tps = B * steps / span
-    log(f"[bench] decode {us:.1f} us/step, {tps / 1e6:.3f} M tokens/s")
+    log(f"[bench] decode {us:.1f} us/step, {tps / 1e6:.3f} M tokens/s "
+        f"(HIP graph of {g_steps} steps: {g_us:.1f} us/step)")
     return {"value": round(tps, 1), "unit": "tokens/s", "us_per_step": round(us, 2),
             "steps": steps, "batch": B,
+            "graph": {"us_per_step": round(g_us, 2), "tokens_per_s": round(B / g_us * 1e6, 1),
+                      "steps_per_graph": g_steps, "replays": reps},
             "workload": "decode, bf16, B=128, 1 token per sequence after 4096 prior tokens, "
                         "window 1024 ring + 128 meta entries, same layer shape" +
                         (f", inside the block wrapper (FFN {block_inter})" if block_inter else ""),

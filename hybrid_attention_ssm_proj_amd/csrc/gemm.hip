@@ -333,6 +333,15 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_void_t* lptr) {
                :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(gptr) : "memory", "m0");
 }
 
+// The same transfer marked non-temporal: for a weight stream that is read once per call
+// and is larger than the caches, so it does not evict data that later kernels re-read
+// (the decode K/V ring).
+__device__ __forceinline__ void dma16_nt(const void* gptr, lds_void_t* lptr) {
+  const uint32_t l = (uint32_t)(uintptr_t)lptr;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(gptr) : "memory", "m0");
+}
+
 // K % 64 == 0.  Two LDS stages of BM x 64 and BN x 64.  Per k-tile t: fragments of
 // k-substeps 1..3 are read one substep ahead of the MFMAs; before the last substep's
 // MFMAs every wave waits for tile t+1 to land, passes a barrier (after which nobody
@@ -620,7 +629,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_fewrow_kernel(GemmOperands g, F
       dma16(A + k0 + a_off[j], (lds_void_t*)(sa(st) + (j * NW + wave) * 512));
 #pragma unroll
     for (int j = 0; j < B_INS; ++j)
-      dma16(Bm + k0 + b_off[j], (lds_void_t*)(sb(st) + (j * NW + wave) * 512));
+      dma16_nt(Bm + k0 + b_off[j], (lds_void_t*)(sb(st) + (j * NW + wave) * 512));
   };
   // Two accumulator sets (even / odd k-steps) so consecutive MFMAs do not wait on each
   // other: with one 32 x 32 block per wave the tile's four k-steps would otherwise form
@@ -824,32 +833,47 @@ hipError_t launch_gemm_bf16_splitk(const GemmOperands& op, float* acc, int64_t l
   dim3 grid((op.N + 63) / 64, ns, (op.M + 127) / 128);
   if (slice_stride > 0)
     gemm_bf16_fewrow_kernel<kFewPartial, 128, 4><<<grid, dim3(256), 0, s>>>(op, out, kslice);
-  else
+  else if ((int64_t)grid.x * grid.y * grid.z < 128) {
+    // a small grid (the narrow decode x_proj: 3 column tiles x 16 slices) takes 64-row
+    // blocks, twice the workgroups (0.7 us faster at 128 rows)
+    grid.z = (op.M + 63) / 64;
+    gemm_bf16_fewrow_kernel<kFewAtomic, 64, 4><<<grid, dim3(256), 0, s>>>(op, out, kslice);
+  } else {
     gemm_bf16_fewrow_kernel<kFewAtomic, 128, 4><<<grid, dim3(256), 0, s>>>(op, out, kslice);
+  }
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ bf16 few-row streaming
 // y[m, n] = sum_k x[m, k] w[n, k] for a few rows (M <= 4: a small decode batch), where the
 // tiled few-row kernel would spend a 128-row MFMA tile on one row and leave the weight
-// stream at a fraction of HBM bandwidth.  A workgroup stages the M rows of x in LDS; each
-// wave streams CPW weight rows with 16-byte loads (lane l takes k = 8l + 512i), the next
-// slice's loads issued before the current slice's dot products (v_dot2_f32_bf16, fp32
-// sums), then sums each column over its 64 lanes and stores it.  Optional epilogue: the
-// producer's K / V columns also go to ring slot pos[m] % slots (decode in_proj).
-template <int M, int CPW>
+// stream at a fraction of HBM bandwidth.  A workgroup stages the M rows of x in LDS.
+// KS = 1: each wave owns CPW columns and streams their whole weight rows; KS = 4: the 4
+// waves share the workgroup's CPW columns and take a quarter of K each (narrow outputs,
+// where one wave per column would leave too few waves streaming), summed through LDS.
+// A wave streams its rows with 16-byte non-temporal loads (lane l takes k = kb + 8l +
+// 512i; the weights are read once per call), the next slice's loads issued before the
+// current slice's dot products (v_dot2_f32_bf16, fp32 sums), then sums each column over
+// its 64 lanes.  Optional epilogue: the producer's K / V columns also go to ring slot
+// pos[m] % slots (decode in_proj).
+template <int M, int CPW, int KS>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(const bf16* __restrict__ x, int64_t ldx,
                                                         const bf16* __restrict__ w, int64_t ldw,
                                                         int N, int K, GemvOut out) {
+  static_assert(KS == 1 || KS == 4, "waves per column group");
   extern __shared__ __attribute__((aligned(16))) bf16 xs[];  // [M][K]
+  __shared__ float red[KS == 4 ? 4 : 1][CPW * M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid * 8; i < M * K; i += 256 * 8) {
     const int m = i / K, k = i % K;
     *(u32x4*)(xs + i) = *(const u32x4*)(x + (int64_t)m * ldx + k);
   }
   __syncthreads();
-  const int n0 = (blockIdx.x * 4 + wave) * CPW;
-  if (n0 >= N) return;
+  const int n0 = (KS == 1 ? blockIdx.x * 4 + wave : blockIdx.x) * CPW;
+  if (n0 >= N) return;  // uniform over the workgroup when KS = 4
+  // this wave's k range: [kb, ke), a multiple of 8 wide
+  const int kq = KS == 1 ? K : ((K / 8 + KS - 1) / KS) * 8;
+  const int kb = KS == 1 ? 0 : min(wave * kq, K), ke = min(kb + kq, K);
   const bf16* wr[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) wr[c] = w + (int64_t)min(n0 + c, N - 1) * ldw;
@@ -862,17 +886,18 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const bf16* __restrict__
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c, false);
   };
-  int k = lane * 8;
+  int k = kb + lane * 8;
   u32x4 wn[CPW];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) wn[c] = k < K ? *(const u32x4*)(wr[c] + k) : u32x4{0, 0, 0, 0};
-  for (; k < K; k += 512) {
+  for (int c = 0; c < CPW; ++c)
+    wn[c] = k < ke ? __builtin_nontemporal_load((const u32x4*)(wr[c] + k)) : u32x4{0, 0, 0, 0};
+  for (; k < ke; k += 512) {
     u32x4 wc[CPW];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) wc[c] = wn[c];
-    if (k + 512 < K) {
+    if (k + 512 < ke) {
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) wn[c] = *(const u32x4*)(wr[c] + k + 512);
+      for (int c = 0; c < CPW; ++c) wn[c] = __builtin_nontemporal_load((const u32x4*)(wr[c] + k + 512));
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -897,6 +922,21 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const bf16* __restrict__
       for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
       acc[c][m] = v;
     }
+  if constexpr (KS == 4) {  // the quarters of K: wave 0 adds the others' sums
+    if (lane == 0) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int m = 0; m < M; ++m) red[wave][c * M + m] = acc[c][m];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        acc[c][m] = red[0][c * M + m] + red[1][c * M + m] + red[2][c * M + m] + red[3][c * M + m];
+  }
   // lane c * M + m stores column n0 + c of row m
 #pragma unroll
   for (int c = 0; c < CPW; ++c)
@@ -942,18 +982,20 @@ hipError_t launch_gemv_bf16(const void* x, int64_t ldx, const void* w, int64_t l
       ((uintptr_t)w & 15))
     return hipErrorInvalidValue;
   const size_t lds = (size_t)M * K * 2;
-  // columns per wave: enough workgroups to cover the CUs, at most 4 weight rows in flight
-  const int cpw = N >= 4096 ? 4 : (N >= 1024 ? 2 : 1);
-  const dim3 grid((N + 4 * cpw - 1) / (4 * cpw)), blk(256);
-  auto go = [&](auto mc, auto cc) {
-    constexpr int MM = decltype(mc)::value, CC = decltype(cc)::value;
-    gemv_bf16_kernel<MM, CC><<<grid, blk, lds, s>>>((const bf16*)x, ldx, (const bf16*)w, ldw, N,
-                                                    K, out);
+  // Wide outputs (in_proj): a wave per 4 columns, N / 16 workgroups.  Narrower ones split
+  // K over the 4 waves of a workgroup: 4 columns per workgroup from N = 1024 (out_proj:
+  // 512 workgroups), 1 column below (x_proj).
+  const int mode = N >= 8192 ? 0 : (N >= 1024 ? 1 : 2);
+  const dim3 grid(mode == 0 ? (N + 15) / 16 : mode == 1 ? (N + 3) / 4 : N), blk(256);
+  auto go = [&](auto mc, auto cc, auto kc) {
+    constexpr int MM = decltype(mc)::value, CC = decltype(cc)::value, KK = decltype(kc)::value;
+    gemv_bf16_kernel<MM, CC, KK><<<grid, blk, lds, s>>>((const bf16*)x, ldx, (const bf16*)w, ldw,
+                                                        N, K, out);
   };
   auto by_cpw = [&](auto mc) {
-    if (cpw == 4) go(mc, std::integral_constant<int, 4>());
-    else if (cpw == 2) go(mc, std::integral_constant<int, 2>());
-    else go(mc, std::integral_constant<int, 1>());
+    if (mode == 0) go(mc, std::integral_constant<int, 4>(), std::integral_constant<int, 1>());
+    else if (mode == 1) go(mc, std::integral_constant<int, 4>(), std::integral_constant<int, 4>());
+    else go(mc, std::integral_constant<int, 1>(), std::integral_constant<int, 4>());
   };
   switch (M) {
     case 1: by_cpw(std::integral_constant<int, 1>()); break;
