@@ -1030,6 +1030,7 @@ static hipError_t run_decode(const AttnDecodeParams& p, hipStream_t s) {
     return hipErrorInvalidValue;  // stream mode is bf16 only
   }
   switch (p.keys_per_split) {
+    case 64: return run_decode_kps<T, DH, 64>(p, s);
     case 128: return run_decode_kps<T, DH, 128>(p, s);
     case 192: return run_decode_kps<T, DH, 192>(p, s);
     case 256: return run_decode_kps<T, DH, 256>(p, s);

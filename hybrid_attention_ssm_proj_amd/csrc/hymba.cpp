@@ -164,14 +164,20 @@ struct Carve {
 
 // Keys per decode-attention split: the largest of 256 / 192 / 128 that tiles the
 // longest key list (meta + window) without a partly empty last split, else 256.
-int decode_kps(const Shape& s, int span_max) {
+// Keys per split of the split-key decode attention: the widest split (256, 192 or 128
+// keys dividing the key count, else 256) whose grid of batch x kv heads x splits still
+// holds at least 128 workgroups; a smaller batch takes 64-key splits, the most
+// workgroups (one sequence with 4 kv heads and 1152 keys: 72 instead of 24).
+int decode_kps(const Shape& s, int span_max, int batch) {
   const int n = s.M + span_max;
+  const int64_t units = (int64_t)std::max(batch, 1) * s.Hkv;
   for (int k : {256, 192, 128})
-    if (n % k == 0) return k;
-  return 256;
+    if (n % k == 0 && units * ((n + k - 1) / k) >= 128) return k;
+  if (units * ((n + 255) / 256) >= 128) return 256;
+  return 64;
 }
-int decode_nsplit(const Shape& s, int span_max) {
-  const int k = decode_kps(s, span_max);
+int decode_nsplit(const Shape& s, int span_max, int batch) {
+  const int k = decode_kps(s, span_max, batch);
   return (s.M + span_max + k - 1) / k;
 }
 
@@ -362,7 +368,7 @@ size_t hymba_layer_workspace_bytes(const hymba_layer_desc* desc, int32_t batch, 
   if (mode == 1) {
     // seq_len carries the ring capacity (slots) for decode.
     const int span_max = s.W > 0 ? std::min(s.W, seq_len) : seq_len;
-    return carve_decode(s, batch, decode_nsplit(s, span_max)).total;
+    return carve_decode(s, batch, decode_nsplit(s, span_max, batch)).total;
   }
   return 0;
 }
@@ -852,7 +858,7 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
   if (any_misaligned(x, y, kv->k, kv->v, kv->k_meta, kv->v_meta, state->h, state->pos, workspace))
     return HYMBA_ERR_ALIGNMENT;
   const int span_max = s.W > 0 ? s.W : kv->slots;
-  const int nsplit = decode_nsplit(s, span_max);
+  const int nsplit = decode_nsplit(s, span_max, B);
   const Carve cv = carve_decode(s, B, nsplit);
   if (B > 0 && (workspace == nullptr || workspace_bytes < cv.total)) return HYMBA_ERR_WORKSPACE;
   hipStream_t stream = (hipStream_t)stream_;
@@ -929,7 +935,7 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     ap.pos = state->pos;
     ap.part = part;
     ap.nsplit = nsplit;
-    ap.keys_per_split = decode_kps(s, span_max);
+    ap.keys_per_split = decode_kps(s, span_max, B);
     ap.n_meta = M;
     ap.B = B;
     ap.Hq = s.Hq;

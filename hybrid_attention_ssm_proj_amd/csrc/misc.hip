@@ -323,26 +323,53 @@ hipError_t launch_row_factors(const float* ssp, int64_t ssp_ld, int na, int ns, 
 // them in registers between the two block sums and the scaled store.
 constexpr int kCombineChunks = 4;
 
+// Merge of any number of splits, 8 at a time: a group's loads are all issued before the
+// first use (one memory round trip per group), and the running sums are rescaled when a
+// group raises the running maximum (the same online rule as the attention kernels).
 template <typename T>
 __device__ __forceinline__ void combine_chunk(const float* ph, int nsplit, int rec, int d0,
                                               float v[8]) {
-  float mx = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, ph[sp * rec + rec - 4]);
-  float lsum = 0.f;
+  constexpr int G = 8;
+  float mx = -INFINITY, lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float* r = ph + sp * rec;
-    const float m = r[rec - 4];
-    if (m == -INFINITY) continue;  // empty split
-    const float w = __expf(m - mx);
-    lsum = fmaf(r[rec - 3], w, lsum);
-    const floatx4 a = *(const floatx4*)(r + d0), c = *(const floatx4*)(r + d0 + 4);
+  for (int s0 = 0; s0 < nsplit; s0 += G) {
+    float m[G], l[G];
+    floatx4 a[G], c[G];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = fmaf(a[e], w, v[e]);
-      v[4 + e] = fmaf(c[e], w, v[4 + e]);
+    for (int j = 0; j < G; ++j) {
+      if (s0 + j < nsplit) {
+        const float* r = ph + (s0 + j) * rec;
+        const floatx4 ml = *(const floatx4*)(r + rec - 4);
+        m[j] = ml[0];
+        l[j] = ml[1];
+        a[j] = *(const floatx4*)(r + d0);
+        c[j] = *(const floatx4*)(r + d0 + 4);
+      } else {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+        a[j] = c[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    float gm = mx;
+#pragma unroll
+    for (int j = 0; j < G; ++j) gm = fmaxf(gm, m[j]);
+    if (gm == -INFINITY) continue;  // every split so far is empty
+    const float sc = mx == -INFINITY ? 0.f : __expf(mx - gm);
+    lsum *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= sc;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float w = m[j] == -INFINITY ? 0.f : __expf(m[j] - gm);  // empty split: 0
+      lsum = fmaf(l[j], w, lsum);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = fmaf(a[j][e], w, v[e]);
+        v[4 + e] = fmaf(c[j][e], w, v[4 + e]);
+      }
+    }
+    mx = gm;
   }
   const float inv = 1.f / lsum;
 #pragma unroll

@@ -210,6 +210,33 @@ def test_small_bf16_decode_ring_wrap():
     assert np.all(st["pos"].cpu().numpy() == L + steps)
 
 
+def test_small_bf16_decode_many_key_splits():
+    """Global attention over a 2400-slot cache at a small batch: 16 meta + 2400 keys make
+    38 key splits of 64 (more than the 8 the fixed-size merge holds, so the grouped merge
+    runs), the last ones past every position (empty splits)."""
+    dims = small_dims(window=0)
+    B, L, S, steps = 2, 2200, 2400, 6
+    w = gen_layer_weights(dims, 86)
+    meta_t, meta, x_t, x = gen_activations(dims, 86, B, L + steps)
+    ref = orc.prefill(dims, w, meta, x[:, :L], contract=True, ring_slots=S)
+    layer = make_layer(dims, w)
+    to_dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(DEV)
+    kv = {k: to_dev(ref[k], torch.bfloat16) for k in ("k_meta", "v_meta", "k", "v")}
+    st = {"h": to_dev(ref["h"], torch.float32),
+          "pos": torch.full((B,), L, dtype=torch.int32, device=DEV)}
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    xb = x_t.to(DEV)
+    for s in range(steps):
+        y = layer.decode(xb[:, L + s].contiguous(), kv_struct(kv), state_struct(st))
+        o = orc.decode_step(dims, w, x[:, L + s], ref["k_meta"], ref["v_meta"], o["k"], o["v"],
+                            o["h"], o["pos"], contract=True)
+        torch.cuda.synchronize()
+        e = rel_err(to_np(y), o["y"])
+        assert e < TOL_BF16, (s, e)
+    assert h_err(to_np(st["h"]), o["h"]) < TOL_H
+    assert np.all(st["pos"].cpu().numpy() == L + steps)
+
+
 def test_bf16_ragged_k_slices():
     """d_model 1024 and out_proj K = 1024 + 3328 = 4352 (17 units of 256): the split-K
     out_proj (meta rows in prefill, the batch in decode) wants 16 slices of its 16 column
