@@ -323,13 +323,13 @@ hipError_t launch_row_factors(const float* ssp, int64_t ssp_ld, int na, int ns, 
 // them in registers between the two block sums and the scaled store.
 constexpr int kCombineChunks = 4;
 
-// Merge of any number of splits, 8 at a time: a group's loads are all issued before the
-// first use (one memory round trip per group), and the running sums are rescaled when a
-// group raises the running maximum (the same online rule as the attention kernels).
-template <typename T>
+// Merge of any number of splits, G at a time: a group's loads are all issued before the
+// first use (one memory round trip per group; the partials come from other CUs' L2
+// through the last-level cache), and the running sums are rescaled when a group raises
+// the running maximum (the same online rule as the attention kernels).
+template <typename T, int G = 16>
 __device__ __forceinline__ void combine_chunk(const float* ph, int nsplit, int rec, int d0,
                                               float v[8]) {
-  constexpr int G = 8;
   float mx = -INFINITY, lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = 0.f;
@@ -429,6 +429,13 @@ __global__ __launch_bounds__(256) void decode_combine_norm_kernel(const float* p
   const int wa = Hq * dh, nch = (wa + ws) / 8, rec = dh + 4;
   float v[kCombineChunks][8];
   float sa = 0.f, ss = 0.f;
+  // the SSM half's chunks are plain loads: issue them first, so they overlap the merges'
+  // round trips
+#pragma unroll
+  for (int c = 0; c < kCombineChunks; ++c) {
+    const int ch = threadIdx.x + c * 256;
+    if (ch < nch && ch * 8 >= wa) Vec8<T>::load(row + ch * 8, v[c]);
+  }
 #pragma unroll
   for (int c = 0; c < kCombineChunks; ++c) {
     const int ch = threadIdx.x + c * 256;
@@ -441,8 +448,6 @@ __global__ __launch_bounds__(256) void decode_combine_norm_kernel(const float* p
         combine_chunk_fixed<T, 8>(ph, nsplit, rec, i - h * dh, v[c]);
       else
         combine_chunk<T>(ph, nsplit, rec, i - h * dh, v[c]);
-    } else {
-      Vec8<T>::load(row + i, v[c]);
     }
     float q = 0.f;
 #pragma unroll
