@@ -996,7 +996,13 @@ hymba_status hymba_layer_decode(const hymba_layer_desc* desc, const hymba_layer_
     HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_group_norm(b16, f, s.fw, B, (int)s.qw, s.Di,
                                                      w->beta_attn, w->beta_ssm, desc->rms_eps,
                                                      s.G, stream));
-  } else if (stream_attn) {
+  } else if (stream_attn || nsplit > 8) {
+    // more than 8 key splits: merge them over (q head, sequence) workgroups into F first;
+    // the per-row merge would read every split of a row on one CU
+    if (!stream_attn) {
+      HYMBA_LAUNCH(HYMBA_STAGE_NORM,
+                   launch_decode_combine(b16, part, nsplit, f, s.fw, B, s.Hq, s.dh, stream));
+    }
     HYMBA_LAUNCH(HYMBA_STAGE_NORM, launch_fuse_norm(b16, f, s.fw, B, (int)s.qw, s.Di,
                                                     w->beta_attn, w->beta_ssm, desc->rms_eps,
                                                     stream));

@@ -494,29 +494,86 @@ __global__ __launch_bounds__(256) void decode_combine_wide_kernel(const float* p
   norm_row<T>(row, wa, ws, ba, bs, eps);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* part, int nsplit, T* f,
-                                                            int64_t stride, int Hq, int dh) {
-  const int b = blockIdx.x;
-  T* row = f + (int64_t)b * stride;
-  const int wa = Hq * dh, rec = dh + 4;
-  for (int i = threadIdx.x * 8; i < wa; i += 256 * 8) {
-    const int h = i / dh;
-    float v[8];
-    combine_chunk<T>(part + ((int64_t)b * Hq + h) * nsplit * rec, nsplit, rec, i - h * dh, v);
-    Vec8<T>::store(row + i, v);
+// Merge of the split partials into O, one workgroup per (q head, sequence): the head's
+// dh / 8 chunks of 8 dims times SL = 256 / (dh / 8) split lanes.  Lane sl of a chunk
+// merges splits sl, sl + SL, ... (online rule), the SL partial merges meet in LDS and the
+// chunk's first lane merges them and stores O rounded to the storage type.  Spreads the
+// read of the partials over B x Hq workgroups (one workgroup per sequence reads all of a
+// row's partials on one CU).
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* part, int nsplit, T* f,
+                                                          int64_t stride, int Hq) {
+  constexpr int CPH = DH / 8, SL = 256 / CPH;
+  __shared__ float s_m[SL][CPH], s_l[SL][CPH];
+  __shared__ float s_v[SL][CPH][8];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int c = threadIdx.x % CPH, sl = threadIdx.x / CPH;
+  const int rec = DH + 4;
+  const float* ph = part + ((int64_t)b * Hq + h) * nsplit * rec;
+  float mx = -INFINITY, lsum = 0.f, v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+#pragma unroll 4
+  for (int sp = sl; sp < nsplit; sp += SL) {
+    const float* r = ph + sp * rec;
+    const floatx4 ml = *(const floatx4*)(r + rec - 4);
+    const floatx4 x0 = *(const floatx4*)(r + c * 8), x1 = *(const floatx4*)(r + c * 8 + 4);
+    const float m = ml[0];
+    if (m == -INFINITY) continue;  // empty split
+    const float nm = fmaxf(mx, m);
+    const float so = mx == -INFINITY ? 0.f : __expf(mx - nm), w = __expf(m - nm);
+    lsum = fmaf(ml[1], w, lsum * so);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = fmaf(x0[e], w, v[e] * so);
+      v[4 + e] = fmaf(x1[e], w, v[4 + e] * so);
+    }
+    mx = nm;
   }
+  s_m[sl][c] = mx;
+  s_l[sl][c] = lsum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_v[sl][c][e] = v[e];
+  __syncthreads();
+  if (sl != 0) return;
+  float gm = -INFINITY;
+  for (int j = 0; j < SL; ++j) gm = fmaxf(gm, s_m[j][c]);
+  float tl = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int j = 0; j < SL; ++j) {
+    const float m = s_m[j][c];
+    if (m == -INFINITY) continue;
+    const float w = __expf(m - gm);
+    tl = fmaf(s_l[j][c], w, tl);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = fmaf(s_v[j][c][e], w, o[e]);
+  }
+  const float inv = 1.f / tl;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= inv;
+  Vec8<T>::store(f + (int64_t)b * stride + h * DH + c * 8, o);
 }
 
 hipError_t launch_decode_combine(bool bf16_, const float* part, int nsplit, void* f,
                                  int64_t f_stride, int B, int Hq, int head_dim, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  if (bf16_)
-    decode_combine_kernel<bf16><<<dim3(B), dim3(256), 0, s>>>(part, nsplit, (bf16*)f, f_stride,
-                                                              Hq, head_dim);
-  else
-    decode_combine_kernel<float><<<dim3(B), dim3(256), 0, s>>>(part, nsplit, (float*)f, f_stride,
-                                                               Hq, head_dim);
+  const dim3 grid(Hq, B), blk(256);
+  if (bf16_) {
+    if (head_dim == 128)
+      decode_merge_kernel<bf16, 128><<<grid, blk, 0, s>>>(part, nsplit, (bf16*)f, f_stride, Hq);
+    else if (head_dim == 64)
+      decode_merge_kernel<bf16, 64><<<grid, blk, 0, s>>>(part, nsplit, (bf16*)f, f_stride, Hq);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    if (head_dim == 64)
+      decode_merge_kernel<float, 64><<<grid, blk, 0, s>>>(part, nsplit, (float*)f, f_stride, Hq);
+    else if (head_dim == 32)
+      decode_merge_kernel<float, 32><<<grid, blk, 0, s>>>(part, nsplit, (float*)f, f_stride, Hq);
+    else
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
