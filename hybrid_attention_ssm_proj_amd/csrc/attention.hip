@@ -146,11 +146,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_dl_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bid = blockIdx.x;
+  // One grid dimension, ordered longest blocks first across every head group and
+  // sequence (the blocks of the last query range see the most keys), so the heaviest
+  // workgroups start first and the short ones fill the tail; the meta blocks come last.
+  const int ngrp = p.Hq / gq;
+  const int hgi = blockIdx.x % ngrp, bid = blockIdx.x / ngrp;
   int b, p0, plim;
   if (bid < p.B * nblk_seq) {
     b = bid % p.B;
-    const int qi = nblk_seq - 1 - bid / p.B;  // longest blocks first
+    const int qi = nblk_seq - 1 - bid / p.B;
     p0 = p.n_meta + qi * qb;
     plim = p.n_meta + min(p.L, (qi + 1) * qb);
   } else {
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_dl_kernel(
     p0 = mi * qb;
     plim = min(p.n_meta, (mi + 1) * qb);
   }
-  const int h0 = blockIdx.y * gq;
+  const int h0 = hgi * gq;
   const int h = h0 + (wave % gq);
   const int g = (h0 * p.Hkv) / p.Hq;
   constexpr int QW = 16 * QT;  // queries per wave
@@ -547,7 +551,7 @@ static hipError_t run_attn_dl(const AttnParams& p, void* vt, hipStream_t s) {
   const int nblk_meta = p.meta_rows > 0 ? (p.n_meta + qb - 1) / qb : 0;
   const int nx = p.B * nblk_seq + nblk_meta;
   if (nx == 0) return hipSuccess;
-  attn_prefill_dl_kernel<DH, NW, NS, QT><<<dim3(nx, p.Hq / gq), dim3(NW * 64), 0, s>>>(
+  attn_prefill_dl_kernel<DH, NW, NS, QT><<<dim3(nx * (p.Hq / gq)), dim3(NW * 64), 0, s>>>(
       p, (const bf16*)vt, tpad, gq, qb, nblk_seq);
   return hipGetLastError();
 }
