@@ -149,17 +149,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_dl_kernel(
   // One grid dimension, ordered longest blocks first across every head group and
   // sequence (the blocks of the last query range see the most keys), so the heaviest
   // workgroups start first and the short ones fill the tail; the meta blocks come last.
+  // The sequence varies fastest: workgroups go to the 8 XCDs round-robin, so with 8
+  // sequences each XCD's L2 serves the K/V of one sequence.
   const int ngrp = p.Hq / gq;
-  const int hgi = blockIdx.x % ngrp, bid = blockIdx.x / ngrp;
-  int b, p0, plim;
-  if (bid < p.B * nblk_seq) {
-    b = bid % p.B;
-    const int qi = nblk_seq - 1 - bid / p.B;
+  const int nseq = p.B * nblk_seq * ngrp;
+  int b, p0, plim, hgi;
+  if ((int)blockIdx.x < nseq) {
+    b = blockIdx.x % p.B;
+    hgi = (blockIdx.x / p.B) % ngrp;
+    const int qi = nblk_seq - 1 - blockIdx.x / (p.B * ngrp);
     p0 = p.n_meta + qi * qb;
     plim = p.n_meta + min(p.L, (qi + 1) * qb);
   } else {
     b = 0;
-    const int mi = bid - p.B * nblk_seq;
+    hgi = (blockIdx.x - nseq) % ngrp;
+    const int mi = (blockIdx.x - nseq) / ngrp;
     p0 = mi * qb;
     plim = min(p.n_meta, (mi + 1) * qb);
   }
