@@ -24,6 +24,33 @@ def _normal(g, shape, std=1.0):
     return (g.standard_normal(size=shape) * std).astype(np.float32)
 
 
+# Shapes nobody picked by hand: drawn once from a fixed seed (the same cases every run),
+# so the kernels' tile, chunk and head-group logic also meets ragged, unaligned sizes.
+def _random_attn_cases(n, seed=2024):
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dh = int(r.choice([64, 128]))
+        hkv = int(r.choice([1, 2, 4]))
+        grp = int(r.choice([1, 2, 4, 8]))
+        window = int(r.choice([0, int(r.integers(1, 300))]))
+        out.append((BF16, hkv * grp, hkv, dh, int(r.integers(0, 140)), int(r.integers(1, 400)),
+                    int(r.integers(1, 4)), window))
+    return out
+
+
+def _random_scan_cases(n, seed=2025):
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        L = int(r.integers(1, 300))
+        chunk = int(r.choice([0, 16 * int(r.integers(1, 21))]))
+        out.append((BF16, int(r.choice([64, 128, 256])), int(r.choice([8, 16, 32, 64, 128])),
+                    int(r.choice([16, 32, 64, 128])), int(r.integers(0, 40)), L,
+                    int(r.integers(1, 4)), chunk))
+    return out
+
+
 @pytest.mark.parametrize("dtype,Hq,Hkv,dh,M,L,B,window", [
     (BF16, 8, 2, 128, 16, 96, 2, 0),
     (BF16, 8, 2, 128, 16, 160, 2, 48),
@@ -39,7 +66,7 @@ def _normal(g, shape, std=1.0):
     (BF16, 8, 1, 64, 64, 191, 1, 65),
     (F32, 4, 2, 32, 8, 64, 2, 0),
     (F32, 2, 1, 64, 4, 40, 1, 16),
-])
+] + _random_attn_cases(8))
 def test_op_attn_matches_oracle(dtype, Hq, Hkv, dh, M, L, B, window):
     g = rng(40 + Hq + dh + window, 1)
     rows = M + B * L
@@ -79,7 +106,7 @@ def test_op_attn_matches_oracle(dtype, Hq, Hkv, dh, M, L, B, window):
     (BF16, 128, 128, 128, 8, 133, 1, 32),  # 5 chunks, ragged last step
     (BF16, 128, 16, 16, 8, 64, 2, 0),      # dt_rank outside the fused set: dt GEMM, then scan
     (F32, 64, 16, 16, 4, 48, 2, 0),
-])
+] + _random_scan_cases(8))
 def test_op_scan_matches_oracle(dtype, Di, N, R, M, L, B, chunk):
     g = rng(60 + Di + N + R, 2)
     rows = M + B * L
