@@ -210,6 +210,38 @@ def test_small_bf16_decode_ring_wrap():
     assert np.all(st["pos"].cpu().numpy() == L + steps)
 
 
+@pytest.mark.parametrize("B", [9, 40])
+def test_small_bf16_decode_fewrow_batches(B):
+    """Batches between the one-to-four-row kernel and the streaming attention: the
+    projections take the 128-row few-row GEMMs with a partly filled row block (in_proj
+    with the ring write, x_proj split-K into atomics in 64-row blocks, out_proj split-K
+    partials and their slice sum), and the attention the key-split path (B x 2 kv heads
+    below 256)."""
+    dims = small_dims(window=48)
+    L, S, steps = 60, 48, 5
+    w = gen_layer_weights(dims, 87)
+    meta_t, meta, x_t, x = gen_activations(dims, 87, B, L + steps)
+    ref = orc.prefill(dims, w, meta, x[:, :L], contract=True, ring_slots=S)
+    layer = make_layer(dims, w)
+    to_dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(DEV)
+    kv = {k: to_dev(ref[k], torch.bfloat16) for k in ("k_meta", "v_meta", "k", "v")}
+    st = {"h": to_dev(ref["h"], torch.float32),
+          "pos": torch.full((B,), L, dtype=torch.int32, device=DEV)}
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    xb = x_t.to(DEV)
+    for s in range(steps):
+        y = layer.decode(xb[:, L + s].contiguous(), kv_struct(kv), state_struct(st))
+        o = orc.decode_step(dims, w, x[:, L + s], ref["k_meta"], ref["v_meta"], o["k"], o["v"],
+                            o["h"], o["pos"], contract=True)
+        torch.cuda.synchronize()
+        e = rel_err(to_np(y), o["y"])
+        assert e < TOL_BF16, (s, e)
+    assert h_err(to_np(st["h"]), o["h"]) < TOL_H
+    assert rel_err(to_np(kv["k"]), o["k"]) < TOL_BF16
+    assert rel_err(to_np(kv["v"]), o["v"]) < TOL_BF16
+    assert np.all(st["pos"].cpu().numpy() == L + steps)
+
+
 def test_small_bf16_decode_many_key_splits():
     """Global attention over a 2400-slot cache at a small batch: 16 meta + 2400 keys make
     38 key splits of 64 (more than the 8 the fixed-size merge holds, so the grouped merge
