@@ -57,6 +57,22 @@ typedef __attribute__((address_space(4))) const floatx2 const_floatx2;
 
 // NS floats at a wave-uniform address, loaded through the scalar data cache.  The buffer
 // is written by an earlier launch and only read here.
+// NS consecutive floats that every lane reads at the same LDS address (a broadcast).
+template <int NS>
+__device__ __forceinline__ void lds_uniform_load(float (&d)[NS], const float* p) {
+  if constexpr (NS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < NS; j += 4) {
+      const floatx4 v = *(const floatx4*)(p + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[j + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) d[j] = p[j];
+  }
+}
+
 template <int NS>
 __device__ __forceinline__ void uniform_load(float (&d)[NS], const float* p) {
   if constexpr (NS % 4 == 0) {
@@ -174,9 +190,17 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
   // with 16 the scalar registers hold one group, loaded just before it runs.
   constexpr bool kDB = NS <= 8;
   constexpr int GT = (kSum ? 16 : 8) / NS > 0 ? (kSum ? 16 : 8) / NS : 1;
+  // kBCL (32-token steps, at most 16 states): the step's B|C rows are staged in LDS with
+  // its other operands and read from there (broadcast reads); the delta rows take one
+  // buffer, refilled for the next step once this step's dt phase has read them, which
+  // keeps the LDS at the 80 KB that lets two workgroups share a CU.  Otherwise B and C
+  // come through the scalar cache and the delta rows are double-buffered.
+  constexpr bool kBCL = TC == 32 && N <= 16;
+  constexpr int DBUF = kBCL ? 1 : 2;
   __shared__ __attribute__((aligned(1024))) bf16 x_s[2][TC * CB];
   __shared__ __attribute__((aligned(1024))) bf16 g_s[2][kSum ? 8 : TC * CB];
-  __shared__ __attribute__((aligned(1024))) bf16 d_s[2][TC * R];
+  __shared__ __attribute__((aligned(1024))) bf16 d_s[DBUF][TC * R];
+  __shared__ __attribute__((aligned(1024))) float bc_s[kBCL ? 2 : 1][kBCL ? TC * 2 * N : 4];
   __shared__ __attribute__((aligned(16))) float2 dd_s[TC * CB];
   __shared__ __attribute__((aligned(16))) float part_s[kSum ? 4 : W * TC * CB];
 
@@ -243,6 +267,18 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
   }
   float dtsum = 0.f;
 
+  const float* bcrow = p.bc + rbase * (2 * N);  // the rows' B|C (every state)
+  auto stage_delta = [&](int buf, int s0) {
+#pragma unroll
+    for (int i = 0; i * NT < C::D_SLOTS; ++i) {
+      const int q0 = i * NT + wave * 64;
+      if (q0 < C::D_SLOTS) {
+        const int q = q0 + lane, tt = q / NC, s = q % NC;
+        const int cidx = s ^ (tt & C::SWM);
+        dma16(dl + min(s0 + tt, te - 1) * R + cidx * 8, (lds_void_t*)(d_s[buf] + q0 * 8));
+      }
+    }
+  };
   // Stage the step starting at sequence token s0 into buffer `buf`.  Piece q of an array
   // is written by lane q % 64 of the wave instruction covering pieces [64*(q/64), +64), at
   // LDS address base + 16*q.  Tokens past the chunk load its last row (never used).
@@ -257,14 +293,18 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
         if (!kSum) dma16(src + gofs, (lds_void_t*)(g_s[buf] + q0 * 8));
       }
     }
+    if constexpr (kBCL) {  // the B|C rows of the step, 2N floats each
+      constexpr int BC_SLOTS = TC * 2 * N / 4;
 #pragma unroll
-    for (int i = 0; i * NT < C::D_SLOTS; ++i) {
-      const int q0 = i * NT + wave * 64;
-      if (q0 < C::D_SLOTS) {
-        const int q = q0 + lane, tt = q / NC, s = q % NC;
-        const int cidx = s ^ (tt & C::SWM);
-        dma16(dl + min(s0 + tt, te - 1) * R + cidx * 8, (lds_void_t*)(d_s[buf] + q0 * 8));
+      for (int i = 0; i * NT < BC_SLOTS; ++i) {
+        const int q0 = i * NT + wave * 64;
+        if (q0 < BC_SLOTS) {
+          const int q = q0 + lane, tt = q / (2 * N / 4), pc = q % (2 * N / 4);
+          dma16(bcrow + min(s0 + tt, te - 1) * (2 * N) + pc * 4, (lds_void_t*)(bc_s[buf] + q0 * 4));
+        }
       }
+    } else {
+      stage_delta(buf, s0);
     }
   };
 
@@ -274,7 +314,10 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
                               : max(0, (TC * 16 - wave * 64 + NT - 1) / NT) *
                                     (ssps != nullptr ? 2 : 1);
   const int nst = (te - tb + TC - 1) / TC;  // 0 for an empty sequence: h passes through
-  if (nst > 0) stage(0, tb);
+  if (nst > 0) {
+    stage(0, tb);
+    if constexpr (kBCL) stage_delta(0, tb);
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
@@ -298,7 +341,8 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
 #pragma unroll
         for (int ks = 0; ks < R / 32; ++ks) {
           const int cidx = ks * 4 + (lane >> 4);
-          const bf16x8 a = *(const bf16x8*)(d_s[cur] + (tt * NC + (cidx ^ (tt & C::SWM))) * 8);
+          const bf16x8 a =
+              *(const bf16x8*)(d_s[kBCL ? 0 : cur] + (tt * NC + (cidx ^ (tt & C::SWM))) * 8);
           acc = mfma16x16x32(a, wfrag[tw][ks], acc);
         }
 #pragma unroll
@@ -311,6 +355,11 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
       }
     }
     lds_barrier();
+    // single delta buffer: every wave has read this step's rows, refill it for the next
+    // step (lands during the recurrence; the step's closing wait covers it)
+    if constexpr (kBCL) {
+      if (st + 1 < nst) stage_delta(0, s0 + TC);
+    }
 
     // The recurrence over the step's tokens, GT at a time; the B (and C) rows of a group
     // arrive in scalar registers through the scalar cache.  Tokens past the chunk have
@@ -330,9 +379,14 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
 #pragma unroll
         for (int u = 0; u < GT; ++u) {
           dd[u] = dd_s[(g0 + u) * CB + lane];
-          const float* brow = bstep + (kFull ? g0 + u : min(g0 + u, tlast)) * (2 * N);
-          uniform_load<NS>(bq[u], brow);
-          if constexpr (!kSum) uniform_load<NS>(cq[u], brow + N);
+          if constexpr (kBCL) {  // staged rows (past the chunk: copies of its last row)
+            lds_uniform_load<NS>(bq[u], bc_s[cur] + (g0 + u) * (2 * N) + n0);
+            if constexpr (!kSum) lds_uniform_load<NS>(cq[u], bc_s[cur] + (g0 + u) * (2 * N) + N + n0);
+          } else {
+            const float* brow = bstep + (kFull ? g0 + u : min(g0 + u, tlast)) * (2 * N);
+            uniform_load<NS>(bq[u], brow);
+            if constexpr (!kSum) uniform_load<NS>(cq[u], brow + N);
+          }
         }
       };
       auto run = [&](const float2 (&dd)[GT], const float (&bq)[GT][NS],
