@@ -1235,10 +1235,11 @@ hymba_status hymba_op_scan(int32_t dtype, const void* z, int64_t z_ld, int32_t x
 
 hymba_status hymba_op_probe(int32_t kind, int32_t blocks, int32_t iters, const void* src,
                             size_t bytes, float* out, void* stream) {
-  if (kind < 0 || kind > 2 || out == nullptr) return HYMBA_ERR_INVALID_ARG;
-  if (kind < 2 && (blocks <= 0 || iters <= 0)) return HYMBA_ERR_INVALID_ARG;
-  if (kind == 2 && (src == nullptr || bytes == 0)) return HYMBA_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 3 || out == nullptr) return HYMBA_ERR_INVALID_ARG;
+  if (kind != 2 && (blocks <= 0 || iters <= 0)) return HYMBA_ERR_INVALID_ARG;
+  if (kind >= 2 && (src == nullptr || bytes == 0)) return HYMBA_ERR_INVALID_ARG;
   if (kind == 2 && bytes % 16) return HYMBA_ERR_UNSUPPORTED;
+  if (kind == 3 && bytes < probe_operand_bytes()) return HYMBA_ERR_INVALID_ARG;
   if (any_misaligned(src, out)) return HYMBA_ERR_ALIGNMENT;
   hipError_t e = launch_probe(kind, blocks, iters, src, bytes, out, (hipStream_t)stream);
   return e == hipSuccess ? HYMBA_OK : fail_hip(e);

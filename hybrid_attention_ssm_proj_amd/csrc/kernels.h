@@ -322,6 +322,7 @@ hipError_t launch_store_rows(bool bf16, const float* acc, void* y, int B, int d,
                              bool silu = false);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // Ceiling probes (probe.hip): kind 0 exponential rate, 1 bf16 MFMA rate, 2 streaming read.
+size_t probe_operand_bytes();
 hipError_t launch_probe(int kind, int blocks, int iters, const void* src, size_t bytes, float* out,
                         hipStream_t s);
 

@@ -361,8 +361,12 @@ hymba_status hymba_op_copy(const void *src, void *dst, size_t bytes, void *strea
  *   benchmark's rooflines (the caller times it).  kind 0: `blocks` x 256 lanes each run
  *   8 independent chains of `iters` base-2 exponentials (v_exp_f32); kind 1: `blocks` x 4
  *   waves each run 4 independent chains of `iters` v_mfma_f32_32x32x16_bf16; kind 2: a
- *   streaming read of `bytes` (multiple of 16) at `src`.  out: fp32, blocks x 256
- *   (kinds 0, 1) or 8192 x 256 (kind 2) values, written so the work is kept. */
+ *   streaming read of `bytes` (multiple of 16) at `src`; kind 3: as kind 1 with 8 rounds
+ *   of MFMAs per iteration whose operands change every instruction, read from `src`
+ *   (bf16, at least 4 MiB = bytes: 64 x 8 x 256 A fragments of 8 values, then as many B
+ *   fragments; the caller fills them, e.g. with the layer's activation and weight
+ *   distributions).  out: fp32, blocks x 256 (kinds 0, 1, 3) or 8192 x 256 (kind 2)
+ *   values, written so the work is kept. */
 hymba_status hymba_op_probe(int32_t kind, int32_t blocks, int32_t iters, const void *src,
                             size_t bytes, float *out, void *stream);
 

@@ -267,7 +267,9 @@ def test_op_gemm_argument_errors(lib):
     assert lib.hymba_op_copy(4096, 8192, 17, None) == 2
     probe = lambda kind, blocks, iters, src, nbytes, out: lib.hymba_op_probe(
         kind, blocks, iters, src, nbytes, out, None)
-    assert probe(3, 8, 8, None, 0, 4096) == 1
+    assert probe(4, 8, 8, None, 0, 4096) == 1
+    assert probe(3, 8, 8, None, 0, 4096) == 1        # kind 3 needs its operands
+    assert probe(3, 8, 8, 4096, 1 << 20, 4096) == 1  # fewer than 4 MiB of them
     assert probe(0, 0, 8, None, 0, 4096) == 1
     assert probe(0, 8, 8, None, 0, None) == 1
     assert probe(2, 0, 0, 4096, 17, 4096) == 2
