@@ -323,6 +323,13 @@ def main():
     roof["avg_launch_ms"] = round(dom_ms / dom_n, 4)
     roof["work_per_launch"] = per_launch
     roof["traffic"] = traffic_for(dominant)
+    if bound == "mfma" and ceilings.get("mfma_bf16_layer_data_tflops"):
+        # context: the MFMA rate this chip sustains on operands with the layer's value
+        # distributions (probe kind 3), beside the published peak the fraction uses
+        md = ceilings["mfma_bf16_layer_data_tflops"]
+        roof["measured_ceiling"] = {"value": md, "unit": "TFLOP/s",
+                                    "frac": round(roof["achieved"] / md, 4),
+                                    "probe": "MFMA loop on the layer's operand distributions"}
     log("[bench] stages: " + ", ".join(f"{k} {v['avg_ms']:.3f} ms x{v['launches_per_step']}"
                                        for k, v in stage_report.items()))
 
