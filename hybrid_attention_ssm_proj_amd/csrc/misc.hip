@@ -108,9 +108,68 @@ __global__ __launch_bounds__(256) void fuse_norm_kernel(T* f, int64_t stride, in
   norm_row<T>(f + (int64_t)blockIdx.x * stride, wa, ws, ba, bs, eps);
 }
 
+// The same for rows of at most 256 x 4 chunks of 8 (the decode rows: 6144 values): every
+// chunk and its beta values are loaded at once and the row stays in registers between the
+// sums and the scaled store (one memory round trip instead of a read, a re-read and the
+// beta loads in turn).
+constexpr int kNormChunks = 4;
+template <typename T>
+__global__ __launch_bounds__(256) void fuse_norm_regs_kernel(T* f, int64_t stride, int wa, int ws,
+                                                             const float* ba, const float* bs,
+                                                             float eps) {
+  T* row = f + (int64_t)blockIdx.x * stride;
+  const int nch = (wa + ws) / 8;
+  float v[kNormChunks][8], bt[kNormChunks][8];
+#pragma unroll
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int ch = threadIdx.x + c * 256;
+    if (ch < nch) {
+      const int i = ch * 8;
+      Vec8<T>::load(row + i, v[c]);
+      const float* beta = i < wa ? ba + i : bs + (i - wa);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bt[c][e] = beta[e];
+    }
+  }
+  float sa = 0.f, ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int ch = threadIdx.x + c * 256;
+    if (ch >= nch) break;
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q = fmaf(v[c][e], v[c][e], q);
+    if (ch * 8 < wa)
+      sa += q;
+    else
+      ss += q;
+  }
+  block_sum2(sa, ss);
+  const float ia = 0.5f * rsqrtf(sa / (float)wa + eps);
+  const float is = 0.5f * rsqrtf(ss / (float)ws + eps);
+#pragma unroll
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int ch = threadIdx.x + c * 256;
+    if (ch >= nch) break;
+    const float sc = ch * 8 < wa ? ia : is;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[c][e] = v[c][e] * sc * bt[c][e];
+    Vec8<T>::store(row + ch * 8, v[c]);
+  }
+}
+
 hipError_t launch_fuse_norm(bool bf16_, void* f, int64_t f_stride, int rows, int wa, int ws,
                             const float* beta_a, const float* beta_s, float eps, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (wa + ws <= 256 * kNormChunks * 8) {
+    if (bf16_)
+      fuse_norm_regs_kernel<bf16><<<dim3(rows), dim3(256), 0, s>>>((bf16*)f, f_stride, wa, ws,
+                                                                   beta_a, beta_s, eps);
+    else
+      fuse_norm_regs_kernel<float><<<dim3(rows), dim3(256), 0, s>>>((float*)f, f_stride, wa, ws,
+                                                                    beta_a, beta_s, eps);
+    return hipGetLastError();
+  }
   if (bf16_)
     fuse_norm_kernel<bf16><<<dim3(rows), dim3(256), 0, s>>>((bf16*)f, f_stride, wa, ws, beta_a,
                                                             beta_s, eps);
