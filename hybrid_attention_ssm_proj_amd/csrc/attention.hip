@@ -70,7 +70,11 @@ __device__ __forceinline__ int slot_key(int s) {
   const int blk = s >> 5, q = (s & 31) >> 3, i = s & 7;
   return blk * 32 + (i < 4 ? q * 4 + i : 16 + q * 4 + (i - 4));
 }
-__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk permutation of a 128-byte LDS row r (8 16-byte chunks) for tiles whose fragment
+// reads take row (lane % 16), chunk (lane / 16) + const: a bit permutation of r's low
+// three bits, free of LDS bank conflicts for that read on gfx950 (measured; the
+// (r & 7) ^ (r >> 3 & 1) form spends half its read cycles in conflicts there).
+__device__ __forceinline__ int swz8(int r) { return (r & 1) | ((r << 1) & 4) | ((r >> 1) & 2); }
 // Sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (same butterflies as below).
 __device__ __forceinline__ float sum_over_key_lanes(float x) {
   const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
