@@ -104,6 +104,34 @@ def test_tiny_fp32_decode_steps_match_oracle():
     assert np.all(st["pos"].cpu().numpy() == L + steps)
 
 
+def test_fp32_wide_rows_norm_matches_oracle():
+    """Rows of F wider than the 8192 values the register-resident row norm holds (128
+    attention + 8192 SSM channels): the prefill's in-place branch norm takes its two-pass
+    form; decode steps from the oracle's state follow."""
+    case = CASES[0]
+    dims = case.dims.replace(d_inner=8192)
+    B, L, S, steps = 2, 32, 40, 3
+    w = gen_layer_weights(dims, 91)
+    meta_t, meta, x_t, x = gen_activations(dims, 91, B, L + steps)
+    ref = orc.prefill(dims, w, meta, x[:, :L], ring_slots=S)
+    g = gpu_prefill(dims, w, meta_t, x_t[:, :L].contiguous(), ring_slots=S)
+    check_prefill(dims, g, ref, TOL_F32, TOL_F32, ring=True)
+    layer = g["layer"]
+    kv = {k: torch.from_numpy(ref[k].astype(np.float32)).to(DEV).contiguous()
+          for k in ("k_meta", "v_meta", "k", "v")}
+    st = {"h": torch.from_numpy(ref["h"].astype(np.float32)).to(DEV),
+          "pos": torch.full((B,), L, dtype=torch.int32, device=DEV)}
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    for s_ in range(steps):
+        xs = torch.from_numpy(x[:, L + s_].copy()).to(DEV)
+        y = layer.decode(xs, kv_struct(kv), state_struct(st))
+        o = orc.decode_step(dims, w, x[:, L + s_], ref["k_meta"], ref["v_meta"], o["k"],
+                            o["v"], o["h"], o["pos"])
+        torch.cuda.synchronize()
+        assert rel_err(to_np(y), o["y"]) < TOL_F32, s_
+    assert rel_err(to_np(st["h"]), o["h"]) < TOL_F32
+
+
 # ---------------------------------------------------------------- bf16, small shapes
 
 @pytest.mark.parametrize("window,head_dim,n_kv,M,L,B", [
@@ -240,6 +268,32 @@ def test_small_bf16_decode_fewrow_batches(B):
     assert rel_err(to_np(kv["k"]), o["k"]) < TOL_BF16
     assert rel_err(to_np(kv["v"]), o["v"]) < TOL_BF16
     assert np.all(st["pos"].cpu().numpy() == L + steps)
+
+
+def test_small_bf16_decode_wide_rows_key_splits():
+    """bf16 decode with rows of F wider than the register-resident row norm holds (1024
+    attention + 7680 SSM channels = 8704 values) and more than 8 key splits (16 meta +
+    640 ring keys in splits of 64): the split merge, then the two-pass row norm."""
+    dims = small_dims(window=0, d_inner=7680)
+    B, L, S, steps = 2, 600, 640, 3
+    w = gen_layer_weights(dims, 92)
+    meta_t, meta, x_t, x = gen_activations(dims, 92, B, L + steps)
+    ref = orc.prefill(dims, w, meta, x[:, :L], contract=True, ring_slots=S)
+    layer = make_layer(dims, w)
+    to_dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(DEV)
+    kv = {k: to_dev(ref[k], torch.bfloat16) for k in ("k_meta", "v_meta", "k", "v")}
+    st = {"h": to_dev(ref["h"], torch.float32),
+          "pos": torch.full((B,), L, dtype=torch.int32, device=DEV)}
+    o = dict(k=ref["k"], v=ref["v"], h=ref["h"], pos=np.full(B, L))
+    xb = x_t.to(DEV)
+    for s_ in range(steps):
+        y = layer.decode(xb[:, L + s_].contiguous(), kv_struct(kv), state_struct(st))
+        o = orc.decode_step(dims, w, x[:, L + s_], ref["k_meta"], ref["v_meta"], o["k"],
+                            o["v"], o["h"], o["pos"], contract=True)
+        torch.cuda.synchronize()
+        e = rel_err(to_np(y), o["y"])
+        assert e < TOL_BF16, (s_, e)
+    assert h_err(to_np(st["h"]), o["h"]) < TOL_H
 
 
 def test_small_bf16_decode_many_key_splits():
