@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhymba.so")
-SOURCES = ["gemm.hip", "gemm_fewrow.hip", "attention.hip", "scan.hip", "scan_chunk.hip", "scan_ssd.hip", "misc.hip", "probe.hip", "hymba.cpp"]
+SOURCES = ["gemm.hip", "gemm_xproj.hip", "gemm_fewrow.hip", "attention.hip", "scan.hip", "scan_chunk.hip", "scan_ssd.hip", "misc.hip", "probe.hip", "hymba.cpp"]
 ARCH = "gfx950"
 
 

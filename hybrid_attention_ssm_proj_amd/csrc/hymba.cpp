@@ -577,7 +577,9 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
                     s.nx, s.Di};
     GemmOutput out = s.H2 ? GemmOutput{EpiKind::StoreF32, bc, s.nx, nullptr, 0, 0, 0, nullptr}
                           : GemmOutput{EpiKind::XProj, delta, s.R, bc, 2 * s.N, 0, s.R, nullptr};
-    HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, gemm(op, out, GemmShape::Narrow));
+    HYMBA_LAUNCH(HYMBA_STAGE_XPROJ, b16 && gemm_xproj_ok(op, out)
+                                        ? launch_gemm_xproj_bf16(op, out, stream)
+                                        : gemm(op, out, GemmShape::Narrow));
   }
   // 5. dt_proj + softplus (unless the scan computes it in place, or the heads take dt
   // straight from x_proj).
