@@ -301,8 +301,8 @@ struct DlCfg {
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "loader tiling");
 };
 
-// Swizzle of the 8 16-byte k-chunks of row r: the 16 rows one fragment read touches
-// land in distinct bank groups fbstep ahead of the MFMAs; before the last substep's
+// The k-loop: two LDS stages of BM x 64 and BN x 64; each wave reads the fragments of
+// k-substep s + 1 (16 k) one substep ahead of the MFMAs; before the last substep's
 // MFMAs every wave waits for tile t+1 to land, passes a barrier (after which nobody
 // reads tile t's stage), refills that stage with tile t+2 and reads tile t+1's first
 // fragments, so the barrier, the DMA issue and the LDS latency hide behind the last
