@@ -209,7 +209,7 @@ __global__ __launch_bounds__(MAXW * 64) void gemm_xproj_kernel(GemmOperands g, G
 
 bool gemm_xproj_ok(const GemmOperands& op, const GemmOutput& out) {
   return out.kind == EpiKind::XProj && out.split_col % 4 == 0 && op.a_split >= op.M &&
-         op.K % 64 == 0 && op.K > 0 && op.N > 32 && op.N <= 15 * 32 && op.lda0 % 8 == 0 &&
+         op.K % 64 == 0 && op.K > 0 && op.N > 32 && op.N <= 12 * 32 && op.lda0 % 8 == 0 &&
          op.ldb % 8 == 0 && ((uintptr_t)op.a0 & 15) == 0 && ((uintptr_t)op.b & 15) == 0;
 }
 
@@ -248,9 +248,7 @@ hipError_t launch_gemm_xproj_bf16(const GemmOperands& op, const GemmOutput& out,
   // LDS budget 160 KB: Xs stages x 12 KB + W_x stages x 4 KB per compute wave.
   // Template arguments: largest wave count, Xs stages, W_x lookahead, producers, pairs.
   if (ncw <= 5) return run_xproj<7, 8, 2, 2, true>(op, out, ncw, s);
-  if (ncw <= 7) return run_xproj<9, 6, 2, 2, false>(op, out, ncw, s);
-  if (ncw <= 12) return run_xproj<14, 4, 1, 2, false>(op, out, ncw, s);
-  return run_xproj<16, 3, 1, 1, false>(op, out, ncw, s);
+  return run_xproj<14, 4, 1, 2, false>(op, out, ncw, s);
 }
 
 }  // namespace hymba

@@ -57,7 +57,7 @@ hipError_t launch_gemm_bf16(const GemmOperands& op, const GemmOutput& out, GemmS
 hipError_t launch_gemm_f32(const GemmOperands& op, const GemmOutput& out, hipStream_t s);
 // x_proj (XProj epilogue, bf16): every output column of up to 96 rows per workgroup, Xs
 // streamed once through a deep LDS ring.  gemm_xproj_ok tells whether the operands fit
-// (single-source A, K % 64 == 0, 32 < N <= 480, 16-byte aligned rows).
+// (single-source A, K % 64 == 0, 32 < N <= 384, 16-byte aligned rows).
 bool gemm_xproj_ok(const GemmOperands& op, const GemmOutput& out);
 hipError_t launch_gemm_xproj_bf16(const GemmOperands& op, const GemmOutput& out, hipStream_t s);
 // Few-row (decode) GEMMs, K % 256 == 0, single-source A.

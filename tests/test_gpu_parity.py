@@ -169,6 +169,7 @@ def test_small_bf16_prefill_state_sizes(d_state):
     (128, 64, 45, 40, 1),    # meta prefix spanning two chunks
     (32, 64, 64, 8, 3),      # exact chunk multiple
     (64, 128, 100, 0, 2),    # no meta tokens
+    (32, 128, 50, 8, 2),     # x_proj of 192 columns (6 column waves)
 ])
 def test_small_bf16_prefill_fused_dt_scan(d_state, dt_rank, L, M, B):
     """Shapes whose dt projection runs inside the scan kernel (dt_rank 64 or 128)."""
