@@ -589,6 +589,7 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
     GemmOutput out{EpiKind::Softplus, dt, s.Di, nullptr, 0, 0, 0, w->dt_bias};
     HYMBA_LAUNCH(HYMBA_STAGE_DTPROJ, gemm(op, out, GemmShape::Narrow));
   }
+  bool pos_written = false;  // the chunked scan writes state_out->pos itself
   // 6. selective scan + gate -> F[:, qw:].
   {
     ScanParams sp{};
@@ -679,6 +680,11 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
         cp.h_out = state_out ? state_out->h : nullptr;
         cp.chunk = scan_chunk_for(s.chunk, B, s.Di, L);
         cp.nchunks = scan_chunk_count(L, cp.chunk);
+        if (state_out != nullptr && state_out->pos != nullptr) {  // pos[b] = L, by the scan
+          cp.pos_out = state_out->pos;
+          cp.pos_val = L;
+          pos_written = true;
+        }
         HYMBA_LAUNCH(HYMBA_STAGE_SCAN, launch_scan_chunk(cp, stream));
       }
     } else {
@@ -728,7 +734,7 @@ hymba_status prefill_impl(const hymba_layer_desc* desc, const hymba_layer_weight
       HYMBA_LAUNCH(HYMBA_STAGE_META, gemm(op, out, GemmShape::Large));
     }
   }
-  if (state_out != nullptr && state_out->pos != nullptr && B > 0) {
+  if (state_out != nullptr && state_out->pos != nullptr && B > 0 && !pos_written) {
     HYMBA_LAUNCH(HYMBA_STAGE_MISC, launch_fill_i32(state_out->pos, L, B, stream));
   }
   return HYMBA_OK;

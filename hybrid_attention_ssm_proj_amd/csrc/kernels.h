@@ -205,6 +205,8 @@ struct ScanChunkParams {
   int64_t ssp_ld;
   int ssp_col0;
   const float* beta;
+  int32_t* pos_out;  // when set: pos_out[b] = pos_val, written by the main pass
+  int pos_val;
 };
 bool scan_chunk_supported(int N, int R, int Di);
 int scan_channel_blocks(int N, int Di);

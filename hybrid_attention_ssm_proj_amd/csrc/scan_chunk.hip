@@ -478,6 +478,10 @@ __global__ __launch_bounds__(64 * W) void scan_chunk_kernel(ScanChunkParams p) {
 
   if (hdst != nullptr) lane_store<NS>(hdst + (int64_t)c * N + n0, h);
   if (kSum && wave == 0) sdst[c] = dtsum;
+  // the sequence's token count (the decode position), once per sequence: by the first
+  // channel block's workgroup of the last chunk
+  if (!kSum && p.pos_out != nullptr && blockIdx.x == 0 && k == p.nchunks - 1 && tid == 0)
+    p.pos_out[b] = p.pos_val;
 }
 
 // Carries of the chunk summaries, in place: on entry hsum[b][k] is chunk k's end state
