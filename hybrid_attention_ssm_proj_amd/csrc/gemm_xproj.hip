@@ -12,8 +12,9 @@
 //    MFMA blocks), so the prefill rows (B L + meta rows) take one workgroup per CU with
 //    no straggler round;
 //  * NP producer waves move the rows' Xs k-tiles (96 rows x 64 k, 12 KB) into a ring of
-//    NSTG LDS stages by DMA, NSTG - 2 tiles ahead; with PAIR two adjacent k-tiles are
-//    issued together, so each row's 256 contiguous bytes are requested back to back;
+//    NSTG LDS stages by DMA, up to NSTG - 1 tiles ahead of the one being multiplied; with
+//    PAIR two adjacent k-tiles are issued together, so each row's 256 contiguous bytes
+//    are requested back to back;
 //  * compute wave w owns columns [32w, 32w + 32): its W_x rows move into its own small
 //    LDS ring by DMA, LB tiles ahead (L2 hits), and it runs the 32 x 32 x 16 MFMAs of
 //    the row blocks against the Xs stage.
@@ -21,9 +22,9 @@
 // short W_x queues live in different waves: each wave waits only for its own transfers.
 // One workgroup barrier per k-tile hands an Xs stage from the producers (their DMA
 // landed) to the compute waves, and the stage read in the previous k-tile back.
-// Measured on the prefill shape (16512 x 160 x 4096): 56 us against 64 us for the tiled
-// GEMM (its 128 x 64 tiles read Xs three times); 82 us with 64-row workgroups (258 of
-// them at one per CU: two ran in a second round).
+// Measured on the prefill shape (16512 x 160 x 4096, kernel traces): 51 us against 61 us
+// for the tiled GEMM (its 128 x 64 tiles read Xs three times); 82 us with 64-row
+// workgroups (258 of them at one per CU: two ran in a second round).
 //
 // MFMA k order: in k-step s of a k-tile, lanes 0-31 supply k = 8s .. 8s + 7 and lanes
 // 32-63 supply k = 32 + 8s .. 32 + 8s + 7 (the same for both operands), so the 64 k of
@@ -244,7 +245,7 @@ hipError_t launch_gemm_xproj_bf16(const GemmOperands& op, const GemmOutput& out,
                                   hipStream_t s) {
   if (op.M <= 0) return hipSuccess;
   if (!gemm_xproj_ok(op, out)) return hipErrorInvalidValue;
-  const int ncw = (op.N + 31) / 32;  // compute waves, plus one producer
+  const int ncw = (op.N + 31) / 32;  // compute waves (the producers come on top)
   // LDS budget 160 KB: Xs stages x 12 KB + W_x stages x 4 KB per compute wave.
   // Template arguments: largest wave count, Xs stages, W_x lookahead, producers, pairs.
   if (ncw <= 5) return run_xproj<7, 8, 2, 2, true>(op, out, ncw, s);
